@@ -1,0 +1,263 @@
+"""Seeded synthetic inputs for the FP8 MQA-logits + top-k prefill path.
+
+This module holds input generation only: random draws, the rounding of those
+draws to e4m3 codes and UE8M0 exponent bytes, and the row ranges. It contains
+none of the method's arithmetic (no decoding, no dot products, no selection),
+and it is the only code shared by the CPU oracle side and the GPU side.
+
+The workloads stand in for the pages' real serving captures (GLM-5.x indexer
+inputs from MRCR and random prompts, vLLM PR #60618, "Performance"), which are
+not available: q and k are N(0,1) rounded to e4m3, each key's UE8M0 scale is
+2^e with e uniform in [-4, 0], and the per-row head weights are N(0,1)/sqrt(32).
+
+Randomness: numpy's PCG64 generator, seed 0xF8A0 + config number, draws taken
+in the fixed order q, k, scales, weights, special-row choices.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+HEADS = 32
+DIM = 128
+SEED_BASE = 0xF8A0
+
+
+def encode_e4m3(x) -> np.ndarray:
+    """Round real values to OCP e4m3fn codes: round to nearest, ties to even,
+    magnitudes saturated at 448 (the largest finite e4m3 value)."""
+    x = np.asarray(x)
+    out = np.empty(x.shape, np.uint8)
+    flat_in = x.reshape(-1)
+    flat_out = out.reshape(-1)
+    chunk = 1 << 22
+    for lo in range(0, flat_in.shape[0], chunk):
+        v = flat_in[lo:lo + chunk].astype(np.float64)
+        sign = np.signbit(v).astype(np.uint8)
+        a = np.minimum(np.abs(v), 448.0)
+        _, e = np.frexp(a)                       # a = m * 2^e, m in [0.5, 1)
+        ex = np.where(a > 0, e - 1, -6)          # floor(log2 a)
+        ex = np.maximum(ex, -6)                  # below 2^-6: subnormal grid 2^-9
+        qv = np.rint(np.ldexp(a, 3 - ex))        # integer on the 3-bit mantissa grid
+        carry = qv >= 16
+        ex = np.where(carry, ex + 1, ex)
+        qv = np.where(carry, 8.0, qv)
+        sub = qv < 8
+        code = np.where(sub, qv, ((ex + 7) * 8) + (qv - 8)).astype(np.uint8)
+        flat_out[lo:lo + chunk] = code | (sign << 7)
+    return out
+
+
+def ue8m0_bytes(exponents) -> np.ndarray:
+    """[keys] int exponents e (scale 2^e) -> [keys, 4] uint8, four equal bytes
+    127 + e, the layout of the gathered indexer K-cache scales."""
+    e = np.asarray(exponents, np.int64)
+    b = (127 + e).astype(np.uint8)
+    return np.repeat(b[:, None], 4, axis=1)
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    rows: int
+    keys: int
+    topk: int
+    q: np.ndarray            # uint8 [rows, 32, 128] e4m3 codes
+    k: np.ndarray            # uint8 [keys, 128] e4m3 codes
+    scale_bytes: np.ndarray  # uint8 [keys, 4] UE8M0 bytes
+    weights: np.ndarray      # float32 [rows, 32]
+    starts: np.ndarray       # int32 [rows]
+    ends: np.ndarray         # int32 [rows]
+    seed: int
+    groups: dict = dataclasses.field(default_factory=dict)  # name -> int32 row ids
+
+    def visible_pairs(self) -> int:
+        s = np.clip(self.starts.astype(np.int64), 0, self.keys)
+        e = np.clip(self.ends.astype(np.int64), s, self.keys)
+        return int((e - s).sum())
+
+    def hashes(self) -> dict:
+        return {n: fnv1a(getattr(self, n)) for n in
+                ("q", "k", "scale_bytes", "weights", "starts", "ends")}
+
+
+def fnv1a(a: np.ndarray) -> str:
+    """64-bit FNV-1a of an array's bytes, folded 8 bytes at a time (fast enough
+    for 100 MB buffers); used only to log that two runs saw the same inputs."""
+    b = np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+    pad = (-b.shape[0]) % 8
+    if pad:
+        b = np.concatenate([b, np.zeros(pad, np.uint8)])
+    words = b.view(np.uint64)
+    h = np.uint64(0xCBF29CE484222325)
+    prime = np.uint64(0x100000001B3)
+    # fold in blocks so that the loop runs in numpy, not per byte
+    with np.errstate(over="ignore"):
+        blk = 1 << 16
+        for lo in range(0, words.shape[0], blk):
+            w = words[lo:lo + blk]
+            mult = np.uint64(1) + np.arange(w.shape[0], dtype=np.uint64) * np.uint64(2)
+            h = (h ^ np.bitwise_xor.reduce(w * mult)) * prime
+    return f"{int(h):016x}"
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def _scales(rng, keys):
+    return ue8m0_bytes(rng.integers(-4, 0, size=keys, endpoint=True))
+
+
+def _weights(rng, rows):
+    return (_normal(rng, (rows, HEADS)) / np.float32(math.sqrt(HEADS))).astype(np.float32)
+
+
+def _causal(rows, keys, first_end, start=0):
+    ends = (np.arange(rows, dtype=np.int64) + first_end).astype(np.int32)
+    starts = np.full(rows, start, np.int32)
+    assert int(ends[-1]) <= keys
+    return starts, ends
+
+
+def config(n: int) -> Workload:
+    """The five benchmark configurations (1 tiny ... 5 stress at 1M keys)."""
+    seed = SEED_BASE + n
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if n == 1:
+        rows, keys, topk = 64, 4096, 512
+        q = encode_e4m3(_normal(rng, (rows, HEADS, DIM)))
+        k = encode_e4m3(_normal(rng, (keys, DIM)))
+        sb = _scales(rng, keys)
+        w = _weights(rng, rows)
+        starts, ends = _causal(rows, keys, 4033)
+        return Workload("cfg1_tiny_64x4096_k512", rows, keys, topk, q, k, sb, w, starts, ends, seed)
+    if n == 2:
+        rows, keys, topk = 2048, 32768, 1024
+        q = encode_e4m3(_normal(rng, (rows, HEADS, DIM)))
+        k = encode_e4m3(_normal(rng, (keys, DIM)))
+        sb = _scales(rng, keys)
+        w = _weights(rng, rows)
+        i = np.arange(rows, dtype=np.int64)
+        req = i // 1024
+        starts = (16384 * req).astype(np.int32)
+        ends = (16384 * req + 15361 + (i % 1024)).astype(np.int32)
+        return Workload("cfg2_2req_2048x32768_k1024", rows, keys, topk, q, k, sb, w, starts, ends,
+                        seed)
+    if n == 3:
+        rows, keys, topk = 16384, 131072, 2048
+        q = encode_e4m3(_normal(rng, (rows, HEADS, DIM)))
+        k = encode_e4m3(_normal(rng, (keys, DIM)))
+        sb = _scales(rng, keys)
+        w = _weights(rng, rows)
+        starts, ends = _causal(rows, keys, 114689)
+        return Workload("cfg3_long_16384x131072_k2048", rows, keys, topk, q, k, sb, w, starts, ends,
+                        seed)
+    if n == 4:
+        rows, keys, topk = 16384, 524288, 2048
+        qf = _normal(rng, (rows, HEADS, DIM))
+        qf[4096:8192] += np.float32(3.0)          # request 1: large common score offset
+        q = encode_e4m3(qf)
+        del qf
+        k = encode_e4m3(_normal(rng, (keys, DIM)))
+        sb = _scales(rng, keys)
+        w = _weights(rng, rows)
+        i = np.arange(rows, dtype=np.int64)
+        req = i // 4096
+        starts = (131072 * req).astype(np.int32)
+        ends = (131072 * req + 126977 + (i % 4096)).astype(np.int32)
+        return Workload("cfg4_4req_16384x524288_k2048", rows, keys, topk, q, k, sb, w, starts, ends,
+                        seed, groups={"biased": np.arange(4096, 8192, dtype=np.int32)})
+    if n == 5:
+        rows, keys, topk = 16384, 1048576, 2048
+        q = encode_e4m3(_normal(rng, (rows, HEADS, DIM)))
+        # each key row is one of 16 distinct e4m3 vectors (heavy score ties)
+        distinct = encode_e4m3(_normal(rng, (16, DIM)))
+        choice = rng.integers(0, 16, size=keys)
+        k = distinct[choice]
+        sb = _scales(rng, keys)
+        w = _weights(rng, rows)
+        starts, ends = _causal(rows, keys, 1032193)
+        nsel = int(0.05 * rows)                   # 819
+        perm = rng.permutation(rows).astype(np.int32)
+        short = np.sort(perm[:nsel])
+        heavy = np.sort(perm[nsel:2 * nsel])
+        lens = rng.integers(0, 2048, size=nsel)   # n in [0, 2047]
+        starts[short] = (ends[short] - lens).astype(np.int32)
+        w[heavy] *= np.float32(1e4)
+        return Workload("cfg5_stress_16384x1048576_k2048", rows, keys, topk, q, k, sb, w, starts,
+                        ends, seed, groups={"short": short, "heavy_weights": heavy})
+    raise ValueError(f"no config {n}")
+
+
+def sweep(keys: int, topk: int, rows: int = 16384, seed: int = SEED_BASE + 100) -> Workload:
+    """Causal tail of a `keys`-key context: row i sees [0, keys - rows + 1 + i)."""
+    rng = np.random.Generator(np.random.PCG64(seed + keys + topk))
+    q = encode_e4m3(_normal(rng, (rows, HEADS, DIM)))
+    k = encode_e4m3(_normal(rng, (keys, DIM)))
+    sb = _scales(rng, keys)
+    w = _weights(rng, rows)
+    starts, ends = _causal(rows, keys, keys - rows + 1)
+    return Workload(f"sweep_{rows}x{keys}_k{topk}", rows, keys, topk, q, k, sb, w, starts, ends,
+                    seed)
+
+
+def extra_common_offset(rows: int = 16384, keys: int = 131072, topk: int = 2048) -> Workload:
+    """Config 3 shape with a true common score offset: k = e4m3(N(0,1) + 2) and
+    every scale 1.0, so every head's dot carries the key-independent term
+    2 * sum_d q[r,h,d]."""
+    seed = SEED_BASE + 11
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = encode_e4m3(_normal(rng, (rows, HEADS, DIM)))
+    k = encode_e4m3(_normal(rng, (keys, DIM)) + np.float32(2.0))
+    sb = ue8m0_bytes(np.zeros(keys, np.int64))
+    w = _weights(rng, rows)
+    starts, ends = _causal(rows, keys, keys - rows + 1)
+    return Workload(f"x1_offset_{rows}x{keys}_k{topk}", rows, keys, topk, q, k, sb, w, starts,
+                    ends, seed)
+
+
+def extra_elementwise_ties(rows: int = 16384, keys: int = 1048576, topk: int = 2048) -> Workload:
+    """Config 5 shape with k drawn per element from 16 distinct e4m3 values."""
+    seed = SEED_BASE + 12
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = encode_e4m3(_normal(rng, (rows, HEADS, DIM)))
+    vals = encode_e4m3(_normal(rng, 16))
+    k = vals[rng.integers(0, 16, size=(keys, DIM))]
+    sb = _scales(rng, keys)
+    w = _weights(rng, rows)
+    starts, ends = _causal(rows, keys, keys - rows + 1)
+    return Workload(f"x2_elemties_{rows}x{keys}_k{topk}", rows, keys, topk, q, k, sb, w, starts,
+                    ends, seed)
+
+
+def custom(rows: int, keys: int, topk: int, starts, ends, seed: int = 1,
+           q_offset: float = 0.0, weight_scale: float = 1.0, name: str = "custom") -> Workload:
+    """Small hand-shaped inputs for edge-case tests (ragged ranges, empty rows)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = encode_e4m3(_normal(rng, (rows, HEADS, DIM)) + np.float32(q_offset))
+    k = encode_e4m3(_normal(rng, (keys, DIM)))
+    sb = _scales(rng, keys)
+    w = (_weights(rng, rows) * np.float32(weight_scale)).astype(np.float32)
+    return Workload(name, rows, keys, topk, q, k, sb, w,
+                    np.asarray(starts, np.int32).copy(), np.asarray(ends, np.int32).copy(), seed)
+
+
+def sample_rows(wl: Workload, n: int = 256, seed: int = 7) -> np.ndarray:
+    """Seeded row sample for oracle checks of large workloads. With groups
+    (config 5) it is stratified: half uniform over ungrouped rows, the rest
+    split evenly over the groups."""
+    if wl.rows <= n:
+        return np.arange(wl.rows, dtype=np.int32)
+    rng = np.random.Generator(np.random.PCG64(seed + wl.seed))
+    if not wl.groups:
+        return np.sort(rng.choice(wl.rows, size=n, replace=False)).astype(np.int32)
+    grouped = np.concatenate(list(wl.groups.values()))
+    rest = np.setdiff1d(np.arange(wl.rows), grouped)
+    per = (n // 2) // len(wl.groups)
+    picks = [rng.choice(rest, size=n - per * len(wl.groups), replace=False)]
+    for g in wl.groups.values():
+        picks.append(rng.choice(g, size=per, replace=False))
+    return np.sort(np.concatenate(picks)).astype(np.int32)

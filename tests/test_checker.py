@@ -1,0 +1,85 @@
+"""The acceptance checker must accept correct results, accept any tie
+resolution, and reject planted mistakes. CPU only."""
+import numpy as np
+
+import mqa_workloads as W
+import oracle
+from oracle import check
+
+
+def _cfg1():
+    wl = W.config(1)
+    p = oracle.Problem(wl.q, wl.k, oracle.key_scales(wl.scale_bytes), wl.weights, wl.starts,
+                       wl.ends)
+    return wl, p
+
+
+def test_checker_accepts_oracle_and_rejects_planted_mistakes():
+    wl, p = _cfg1()
+    rows = [0, 31, 63]
+    idx, kth, mx = oracle.topk(p, rows, wl.topk)
+    assert check.check_topk(idx, rows, p, wl.topk) == []
+    assert check.check_valid(idx, wl.starts, wl.ends, wl.keys, wl.topk, rows=rows) == []
+    # shuffled order is fine (the output is unordered)
+    shuf = idx[:, ::-1].copy()
+    assert check.check_topk(shuf, rows, p, wl.topk) == []
+    # swap the best selected key for the worst visible key
+    s, e = p.visible(0)
+    lg = oracle.logits(p, [0], col0=s, ncols=e - s)[0]
+    worst = int(np.argmin(lg))
+    bad = idx.copy()
+    bad[0, 0] = worst
+    assert check.check_topk(bad, rows, p, wl.topk)
+    # duplicate
+    bad = idx.copy()
+    bad[1, 5] = bad[1, 6]
+    assert check.check_topk(bad, rows, p, wl.topk)
+    assert check.check_valid(bad, wl.starts, wl.ends, wl.keys, wl.topk, rows=rows)
+    # out of range
+    bad = idx.copy()
+    bad[2, 0] = e - s + 3
+    assert check.check_topk(bad, rows, p, wl.topk)
+    assert check.check_valid(bad, wl.starts, wl.ends, wl.keys, wl.topk, rows=rows)
+
+
+def test_checker_padding_rules():
+    starts = np.array([0, 0, 5], np.int32)
+    ends = np.array([3, 0, 4], np.int32)
+    good = np.array([[2, 0, 1, -1, -1], [-1] * 5, [-1] * 5], np.int32)
+    assert check.check_valid(good, starts, ends, 10, 5) == []
+    bad = good.copy()
+    bad[0] = [2, -1, 1, 0, -1]          # padding not trailing
+    assert check.check_valid(bad, starts, ends, 10, 5)
+    bad = good.copy()
+    bad[1, 0] = 0                       # empty row must be all -1
+    assert check.check_valid(bad, starts, ends, 10, 5)
+
+
+def test_checker_accepts_any_tie_resolution():
+    lg = np.array([5, 3, 3, 3, 1, 0], np.float32)
+    assert check.check_topk_row(np.array([0, 1]), lg, 2) is None
+    assert check.check_topk_row(np.array([0, 3]), lg, 2) is None
+    assert check.check_topk_row(np.array([0, 4]), lg, 2) is not None
+    assert check.check_topk_row(np.array([1, 2]), lg, 2) is not None
+
+
+def test_checker_tolerance_is_relative_to_row_max():
+    lg = np.array([1000.0, 10.0, 10.0 - 5e-3, 9.0], np.float32)
+    # tol = 1e-5 * 1000 = 1e-2: keys within 1e-2 of the k-th score may swap
+    assert check.check_topk_row(np.array([0, 2]), lg, 2) is None
+    lg2 = np.array([1000.0, 10.0, 10.0 - 5e-2, 9.0], np.float32)
+    assert check.check_topk_row(np.array([0, 2]), lg2, 2) is not None
+
+
+def test_dense_checker():
+    ref = np.array([[1.0, -np.inf, 2.0], [100.0, 50.0, -np.inf]], np.float32)
+    assert check.check_dense(ref.copy(), ref) == []
+    g = ref.copy()
+    g[1, 1] += 100.0 * 2e-5
+    assert check.check_dense(g, ref)
+    g = ref.copy()
+    g[0, 1] = 0.0
+    assert check.check_dense(g, ref)
+    g = ref.copy()
+    g[1, 1] += 100.0 * 5e-6
+    assert check.check_dense(g, ref) == []
