@@ -1,0 +1,215 @@
+"""Python binding of libmqa_topk.so: FP8 MQA logits + per-row top-k on gfx950.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+the library. PyTorch provides device memory and the current stream. The C ABI
+and its contract are declared in include/mqa_topk.h. If the library is not
+built, every entry point raises (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+HEADS = 32
+HEAD_DIM = 128
+MAX_KEYS = 1 << 20
+TOPKS = (512, 1024, 2048)
+
+FLAG_FORCE_EXACT = 1
+FLAG_FORCE_GATE_MISS = 2
+FLAG_SMALL_CAP = 4
+FLAG_STATS = 8
+
+ERR_NAMES = {0: "MQA_OK", 1: "MQA_ERR_NULL", 2: "MQA_ERR_ALIGN", 3: "MQA_ERR_SHAPE",
+             4: "MQA_ERR_WORKSPACE", 5: "MQA_ERR_DEVICE", 6: "MQA_ERR_LAUNCH"}
+
+EXPORTS = ("workspace_size", "mqa_topk_prefill", "mqa_logits_dense", "mqa_topk_dense",
+           "mqa_key_scales", "mqa_strerror")
+
+
+class MQAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {ERR_NAMES.get(code, code)} ({strerror(code)})")
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(f"{_build.LIB} is missing: build it with "
+                               "`python -m fp8_mqa_logits_amd.build` or __graft_entry__.build()")
+        lib = ctypes.CDLL(_build.LIB)
+        P, I, I64, SZ, U = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                            ctypes.c_uint)
+        lib.workspace_size.argtypes = [I, I]
+        lib.workspace_size.restype = SZ
+        lib.mqa_topk_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, P, SZ, U, P]
+        lib.mqa_topk_prefill.restype = I
+        lib.mqa_logits_dense.argtypes = [P, P, P, P, P, P, P, I64, I, I, I, I, P]
+        lib.mqa_logits_dense.restype = I
+        lib.mqa_topk_dense.argtypes = [P, I64, I, I, P, P, P, I, I, I, P]
+        lib.mqa_topk_dense.restype = I
+        lib.mqa_key_scales.argtypes = [P, P, I, P]
+        lib.mqa_key_scales.restype = I
+        lib.mqa_strerror.argtypes = [I]
+        lib.mqa_strerror.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return load().mqa_strerror(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise MQAError(code, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must live on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+FP8 = (torch.float8_e4m3fn, torch.uint8)
+
+
+def workspace_size(rows: int, device: int | None = None) -> int:
+    """Bytes of workspace one mqa_topk_prefill call over `rows` rows needs."""
+    if device is None:
+        device = torch.cuda.current_device()
+    return int(load().workspace_size(int(rows), int(device)))
+
+
+def alloc_workspace(rows: int, device=None) -> torch.Tensor:
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+    n = workspace_size(rows, dev.index)
+    if n == 0:
+        raise MQAError(5, "workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=dev)
+
+
+def mqa_topk_prefill(q, k, scales, weights, starts, ends, topk: int, out=None, workspace=None,
+                     flags: int = 0, stream=None) -> torch.Tensor:
+    """Fused scores + per-row top-k. q [rows,32,128] e4m3 (or its uint8 bytes),
+    k [keys,128] e4m3, scales [keys] fp32, weights [rows,32] fp32, starts/ends
+    [rows] int32; returns out [rows, topk] int32 (key - start, -1 padded)."""
+    dev = q.device
+    _need(q, "q", FP8, dev)
+    _need(k, "k", FP8, dev)
+    _need(scales, "scales", (torch.float32,), dev)
+    _need(weights, "weights", (torch.float32,), dev)
+    _need(starts, "starts", (torch.int32,), dev)
+    _need(ends, "ends", (torch.int32,), dev)
+    rows, keys = q.shape[0], k.shape[0]
+    if q.shape[1:] != (HEADS, HEAD_DIM) or k.shape[1:] != (HEAD_DIM,):
+        raise ValueError("q must be [rows,32,128] and k [keys,128]")
+    if out is None:
+        out = torch.empty((rows, topk), dtype=torch.int32, device=dev)
+    _need(out, "out", (torch.int32,), dev)
+    if workspace is None:
+        workspace = alloc_workspace(rows, dev.index)
+    _need(workspace, "workspace", (torch.uint8,), dev)
+    with torch.cuda.device(dev):
+        rc = load().mqa_topk_prefill(_ptr(q), _ptr(k), _ptr(scales), _ptr(weights), _ptr(starts),
+                                     _ptr(ends), _ptr(out), rows, keys, int(topk),
+                                     _ptr(workspace), workspace.numel(), int(flags),
+                                     _stream(dev, stream))
+    _check(rc, "mqa_topk_prefill")
+    return out
+
+
+def mqa_logits_dense(q, k, scales, weights, starts, ends, col0: int = 0, ncols: int | None = None,
+                     logits=None, stream=None) -> torch.Tensor:
+    """fp32 logits [rows, ncols] for keys col0 .. col0+ncols-1 (-inf where not visible)."""
+    dev = q.device
+    for t, n, d in ((q, "q", FP8), (k, "k", FP8), (scales, "scales", (torch.float32,)),
+                    (weights, "weights", (torch.float32,)), (starts, "starts", (torch.int32,)),
+                    (ends, "ends", (torch.int32,))):
+        _need(t, n, d, dev)
+    rows, keys = q.shape[0], k.shape[0]
+    if ncols is None:
+        ncols = keys - col0
+    if logits is None:
+        ld = (ncols + 3) // 4 * 4
+        logits = torch.empty((rows, ld), dtype=torch.float32, device=dev)[:, :ncols]
+    ld = logits.stride(0)
+    if logits.dtype != torch.float32 or logits.stride(1) != 1:
+        raise ValueError("logits must be fp32 with unit column stride")
+    with torch.cuda.device(dev):
+        rc = load().mqa_logits_dense(_ptr(q), _ptr(k), _ptr(scales), _ptr(weights), _ptr(starts),
+                                     _ptr(ends), _ptr(logits), ld, rows, keys, int(col0),
+                                     int(ncols), _stream(dev, stream))
+    _check(rc, "mqa_logits_dense")
+    return logits
+
+
+def mqa_topk_dense(logits, starts, ends, topk: int, keys: int, col0: int = 0, out=None,
+                   stream=None) -> torch.Tensor:
+    """Per-row top-k of a logits window [rows, ncols] (columns = keys col0 ..)."""
+    dev = logits.device
+    _need(starts, "starts", (torch.int32,), dev)
+    _need(ends, "ends", (torch.int32,), dev)
+    if logits.dtype != torch.float32 or logits.stride(1) != 1:
+        raise ValueError("logits must be fp32 with unit column stride")
+    rows, ncols = logits.shape
+    if out is None:
+        out = torch.empty((rows, topk), dtype=torch.int32, device=dev)
+    _need(out, "out", (torch.int32,), dev)
+    with torch.cuda.device(dev):
+        rc = load().mqa_topk_dense(_ptr(logits), logits.stride(0), int(col0), int(ncols),
+                                   _ptr(starts), _ptr(ends), _ptr(out), rows, int(keys),
+                                   int(topk), _stream(dev, stream))
+    _check(rc, "mqa_topk_dense")
+    return out
+
+
+def mqa_key_scales(scale_bytes, out=None, stream=None) -> torch.Tensor:
+    """UE8M0 [keys,4] uint8 -> fp32 [keys] (bit pattern e << 23), on the GPU."""
+    dev = scale_bytes.device
+    _need(scale_bytes, "scale_bytes", (torch.uint8,), dev)
+    keys = scale_bytes.shape[0]
+    if out is None:
+        out = torch.empty(keys, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        rc = load().mqa_key_scales(_ptr(scale_bytes), _ptr(out), keys, _stream(dev, stream))
+    _check(rc, "mqa_key_scales")
+    return out
+
+
+def read_stats(workspace: torch.Tensor) -> dict:
+    """The mqa_stats header of a workspace used with FLAG_STATS (synchronizes)."""
+    h = workspace[:64].cpu().numpy().view("<u4")
+    return {"rows_short": int(h[1]), "rows_gated": int(h[2]), "rows_exact": int(h[3]),
+            "rows_overflow": int(h[4]), "rows_undercount": int(h[5]),
+            "compactions": int(h[6]), "rows_uncertified": int(h[7]),
+            "candidates": int(h[8]) | (int(h[9]) << 32),
+            "band_keys": int(h[10]) | (int(h[11]) << 32)}

@@ -1,0 +1,219 @@
+// C ABI of libmqa_topk.so: argument checks, workspace layout and launches.
+// The declarations and their contracts are in include/mqa_topk.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "launch.h"
+#include "mqa_topk.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kHeaderWords = 64;
+constexpr size_t kCap = 16384;
+constexpr size_t kMaxTopk = 2048;
+
+thread_local char g_err[256] = "";
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct DeviceInfo {
+  bool probed = false;
+  bool ok = false;
+  int cus = 0;
+  int wg_per_cu = 0;
+};
+
+std::mutex g_mu;
+DeviceInfo g_dev[64];
+
+// Compute-unit count and persistent-grid occupancy of a gfx950 device.
+const DeviceInfo* device_info(int device) {
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev || device >= 64) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceInfo& d = g_dev[device];
+  if (!d.probed) {
+    d.probed = true;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) == hipSuccess &&
+        std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) {
+      int cur = 0;
+      (void)hipGetDevice(&cur);
+      (void)hipSetDevice(device);
+      int occ = 0;
+      if (mqa_fused_occupancy(&occ) == 0 && occ > 0) {
+        d.ok = true;
+        d.cus = prop.multiProcessorCount;
+        d.wg_per_cu = occ;
+      }
+      (void)hipSetDevice(cur);
+    }
+    (void)hipGetLastError();
+  }
+  return d.ok ? &d : nullptr;
+}
+
+struct Layout {
+  size_t header, order, slabE, slabI, tmpE, tmpI, total;
+  int grid, nblocks;
+};
+
+Layout layout(int rows, const DeviceInfo& d) {
+  Layout L{};
+  L.grid = d.cus * d.wg_per_cu;
+  L.nblocks = (rows + mqa::kFusedBlockRows - 1) / mqa::kFusedBlockRows;
+  size_t off = 0;
+  L.header = off;
+  off = align_up(off + kHeaderWords * 4);
+  L.order = off;
+  off = align_up(off + (size_t)L.nblocks * 4);
+  const size_t slab = (size_t)L.grid * mqa::kFusedBlockRows * kCap * 4;
+  L.slabE = off;
+  off = align_up(off + slab);
+  L.slabI = off;
+  off = align_up(off + slab);
+  const size_t tmp = (size_t)L.grid * mqa::kFusedWaves * kMaxTopk * 4;
+  L.tmpE = off;
+  off = align_up(off + tmp);
+  L.tmpI = off;
+  off = align_up(off + tmp);
+  L.total = off;
+  return L;
+}
+
+int launch_error(int hip_code) {
+  std::snprintf(g_err, sizeof(g_err), "HIP launch failed: %s",
+                hipGetErrorString(static_cast<hipError_t>(hip_code)));
+  return MQA_ERR_LAUNCH;
+}
+
+const DeviceInfo* current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return device_info(dev);
+}
+
+bool topk_ok(int topk) { return topk == 512 || topk == 1024 || topk == 2048; }
+
+}  // namespace
+
+extern "C" {
+
+size_t workspace_size(int rows, int device) {
+  if (rows < 1 || rows > MQA_MAX_ROWS) return 0;
+  const DeviceInfo* d = device_info(device);
+  if (!d) return 0;
+  return layout(rows, *d).total;
+}
+
+int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
+                     const float* weights, const int32_t* starts, const int32_t* ends,
+                     int32_t* out, int rows, int keys, int topk, void* workspace,
+                     size_t workspace_bytes, unsigned flags, void* stream) {
+  if (!q || !k || !scales || !weights || !starts || !ends || !out || !workspace)
+    return MQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scales, 16) || !aligned(weights, 16) ||
+      !aligned(out, 16) || !aligned(starts, 4) || !aligned(ends, 4) || !aligned(workspace, 256))
+    return MQA_ERR_ALIGN;
+  if (rows < 1 || rows > MQA_MAX_ROWS || keys < 1 || keys > MQA_MAX_KEYS || !topk_ok(topk))
+    return MQA_ERR_SHAPE;
+  const DeviceInfo* d = current_device();
+  if (!d) return MQA_ERR_DEVICE;
+  const Layout L = layout(rows, *d);
+  if (workspace_bytes < L.total) return MQA_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  mqa::FusedParams p;
+  p.q = q;
+  p.k = k;
+  p.scales = scales;
+  p.weights = weights;
+  p.starts = starts;
+  p.ends = ends;
+  p.out = out;
+  p.rows = rows;
+  p.keys = keys;
+  p.topk = topk;
+  p.nblocks = L.nblocks;
+  p.flags = flags;
+  p.header = reinterpret_cast<uint32_t*>(ws + L.header);
+  p.order = reinterpret_cast<int32_t*>(ws + L.order);
+  p.slabE = reinterpret_cast<float*>(ws + L.slabE);
+  p.slabI = reinterpret_cast<int32_t*>(ws + L.slabI);
+  p.tmpE = reinterpret_cast<float*>(ws + L.tmpE);
+  p.tmpI = reinterpret_cast<int32_t*>(ws + L.tmpI);
+  const int grid = L.grid < L.nblocks ? L.grid : L.nblocks;
+  const int rc = mqa_fused_launch(&p, grid, static_cast<hipStream_t>(stream));
+  if (rc != 0) return launch_error(rc);
+  return MQA_OK;
+}
+
+int mqa_logits_dense(const uint8_t* q, const uint8_t* k, const float* scales,
+                     const float* weights, const int32_t* starts, const int32_t* ends,
+                     float* logits, int64_t ld, int rows, int keys, int col0, int ncols,
+                     void* stream) {
+  if (!q || !k || !scales || !weights || !starts || !ends || !logits) return MQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scales, 16) || !aligned(weights, 16) ||
+      !aligned(logits, 16) || !aligned(starts, 4) || !aligned(ends, 4))
+    return MQA_ERR_ALIGN;
+  if (rows < 1 || rows > MQA_MAX_ROWS || keys < 1 || keys > MQA_MAX_KEYS || col0 < 0 ||
+      ncols < 1 || (int64_t)col0 + ncols > keys || ld < ncols || ld % 4 != 0)
+    return MQA_ERR_SHAPE;
+  if (!current_device()) return MQA_ERR_DEVICE;
+  mqa::DenseParams p{q, k, scales, weights, starts, ends, logits, ld, rows, keys, col0, ncols};
+  const int rc = mqa_dense_logits_launch(&p, static_cast<hipStream_t>(stream));
+  if (rc != 0) return launch_error(rc);
+  return MQA_OK;
+}
+
+int mqa_topk_dense(const float* logits, int64_t ld, int col0, int ncols, const int32_t* starts,
+                   const int32_t* ends, int32_t* out, int rows, int keys, int topk,
+                   void* stream) {
+  if (!logits || !starts || !ends || !out) return MQA_ERR_NULL;
+  if (!aligned(logits, 16) || !aligned(out, 16) || !aligned(starts, 4) || !aligned(ends, 4))
+    return MQA_ERR_ALIGN;
+  if (rows < 1 || rows > MQA_MAX_ROWS || keys < 1 || keys > MQA_MAX_KEYS || col0 < 0 ||
+      ncols < 1 || (int64_t)col0 + ncols > keys || ld < ncols || ld % 4 != 0 || !topk_ok(topk))
+    return MQA_ERR_SHAPE;
+  if (!current_device()) return MQA_ERR_DEVICE;
+  mqa::DenseTopkParams p{logits, ld, col0, ncols, starts, ends, out, rows, keys, topk};
+  const int rc = mqa_dense_topk_launch(&p, static_cast<hipStream_t>(stream));
+  if (rc != 0) return launch_error(rc);
+  return MQA_OK;
+}
+
+int mqa_key_scales(const uint8_t* scale_bytes, float* scales, int keys, void* stream) {
+  if (!scale_bytes || !scales) return MQA_ERR_NULL;
+  if (!aligned(scale_bytes, 4) || !aligned(scales, 4)) return MQA_ERR_ALIGN;
+  if (keys < 1 || keys > MQA_MAX_KEYS) return MQA_ERR_SHAPE;
+  if (!current_device()) return MQA_ERR_DEVICE;
+  const int rc = mqa_key_scales_launch(scale_bytes, scales, keys, static_cast<hipStream_t>(stream));
+  if (rc != 0) return launch_error(rc);
+  return MQA_OK;
+}
+
+const char* mqa_strerror(int code) {
+  switch (code) {
+    case MQA_OK: return "ok";
+    case MQA_ERR_NULL: return "a required pointer is NULL";
+    case MQA_ERR_ALIGN: return "a pointer is not aligned as the contract requires";
+    case MQA_ERR_SHAPE: return "a size or shape argument is outside the contract";
+    case MQA_ERR_WORKSPACE: return "the workspace is smaller than workspace_size(rows, device)";
+    case MQA_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
+    case MQA_ERR_LAUNCH: return g_err[0] ? g_err : "HIP launch failed";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,406 @@
+// Device building blocks shared by the fused and dense kernels (gfx950 only).
+//
+// Scoring tile (FP8 MFMA 16x16x128, measured operand layouts on gfx950):
+//   A operand (one 16-head half of one query row): lane l holds head
+//     16*hh + (l % 16), bytes [32*(l/16), 32*(l/16) + 32) of its 128-dim vector.
+//   B operand (16 keys): lane l holds key (l % 16), the same 32-byte K slice.
+//   C (fp32 16x16): lane l, element v holds head 4*(l/16) + v, key (l % 16).
+// One query row against 64 keys is 4 key sub-tiles x 2 head halves = 8 MFMAs.
+// Each lane then owns 8 heads of 4 keys; it applies relu and the head weights
+// (vLLM PR #60618, "What this PR does": per-head relu, weighted head sum), and
+// two permlane swap+add steps leave lane l holding the unscaled score of key l
+// of the 64-key chunk.
+//
+// Precision (measured on gfx950): the FP8 MFMA sums its products in groups of
+// 8 and truncates each product toward zero on a grid of 2^(e - 13), e being
+// the exponent of the group's largest product, so its dot products carry
+// errors of up to ~2^-12 of sum|q_d k_d|. The bf16 MFMA, fed the same e4m3
+// values converted exactly to bf16, accumulates them to fp32 accuracy. The
+// scan therefore ranks with FP8 scores, and every score that decides the
+// result near a row's k-th key is recomputed with score_chunk_exact below.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mqa {
+
+constexpr int kHeads = 32;
+constexpr int kDim = 128;
+constexpr int kWave = 64;
+constexpr int kChunk = 64;                 // keys per LDS stage
+constexpr int kChunkBytes = kChunk * kDim; // 8 KiB
+constexpr int kCap = 16384;                // candidate slab capacity per row
+constexpr int kMaxTopk = 2048;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b, v4f c) {
+  // cbsz = blgp = 0: both operands OCP e4m3; scale bytes 127 = 2^0.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 8 e4m3 bytes (two dwords) -> 8 bf16, exact (every e4m3 value is a bf16).
+__device__ __forceinline__ v8bf fp8x8_to_bf16(int lo, int hi) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
+
+// LDS placement of a 64-key chunk: key j's 16-byte slice c (0..7) lives at
+// slot (c ^ swz(j)) of its 128-byte row, so that the 16 lanes reading one
+// slice of 16 different keys touch 16 different bank groups.
+__device__ __forceinline__ int swz(int j) { return (j & 7) ^ ((j >> 3) & 1); }
+
+// Order-preserving map fp32 -> uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t fkey(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float kfloat(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Query operands of one row: qa[hh] for heads 16*hh .. 16*hh+15.
+struct QueryRow {
+  v8i qa[2];
+  float w[8];  // w[r, 16*hh + 4*(l/16) + v] at index 4*hh + v
+};
+
+__device__ __forceinline__ void load_query(QueryRow& qr, const uint8_t* __restrict__ q,
+                                           const float* __restrict__ weights, int64_t r) {
+  const int l = lane_id();
+  const int g = l >> 4;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const uint8_t* p = q + (r * kHeads + 16 * hh + (l & 15)) * kDim + 32 * g;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(p);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(p + 16);
+    qr.qa[hh] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                    (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    const float4 wv = *reinterpret_cast<const float4*>(weights + r * kHeads + 16 * hh + 4 * g);
+    qr.w[4 * hh + 0] = wv.x;
+    qr.w[4 * hh + 1] = wv.y;
+    qr.w[4 * hh + 2] = wv.z;
+    qr.w[4 * hh + 3] = wv.w;
+  }
+}
+
+// B operands of the 4 key sub-tiles of a chunk staged in LDS.
+struct KeyTile {
+  v8i kb[4];
+};
+
+__device__ __forceinline__ void load_keys_lds(KeyTile& kt, const uint8_t* lds_chunk) {
+  const int l = lane_id();
+  const int g = l >> 4;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int j = 16 * t + (l & 15);
+    const uint8_t* row = lds_chunk + j * kDim;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(row + 16 * ((2 * g) ^ swz(j)));
+    const uint4 x1 = *reinterpret_cast<const uint4*>(row + 16 * ((2 * g + 1) ^ swz(j)));
+    kt.kb[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                   (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  }
+}
+
+// Unscaled score sum_h w[r,h] * relu(q[r,h,:] . k[j,:]) of key j = lane id
+// of the chunk, for one query row.
+__device__ __forceinline__ float score_chunk(const QueryRow& qr, const KeyTile& kt) {
+  float part[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
+    const v4f a0 = mfma_fp8(qr.qa[0], kt.kb[t], z);
+    const v4f a1 = mfma_fp8(qr.qa[1], kt.kb[t], z);
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s = __builtin_fmaf(qr.w[v], __builtin_fmaxf(a0[v], 0.f), s);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s = __builtin_fmaf(qr.w[4 + v], __builtin_fmaxf(a1[v], 0.f), s);
+    part[t] = s;
+  }
+  // lanes 0-31 | 32-63 hold head groups {0,1} | {2,3}; fold them pairwise
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
+                                                    __float_as_uint(part[2]), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]),
+                                                    __float_as_uint(part[3]), false, false);
+  const float y02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float y13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  const auto s4 = __builtin_amdgcn_permlane16_swap(__float_as_uint(y02), __float_as_uint(y13),
+                                                   false, false);
+  return __uint_as_float(s4[0]) + __uint_as_float(s4[1]);
+}
+
+// The same 64-key scores as score_chunk, with the head dots taken by the
+// bf16 MFMA (16x16x32) on the exactly converted e4m3 values: fp32-accurate.
+// Each lane's 32 bytes (dims 32g .. 32g+31) feed 4 K-steps of 8 elements;
+// A and B use the same dim order, so every dot product covers all 128 dims.
+__device__ __forceinline__ float score_chunk_exact(const QueryRow& qr, const KeyTile& kt) {
+  float part[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    v4f a0 = {0.f, 0.f, 0.f, 0.f};
+    v4f a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const v8bf bk = fp8x8_to_bf16(kt.kb[t][2 * st], kt.kb[t][2 * st + 1]);
+      a0 = mfma_bf16(fp8x8_to_bf16(qr.qa[0][2 * st], qr.qa[0][2 * st + 1]), bk, a0);
+      a1 = mfma_bf16(fp8x8_to_bf16(qr.qa[1][2 * st], qr.qa[1][2 * st + 1]), bk, a1);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s = __builtin_fmaf(qr.w[v], __builtin_fmaxf(a0[v], 0.f), s);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s = __builtin_fmaf(qr.w[4 + v], __builtin_fmaxf(a1[v], 0.f), s);
+    part[t] = s;
+  }
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
+                                                    __float_as_uint(part[2]), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]),
+                                                    __float_as_uint(part[3]), false, false);
+  const float y02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float y13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  const auto s4 = __builtin_amdgcn_permlane16_swap(__float_as_uint(y02), __float_as_uint(y13),
+                                                   false, false);
+  return __uint_as_float(s4[0]) + __uint_as_float(s4[1]);
+}
+
+// B operands of up to 64 arbitrary keys read straight from global memory:
+// lane l loads key idx[16t + l%16] of sub-tile t (bytes 32*(l/16) ..).
+__device__ __forceinline__ void load_keys_gather(KeyTile& kt, const uint8_t* __restrict__ k,
+                                                 const int* keyidx) {
+  const int l = lane_id();
+  const int g = l >> 4;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t key = keyidx[t];
+    const uint8_t* p = k + key * kDim + 32 * g;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(p);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(p + 16);
+    kt.kb[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                   (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  }
+}
+
+// Cooperative stage of keys [key0, key0 + 64) into an LDS chunk by `nthreads`
+// threads (multiple of 64, <= 512): thread t moves 16-byte slices t, t +
+// nthreads, ... Keys at or past `keys` are clamped to the last key (their
+// scores are masked by the caller).
+__device__ __forceinline__ void stage_chunk_regs(uint4* regs, const uint8_t* __restrict__ k,
+                                                 int64_t key0, int keys, int tid, int nthreads,
+                                                 const int64_t* gather = nullptr) {
+  for (int i = 0, p = tid; p < kChunk * 8; ++i, p += nthreads) {
+    const int j = p >> 3;
+    const int slot = p & 7;
+    const int c = slot ^ swz(j);
+    int64_t key = gather ? gather[j] : key0 + j;
+    key = key < keys ? key : keys - 1;
+    regs[i] = *reinterpret_cast<const uint4*>(k + key * kDim + 16 * c);
+  }
+}
+__device__ __forceinline__ void store_chunk_regs(const uint4* regs, uint8_t* lds_chunk, int tid,
+                                                 int nthreads) {
+  for (int i = 0, p = tid; p < kChunk * 8; ++i, p += nthreads)
+    *reinterpret_cast<uint4*>(lds_chunk + 16 * p) = regs[i];
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = __builtin_fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int rank_in_mask(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// ---------------------------------------------------------------------------
+// One level of a wave-level radix select: hist[0..nb) holds the counts of the
+// current digit among the records matching the prefix; find the digit of the
+// `need`-th largest record. Returns the digit; `above` receives the number of
+// records in higher digits and `cnt` the count of the chosen digit.
+__device__ __forceinline__ int radix_digit(const uint32_t* hist, int nb, int need, int& above,
+                                           int& cnt) {
+  const int l = lane_id();
+  const int per = nb / kWave;
+  int mine = 0;
+  for (int b = 0; b < per; ++b) mine += (int)hist[nb - 1 - (l * per + b)];
+  const int incl = wave_incl_scan(mine);
+  const int excl = incl - mine;
+  const uint64_t hit = __ballot(incl >= need);
+  const int src = hit ? __builtin_ctzll(hit) : 63;  // hit != 0: the total is >= need
+  int digit = 0, ab = 0, ct = 0;
+  if (l == src) {
+    int c = excl;
+    for (int b = 0; b < per; ++b) {
+      const int bin = nb - 1 - (l * per + b);
+      const int h = (int)hist[bin];
+      if (c + h >= need) {
+        digit = bin;
+        ab = c;
+        ct = h;
+        break;
+      }
+      c += h;
+    }
+  }
+  above = __shfl(ab, src, 64);
+  cnt = __shfl(ct, src, 64);
+  return __shfl(digit, src, 64);
+}
+
+// Histogram of one radix level over E[0..n) restricted to a prefix.
+__device__ __forceinline__ void radix_hist(const float* __restrict__ E, int n, uint32_t prefix,
+                                           uint32_t pmask, int sh, uint32_t dmask, int nb,
+                                           uint32_t* hist) {
+  const int l = lane_id();
+  for (int b = l; b < nb; b += kWave) hist[b] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  for (int i = l; i < n; i += kWave) {
+    const uint32_t key = fkey(E[i]);
+    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dmask], 1u);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The rank-th largest of E[0..n) (1 <= rank <= n), exactly, by a three-level
+// radix select (11, 11 and 10 bits of the order-preserving key).
+__device__ float wave_kth_value(const float* __restrict__ E, int n, int rank, uint32_t* hist) {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  uint32_t prefix = 0, pmask = 0;
+  int need = rank;
+  const int shifts[3] = {21, 10, 0};
+  const int widths[3] = {11, 11, 10};
+  for (int lev = 0; lev < 3; ++lev) {
+    const int sh = shifts[lev];
+    const uint32_t dmask = (1u << widths[lev]) - 1u;
+    const int nb = 1 << widths[lev];
+    radix_hist(E, n, prefix, pmask, sh, dmask, nb, hist);
+    int above, cnt;
+    const int digit = radix_digit(hist, nb, need, above, cnt);
+    need -= above;
+    prefix |= (uint32_t)digit << sh;
+    pmask |= dmask << sh;
+    __builtin_amdgcn_wave_barrier();
+  }
+  return kfloat(prefix);
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level exact top-k select over n (score, key) records held in global
+// memory (E[i], I[i]). Radix select on the order-preserving uint32 of the
+// score with digits of 11, 11 and 10 bits, counted in an LDS histogram of
+// 2048 words private to the wave; then one output pass. Records strictly
+// above the selected prefix are all taken; records equal to it fill the
+// remaining slots in slab order (any subset of ties at the k-th score is a
+// correct answer). `emit(slot, score, key)` is called once per selected
+// record with distinct slots in [0, min(n, k)). Returns the smallest selected
+// score (or +inf when nothing is selected).
+template <class Emit>
+__device__ float wave_select(const float* __restrict__ E, const int* __restrict__ I, int n,
+                             int k, uint32_t* hist, Emit emit) {
+  const int l = lane_id();
+  // the records were stored by this wave: make them visible to all its lanes
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  if (n <= k) {
+    float mn = __builtin_inff();
+    for (int i = l; i < n; i += kWave) {
+      const float e = E[i];
+      emit(i, e, I[i]);
+      mn = __builtin_fminf(mn, e);
+    }
+    return wave_min(mn);
+  }
+  uint32_t prefix = 0, pmask = 0;
+  int need = k;
+  bool done = false;
+  const int shifts[3] = {21, 10, 0};
+  const int widths[3] = {11, 11, 10};
+  for (int lev = 0; lev < 3 && !done; ++lev) {
+    const int sh = shifts[lev];
+    const uint32_t dmask = (1u << widths[lev]) - 1u;
+    const int nb = 1 << widths[lev];
+    radix_hist(E, n, prefix, pmask, sh, dmask, nb, hist);
+    int above, cnt;
+    const int digit = radix_digit(hist, nb, need, above, cnt);
+    need -= above;
+    prefix |= (uint32_t)digit << sh;
+    pmask |= dmask << sh;
+    if (cnt == need) done = true;
+    __builtin_amdgcn_wave_barrier();
+  }
+  // output: strictly-above records fill slots [0, k - need), ties the rest
+  const int n_above = k - need;
+  int taken_above = 0, taken_tie = 0;
+  float mn = __builtin_inff();
+  for (int i0 = 0; i0 < n; i0 += kWave) {
+    const int i = i0 + l;
+    uint32_t key = 0;
+    float e = 0.f;
+    if (i < n) {
+      e = E[i];
+      key = fkey(e);
+    }
+    const bool in = i < n;
+    const bool up = in && (key & pmask) > prefix;
+    const bool tie = in && (key & pmask) == prefix;
+    const uint64_t mu = __ballot(up);
+    const uint64_t mt = __ballot(tie);
+    if (up) {
+      const int slot = taken_above + rank_in_mask(mu);
+      if (slot < n_above) {
+        emit(slot, e, I[i]);
+        mn = __builtin_fminf(mn, e);
+      }
+    }
+    if (tie) {
+      const int rk = taken_tie + rank_in_mask(mt);
+      if (rk < need) {
+        emit(n_above + rk, e, I[i]);
+        mn = __builtin_fminf(mn, e);
+      }
+    }
+    taken_above += __popcll(mu);
+    taken_tie += __popcll(mt);
+  }
+  return wave_min(mn);
+}
+
+}  // namespace mqa

@@ -1,0 +1,61 @@
+// Kernel parameter blocks and launch entry points shared by the kernel
+// translation units and the C ABI (api.hip). Host-visible plain structs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mqa {
+
+struct FusedParams {
+  const uint8_t* q;
+  const uint8_t* k;
+  const float* scales;
+  const float* weights;
+  const int32_t* starts;
+  const int32_t* ends;
+  int32_t* out;
+  int rows, keys, topk, nblocks;
+  unsigned flags;
+  uint32_t* header;  // 64 words: stats + claim counter
+  int32_t* order;    // [nblocks] heaviest-first block order
+  float* slabE;      // [grid][32 rows][16384] candidate scores
+  int32_t* slabI;    // [grid][32 rows][16384] candidate keys
+  float* tmpE;       // [grid][8 waves][2048] compaction buffers
+  int32_t* tmpI;
+};
+
+struct DenseParams {
+  const uint8_t* q;
+  const uint8_t* k;
+  const float* scales;
+  const float* weights;
+  const int32_t* starts;
+  const int32_t* ends;
+  float* logits;
+  int64_t ld;
+  int rows, keys, col0, ncols;
+};
+
+struct DenseTopkParams {
+  const float* logits;
+  int64_t ld;
+  int col0, ncols;
+  const int32_t* starts;
+  const int32_t* ends;
+  int32_t* out;
+  int rows, keys, topk;
+};
+
+constexpr int kFusedBlockRows = 32;
+constexpr int kFusedWaves = 8;
+
+}  // namespace mqa
+
+extern "C" {
+int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t stream);
+int mqa_fused_occupancy(int* wg_per_cu);
+int mqa_dense_logits_launch(const mqa::DenseParams* p, hipStream_t stream);
+int mqa_dense_topk_launch(const mqa::DenseTopkParams* p, hipStream_t stream);
+int mqa_key_scales_launch(const uint8_t* b, float* s, int keys, hipStream_t stream);
+}

@@ -1,0 +1,161 @@
+/*
+ * mqa_topk.h -- C ABI of the MI355X (gfx950) FP8 MQA-logits + top-k prefill
+ * library (libmqa_topk.so).
+ *
+ * The operation (vLLM API page "fused_mqa_topk", fused_mqa_topk_prefill; vLLM
+ * PR #60618, "What this PR does"): for every query row r and every visible key
+ * j in [start_r, end_r),
+ *
+ *     logit[r,j] = scale_j * sum_{h<32} w[r,h] * relu(q[r,h,:] . k[j,:])
+ *
+ * with q [rows,32,128] and k [keys,128] in OCP FP8 e4m3 (e4m3fn), scale_j the
+ * fp32 decoded from a UE8M0 byte e as the bit pattern e << 23 (same page,
+ * fused_mqa_topk_key_scales) and w [rows,32] fp32; then return each row's k
+ * largest keys (k = 512, 1024 or 2048) as key - start_r, unordered, -1 padded
+ * when fewer than k keys are visible.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no device memory and keeps no state between calls.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; 0 is the null
+ *     stream). A return of MQA_OK means the work was queued.
+ *   - On any error code nothing has been launched.
+ *   - Nothing traps or aborts, on the host or on the device.
+ *   - starts/ends are read on the device. A row's range is clamped there to
+ *     s = clamp(start, 0, keys), e = clamp(end, s, keys); an empty range gives
+ *     an all -1 output row.
+ *   - Output rows hold min(n, k) distinct valid entries in slots [0, min(n,k))
+ *     and -1 in the remaining slots (n = e - s). Order is otherwise unspecified;
+ *     among keys tied at the k-th score any subset may be returned.
+ */
+#ifndef MQA_TOPK_H
+#define MQA_TOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MQA_OK 0
+#define MQA_ERR_NULL 1      /* a required pointer is NULL */
+#define MQA_ERR_ALIGN 2     /* q, k, scales, weights, out/logits not 16-B aligned;
+                               starts/ends not 4-B aligned; workspace not 256-B aligned */
+#define MQA_ERR_SHAPE 3     /* rows < 1, keys < 1 or > MQA_MAX_KEYS, topk not in
+                               {512,1024,2048}, or a bad column window / leading dim */
+#define MQA_ERR_WORKSPACE 4 /* workspace_bytes < workspace_size(rows, device) */
+#define MQA_ERR_DEVICE 5    /* no current HIP device, or it is not gfx950 */
+#define MQA_ERR_LAUNCH 6    /* a HIP launch failed; mqa_strerror names the HIP error */
+
+#define MQA_HEADS 32
+#define MQA_HEAD_DIM 128
+#define MQA_MAX_KEYS (1 << 20) /* 1M keys per call (PR #60618, "Limitations") */
+#define MQA_MAX_ROWS (1 << 20)
+
+/* Test-only flags for mqa_topk_prefill (0 in normal use). The output never
+ * depends on them: they force the exact fallback (PR #60618, "What this PR
+ * does": exact rescan) so that tests can reach it. */
+#define MQA_FLAG_FORCE_EXACT 1u     /* every row takes the exact streaming rescan */
+#define MQA_FLAG_FORCE_GATE_MISS 2u /* the gate admits nothing: every gated row falls back */
+#define MQA_FLAG_SMALL_CAP 4u       /* per-row candidate slab limited to topk + 64 */
+#define MQA_FLAG_STATS 8u           /* fill the mqa_stats header of the workspace */
+
+/* Counters written to the first bytes of the workspace when MQA_FLAG_STATS is
+ * set (read them after the stream has finished the call). */
+typedef struct mqa_stats {
+  uint32_t claim_counter;   /* internal: blocks claimed (== number of blocks) */
+  uint32_t rows_short;      /* rows with n <= k (no scoring) */
+  uint32_t rows_gated;      /* rows served by the gate + certified select */
+  uint32_t rows_exact;      /* rows served by the exact streaming rescan */
+  uint32_t rows_overflow;   /* gated rows whose candidates overflowed the slab */
+  uint32_t rows_undercount; /* gated rows with fewer than k candidates */
+  uint32_t compactions;     /* streaming-rescan compactions */
+  uint32_t rows_uncertified;/* gated rows whose exact band could not certify the cut */
+  uint64_t candidates;      /* candidates emitted by gated rows */
+  uint64_t band_keys;       /* keys rescored exactly around the rows' k-th scores */
+} mqa_stats;
+
+/*
+ * Bytes of device workspace one mqa_topk_prefill call over `rows` query rows
+ * needs on HIP device `device` (the pages' get_fused_mqa_topk_workspaces, API
+ * page "fused_mqa_topk"). It holds the block queue, one candidate slab of
+ * 16384 (score, key) records per row of every block a persistent workgroup can
+ * hold at once, and per-wave compaction buffers; it grows with the device's
+ * compute-unit count, and with rows only through a 4-byte-per-block queue.
+ * Returns 0 if the device does not exist or is not gfx950, or rows is out of
+ * range.
+ */
+size_t workspace_size(int rows, int device);
+
+/*
+ * The fused path (API page "fused_mqa_topk", fused_mqa_topk_prefill; PR
+ * #60618, "What this PR does"): scores every visible key of every row and
+ * writes each row's top-k without writing the [rows, keys] logits.
+ *   q        [rows,32,128] e4m3 bytes, row-major, 16-B aligned
+ *   k        [keys,128]    e4m3 bytes, row-major, 16-B aligned
+ *   scales   [keys] fp32 (decoded UE8M0, >= 0), 16-B aligned
+ *   weights  [rows,32] fp32, 16-B aligned
+ *   starts, ends [rows] int32, 4-B aligned
+ *   out      [rows,topk] int32, 16-B aligned (written entirely)
+ *   rows in [1, MQA_MAX_ROWS], keys in [1, MQA_MAX_KEYS], topk in {512,1024,2048}
+ *   workspace: >= workspace_size(rows, current device) bytes, 256-B aligned;
+ *     scratch owned by this call until the stream reaches its end (calls that
+ *     share one workspace must be ordered on one stream). No prior contents
+ *     are needed: the call resets what it uses.
+ *   flags: 0, or MQA_FLAG_* bits (test-only).
+ * Returns MQA_OK or an MQA_ERR_* code (checked in the order NULL, ALIGN,
+ * SHAPE, DEVICE, WORKSPACE).
+ */
+int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
+                     const float* weights, const int32_t* starts, const int32_t* ends,
+                     int32_t* out, int rows, int keys, int topk, void* workspace,
+                     size_t workspace_bytes, unsigned flags, void* stream);
+
+/*
+ * Dense logits (the first half of the dense path the fused op replaces: PR
+ * #60618, "Motivation"; API page, fused_mqa_topk_prefill names the
+ * fp8_mqa_logits + top_k_per_row_prefill pair): writes
+ *   logits[r * ld + c] = logit[r, col0 + c]   for c in [0, ncols)
+ * as fp32, and -inf where col0 + c lies outside row r's visible range.
+ *   logits: [rows, ld] fp32, 16-B aligned, ld >= ncols, ld % 4 == 0
+ *   col0 >= 0, ncols >= 1, col0 + ncols <= keys
+ * Other arguments as for mqa_topk_prefill.
+ */
+int mqa_logits_dense(const uint8_t* q, const uint8_t* k, const float* scales,
+                     const float* weights, const int32_t* starts, const int32_t* ends,
+                     float* logits, int64_t ld, int rows, int keys, int col0, int ncols,
+                     void* stream);
+
+/*
+ * Dense per-row top-k (the second half of the dense path): for each row r,
+ * the topk largest logits among columns c whose key col0 + c lies in the
+ * row's visible range [s, e) and inside the window [col0, col0 + ncols);
+ * writes key - s, unordered, -1 padded (slots [n', topk) when the row has
+ * n' <= topk such columns, in which case slots [0, n') hold 0..n'-1 shifted
+ * by max(0, col0 - s)).
+ *   logits [rows, ld] fp32 as written by mqa_logits_dense; out [rows, topk].
+ */
+int mqa_topk_dense(const float* logits, int64_t ld, int col0, int ncols,
+                   const int32_t* starts, const int32_t* ends, int32_t* out, int rows,
+                   int keys, int topk, void* stream);
+
+/*
+ * UE8M0 key-scale decode (API page, fused_mqa_topk_key_scales): the gathered
+ * indexer K-cache scales [keys,4] uint8 (four equal bytes per key) viewed as a
+ * little-endian int32, low byte e -> fp32 with bit pattern e << 23 (e = 0 gives
+ * +0.0, e = 255 gives +inf, which is outside the contract of the other calls).
+ *   scale_bytes: [keys,4] uint8, 4-B aligned; scales: [keys] fp32, 4-B aligned.
+ */
+int mqa_key_scales(const uint8_t* scale_bytes, float* scales, int keys, void* stream);
+
+/* Human-readable text of a return code (for MQA_ERR_LAUNCH it names the HIP
+ * error of the failing call on this thread). Never NULL. */
+const char* mqa_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQA_TOPK_H */

@@ -87,18 +87,22 @@ def check_topk_row(sel_idx: np.ndarray, row_logits: np.ndarray, topk: int,
 def check_topk(out_rows: np.ndarray, rows, oracle_problem, topk: int,
                rel_tol: float = REL_TOL, batch: int = 16, threads: int = 0):
     """Rule (ii) on the given rows. out_rows: [len(rows), topk] result rows.
-    The oracle's logits are computed batch by batch (bounded memory)."""
+    The oracle's logits are computed a batch of rows at a time over the
+    batch's union key range (bounded memory, all cores)."""
     import oracle  # test infrastructure: this module lives beside it
 
     rows = np.asarray(rows, np.int32)
     fails = []
     for lo in range(0, rows.shape[0], batch):
         rb = rows[lo:lo + batch]
+        rng = [oracle_problem.visible(int(r)) for r in rb]
+        c0 = min(s for s, _ in rng)
+        c1 = max(e for _, e in rng)
+        lg = oracle.logits(oracle_problem, rb, col0=c0, ncols=max(c1 - c0, 1), threads=threads)
         for i, r in enumerate(rb):
-            s, e = oracle_problem.visible(int(r))
-            lg = oracle.logits(oracle_problem, [int(r)], col0=s, ncols=e - s,
-                               threads=threads)[0]
-            msg = check_topk_row(np.asarray(out_rows[lo + i]), lg, topk, rel_tol)
+            s, e = rng[i]
+            msg = check_topk_row(np.asarray(out_rows[lo + i]), lg[i, s - c0:e - c0], topk,
+                                 rel_tol)
             if msg:
                 fails.append((int(r), msg))
     return fails

@@ -68,16 +68,13 @@ double e4m3_value(uint8_t code) {
   return sign ? -mag : mag;
 }
 
-struct Table {
-  double v[256];
-  Table() {
-    for (int c = 0; c < 256; ++c) v[c] = e4m3_value(static_cast<uint8_t>(c));
+// Decoded value of every code, filled once when the library loads.
+alignas(64) double g_e4m3[256];
+struct TableInit {
+  TableInit() {
+    for (int c = 0; c < 256; ++c) g_e4m3[c] = e4m3_value(static_cast<uint8_t>(c));
   }
-};
-const Table& table() {
-  static const Table t;
-  return t;
-}
+} g_table_init;
 
 // fused_mqa_topk_key_scales: view the four bytes as a little-endian int32,
 // keep the low byte e, and shift it into the fp32 exponent field.
@@ -113,24 +110,24 @@ void row_range(const Problem& p, int64_t r, int64_t* s, int64_t* e) {
 
 // Decoded query of one row, stored dimension-major: qd[d*32 + h].
 void decode_query(const Problem& p, int64_t r, double* qd) {
-  const Table& t = table();
   const uint8_t* qr = p.q + r * kHeads * kDim;
   for (int h = 0; h < kHeads; ++h)
-    for (int d = 0; d < kDim; ++d) qd[d * kHeads + h] = t.v[qr[h * kDim + d]];
+    for (int d = 0; d < kDim; ++d) qd[d * kHeads + h] = g_e4m3[qr[h * kDim + d]];
 }
 
 // The 32 per-head dot products s[h] = sum_d q[h,d] * k[j,d] of one key.
 // Each s[h] is accumulated over d = 0..127 in order; the loop runs over the
 // heads innermost only so that the 32 independent sums advance together.
-__attribute__((target_clones("avx2", "default")))
-void head_dots(const double* qd, const uint8_t* kj, double* s) {
-  const Table& t = table();
+__attribute__((target_clones("avx512f", "avx2", "default")))
+void head_dots(const double* __restrict__ qd, const uint8_t* __restrict__ kj,
+               double* __restrict__ s) {
+  double kd[kDim];
+  for (int d = 0; d < kDim; ++d) kd[d] = g_e4m3[kj[d]];
   double acc[kHeads];
   for (int h = 0; h < kHeads; ++h) acc[h] = 0.0;
   for (int d = 0; d < kDim; ++d) {
-    const double kv = t.v[kj[d]];
     const double* qrow = qd + d * kHeads;
-    for (int h = 0; h < kHeads; ++h) acc[h] += qrow[h] * kv;
+    for (int h = 0; h < kHeads; ++h) acc[h] += qrow[h] * kd[d];
   }
   for (int h = 0; h < kHeads; ++h) s[h] = acc[h];
 }
@@ -198,7 +195,7 @@ extern "C" {
 
 // Returns the decoded value of every e4m3 code (NaN for 0x7F and 0xFF).
 void oracle_e4m3_table(double* out256) {
-  for (int c = 0; c < 256; ++c) out256[c] = table().v[c];
+  for (int c = 0; c < 256; ++c) out256[c] = g_e4m3[c];
 }
 
 // UE8M0 [keys,4] bytes -> fp32 [keys].
@@ -209,9 +206,8 @@ void oracle_key_scales(const uint8_t* bytes, int64_t keys, float* out) {
 // Exact per-head dot products of query row r against key j (for the pins).
 int oracle_head_dots(const uint8_t* q_row, const uint8_t* k_row, double* out32) {
   double qd[kDim * kHeads];
-  const Table& t = table();
   for (int h = 0; h < kHeads; ++h)
-    for (int d = 0; d < kDim; ++d) qd[d * kHeads + h] = t.v[q_row[h * kDim + d]];
+    for (int d = 0; d < kDim; ++d) qd[d * kHeads + h] = g_e4m3[q_row[h * kDim + d]];
   head_dots(qd, k_row, out32);
   return 0;
 }

@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry
+point include/mqa_topk.h declares, and rejects bad arguments before touching
+any device memory. No GPU needed (and nothing here launches work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_mqa_logits_amd as mqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mqa_topk.h")
+
+# fake, never-dereferenced device addresses (all checks fail before any use)
+A16 = 0x10000
+MIS = 0x10004
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[a-z_][a-z0-9_ ]*[ *]+(\w+)\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert set(names) == {"workspace_size", "mqa_topk_prefill", "mqa_logits_dense",
+                          "mqa_topk_dense", "mqa_key_scales", "mqa_strerror"}
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mqa.load()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(mqa.EXPORTS) == set(declared_functions())
+
+
+def _prefill(**kw):
+    a = dict(q=A16, k=A16, scales=A16, weights=A16, starts=A16, ends=A16, out=A16, rows=64,
+             keys=4096, topk=512, ws=0x20000, wsb=1 << 40, flags=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return mqa.load().mqa_topk_prefill(P(a["q"]), P(a["k"]), P(a["scales"]), P(a["weights"]),
+                                       P(a["starts"]), P(a["ends"]), P(a["out"]), a["rows"],
+                                       a["keys"], a["topk"], P(a["ws"]), a["wsb"], a["flags"],
+                                       None)
+
+
+def test_prefill_null_align_shape_errors():
+    assert _prefill(q=0) == 1
+    assert _prefill(ws=0) == 1
+    assert _prefill(k=MIS) == 2
+    assert _prefill(out=MIS) == 2
+    assert _prefill(starts=0x10002) == 2
+    assert _prefill(ws=0x20080) == 2
+    assert _prefill(rows=0) == 3
+    assert _prefill(keys=0) == 3
+    assert _prefill(keys=(1 << 20) + 1) == 3
+    assert _prefill(topk=256) == 3
+    assert _prefill(topk=4096) == 3
+
+
+def test_dense_errors():
+    P = ctypes.c_void_p
+    L = mqa.load()
+
+    def dense(**kw):
+        a = dict(q=A16, logits=A16, ld=4096, rows=8, keys=4096, col0=0, ncols=4096)
+        a.update(kw)
+        return L.mqa_logits_dense(P(a["q"]), P(A16), P(A16), P(A16), P(A16), P(A16),
+                                  P(a["logits"]), a["ld"], a["rows"], a["keys"], a["col0"],
+                                  a["ncols"], None)
+
+    assert dense(q=0) == 1
+    assert dense(logits=MIS) == 2
+    assert dense(ld=4095) == 3
+    assert dense(ld=4098) == 3
+    assert dense(col0=1) == 3        # window past the last key
+    assert dense(ncols=0) == 3
+    assert dense(col0=-1) == 3
+
+    def topk(**kw):
+        a = dict(logits=A16, ld=4096, col0=0, ncols=4096, out=A16, rows=8, keys=4096, topk=512)
+        a.update(kw)
+        return L.mqa_topk_dense(P(a["logits"]), a["ld"], a["col0"], a["ncols"], P(A16), P(A16),
+                                P(a["out"]), a["rows"], a["keys"], a["topk"], None)
+
+    assert topk(out=0) == 1
+    assert topk(out=MIS) == 2
+    assert topk(topk=100) == 3
+    assert topk(ncols=5000) == 3
+    assert L.mqa_key_scales(None, P(A16), 10, None) == 1
+    assert L.mqa_key_scales(P(0x10001), P(A16), 10, None) == 2
+    assert L.mqa_key_scales(P(A16), P(A16), 0, None) == 3
+
+
+def test_strerror_covers_every_code():
+    for c in range(0, 7):
+        assert mqa.strerror(c)
+    assert "unknown" in mqa.strerror(99)
+
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="only meaningful on a host without a GPU")
+def test_device_error_without_gpu():
+    # valid arguments on a host with no HIP device: MQA_ERR_DEVICE, nothing launched
+    assert _prefill() == 5
+    assert mqa.load().workspace_size(64, 0) == 0

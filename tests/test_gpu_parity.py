@@ -1,0 +1,177 @@
+"""GPU parity: every HIP entry point against the CPU oracle (rules in
+oracle/check.py: validity on all rows, the tie-tolerant set rule with
+tol = 1e-5 * max|logit| of the row, dense logits within the same tolerance).
+Small configurations are checked on all rows, the large ones on 256 seeded
+sample rows (plus validity on every row)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_mqa_logits_amd as mqa
+import mqa_workloads as W
+import oracle
+from oracle import check
+
+from gpu_helpers import fused, oracle_problem, say, to_device
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TOL = 1e-5  # relative to the row's max |logit|
+
+
+def test_key_scales_decode_exhaustive():
+    say("case: key scales e=0..254")
+    e = np.arange(0, 255, dtype=np.int64)
+    b = np.repeat(e.astype(np.uint8)[:, None], 4, axis=1)
+    got = mqa.mqa_key_scales(torch.from_numpy(b).cuda()).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), oracle.key_scales(b).view(np.uint32))
+
+
+def _hand(start=0):
+    g = json.load(open(os.path.join(GOLDEN, "hand_4key.json")))
+    enc = lambda x: int(W.encode_e4m3(np.array([x], np.float32))[0])
+    keys = np.zeros((4, 128), np.uint8)
+    for j, (a, b) in enumerate(g["keys"]):
+        keys[j, 0], keys[j, 1] = enc(a), enc(b)
+    q = np.zeros((1, 32, 128), np.uint8)
+    for h, vec in g["query_heads"].items():
+        q[0, int(h), 0], q[0, int(h), 1] = enc(vec[0]), enc(vec[1])
+    w = np.full((1, 32), g["weights"]["other"], np.float32)
+    w[0, 0], w[0, 1] = g["weights"]["0"], g["weights"]["1"]
+    sb = np.repeat(np.array(g["scale_exponent_bytes"], np.uint8)[:, None], 4, axis=1)
+    wl = W.Workload("hand", 1, 4, 512, q, keys, sb, w, np.array([start], np.int32),
+                    np.array([4], np.int32), 0)
+    return g, wl
+
+
+def test_dense_logits_hand_example_exact():
+    g, wl = _hand()
+    say("case: dense logits, hand-worked 4-key example")
+    d = to_device(wl)
+    lg = mqa.mqa_logits_dense(d["q"], d["k"], d["scales"], d["weights"], d["starts"], d["ends"])
+    torch.cuda.synchronize()
+    assert lg.cpu().numpy()[0].tolist() == g["logits"]
+    out = fused(d, 512)
+    assert out.cpu().numpy()[0, :4].tolist() == [0, 1, 2, 3] and (out.cpu() == -1).sum() == 508
+    g, wl = _hand(start=1)
+    d = to_device(wl)
+    out = fused(d, 512)
+    o = out.cpu().numpy()[0]
+    assert o[:3].tolist() == [0, 1, 2] and (o[3:] == -1).all()
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_dense_logits_all_rows(cfg):
+    wl = W.config(cfg)
+    say(f"case: dense logits config {cfg} ({wl.name}) all rows")
+    d = to_device(wl)
+    lg = mqa.mqa_logits_dense(d["q"], d["k"], d["scales"], d["weights"], d["starts"], d["ends"])
+    torch.cuda.synchronize()
+    p = oracle_problem(wl)
+    for lo in range(0, wl.rows, 256):
+        rows = np.arange(lo, min(lo + 256, wl.rows))
+        ref = oracle.logits(p, rows, col0=0, ncols=wl.keys)
+        fails = check.check_dense(lg[lo:lo + len(rows)].cpu().numpy(), ref, TOL)
+        assert not fails, fails[:5]
+
+
+def test_dense_logits_window_and_ragged_rows():
+    wl = W.custom(77, 5000, 512, starts=np.arange(77) * 13, ends=4000 + np.arange(77) * 11,
+                  seed=5)
+    say("case: dense logits window col0=150 ncols=4500 ld=4608, 77 rows")
+    d = to_device(wl)
+    buf = torch.full((77, 4608), 7.0, device="cuda")
+    lg = mqa.mqa_logits_dense(d["q"], d["k"], d["scales"], d["weights"], d["starts"], d["ends"],
+                              col0=150, ncols=4500, logits=buf[:, :4500])
+    torch.cuda.synchronize()
+    ref = oracle.logits(oracle_problem(wl), np.arange(77), col0=150, ncols=4500)
+    assert not check.check_dense(buf[:, :4500].cpu().numpy(), ref, TOL)
+    assert (buf[:, 4500:] == 7.0).all()  # nothing written past the window
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_dense_topk_all_rows(cfg):
+    wl = W.config(cfg)
+    say(f"case: dense logits + top-k config {cfg} all rows")
+    d = to_device(wl)
+    lg = mqa.mqa_logits_dense(d["q"], d["k"], d["scales"], d["weights"], d["starts"], d["ends"])
+    out = mqa.mqa_topk_dense(lg, d["starts"], d["ends"], wl.topk, wl.keys)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, wl.topk)
+    fails = check.check_topk(o, np.arange(wl.rows), oracle_problem(wl), wl.topk, TOL)
+    assert not fails, fails[:5]
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_fused_all_rows(cfg):
+    wl = W.config(cfg)
+    say(f"case: fused config {cfg} ({wl.name}) all rows")
+    d = to_device(wl)
+    ws = mqa.alloc_workspace(wl.rows)
+    out = fused(d, wl.topk, flags=mqa.FLAG_STATS, workspace=ws)
+    st = mqa.read_stats(ws)
+    say("stats", st)
+    o = out.cpu().numpy()
+    assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, wl.topk)
+    fails = check.check_topk(o, np.arange(wl.rows), oracle_problem(wl), wl.topk, TOL)
+    assert not fails, fails[:5]
+    assert st["rows_gated"] + st["rows_exact"] + st["rows_short"] == wl.rows
+
+
+@pytest.mark.parametrize("flag", [mqa.FLAG_FORCE_EXACT, mqa.FLAG_FORCE_GATE_MISS,
+                                  mqa.FLAG_SMALL_CAP])
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_fused_forced_fallback(cfg, flag):
+    wl = W.config(cfg)
+    say(f"case: fused config {cfg} flags={flag}")
+    d = to_device(wl)
+    ws = mqa.alloc_workspace(wl.rows)
+    out = fused(d, wl.topk, flags=flag | mqa.FLAG_STATS, workspace=ws)
+    st = mqa.read_stats(ws)
+    say("stats", st)
+    o = out.cpu().numpy()
+    assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, wl.topk)
+    rows = np.arange(wl.rows) if cfg == 1 else W.sample_rows(wl, 128)
+    fails = check.check_topk(o[rows], rows, oracle_problem(wl), wl.topk, TOL)
+    assert not fails, fails[:5]
+    if flag != mqa.FLAG_SMALL_CAP:
+        assert st["rows_exact"] == wl.rows - st["rows_short"]
+
+
+def test_fused_edge_ranges():
+    keys, topk = 5000, 512
+    starts = [0, 0, 100, 4000, -50, 4990, 3000, 10, 0, 2500, 0, 0, 7, 700]
+    ends = [5000, 512, 612, 4513, 900, 6000, 2000, 10, 513, 5000, 1, 4999, 4900, 701]
+    rows = 77
+    st = np.array((starts * 6)[:rows], np.int32)
+    en = np.array((ends * 6)[:rows], np.int32)
+    wl = W.custom(rows, keys, topk, st, en, seed=9)
+    say("case: fused edge ranges (empty, n<k, n==k, n==k+1, clamped, start>end), 77 rows")
+    d = to_device(wl)
+    for flags in (0, mqa.FLAG_FORCE_EXACT, mqa.FLAG_SMALL_CAP):
+        out = fused(d, topk, flags=flags)
+        o = out.cpu().numpy()
+        assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, topk), flags
+        fails = check.check_topk(o, np.arange(rows), oracle_problem(wl), topk, TOL)
+        assert not fails, (flags, fails[:5])
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_fused_large_sampled(cfg):
+    wl = W.config(cfg)
+    say(f"case: fused config {cfg} ({wl.name}); validity all rows, set rule on 256 rows")
+    d = to_device(wl)
+    ws = mqa.alloc_workspace(wl.rows)
+    out = fused(d, wl.topk, flags=mqa.FLAG_STATS, workspace=ws)
+    st = mqa.read_stats(ws)
+    say("stats", st)
+    o = out.cpu().numpy()
+    del d
+    assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, wl.topk)
+    rows = W.sample_rows(wl, 256)
+    fails = check.check_topk(o[rows], rows, oracle_problem(wl), wl.topk, TOL)
+    assert not fails, fails[:5]
