@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused FP8 MQA-logits + top-k prefill path on one MI355X.
+
+One step = one mqa_topk_prefill call over the whole 16384-row x 131072-key
+chunk (row i sees keys [0, 114689 + i), top-2048), inputs resident in HBM.
+Prints ONE JSON line (rank 0):
+  value    = visible (row, key) scores per second (sum of the rows' visible
+             keys / seconds per step);
+  roofline = FP8 MFMA roofline of the fused kernel: 8192 flop per visible
+             pair (2 * 32 heads * 128 dims) / its average duration, against
+             the MI355X dense FP8 peak (5.0 PFLOP/s); traffic = HBM bytes per
+             launch from the committed rocprofv3 counter summary when it was
+             taken on the current kernel sources, else null;
+  cpu_baseline = the CPU oracle (exact logits + full sort) timed on this
+             host's cores over a bounded sample of the same rows.
+Flags: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu,
+--dense (also time the chunked dense logits + top-k path, for context).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (published)
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E (published)
+FLOP_PER_PAIR = 2 * 32 * 128
+COUNTERS = os.path.join(ROOT, "profiles", "fused_topk_cfg3_counters.json")
+SOURCES = ["fp8_mqa_logits_amd/csrc/fused.hip", "fp8_mqa_logits_amd/csrc/common.h",
+           "fp8_mqa_logits_amd/csrc/launch.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for s in SOURCES:
+        with open(os.path.join(ROOT, s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters():
+    """HBM bytes per fused-kernel launch from the committed counter summary,
+    or None when the summary is missing or was taken on other sources."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, target_s: float = 12.0):
+    """Time the oracle (as it stands) on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+
+    threads = min(16, os.cpu_count() or 1)
+    p = oracle.Problem(wl.q, wl.k, oracle.key_scales(wl.scale_bytes), wl.weights, wl.starts,
+                       wl.ends)
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(wl.rows, size=wl.rows, replace=False))
+    s = np.clip(wl.starts.astype(np.int64), 0, wl.keys)
+    e = np.clip(wl.ends.astype(np.int64), s, wl.keys)
+    # calibrate on a few rows, then size the sample to about target_s seconds
+    probe = rows[:threads]
+    t0 = time.perf_counter()
+    oracle.topk(p, probe, wl.topk, threads=threads)
+    dt = time.perf_counter() - t0
+    rate = float((e[probe] - s[probe]).sum()) / max(dt, 1e-6)
+    per_row = float((e - s).mean())
+    nrows = int(max(threads, min(wl.rows, target_s * rate / per_row)))
+    nrows = (nrows + threads - 1) // threads * threads
+    sample = rows[threads:threads + nrows]
+    t0 = time.perf_counter()
+    oracle.topk(p, sample, wl.topk, threads=threads)
+    dt = time.perf_counter() - t0
+    pairs = float((e[sample] - s[sample]).sum())
+    return {"value": pairs / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sample)} seeded random rows of the same workload "
+                      f"({int(pairs)} visible pairs), exact logits + full sort per row, "
+                      f"{dt:.1f} s"}
+
+
+def time_dense(d, wl, steps: int, warmup: int):
+    """Chunked dense path: logits for floor(2^27 / ncols) rows at a time (the
+    512 MiB logits budget) over each chunk's key window, then per-row top-k."""
+    import torch
+
+    import fp8_mqa_logits_amd as mqa
+
+    starts, ends = wl.starts.astype("int64"), wl.ends.astype("int64")
+    chunks = []
+    r0 = 0
+    while r0 < wl.rows:
+        # rows per call from the remaining rows' key window, then that chunk's own window
+        nr = max(1, (1 << 27) // max(int(ends[r0:].max() - starts[r0:].min()), 1))
+        r1 = min(wl.rows, r0 + nr)
+        lo, hi = int(starts[r0:r1].min()), int(ends[r0:r1].max())
+        chunks.append((r0, r1, lo, max(hi - lo, 1)))
+        r0 = r1
+    max_r = max(c[1] - c[0] for c in chunks)
+    max_c = max(c[3] for c in chunks)
+    buf = torch.empty(max_r * ((max_c + 3) // 4 * 4), dtype=torch.float32, device="cuda")
+    out = torch.empty((wl.rows, wl.topk), dtype=torch.int32, device="cuda")
+
+    def step():
+        for r0, r1, lo, nc in chunks:
+            ld = (nc + 3) // 4 * 4
+            lg = buf[:(r1 - r0) * ld].view(r1 - r0, ld)[:, :nc]
+            mqa.mqa_logits_dense(d["q"][r0:r1], d["k"], d["scales"], d["weights"][r0:r1],
+                                 d["starts"][r0:r1], d["ends"][r0:r1], col0=lo, ncols=nc,
+                                 logits=lg)
+            mqa.mqa_topk_dense(lg, d["starts"][r0:r1], d["ends"][r0:r1], wl.topk, wl.keys,
+                               col0=lo, out=out[r0:r1])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps, len(chunks)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this path runs on one GPU; multi-GPU runs are not supported "
+              "(the row-sharded design is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import fp8_mqa_logits_amd as mqa
+    import mqa_workloads as W
+
+    wl = W.config(args.config)
+    print(f"[bench] workload {wl.name}: {wl.visible_pairs()} visible pairs, hashes "
+          f"{wl.hashes()}", file=sys.stderr, flush=True)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    d = {
+        "q": torch.from_numpy(wl.q).to(dev),
+        "k": torch.from_numpy(wl.k).to(dev),
+        "weights": torch.from_numpy(wl.weights).to(dev),
+        "starts": torch.from_numpy(wl.starts).to(dev),
+        "ends": torch.from_numpy(wl.ends).to(dev),
+    }
+    d["scales"] = mqa.mqa_key_scales(torch.from_numpy(wl.scale_bytes).to(dev))
+    ws = mqa.alloc_workspace(wl.rows)
+    out = torch.empty((wl.rows, wl.topk), dtype=torch.int32, device=dev)
+
+    def step(flags=0):
+        mqa.mqa_topk_prefill(d["q"], d["k"], d["scales"], d["weights"], d["starts"], d["ends"],
+                             wl.topk, out=out, workspace=ws, flags=flags)
+
+    # path statistics (one extra call outside the timed region)
+    step(mqa.FLAG_STATS)
+    torch.cuda.synchronize()
+    stats = mqa.read_stats(ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    pairs = wl.visible_pairs()
+    value = pairs / (ms / 1e3)
+    achieved = pairs * FLOP_PER_PAIR / (ms / 1e3) / 1e12
+    line = {
+        "metric": "(row,key) scores/s + % FP8 MFMA peak, top-2048, 16K rows x 128K keys",
+        "value": value,
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 MFMA, fp32 scores",
+        "data": "synthetic (seeded N(0,1) e4m3 q/k, UE8M0 scales 2^[-4,0], N(0,1)/sqrt(32) weights)",
+        "config": {"workload": wl.name, "rows": wl.rows, "keys": wl.keys, "topk": wl.topk,
+                   "visible_pairs": pairs, "parallelism": "1 GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS,
+                     "traffic": traffic_from_counters()},
+        "path_stats": stats,
+    }
+    if args.dense:
+        dms, ncalls = time_dense(d, wl, max(1, args.steps // 4), 1)
+        line["dense_ms_per_step"] = dms
+        line["dense_call_pairs"] = ncalls
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,7 +14,6 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kHeaderWords = 64;
 constexpr size_t kCap = 16384;
-constexpr size_t kMaxTopk = 2048;
 
 thread_local char g_err[256] = "";
 
@@ -63,7 +62,7 @@ const DeviceInfo* device_info(int device) {
 }
 
 struct Layout {
-  size_t header, order, slabE, slabI, tmpE, tmpI, total;
+  size_t header, order, xrow, xqueue, slabE, slabI, tmpE, tmpI, total;
   int grid, nblocks;
 };
 
@@ -76,12 +75,16 @@ Layout layout(int rows, const DeviceInfo& d) {
   off = align_up(off + kHeaderWords * 4);
   L.order = off;
   off = align_up(off + (size_t)L.nblocks * 4);
+  L.xrow = off;
+  off = align_up(off + (size_t)rows);
+  L.xqueue = off;
+  off = align_up(off + (size_t)L.nblocks * 4);
   const size_t slab = (size_t)L.grid * mqa::kFusedBlockRows * kCap * 4;
   L.slabE = off;
   off = align_up(off + slab);
   L.slabI = off;
   off = align_up(off + slab);
-  const size_t tmp = (size_t)L.grid * mqa::kFusedWaves * kMaxTopk * 4;
+  const size_t tmp = (size_t)L.grid * mqa::kFusedWaves * mqa::kTmp * 4;
   L.tmpE = off;
   off = align_up(off + tmp);
   L.tmpI = off;
@@ -149,6 +152,8 @@ int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
   p.flags = flags;
   p.header = reinterpret_cast<uint32_t*>(ws + L.header);
   p.order = reinterpret_cast<int32_t*>(ws + L.order);
+  p.xrow = ws + L.xrow;
+  p.xqueue = reinterpret_cast<int32_t*>(ws + L.xqueue);
   p.slabE = reinterpret_cast<float*>(ws + L.slabE);
   p.slabI = reinterpret_cast<int32_t*>(ws + L.slabI);
   p.tmpE = reinterpret_cast<float*>(ws + L.tmpE);

@@ -56,6 +56,11 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(int lo, int hi) {
   return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
 
 // LDS placement of a 64-key chunk: key j's 16-byte slice c (0..7) lives at
@@ -117,20 +122,38 @@ __device__ __forceinline__ void load_keys_lds(KeyTile& kt, const uint8_t* lds_ch
   }
 }
 
-// Unscaled score sum_h w[r,h] * relu(q[r,h,:] . k[j,:]) of key j = lane id
-// of the chunk, for one query row.
-__device__ __forceinline__ float score_chunk(const QueryRow& qr, const KeyTile& kt) {
-  float part[4];
+// relu of an fp32 value as an integer max of its bit pattern (negative floats
+// have the sign bit set, so they compare below 0): one VALU op, no NaN
+// canonicalization.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(__builtin_elementwise_max(__float_as_int(x), 0));
+}
+
+// The 8 head-dot tiles of one query row against a 64-key chunk.
+struct RowAcc {
+  v4f a[4][2];
+};
+
+__device__ __forceinline__ void mfma_row(RowAcc& acc, const QueryRow& qr, const KeyTile& kt) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const v4f z = {0.f, 0.f, 0.f, 0.f};
-    const v4f a0 = mfma_fp8(qr.qa[0], kt.kb[t], z);
-    const v4f a1 = mfma_fp8(qr.qa[1], kt.kb[t], z);
+    acc.a[t][0] = mfma_fp8(qr.qa[0], kt.kb[t], z);
+    acc.a[t][1] = mfma_fp8(qr.qa[1], kt.kb[t], z);
+  }
+}
+
+// Weighted relu sum over the lane's 8 heads of each sub-tile, then two
+// permlane swap+add steps: lane l ends with the unscaled score of key l.
+__device__ __forceinline__ float reduce_heads(const QueryRow& qr, const RowAcc& acc) {
+  float part[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
     float s = 0.f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s = __builtin_fmaf(qr.w[v], __builtin_fmaxf(a0[v], 0.f), s);
+    for (int v = 0; v < 4; ++v) s = __builtin_fmaf(qr.w[v], relu(acc.a[t][0][v]), s);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s = __builtin_fmaf(qr.w[4 + v], __builtin_fmaxf(a1[v], 0.f), s);
+    for (int v = 0; v < 4; ++v) s = __builtin_fmaf(qr.w[4 + v], relu(acc.a[t][1][v]), s);
     part[t] = s;
   }
   // lanes 0-31 | 32-63 hold head groups {0,1} | {2,3}; fold them pairwise
@@ -145,12 +168,20 @@ __device__ __forceinline__ float score_chunk(const QueryRow& qr, const KeyTile& 
   return __uint_as_float(s4[0]) + __uint_as_float(s4[1]);
 }
 
+// Unscaled score sum_h w[r,h] * relu(q[r,h,:] . k[j,:]) of key j = lane id
+// of the chunk, for one query row, from FP8 MFMA head dots.
+__device__ __forceinline__ float score_chunk(const QueryRow& qr, const KeyTile& kt) {
+  RowAcc acc;
+  mfma_row(acc, qr, kt);
+  return reduce_heads(qr, acc);
+}
+
 // The same 64-key scores as score_chunk, with the head dots taken by the
 // bf16 MFMA (16x16x32) on the exactly converted e4m3 values: fp32-accurate.
 // Each lane's 32 bytes (dims 32g .. 32g+31) feed 4 K-steps of 8 elements;
 // A and B use the same dim order, so every dot product covers all 128 dims.
 __device__ __forceinline__ float score_chunk_exact(const QueryRow& qr, const KeyTile& kt) {
-  float part[4];
+  RowAcc acc;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     v4f a0 = {0.f, 0.f, 0.f, 0.f};
@@ -161,22 +192,10 @@ __device__ __forceinline__ float score_chunk_exact(const QueryRow& qr, const Key
       a0 = mfma_bf16(fp8x8_to_bf16(qr.qa[0][2 * st], qr.qa[0][2 * st + 1]), bk, a0);
       a1 = mfma_bf16(fp8x8_to_bf16(qr.qa[1][2 * st], qr.qa[1][2 * st + 1]), bk, a1);
     }
-    float s = 0.f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) s = __builtin_fmaf(qr.w[v], __builtin_fmaxf(a0[v], 0.f), s);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) s = __builtin_fmaf(qr.w[4 + v], __builtin_fmaxf(a1[v], 0.f), s);
-    part[t] = s;
+    acc.a[t][0] = a0;
+    acc.a[t][1] = a1;
   }
-  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
-                                                    __float_as_uint(part[2]), false, false);
-  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]),
-                                                    __float_as_uint(part[3]), false, false);
-  const float y02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
-  const float y13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
-  const auto s4 = __builtin_amdgcn_permlane16_swap(__float_as_uint(y02), __float_as_uint(y13),
-                                                   false, false);
-  return __uint_as_float(s4[0]) + __uint_as_float(s4[1]);
+  return reduce_heads(qr, acc);
 }
 
 // B operands of up to 64 arbitrary keys read straight from global memory:
@@ -201,21 +220,31 @@ __device__ __forceinline__ void load_keys_gather(KeyTile& kt, const uint8_t* __r
 // nthreads, ... Keys at or past `keys` are clamped to the last key (their
 // scores are masked by the caller).
 __device__ __forceinline__ void stage_chunk_regs(uint4* regs, const uint8_t* __restrict__ k,
-                                                 int64_t key0, int keys, int tid, int nthreads,
-                                                 const int64_t* gather = nullptr) {
+                                                 int key0, int keys, int tid, int nthreads,
+                                                 const int* gather = nullptr) {
   for (int i = 0, p = tid; p < kChunk * 8; ++i, p += nthreads) {
     const int j = p >> 3;
     const int slot = p & 7;
     const int c = slot ^ swz(j);
-    int64_t key = gather ? gather[j] : key0 + j;
+    int key = gather ? gather[j] : key0 + j;
     key = key < keys ? key : keys - 1;
-    regs[i] = *reinterpret_cast<const uint4*>(k + key * kDim + 16 * c);
+    regs[i] = *reinterpret_cast<const uint4*>(k + (int64_t)key * kDim + 16 * c);
   }
 }
 __device__ __forceinline__ void store_chunk_regs(const uint4* regs, uint8_t* lds_chunk, int tid,
                                                  int nthreads) {
   for (int i = 0, p = tid; p < kChunk * 8; ++i, p += nthreads)
     *reinterpret_cast<uint4*>(lds_chunk + 16 * p) = regs[i];
+}
+
+// The chunk's 64 per-key scales travel through LDS with its keys (threads
+// 0..63 move one each), so that reading them never waits on vector memory.
+__device__ __forceinline__ float stage_scale(const float* __restrict__ scales, int key0, int keys,
+                                             int tid, const int* gather = nullptr) {
+  if (tid >= kChunk) return 0.f;
+  int key = gather ? gather[tid] : key0 + tid;
+  key = key < keys ? key : keys - 1;
+  return scales[key];
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -321,6 +350,71 @@ __device__ float wave_kth_value(const float* __restrict__ E, int n, int rank, ui
     __builtin_amdgcn_wave_barrier();
   }
   return kfloat(prefix);
+}
+
+// ---------------------------------------------------------------------------
+// The `need` best of nb records (E, I)[0..nb) by exact comparison, for small
+// nb: the scores are copied to LDS (e_lds, >= nb floats, private to the wave)
+// and record i takes slot rank(i) = #{j : E[j] > E[i] or (E[j] == E[i] and
+// j < i)} when rank(i) < need. Returns the smallest selected score.
+template <class Emit>
+__device__ float small_select(const float* __restrict__ E, const int* __restrict__ I, int nb,
+                              int need, float* e_lds, Emit emit) {
+  const int l = lane_id();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  for (int i = l; i < nb; i += kWave) e_lds[i] = E[i];
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  float tau = __builtin_inff();
+  for (int i0 = 0; i0 < nb; i0 += kWave) {
+    const int i = i0 + l;
+    const float e = i < nb ? e_lds[i] : 0.f;
+    int rank = 0;
+    for (int j = 0; j < nb; ++j) {
+      const float ej = e_lds[j];
+      rank += (ej > e) | ((ej == e) & (j < i));
+    }
+    if (i < nb && rank < need) {
+      emit(rank, e, I[i]);
+      tau = __builtin_fminf(tau, e);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  return wave_min(tau);
+}
+
+// First bin b (scanning bins 0, 1, ... of hist[0..nb)) whose cumulative count
+// reaches `need`; `before` receives the count of bins < b. Returns nb - 1 when
+// the total is below `need`.
+__device__ __forceinline__ int first_bin_reaching(const uint32_t* hist, int nb, int need,
+                                                  int& before) {
+  const int l = lane_id();
+  const int per = nb / kWave;
+  int mine = 0;
+  for (int b = 0; b < per; ++b) mine += (int)hist[l * per + b];
+  const int incl = wave_incl_scan(mine);
+  const int excl = incl - mine;
+  const uint64_t hit = __ballot(incl >= need);
+  if (hit == 0) {
+    before = __shfl(incl, 63, 64) - (int)hist[nb - 1];
+    return nb - 1;
+  }
+  const int src = __builtin_ctzll(hit);
+  int bin = nb - 1, bf = 0;
+  if (l == src) {
+    int c = excl;
+    for (int b = 0; b < per; ++b) {
+      const int h = (int)hist[l * per + b];
+      if (c + h >= need) {
+        bin = l * per + b;
+        bf = c;
+        break;
+      }
+      c += h;
+    }
+  }
+  before = __shfl(bf, src, 64);
+  return __shfl(bin, src, 64);
 }
 
 // ---------------------------------------------------------------------------

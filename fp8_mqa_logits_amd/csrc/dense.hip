@@ -19,7 +19,7 @@ constexpr int kDCols = 4 * kChunk;                    // 256 columns per workgro
 __global__ __launch_bounds__(kDThreads) void dense_logits_kernel(DenseParams p) {
   __shared__ __align__(16) uint8_t kbuf[2][kChunkBytes];
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = wave_id();
   const int l = lane_id();
   const int c_begin = blockIdx.x * kDCols;
   const int c_end = c_begin + kDCols < p.ncols ? c_begin + kDCols : p.ncols;
@@ -41,13 +41,13 @@ __global__ __launch_bounds__(kDThreads) void dense_logits_kernel(DenseParams p) 
   }
   const int nch = (c_end - c_begin + kChunk - 1) / kChunk;
   uint4 regs[1];
-  stage_chunk_regs(regs, p.k, (int64_t)p.col0 + c_begin, p.keys, tid, kDThreads);
+  stage_chunk_regs(regs, p.k, p.col0 + c_begin, p.keys, tid, kDThreads);
   store_chunk_regs(regs, kbuf[0], tid, kDThreads);
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
     const int cc0 = c_begin + c * kChunk;
     const bool more = c + 1 < nch;
-    if (more) stage_chunk_regs(regs, p.k, (int64_t)p.col0 + cc0 + kChunk, p.keys, tid, kDThreads);
+    if (more) stage_chunk_regs(regs, p.k, p.col0 + cc0 + kChunk, p.keys, tid, kDThreads);
     const int cc = cc0 + l;
     const int64_t key = (int64_t)p.col0 + cc;
     const float sc = p.scales[key < p.keys ? key : p.keys - 1];

@@ -1,4 +1,4 @@
-// Fused FP8 MQA logits + per-row top-k, one persistent launch per call.
+// Fused FP8 MQA logits + per-row top-k without a logits matrix in HBM.
 //
 // Follows vLLM PR #60618, "What this PR does" (scoring, sampled gate,
 // candidate emission, per-row selection, exact rescan, heaviest-first block
@@ -8,7 +8,8 @@
 //     rows, 4 per wave, whose q and weights stay in VGPRs for the whole scan;
 //   * keys stream through a double-buffered 8 KiB LDS stage (64 keys) loaded
 //     with coalesced 16-byte global loads; every wave reads the stage as FP8
-//     MFMA B operands and scores its 4 rows (common.h);
+//     MFMA B operands and scores its 4 rows, issuing the next row's MFMAs
+//     before the current row's relu/weight epilogue (common.h);
 //   * each wave owns its rows, so the gate threshold, the candidate count and
 //     the slab cursor of a row are wave-uniform values: emission is a ballot,
 //     a popcount and one 8-byte store per passing lane, with no atomics;
@@ -18,10 +19,10 @@
 //     and accepts the row only when the band's largest measured error, times
 //     a safety factor, cannot move any key across the cut;
 //   * rows whose gate misses, whose slab overflows or whose band cannot be
-//     certified are rescanned with exact scores and a streaming top-k merge;
-//   * the select, the fallback rescan and its compactions run in the same
-//     workgroup right after the block's scan, so no workgroup ever waits for
-//     another one.
+//     certified are queued; a second persistent kernel rescans their blocks
+//     with exact scores and a streaming top-k merge;
+//   * blocks are claimed heaviest first from a global counter; no workgroup
+//     ever waits for another one.
 #include "common.h"
 #include "launch.h"
 
@@ -35,18 +36,18 @@ static_assert(kBlockRows == kFusedBlockRows, "block rows");
 constexpr int kGateBins = 128;
 constexpr int kGateOff = 16;  // bins above the first-tile maximum
 constexpr int kHistWords = 2048;
-
-// Header words (mirror of struct mqa_stats in mqa_topk.h).
-enum : int {
-  H_CLAIM = 0, H_SHORT = 1, H_GATED = 2, H_EXACT = 3, H_OVERFLOW = 4, H_UNDER = 5,
-  H_COMPACT = 6, H_UNCERT = 7, H_CAND_LO = 8, H_CAND_HI = 9, H_BAND_LO = 10, H_BAND_HI = 11
-};
 constexpr int kBand = 32;           // keys on each side of rank k that are rescored exactly
 constexpr float kBandSafety = 8.f;  // certificate margin, in units of the band's largest error
 
+// Header words (the first 12 mirror struct mqa_stats in mqa_topk.h).
+enum : int {
+  H_CLAIM = 0, H_SHORT = 1, H_GATED = 2, H_EXACT = 3, H_OVERFLOW = 4, H_UNDER = 5,
+  H_COMPACT = 6, H_UNCERT = 7, H_CAND_LO = 8, H_CAND_HI = 9, H_BAND_LO = 10, H_BAND_HI = 11,
+  H_XQ = 16,     // blocks queued for the exact rescan
+  H_XCLAIM = 17  // exact-rescan claim counter
+};
+
 enum RowMode : int { M_OFF = 0, M_SHORT = 1, M_ALL = 2, M_GATED = 3, M_EXACT = 4 };
-
-
 
 __device__ __forceinline__ void row_range(const FusedParams& p, int r, int& s, int& e) {
   int a = p.starts[r], b = p.ends[r];
@@ -112,44 +113,58 @@ struct RowState {
   float m0, inv;  // gate: first-tile maximum and inverse bin width
   int have_m0;
   int nsamp;    // gate: sample keys inside the row's range
+  float vmax;   // per lane: largest score this lane appended to the slab
 };
 
 struct __align__(16) FusedSmem {
   uint8_t kbuf[2][kChunkBytes];
+  float sbuf[2][kChunk];
   uint32_t hist[kWaves][kHistWords];
-  int64_t gath[kChunk];
-  int lo, hi, any_gated, any_exact, block;
+  int gath[kChunk];
+  int block;
   int wlo[kWaves], whi[kWaves], wg[kWaves], wx[kWaves];
 };
 
-// Append the passing lanes of one chunk to a row's slab; a full slab in
-// streaming mode is first compacted to the row's k best records.
-__device__ __forceinline__ void emit_chunk(const FusedParams& p, RowState& rs, float E, bool valid,
-                                           int64_t key, int cap, float* sE, int32_t* sI,
+__device__ __forceinline__ void init_row(RowState& r, int row) {
+  r.r = row;
+  r.cnt = 0;
+  r.strict = 0;
+  r.thr = -__builtin_inff();
+  r.have_m0 = 0;
+  r.nsamp = 0;
+  r.m0 = 0.f;
+  r.inv = 1.f;
+  r.mode = M_OFF;
+  r.s = r.e = 0;
+  r.vmax = -__builtin_inff();
+}
+
+// Append the passing lanes of one chunk to a row's slab. A slab that would
+// overflow is first compacted to the row's `keep` best records by score and
+// the admission threshold rises to the smallest of them (a streaming top-k
+// merge; later records must beat it strictly).
+__device__ __forceinline__ void emit_merge(const FusedParams& p, RowState& rs, float E, bool valid,
+                                           int key, int cap, int keep, float* sE, int32_t* sI,
                                            float* tE, int32_t* tI, uint32_t* hist) {
   bool pass = valid && (rs.strict ? (E > rs.thr) : (E >= rs.thr));
   uint64_t m = __ballot(pass);
   if (m == 0) return;
   int c = __popcll(m);
-  if (rs.mode == M_EXACT && rs.cnt + c > cap) {
-    // streaming top-k merge: keep the k best so far, raise the threshold
-    const int k = p.topk;
-    const float kth = wave_select(sE, sI, rs.cnt, k, hist, [&](int slot, float e, int idx) {
+  if (rs.cnt + c > cap) {
+    const float kth = wave_select(sE, sI, rs.cnt, keep, hist, [&](int slot, float e, int idx) {
       tE[slot] = e;
       tI[slot] = idx;
     });
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    for (int i = lane_id(); i < k; i += kWave) {
+    for (int i = lane_id(); i < keep; i += kWave) {
       sE[i] = tE[i];
       sI[i] = tI[i];
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    rs.cnt = k;
+    rs.cnt = keep;
     rs.thr = kth;
     rs.strict = 1;
-    if (p.flags & 8u) {
-      if (lane_id() == 0) atomicAdd(&p.header[H_COMPACT], 1u);
-    }
+    if ((p.flags & 8u) && lane_id() == 0) atomicAdd(&p.header[H_COMPACT], 1u);
     pass = valid && E > rs.thr;
     m = __ballot(pass);
     if (m == 0) return;
@@ -157,162 +172,118 @@ __device__ __forceinline__ void emit_chunk(const FusedParams& p, RowState& rs, f
   }
   if (pass) {
     const int pos = rs.cnt + rank_in_mask(m);
-    if (pos < cap) {
-      sE[pos] = E;
-      sI[pos] = (int32_t)key;
-    }
+    sE[pos] = E;
+    sI[pos] = key;
+    rs.vmax = __builtin_fmaxf(rs.vmax, E);
   }
   rs.cnt += c;
 }
 
-// One sweep over the keys [lo, hi) for the rows of this wave whose mode is in
-// `mode_bits`, with FP8 MFMA scores (EXACT = false) or exact scores.
+__device__ __forceinline__ bool row_in_chunk(const RowState& r, int mode, int key0) {
+  return r.mode == mode && r.s < key0 + kChunk && r.e > key0;
+}
+
+// Emit one active row's scores of a chunk.
+struct SlabRefs {
+  float* sE[4];
+  int32_t* sI[4];
+  float* tE;
+  int32_t* tI;
+  uint32_t* hist;
+  int cap, keep;
+};
+
+__device__ __forceinline__ void finish_row(const FusedParams& p, RowState& r, float E, int key,
+                                           int key0, const SlabRefs& sr, int i) {
+  const bool full = r.s <= key0 && key0 + kChunk <= r.e;
+  const bool valid = full || (key >= r.s && key < r.e);
+  emit_merge(p, r, E, valid, key, sr.cap, sr.keep, sr.sE[i], sr.sI[i], sr.tE, sr.tI, sr.hist);
+}
+
+// One scan of keys [lo, hi) for the rows of this wave in `mode` (M_ALL and
+// M_GATED rows together, or M_EXACT rows): FP8 MFMA scores, or exact scores
+// for EXACT. FP8 rows are pipelined: the MFMAs of the next row are issued
+// before the epilogue of the current one.
 template <bool EXACT>
-__device__ __forceinline__ void scan_block(const FusedParams& p, FusedSmem& sm, const QueryRow* qr, RowState* rs,
-                           int mode_bits, int lo, int hi, int cap, float* slabE, int32_t* slabI,
-                           float* tE, int32_t* tI) {
+__device__ __forceinline__ void scan_rows(const FusedParams& p, FusedSmem& sm, const QueryRow* qr,
+                                          RowState* rs, int mode, int lo, int hi,
+                                          const SlabRefs& sr) {
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
   const int l = lane_id();
   const int nch = (hi - lo + kChunk - 1) / kChunk;
   uint4 regs[1];
+  float sreg = stage_scale(p.scales, lo, p.keys, tid);
   stage_chunk_regs(regs, p.k, lo, p.keys, tid, kThreads);
   store_chunk_regs(regs, sm.kbuf[0], tid, kThreads);
+  if (tid < kChunk) sm.sbuf[0][tid] = sreg;
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
-    const int64_t key0 = (int64_t)lo + (int64_t)c * kChunk;
+    const int key0 = lo + c * kChunk;
     const bool more = c + 1 < nch;
-    if (more) stage_chunk_regs(regs, p.k, key0 + kChunk, p.keys, tid, kThreads);
-    const int64_t key = key0 + l;
-    const float sc = p.scales[key < p.keys ? key : p.keys - 1];
+    if (more) {
+      sreg = stage_scale(p.scales, key0 + kChunk, p.keys, tid);
+      stage_chunk_regs(regs, p.k, key0 + kChunk, p.keys, tid, kThreads);
+    }
+    const int key = key0 + l;
+    const float sc = sm.sbuf[c & 1][l];
+    bool act[kRowsPerWave];
     bool any = false;
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i)
-      any |= ((mode_bits >> rs[i].mode) & 1) && rs[i].s < key0 + kChunk && rs[i].e > key0;
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      act[i] = mode == M_EXACT ? row_in_chunk(rs[i], M_EXACT, key0)
+                               : (row_in_chunk(rs[i], M_ALL, key0) ||
+                                  row_in_chunk(rs[i], M_GATED, key0));
+      any |= act[i];
+    }
     if (any) {
       KeyTile kt;
       load_keys_lds(kt, sm.kbuf[c & 1]);
+      if (EXACT) {
 #pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i) {
-        RowState& r = rs[i];
-        if (!((mode_bits >> r.mode) & 1) || r.s >= key0 + kChunk || r.e <= key0) continue;
-        const float E = (EXACT ? score_chunk_exact(qr[i], kt) : score_chunk(qr[i], kt)) * sc;
-        const bool valid = key >= r.s && key < r.e;
-        const int slot = w * kRowsPerWave + i;
-        emit_chunk(p, r, E, valid, key, cap, slabE + (int64_t)slot * kCap,
-                   slabI + (int64_t)slot * kCap, tE, tI, sm.hist[w]);
+        for (int i = 0; i < kRowsPerWave; ++i)
+          if (act[i]) finish_row(p, rs[i], score_chunk_exact(qr[i], kt) * sc, key, key0, sr, i);
+      } else {
+        RowAcc a0, a1;
+        if (act[0]) mfma_row(a0, qr[0], kt);
+        if (act[1]) mfma_row(a1, qr[1], kt);
+        if (act[0]) finish_row(p, rs[0], reduce_heads(qr[0], a0) * sc, key, key0, sr, 0);
+        if (act[2]) mfma_row(a0, qr[2], kt);
+        if (act[1]) finish_row(p, rs[1], reduce_heads(qr[1], a1) * sc, key, key0, sr, 1);
+        if (act[3]) mfma_row(a1, qr[3], kt);
+        if (act[2]) finish_row(p, rs[2], reduce_heads(qr[2], a0) * sc, key, key0, sr, 2);
+        if (act[3]) finish_row(p, rs[3], reduce_heads(qr[3], a1) * sc, key, key0, sr, 3);
       }
     }
-    if (more) store_chunk_regs(regs, sm.kbuf[(c + 1) & 1], tid, kThreads);
+    if (more) {
+      store_chunk_regs(regs, sm.kbuf[(c + 1) & 1], tid, kThreads);
+      if (tid < kChunk) sm.sbuf[(c + 1) & 1][tid] = sreg;
+    }
     __syncthreads();
   }
-}
-
-// Top-k of a row from its FP8-scored candidates (sE, sI)[0..n), n >= k, all
-// with approximate score >= T (non-candidates score below T):
-//   1. the (k-kBand)-th and (k+kBand)-th largest approximate scores vhi, vlo;
-//   2. records above vhi are taken; records in [vlo, vhi] (the band) are
-//      compacted to the front of the slab; the largest approximate score
-//      below the band (or T) and the smallest one above it are kept;
-//   3. the band's scores are recomputed exactly and its best k - |above|
-//      records are taken by exact score;
-//   4. certificate: with D = kBandSafety * (largest |exact - approximate| in
-//      the band, floored at 2^-18 of the row's largest score magnitude), the
-//      result is exact when every record above the band scores >= tau + D and
-//      every record below it <= tau - D (tau = the k-th exact score).
-// Returns false when the certificate fails (the caller rescans the row).
-template <class Emit>
-__device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int n, int k, float T,
-                              const QueryRow& qr, uint32_t* hist, unsigned* band_count,
-                              Emit emit) {
-  const int l = lane_id();
-  const float vhi = (k - kBand >= 1) ? wave_kth_value(sE, n, k - kBand, hist) : __builtin_inff();
-  const float vlo = (k + kBand <= n) ? wave_kth_value(sE, n, k + kBand, hist) : -__builtin_inff();
-  int na = 0, nb = 0;
-  float min_above = __builtin_inff(), max_below = -__builtin_inff(), maxabs = 0.f;
-  for (int i0 = 0; i0 < n; i0 += kWave) {
-    const int i = i0 + l;
-    const bool in = i < n;
-    const float e = in ? sE[i] : 0.f;
-    const int32_t idx = in ? sI[i] : 0;
-    const bool up = in && e > vhi;
-    const bool band = in && e >= vlo && e <= vhi;
-    const uint64_t mu = __ballot(up);
-    const uint64_t mb = __ballot(band);
-    if (up) {
-      const int slot = na + rank_in_mask(mu);
-      if (slot < k) emit(slot, idx);
-      min_above = __builtin_fminf(min_above, e);
-    }
-    if (in && e < vlo) max_below = __builtin_fmaxf(max_below, e);
-    if (in) maxabs = __builtin_fmaxf(maxabs, __builtin_fabsf(e));
-    // in-place compaction: targets lie at or before this chunk, already read
-    if (band) {
-      const int pos = nb + rank_in_mask(mb);
-      sE[pos] = e;
-      sI[pos] = idx;
-    }
-    na += __popcll(mu);
-    nb += __popcll(mb);
-  }
-  min_above = wave_min(min_above);
-  max_below = wave_max(max_below);
-  maxabs = wave_max(maxabs);
-  const int need = k - na;
-  if (na >= k || nb < need) return false;
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  // exact scores of the band, 64 records at a time
-  float err = 0.f;
-  for (int b0 = 0; b0 < nb; b0 += kWave) {
-    int keyidx[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int j = b0 + 16 * t + (l & 15);
-      keyidx[t] = sI[j < nb ? j : nb - 1];
-    }
-    KeyTile kt;
-    load_keys_gather(kt, p.k, keyidx);
-    const int j = b0 + l;
-    const int jj = j < nb ? j : nb - 1;
-    const float E = score_chunk_exact(qr, kt) * p.scales[sI[jj]];
-    if (j < nb) {
-      err = __builtin_fmaxf(err, __builtin_fabsf(E - sE[j]));
-      sE[j] = E;
-    }
-  }
-  err = wave_max(err);
-  if (l == 0 && band_count) atomicAdd(band_count, (unsigned)nb);
-  const float tau = wave_select(sE, sI, nb, need, hist,
-                                [&](int slot, float, int idx) { emit(na + slot, idx); });
-  const float d = kBandSafety * __builtin_fmaxf(err, maxabs * 0x1p-18f);
-  const float below = __builtin_fmaxf(max_below, T);
-  const bool ok_above = na == 0 || min_above - d >= tau;
-  const bool ok_below = below + d <= tau;
-  return ok_above && ok_below;
 }
 
 // Sampled gate: a strided sample of the block's keys gives each gated row a
 // threshold that should keep about 2k candidates. The sample histogram is
 // binned relative to the row's maximum over the first sample tile.
-__device__ __forceinline__ void gate_block(const FusedParams& p, FusedSmem& sm, const QueryRow* qr, RowState* rs,
-                           int lo, int hi) {
+__device__ __forceinline__ void gate_block(const FusedParams& p, FusedSmem& sm, const QueryRow* qr,
+                                           RowState* rs, int lo, int hi) {
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = wave_id();
   const int l = lane_id();
-  const int64_t span = hi - lo;
-  int S = (int)(span / 16) & ~(kChunk - 1);
+  const int span = hi - lo;
+  int S = (span / 16) & ~(kChunk - 1);
   S = S < 1024 ? 1024 : (S > 4096 ? 4096 : S);
   const int nch = S / kChunk;
   uint32_t* hist = sm.hist[w];
   for (int i = l; i < kRowsPerWave * kGateBins; i += kWave) hist[i] = 0;
   uint4 regs[1];
   for (int c = 0; c < nch; ++c) {
-    if (tid < kChunk) sm.gath[tid] = lo + ((int64_t)(c * kChunk + tid) * span) / S;
+    if (tid < kChunk) sm.gath[tid] = lo + (int)(((int64_t)(c * kChunk + tid) * span) / S);
     __syncthreads();
     stage_chunk_regs(regs, p.k, 0, p.keys, tid, kThreads, sm.gath);
     store_chunk_regs(regs, sm.kbuf[0], tid, kThreads);
     __syncthreads();
-    const int64_t key = sm.gath[l];
+    const int key = sm.gath[l];
     const float sc = p.scales[key];
     KeyTile kt;
     load_keys_lds(kt, sm.kbuf[0]);
@@ -336,8 +307,9 @@ __device__ __forceinline__ void gate_block(const FusedParams& p, FusedSmem& sm, 
       }
       r.nsamp += __popcll(vm);
       if (valid) {
-        float fb = (r.m0 - E) * r.inv;
-        int bin = fb < -1e6f ? 0 : (fb > 1e6f ? kGateBins - 1 : (int)__builtin_floorf(fb) + kGateOff);
+        const float fb = (r.m0 - E) * r.inv;
+        int bin = fb < -1e6f ? 0
+                             : (fb > 1e6f ? kGateBins - 1 : (int)__builtin_floorf(fb) + kGateOff);
         bin = bin < 0 ? 0 : (bin > kGateBins - 1 ? kGateBins - 1 : bin);
         atomicAdd(&hist[i * kGateBins + bin], 1u);
       }
@@ -369,18 +341,223 @@ __device__ __forceinline__ void gate_block(const FusedParams& p, FusedSmem& sm, 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
-  __shared__ FusedSmem sm;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
+// Top-k of a row from its FP8-scored candidates (sE, sI)[0..n), n >= k, all
+// with approximate score >= T (non-candidates score below T):
+//   1. one pass for the candidates' score range, one histogram pass over
+//      2048 equal-width bins of that range (descending scores);
+//   2. the bins holding ranks k-kBand and k+kBand bound the band: records in
+//      better bins are taken, band records are compacted to the front of the
+//      slab, and the smallest score above / largest below the band are kept;
+//   3. the band's scores are recomputed exactly and its best k - |above|
+//      records are taken by exact score;
+//   4. certificate: with D = kBandSafety * (largest |exact - approximate| in
+//      the band, floored at 2^-18 of the row's largest score magnitude), the
+//      result is exact when every record above the band scores >= tau + D and
+//      every record below it (and every non-candidate, < T) <= tau - D, tau
+//      being the k-th exact score.
+// Returns false when the certificate fails (the caller rescans the row).
+template <class Emit>
+__device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int n, int k, float T,
+                              float vmax, const QueryRow& qr, uint32_t* hist,
+                              unsigned* band_count, Emit emit) {
+  const int l = lane_id();
+  constexpr int kBins = kHistWords;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  const float4* e4 = reinterpret_cast<const float4*>(sE);  // slab rows are 64 KiB aligned
+  const int n4 = n >> 2;
+  const float mx = wave_max(vmax);
+  float mn = T;
+  if (!(mn > -__builtin_inff())) {
+    float m = __builtin_inff();
+#pragma unroll 4
+    for (int i = l; i < n4; i += kWave) {
+      const float4 v = e4[i];
+      m = __builtin_fminf(m, __builtin_fminf(__builtin_fminf(v.x, v.y), __builtin_fminf(v.z, v.w)));
+    }
+    for (int i = 4 * n4 + l; i < n; i += kWave) m = __builtin_fminf(m, sE[i]);
+    mn = wave_min(m);
+  }
+  const float span = mx - mn;
+  const float inv = span > 0.f ? (float)(kBins - 1) / span : 0.f;
+  auto bin_of = [&](float e) {
+    const float f = (mx - e) * inv;
+    int b = f < (float)(kBins - 1) ? (int)f : kBins - 1;
+    return b < 0 ? 0 : b;
+  };
+  for (int b = l; b < kBins; b += kWave) hist[b] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+  for (int i = l; i < n4; i += kWave) {
+    const float4 v = e4[i];
+    atomicAdd(&hist[bin_of(v.x)], 1u);
+    atomicAdd(&hist[bin_of(v.y)], 1u);
+    atomicAdd(&hist[bin_of(v.z)], 1u);
+    atomicAdd(&hist[bin_of(v.w)], 1u);
+  }
+  for (int i = 4 * n4 + l; i < n; i += kWave) atomicAdd(&hist[bin_of(sE[i])], 1u);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  int before_hi, before_lo;
+  const int b_hi = first_bin_reaching(hist, kBins, k - kBand, before_hi);
+  const int b_lo = first_bin_reaching(hist, kBins, k + kBand, before_lo);
+  __builtin_amdgcn_wave_barrier();
+  int na = 0, nb = 0;
+  float min_above = __builtin_inff(), max_below = -__builtin_inff();
+  for (int i0 = 0; i0 < n; i0 += kWave) {
+    const int i = i0 + l;
+    const bool in = i < n;
+    const float e = in ? sE[i] : 0.f;
+    const int32_t idx = in ? sI[i] : 0;
+    const int b = bin_of(e);
+    const bool up = in && b < b_hi;
+    const bool band = in && b >= b_hi && b <= b_lo;
+    const uint64_t mu = __ballot(up);
+    const uint64_t mb = __ballot(band);
+    if (up) {
+      const int slot = na + rank_in_mask(mu);
+      if (slot < k) emit(slot, idx);
+      min_above = __builtin_fminf(min_above, e);
+    }
+    if (in && b > b_lo) max_below = __builtin_fmaxf(max_below, e);
+    // in-place compaction: targets lie at or before this chunk, already read
+    if (band) {
+      const int pos = nb + rank_in_mask(mb);
+      sE[pos] = e;
+      sI[pos] = idx;
+    }
+    na += __popcll(mu);
+    nb += __popcll(mb);
+  }
+  min_above = wave_min(min_above);
+  max_below = wave_max(max_below);
+  const float maxabs = __builtin_fmaxf(__builtin_fabsf(mx), __builtin_fabsf(mn));
+  const int need = k - na;
+  if (na >= k || nb < need) return false;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  // exact scores of the band, 64 records at a time
+  float err = 0.f;
+  for (int b0 = 0; b0 < nb; b0 += kWave) {
+    int keyidx[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int j = b0 + 16 * t + (l & 15);
+      keyidx[t] = sI[j < nb ? j : nb - 1];
+    }
+    KeyTile kt;
+    load_keys_gather(kt, p.k, keyidx);
+    const int j = b0 + l;
+    const int jj = j < nb ? j : nb - 1;
+    const float E = score_chunk_exact(qr, kt) * p.scales[sI[jj]];
+    if (j < nb) {
+      err = __builtin_fmaxf(err, __builtin_fabsf(E - sE[j]));
+      sE[j] = E;
+    }
+  }
+  err = wave_max(err);
+  if (l == 0 && band_count)
+    atomicAdd(reinterpret_cast<unsigned long long*>(band_count), (unsigned long long)nb);
+  auto take = [&](int slot, float, int idx) { emit(na + slot, idx); };
+  const float tau = nb <= 256
+      ? small_select(sE, sI, nb, need, reinterpret_cast<float*>(hist), take)
+      : wave_select(sE, sI, nb, need, hist, take);
+  const float d = kBandSafety * __builtin_fmaxf(err, maxabs * 0x1p-18f);
+  const float below = __builtin_fmaxf(max_below, T);
+  const bool ok_above = na == 0 || min_above - d >= tau;
+  const bool ok_below = below + d <= tau;
+  return ok_above && ok_below;
+}
+
+// Per-wave setup of a block's rows; writes the output of short rows (n <= k:
+// keys 0..n-1 then -1) in the main pass. Returns the wave's union range of
+// the rows it will scan.
+__device__ __forceinline__ void setup_rows(const FusedParams& p, int b, RowState* rs, QueryRow* qr,
+                                           bool exact_pass, int& wlo, int& whi) {
+  const int w = wave_id();
   const int l = lane_id();
   const int k = p.topk;
   const int cap = (p.flags & 4u) ? k + 64 : kCap;
+  wlo = p.keys;
+  whi = 0;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    RowState& r = rs[i];
+    init_row(r, b * kBlockRows + w * kRowsPerWave + i);
+    if (r.r >= p.rows) continue;
+    row_range(p, r.r, r.s, r.e);
+    const int n = r.e - r.s;
+    if (exact_pass) {
+      if (n <= k || !p.xrow[r.r]) continue;
+      r.mode = M_EXACT;
+    } else if (n <= k) {
+      r.mode = M_SHORT;
+      int32_t* o = p.out + (int64_t)r.r * k;
+      for (int j = l; j < k; j += kWave) o[j] = j < n ? j : -1;
+      if ((p.flags & 8u) && l == 0) atomicAdd(&p.header[H_SHORT], 1u);
+      if (l == 0) p.xrow[r.r] = 0;
+      continue;
+    } else if (p.flags & 1u) {
+      r.mode = M_EXACT;  // forced: straight to the exact rescan
+    } else if (n <= 4 * k && n <= cap) {
+      r.mode = M_ALL;  // every visible key is a candidate
+    } else {
+      r.mode = M_GATED;
+    }
+    load_query(qr[i], p.q, p.weights, r.r);
+    wlo = r.s < wlo ? r.s : wlo;
+    whi = r.e > whi ? r.e : whi;
+  }
+}
+
+// Slab, merge buffers and histogram of this wave.
+__device__ __forceinline__ SlabRefs slab_refs(const FusedParams& p, FusedSmem& sm, int cap) {
+  const int w = wave_id();
+  SlabRefs sr;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int64_t slot = (int64_t)blockIdx.x * kBlockRows + w * kRowsPerWave + i;
+    sr.sE[i] = p.slabE + slot * kCap;
+    sr.sI[i] = p.slabI + slot * kCap;
+  }
+  sr.tE = p.tmpE + ((int64_t)blockIdx.x * kWaves + w) * kTmp;
+  sr.tI = p.tmpI + ((int64_t)blockIdx.x * kWaves + w) * kTmp;
+  sr.hist = sm.hist[w];
+  sr.cap = cap;
+  const int keep = 2 * p.topk;
+  sr.keep = keep < cap - kWave ? keep : cap - kWave;
+  return sr;
+}
+
+// The block's union range over the waves' rows and the OR of a per-wave flag.
+__device__ __forceinline__ void block_union(FusedSmem& sm, int wlo, int whi, int flag, int keys,
+                                            int& lo, int& hi, int& any) {
+  const int w = wave_id();
+  if (lane_id() == 0) {
+    sm.wlo[w] = wlo;
+    sm.whi[w] = whi;
+    sm.wg[w] = flag;
+  }
+  __syncthreads();
+  lo = keys;
+  hi = 0;
+  any = 0;
+  for (int i = 0; i < kWaves; ++i) {
+    lo = sm.wlo[i] < lo ? sm.wlo[i] : lo;
+    hi = sm.whi[i] > hi ? sm.whi[i] : hi;
+    any |= sm.wg[i];
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
+  __shared__ FusedSmem sm;
+  const int tid = threadIdx.x;
+  const int w = wave_id();
+  const int l = lane_id();
+  const int k = p.topk;
+  const int cap = (p.flags & 4u) ? k + 2 * kWave : kCap;
   const bool stats = p.flags & 8u;
-  float* slabE = p.slabE + (int64_t)blockIdx.x * kBlockRows * kCap;
-  int32_t* slabI = p.slabI + (int64_t)blockIdx.x * kBlockRows * kCap;
-  float* tE = p.tmpE + ((int64_t)blockIdx.x * kWaves + w) * kMaxTopk;
-  int32_t* tI = p.tmpI + ((int64_t)blockIdx.x * kWaves + w) * kMaxTopk;
+  const SlabRefs sr = slab_refs(p, sm, cap);
 
   for (;;) {
     if (tid == 0) sm.block = (int)atomicAdd(&p.header[H_CLAIM], 1u);
@@ -389,122 +566,92 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
     if (bi >= p.nblocks) break;
     const int b = p.order[bi];
 
-    // ---- per-row setup (each wave: its 4 rows)
     RowState rs[kRowsPerWave];
     QueryRow qr[kRowsPerWave];
-    int wlo = p.keys, whi = 0, wgated = 0, wexact = 0;
+    int wlo, whi;
+    setup_rows(p, b, rs, qr, false, wlo, whi);
+    int wgated = 0;
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      RowState& r = rs[i];
-      r.r = b * kBlockRows + w * kRowsPerWave + i;
-      r.cnt = 0;
-      r.strict = 0;
-      r.thr = -__builtin_inff();
-      r.have_m0 = 0;
-      r.nsamp = 0;
-      r.m0 = 0.f;
-      r.inv = 1.f;
-      if (r.r >= p.rows) {
-        r.mode = M_OFF;
-        r.s = r.e = 0;
-        continue;
-      }
-      row_range(p, r.r, r.s, r.e);
-      const int n = r.e - r.s;
-      if (n <= k) {
-        r.mode = M_SHORT;
-        int32_t* o = p.out + (int64_t)r.r * k;
-        for (int j = l; j < k; j += kWave) o[j] = j < n ? j : -1;
-        if (stats && l == 0) atomicAdd(&p.header[H_SHORT], 1u);
-        continue;
-      }
-      load_query(qr[i], p.q, p.weights, r.r);
-      wlo = r.s < wlo ? r.s : wlo;
-      whi = r.e > whi ? r.e : whi;
-      if (p.flags & 1u) {
-        r.mode = M_EXACT;
-        wexact = 1;
-      } else if (n <= 4 * k && n <= cap) {
-        r.mode = M_ALL;  // every visible key is a candidate
-      } else {
-        r.mode = M_GATED;
-        wgated = 1;
-      }
-    }
-    if (l == 0) {
-      sm.wlo[w] = wlo;
-      sm.whi[w] = whi;
-      sm.wg[w] = wgated;
-      sm.wx[w] = wexact;
-    }
-    __syncthreads();
-    int lo = p.keys, hi = 0, any_g = 0, any_x = 0;
-    for (int i = 0; i < kWaves; ++i) {
-      lo = sm.wlo[i] < lo ? sm.wlo[i] : lo;
-      hi = sm.whi[i] > hi ? sm.whi[i] : hi;
-      any_g |= sm.wg[i];
-      any_x |= sm.wx[i];
-    }
-    __syncthreads();
+    for (int i = 0; i < kRowsPerWave; ++i) wgated |= rs[i].mode == M_GATED;
+    int lo, hi, any_g;
+    block_union(sm, wlo, whi, wgated, p.keys, lo, hi, any_g);
+    int wx = 0;
     if (hi > lo) {
       if (any_g) gate_block(p, sm, qr, rs, lo, hi);
-      // ---- normal scan (all-candidate and gated rows)
-      if (!(p.flags & 1u)) {
-        scan_block<false>(p, sm, qr, rs, (1 << M_ALL) | (1 << M_GATED), lo, hi, cap, slabE, slabI,
-                          tE, tI);
-        // validity check + certified select, per row
-        int wx = 0;
+      if (!(p.flags & 1u)) scan_rows<false>(p, sm, qr, rs, M_GATED, lo, hi, sr);
+      // validity check + certified select, per row
 #pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i) {
-          RowState& r = rs[i];
-          if (r.mode != M_ALL && r.mode != M_GATED) continue;
-          const int slot = w * kRowsPerWave + i;
-          bool ok = false;
-          if (r.cnt >= k && r.cnt <= cap) {
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        RowState& r = rs[i];
+        if (r.mode == M_OFF || r.mode == M_SHORT) continue;
+        bool ok = false;
+        if (r.mode != M_EXACT) {
+          if (r.cnt >= k) {
             int32_t* o = p.out + (int64_t)r.r * k;
             const int base = r.s;
-            ok = select_banded(p, slabE + (int64_t)slot * kCap, slabI + (int64_t)slot * kCap,
-                               r.cnt, k, r.thr, qr[i], sm.hist[w],
+            ok = select_banded(p, sr.sE[i], sr.sI[i], r.cnt, k, r.thr, r.vmax, qr[i], sr.hist,
                                stats ? &p.header[H_BAND_LO] : nullptr,
                                [&](int sl, int idx) { o[sl] = idx - base; });
             if (stats && l == 0) {
               atomicAdd(&p.header[ok ? H_GATED : H_UNCERT], 1u);
-              const unsigned long long c = (unsigned long long)r.cnt;
-              atomicAdd(reinterpret_cast<unsigned long long*>(&p.header[H_CAND_LO]), c);
+              atomicAdd(reinterpret_cast<unsigned long long*>(&p.header[H_CAND_LO]),
+                        (unsigned long long)r.cnt);
             }
           } else if (stats && l == 0) {
-            atomicAdd(&p.header[r.cnt > cap ? H_OVERFLOW : H_UNDER], 1u);
-          }
-          if (!ok) {
-            r.mode = M_EXACT;
-            r.cnt = 0;
-            r.thr = -__builtin_inff();
-            r.strict = 0;
-            wx = 1;
+            atomicAdd(&p.header[H_UNDER], 1u);
           }
         }
-        if (l == 0) sm.wx[w] = wx;
-        __syncthreads();
-        any_x = 0;
-        for (int i = 0; i < kWaves; ++i) any_x |= sm.wx[i];
-        __syncthreads();
+        if (l == 0) p.xrow[r.r] = ok ? 0 : 1;
+        wx |= !ok;
       }
-      // ---- exact streaming rescan for the rows that need it
-      if (any_x) {
-        scan_block<true>(p, sm, qr, rs, 1 << M_EXACT, lo, hi, cap, slabE, slabI, tE, tI);
+    }
+    if (l == 0) sm.wx[w] = wx;
+    __syncthreads();
+    if (tid == 0) {
+      int any_x = 0;
+      for (int i = 0; i < kWaves; ++i) any_x |= sm.wx[i];
+      if (any_x) p.xqueue[atomicAdd(&p.header[H_XQ], 1u)] = b;
+    }
+    __syncthreads();
+  }
+}
+
+// Exact rescan of the queued blocks: exact (bf16 MFMA) scores of every key of
+// the flagged rows with a streaming top-k merge, then an exact select.
+__global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
+  __shared__ FusedSmem sm;
+  const int tid = threadIdx.x;
+  const int l = lane_id();
+  const int k = p.topk;
+  const int cap = (p.flags & 4u) ? k + 2 * kWave : kCap;
+  const int nq = (int)p.header[H_XQ];
+  SlabRefs sr = slab_refs(p, sm, cap);
+  sr.keep = k;
+  for (;;) {
+    if (tid == 0) sm.block = (int)atomicAdd(&p.header[H_XCLAIM], 1u);
+    __syncthreads();
+    const int qi = sm.block;
+    if (qi >= nq) break;
+    const int b = p.xqueue[qi];
+    RowState rs[kRowsPerWave];
+    QueryRow qr[kRowsPerWave];
+    int wlo, whi;
+    setup_rows(p, b, rs, qr, true, wlo, whi);
+    int lo, hi, unused;
+    block_union(sm, wlo, whi, 0, p.keys, lo, hi, unused);
+    if (hi > lo) {
+      scan_rows<true>(p, sm, qr, rs, M_EXACT, lo, hi, sr);
 #pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i) {
-          RowState& r = rs[i];
-          if (r.mode != M_EXACT) continue;
-          const int slot = w * kRowsPerWave + i;
-          int32_t* o = p.out + (int64_t)r.r * k;
-          const int base = r.s;
-          const int have = r.cnt < cap ? r.cnt : cap;
-          wave_select(slabE + (int64_t)slot * kCap, slabI + (int64_t)slot * kCap, have, k,
-                      sm.hist[w], [&](int sl, float, int idx) { o[sl] = idx - base; });
-          for (int j = have + l; j < k; j += kWave) o[j] = -1;
-          if (stats && l == 0) atomicAdd(&p.header[H_EXACT], 1u);
-        }
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        RowState& r = rs[i];
+        if (r.mode != M_EXACT) continue;
+        int32_t* o = p.out + (int64_t)r.r * k;
+        const int base = r.s;
+        const int have = r.cnt < cap ? r.cnt : cap;
+        wave_select(sr.sE[i], sr.sI[i], have, k, sr.hist,
+                    [&](int sl, float, int idx) { o[sl] = idx - base; });
+        for (int j = have + l; j < k; j += kWave) o[j] = -1;
+        if ((p.flags & 8u) && l == 0) atomicAdd(&p.header[H_EXACT], 1u);
       }
     }
     __syncthreads();
@@ -518,10 +665,19 @@ extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL(mqa::fused_topk_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  hipLaunchKernelGGL(mqa::fused_exact_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
   return (int)hipGetLastError();
 }
 
 extern "C" int mqa_fused_occupancy(int* wg_per_cu) {
-  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(wg_per_cu, mqa::fused_topk_kernel,
-                                                           mqa::kThreads, 0);
+  int a = 0, b = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, mqa::fused_topk_kernel,
+                                                              mqa::kThreads, 0);
+  if (e != hipSuccess) return (int)e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, mqa::fused_exact_kernel, mqa::kThreads, 0);
+  if (e != hipSuccess) return (int)e;
+  *wg_per_cu = a < b ? a : b;
+  return 0;
 }

@@ -19,9 +19,11 @@ struct FusedParams {
   unsigned flags;
   uint32_t* header;  // 64 words: stats + claim counter
   int32_t* order;    // [nblocks] heaviest-first block order
+  uint8_t* xrow;     // [rows] 1 = the row needs the exact rescan
+  int32_t* xqueue;   // [nblocks] blocks queued for the exact rescan
   float* slabE;      // [grid][32 rows][16384] candidate scores
   int32_t* slabI;    // [grid][32 rows][16384] candidate keys
-  float* tmpE;       // [grid][8 waves][2048] compaction buffers
+  float* tmpE;       // [grid][8 waves][kTmp] merge buffers
   int32_t* tmpI;
 };
 
@@ -48,6 +50,7 @@ struct DenseTopkParams {
 };
 
 constexpr int kFusedBlockRows = 32;
+constexpr int kTmp = 4096;  // merge-buffer records per wave
 constexpr int kFusedWaves = 8;
 
 }  // namespace mqa

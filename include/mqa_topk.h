@@ -59,7 +59,7 @@ extern "C" {
  * does": exact rescan) so that tests can reach it. */
 #define MQA_FLAG_FORCE_EXACT 1u     /* every row takes the exact streaming rescan */
 #define MQA_FLAG_FORCE_GATE_MISS 2u /* the gate admits nothing: every gated row falls back */
-#define MQA_FLAG_SMALL_CAP 4u       /* per-row candidate slab limited to topk + 64 */
+#define MQA_FLAG_SMALL_CAP 4u       /* per-row candidate slab limited to topk + 128 */
 #define MQA_FLAG_STATS 8u           /* fill the mqa_stats header of the workspace */
 
 /* Counters written to the first bytes of the workspace when MQA_FLAG_STATS is
@@ -69,9 +69,9 @@ typedef struct mqa_stats {
   uint32_t rows_short;      /* rows with n <= k (no scoring) */
   uint32_t rows_gated;      /* rows served by the gate + certified select */
   uint32_t rows_exact;      /* rows served by the exact streaming rescan */
-  uint32_t rows_overflow;   /* gated rows whose candidates overflowed the slab */
+  uint32_t rows_overflow;   /* unused (a full slab is merged in place) */
   uint32_t rows_undercount; /* gated rows with fewer than k candidates */
-  uint32_t compactions;     /* streaming-rescan compactions */
+  uint32_t compactions;     /* slab merges (keep the best records, raise the threshold) */
   uint32_t rows_uncertified;/* gated rows whose exact band could not certify the cut */
   uint64_t candidates;      /* candidates emitted by gated rows */
   uint64_t band_keys;       /* keys rescored exactly around the rows' k-th scores */
