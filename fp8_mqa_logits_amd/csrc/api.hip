@@ -13,7 +13,6 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kHeaderWords = 64;
-constexpr size_t kCap = 16384;
 
 thread_local char g_err[256] = "";
 
@@ -79,7 +78,7 @@ Layout layout(int rows, const DeviceInfo& d) {
   off = align_up(off + (size_t)rows);
   L.xqueue = off;
   off = align_up(off + (size_t)L.nblocks * 4);
-  const size_t slab = (size_t)L.grid * mqa::kFusedBlockRows * kCap * 4;
+  const size_t slab = (size_t)L.grid * mqa::kFusedBlockRows * mqa::kSlabRow * 4;
   L.slabE = off;
   off = align_up(off + slab);
   L.slabI = off;

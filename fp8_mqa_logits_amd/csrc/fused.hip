@@ -49,6 +49,12 @@ enum : int {
 
 enum RowMode : int { M_OFF = 0, M_SHORT = 1, M_ALL = 2, M_GATED = 3, M_EXACT = 4 };
 
+// Candidate capacity of a slab row (SMALL_CAP: just above k, to exercise the
+// merges in tests).
+__device__ __forceinline__ int slab_cap(const FusedParams& p) {
+  return (p.flags & 4u) ? p.topk + 2 * kWave : kCap;
+}
+
 __device__ __forceinline__ void row_range(const FusedParams& p, int r, int& s, int& e) {
   int a = p.starts[r], b = p.ends[r];
   a = a < 0 ? 0 : (a > p.keys ? p.keys : a);
@@ -139,44 +145,21 @@ __device__ __forceinline__ void init_row(RowState& r, int row) {
   r.vmax = -__builtin_inff();
 }
 
-// Append the passing lanes of one chunk to a row's slab. A slab that would
-// overflow is first compacted to the row's `keep` best records by score and
-// the admission threshold rises to the smallest of them (a streaming top-k
-// merge; later records must beat it strictly).
-__device__ __forceinline__ void emit_merge(const FusedParams& p, RowState& rs, float E, bool valid,
-                                           int key, int cap, int keep, float* sE, int32_t* sI,
-                                           float* tE, int32_t* tI, uint32_t* hist) {
-  bool pass = valid && (rs.strict ? (E > rs.thr) : (E >= rs.thr));
-  uint64_t m = __ballot(pass);
+// Append the passing lanes of one chunk to a row's slab. A slab row has
+// kSlack records of room past `cap`, so one chunk always fits; a row that
+// went past `cap` is merged down once the whole chunk is scored (merge_rows).
+__device__ __forceinline__ void emit_rec(RowState& rs, float E, bool valid, int key, float* sE,
+                                         int32_t* sI) {
+  const bool pass = valid && (rs.strict ? (E > rs.thr) : (E >= rs.thr));
+  const uint64_t m = __ballot(pass);
   if (m == 0) return;
-  int c = __popcll(m);
-  if (rs.cnt + c > cap) {
-    const float kth = wave_select(sE, sI, rs.cnt, keep, hist, [&](int slot, float e, int idx) {
-      tE[slot] = e;
-      tI[slot] = idx;
-    });
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    for (int i = lane_id(); i < keep; i += kWave) {
-      sE[i] = tE[i];
-      sI[i] = tI[i];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    rs.cnt = keep;
-    rs.thr = kth;
-    rs.strict = 1;
-    if ((p.flags & 8u) && lane_id() == 0) atomicAdd(&p.header[H_COMPACT], 1u);
-    pass = valid && E > rs.thr;
-    m = __ballot(pass);
-    if (m == 0) return;
-    c = __popcll(m);
-  }
   if (pass) {
-    const int pos = rs.cnt + rank_in_mask(m);
+    const unsigned pos = (unsigned)(rs.cnt + rank_in_mask(m));
     sE[pos] = E;
     sI[pos] = key;
     rs.vmax = __builtin_fmaxf(rs.vmax, E);
   }
-  rs.cnt += c;
+  rs.cnt += __popcll(m);
 }
 
 __device__ __forceinline__ bool row_in_chunk(const RowState& r, int mode, int key0) {
@@ -197,7 +180,50 @@ __device__ __forceinline__ void finish_row(const FusedParams& p, RowState& r, fl
                                            int key0, const SlabRefs& sr, int i) {
   const bool full = r.s <= key0 && key0 + kChunk <= r.e;
   const bool valid = full || (key >= r.s && key < r.e);
-  emit_merge(p, r, E, valid, key, sr.cap, sr.keep, sr.sE[i], sr.sI[i], sr.tE, sr.tI, sr.hist);
+  emit_rec(r, E, valid, key, sr.sE[i], sr.sI[i]);
+}
+
+// Streaming top-k merge: every row whose slab went past `cap` is cut down to
+// its `keep` best records by score, and its admission threshold rises to the
+// smallest of them (later records must beat it strictly). One merge site for
+// the wave's rows, so the select code appears once in the scan loop.
+__device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, const SlabRefs& sr) {
+  unsigned todo = 0;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) todo |= (rs[i].cnt > sr.cap ? 1u : 0u) << i;
+  while (todo) {
+    const int i = __builtin_ctz(todo);
+    todo &= todo - 1;
+    float* sE = sr.sE[0];
+    int32_t* sI = sr.sI[0];
+    int cnt = rs[0].cnt;
+#pragma unroll
+    for (int j = 1; j < kRowsPerWave; ++j)
+      if (i == j) {
+        sE = sr.sE[j];
+        sI = sr.sI[j];
+        cnt = rs[j].cnt;
+      }
+    const float kth = wave_select(sE, sI, cnt, sr.keep, sr.hist,
+                                  [&](int slot, float e, int idx) {
+                                    sr.tE[slot] = e;
+                                    sr.tI[slot] = idx;
+                                  });
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    for (int t = lane_id(); t < sr.keep; t += kWave) {
+      sE[t] = sr.tE[t];
+      sI[t] = sr.tI[t];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j)
+      if (i == j) {
+        rs[j].cnt = sr.keep;
+        rs[j].thr = kth;
+        rs[j].strict = 1;
+      }
+    if ((p.flags & 8u) && lane_id() == 0) atomicAdd(&p.header[H_COMPACT], 1u);
+  }
 }
 
 // One scan of keys [lo, hi) for the rows of this wave in `mode` (M_ALL and
@@ -253,6 +279,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, FusedSmem& sm, c
         if (act[2]) finish_row(p, rs[2], reduce_heads(qr[2], a0) * sc, key, key0, sr, 2);
         if (act[3]) finish_row(p, rs[3], reduce_heads(qr[3], a1) * sc, key, key0, sr, 3);
       }
+      merge_rows(p, rs, sr);
     }
     if (more) {
       store_chunk_regs(regs, sm.kbuf[(c + 1) & 1], tid, kThreads);
@@ -476,7 +503,7 @@ __device__ __forceinline__ void setup_rows(const FusedParams& p, int b, RowState
   const int w = wave_id();
   const int l = lane_id();
   const int k = p.topk;
-  const int cap = (p.flags & 4u) ? k + 64 : kCap;
+  const int cap = slab_cap(p);
   wlo = p.keys;
   whi = 0;
 #pragma unroll
@@ -516,8 +543,8 @@ __device__ __forceinline__ SlabRefs slab_refs(const FusedParams& p, FusedSmem& s
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
     const int64_t slot = (int64_t)blockIdx.x * kBlockRows + w * kRowsPerWave + i;
-    sr.sE[i] = p.slabE + slot * kCap;
-    sr.sI[i] = p.slabI + slot * kCap;
+    sr.sE[i] = p.slabE + slot * kSlabRow;
+    sr.sI[i] = p.slabI + slot * kSlabRow;
   }
   sr.tE = p.tmpE + ((int64_t)blockIdx.x * kWaves + w) * kTmp;
   sr.tI = p.tmpI + ((int64_t)blockIdx.x * kWaves + w) * kTmp;
@@ -555,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
   const int w = wave_id();
   const int l = lane_id();
   const int k = p.topk;
-  const int cap = (p.flags & 4u) ? k + 2 * kWave : kCap;
+  const int cap = slab_cap(p);
   const bool stats = p.flags & 8u;
   const SlabRefs sr = slab_refs(p, sm, cap);
 
@@ -623,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
   const int tid = threadIdx.x;
   const int l = lane_id();
   const int k = p.topk;
-  const int cap = (p.flags & 4u) ? k + 2 * kWave : kCap;
+  const int cap = slab_cap(p);
   const int nq = (int)p.header[H_XQ];
   SlabRefs sr = slab_refs(p, sm, cap);
   sr.keep = k;
@@ -647,7 +674,7 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
         if (r.mode != M_EXACT) continue;
         int32_t* o = p.out + (int64_t)r.r * k;
         const int base = r.s;
-        const int have = r.cnt < cap ? r.cnt : cap;
+        const int have = r.cnt;
         wave_select(sr.sE[i], sr.sI[i], have, k, sr.hist,
                     [&](int sl, float, int idx) { o[sl] = idx - base; });
         for (int j = have + l; j < k; j += kWave) o[j] = -1;

@@ -21,8 +21,8 @@ struct FusedParams {
   int32_t* order;    // [nblocks] heaviest-first block order
   uint8_t* xrow;     // [rows] 1 = the row needs the exact rescan
   int32_t* xqueue;   // [nblocks] blocks queued for the exact rescan
-  float* slabE;      // [grid][32 rows][16384] candidate scores
-  int32_t* slabI;    // [grid][32 rows][16384] candidate keys
+  float* slabE;      // [grid][32 rows][kSlabRow] candidate scores
+  int32_t* slabI;    // [grid][32 rows][kSlabRow] candidate keys
   float* tmpE;       // [grid][8 waves][kTmp] merge buffers
   int32_t* tmpI;
 };
@@ -51,6 +51,9 @@ struct DenseTopkParams {
 
 constexpr int kFusedBlockRows = 32;
 constexpr int kTmp = 4096;  // merge-buffer records per wave
+// Records per slab row: a capacity of 16384 plus room for one more chunk of
+// 64 records past it (rows stay 1 KiB aligned).
+constexpr int kSlabRow = 16384 + 256;
 constexpr int kFusedWaves = 8;
 
 }  // namespace mqa
