@@ -168,6 +168,164 @@ __device__ __forceinline__ float reduce_heads(const QueryRow& qr, const RowAcc& 
   return __uint_as_float(s4[0]) + __uint_as_float(s4[1]);
 }
 
+// ---------------------------------------------------------------------------
+// relu fold (vLLM PR #60618, "What this PR does"): relu(s) = (s + |s|) / 2, so
+//   sum_h w_h relu(s_h) = ( sum_h w_h s_h + sum_h w_h |s_h| ) / 2
+// and the linear half is one dot product of the key with the folded query
+// f = sum_h w_h q_h. f (fp32) is carried as 4 e4m3 terms, each with a
+// power-of-two scale per 32-element block of the MFMA's K order (its E8M0 A
+// scales):
+// term t encodes what terms 0..t-1 left over, so the sum of the terms
+// matches f to about 2^-16 of each block's largest magnitude. The 4 terms of
+// the wave's 4 rows are the 16 A rows of one extra MFMA per 16 keys: M row
+// 4r + t = term t of row r. The head epilogue then only accumulates |s|.
+
+struct FoldOp {
+  v8i fa;      // this lane's 32 e4m3 codes: M row (l%16), dims 32*(l/16) ..
+  int fscale;  // E8M0 scale byte of those codes
+};
+
+__device__ __forceinline__ float e4m3_to_f32(int word, int byte) {
+  switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8(word, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8(word, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8(word, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8(word, 3);
+  }
+}
+
+// Builds this lane's fold operand for the wave's rows rows[0..3] (-1: unused
+// row, zero terms). Lane l covers row (l%16)/4, term (l%16)%4, dims
+// 32*(l/16) .. +31.
+__device__ __forceinline__ void build_fold(FoldOp& fo, const uint8_t* __restrict__ q,
+                                           const float* __restrict__ weights, const int* rows) {
+  const int l = lane_id();
+  const int m = l & 15;
+  const int rr = m >> 2;
+  const int term = m & 3;
+  const int g = l >> 4;
+  int row = rows[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+    if (rr == i) row = rows[i];
+  float rho[32];
+#pragma unroll
+  for (int d = 0; d < 32; ++d) rho[d] = 0.f;
+  if (row >= 0) {
+    for (int h = 0; h < kHeads; ++h) {
+      const float wv = weights[(int64_t)row * kHeads + h];
+      const int* qp = reinterpret_cast<const int*>(q + ((int64_t)row * kHeads + h) * kDim + 32 * g);
+#pragma unroll
+      for (int d4 = 0; d4 < 8; ++d4) {
+        const int word = qp[d4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          rho[4 * d4 + b] = __builtin_fmaf(wv, e4m3_to_f32(word, b), rho[4 * d4 + b]);
+      }
+    }
+  }
+  // Scale blocks follow the MFMA's K order: lane group g's bytes 0-15 and
+  // 16-31 fall in the 32-wide blocks g/2 and 2 + g/2, each shared with the
+  // same half of lane group g^1; block b's scale for A row m is read from
+  // lane 16*b + m (both measured on gfx950).
+  int codes[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int e_kept[2] = {0, 0};
+  auto exponent_for = [](float mx) {  // smallest e with mx * 2^-e <= 448
+    int e = 0;
+    if (mx > 0.f) {
+      int ex;
+      (void)__builtin_frexpf(mx / 448.f, &ex);
+      e = ex;
+      if (__builtin_ldexpf(448.f, e) < mx) e += 1;
+      if (__builtin_ldexpf(448.f, e - 1) >= mx) e -= 1;
+    }
+    return e < -100 ? -100 : (e > 100 ? 100 : e);
+  };
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float hm[2] = {0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < 32; ++d) hm[d >> 4] = __builtin_fmaxf(hm[d >> 4], __builtin_fabsf(rho[d]));
+    int e[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) e[h] = exponent_for(__builtin_fmaxf(hm[h], __shfl_xor(hm[h], 16, 64)));
+    int cw[8];
+#pragma unroll
+    for (int d4 = 0; d4 < 8; ++d4) {
+      const int h = d4 >> 2;
+      const float down = __builtin_ldexpf(1.f, -e[h]);
+      const float up = __builtin_ldexpf(1.f, e[h]);
+      int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(rho[4 * d4] * down, rho[4 * d4 + 1] * down, 0, false);
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(rho[4 * d4 + 2] * down, rho[4 * d4 + 3] * down, w0, true);
+      cw[d4] = w0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) rho[4 * d4 + b] -= e4m3_to_f32(w0, b) * up;
+    }
+    if (t == term) {
+#pragma unroll
+      for (int d4 = 0; d4 < 8; ++d4) codes[d4] = cw[d4];
+      e_kept[0] = e[0];
+      e_kept[1] = e[1];
+    }
+  }
+  // the scale this lane supplies: block g, whose halves live in lane groups
+  // {0,1} (blocks 0, 2) or {2,3} (blocks 1, 3)
+  const int from_g2 = __shfl(e_kept[0], m + 32, 64);  // block 1: half 0 of group 2
+  const int from_g0 = __shfl(e_kept[1], m, 64);       // block 2: half 1 of group 0
+  const int es = g == 0 ? e_kept[0] : (g == 1 ? from_g2 : (g == 2 ? from_g0 : e_kept[1]));
+  fo.fa = v8i{codes[0], codes[1], codes[2], codes[3], codes[4], codes[5], codes[6], codes[7]};
+  fo.fscale = 127 + es;
+}
+
+// Linear halves L = f . k of the wave's 4 rows for a 64-key chunk: 4 scaled
+// MFMAs (one per 16-key sub-tile), the 4 terms summed per lane, then a 4x4
+// transpose of lane groups so that L[r] holds row r with lane l <-> key l.
+__device__ __forceinline__ void fold_linear(float L[4], const FoldOp& fo, const KeyTile& kt) {
+  float x[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
+    const v4f c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fo.fa, kt.kb[t], z, 0, 0, 0,
+                                                                    fo.fscale, 0, 127);
+    x[t] = (c[0] + c[1]) + (c[2] + c[3]);  // lane group g: row g, sub-tile t
+  }
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[0]), __float_as_uint(x[2]),
+                                                  false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[1]), __float_as_uint(x[3]),
+                                                  false, false);
+  const auto c01 = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto c23 = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  L[0] = __uint_as_float(c01[0]);
+  L[1] = __uint_as_float(c01[1]);
+  L[2] = __uint_as_float(c23[0]);
+  L[3] = __uint_as_float(c23[1]);
+}
+
+// Weighted |s| sum over the lane's 8 heads of each sub-tile (one abs-modified
+// FMA per head), reduced across lane groups like reduce_heads.
+__device__ __forceinline__ float reduce_heads_abs(const QueryRow& qr, const RowAcc& acc) {
+  float part[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s = __builtin_fmaf(qr.w[v], __builtin_fabsf(acc.a[t][0][v]), s);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      s = __builtin_fmaf(qr.w[4 + v], __builtin_fabsf(acc.a[t][1][v]), s);
+    part[t] = s;
+  }
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
+                                                    __float_as_uint(part[2]), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]),
+                                                    __float_as_uint(part[3]), false, false);
+  const float y02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float y13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  const auto s4 = __builtin_amdgcn_permlane16_swap(__float_as_uint(y02), __float_as_uint(y13),
+                                                   false, false);
+  return __uint_as_float(s4[0]) + __uint_as_float(s4[1]);
+}
+
 // Unscaled score sum_h w[r,h] * relu(q[r,h,:] . k[j,:]) of key j = lane id
 // of the chunk, for one query row, from FP8 MFMA head dots.
 __device__ __forceinline__ float score_chunk(const QueryRow& qr, const KeyTile& kt) {

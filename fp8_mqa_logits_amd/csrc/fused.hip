@@ -232,8 +232,8 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
 // before the epilogue of the current one.
 template <bool EXACT>
 __device__ __forceinline__ void scan_rows(const FusedParams& p, FusedSmem& sm, const QueryRow* qr,
-                                          RowState* rs, int mode, int lo, int hi,
-                                          const SlabRefs& sr) {
+                                          const FoldOp& fo, RowState* rs, int mode, int lo,
+                                          int hi, const SlabRefs& sr) {
   const int tid = threadIdx.x;
   const int l = lane_id();
   const int nch = (hi - lo + kChunk - 1) / kChunk;
@@ -269,15 +269,25 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, FusedSmem& sm, c
         for (int i = 0; i < kRowsPerWave; ++i)
           if (act[i]) finish_row(p, rs[i], score_chunk_exact(qr[i], kt) * sc, key, key0, sr, i);
       } else {
+        // One branch-free block computes the four rows' score vectors (the
+        // next row's MFMAs overlap the current row's epilogue); rows that are
+        // not live in this chunk are computed from zeroed operands and never
+        // emit. score = (f.k + sum_h w_h |s_h|) / 2 * scale
+        const float sch = 0.5f * sc;
+        float L[4], E[4];
         RowAcc a0, a1;
-        if (act[0]) mfma_row(a0, qr[0], kt);
-        if (act[1]) mfma_row(a1, qr[1], kt);
-        if (act[0]) finish_row(p, rs[0], reduce_heads(qr[0], a0) * sc, key, key0, sr, 0);
-        if (act[2]) mfma_row(a0, qr[2], kt);
-        if (act[1]) finish_row(p, rs[1], reduce_heads(qr[1], a1) * sc, key, key0, sr, 1);
-        if (act[3]) mfma_row(a1, qr[3], kt);
-        if (act[2]) finish_row(p, rs[2], reduce_heads(qr[2], a0) * sc, key, key0, sr, 2);
-        if (act[3]) finish_row(p, rs[3], reduce_heads(qr[3], a1) * sc, key, key0, sr, 3);
+        fold_linear(L, fo, kt);
+        mfma_row(a0, qr[0], kt);
+        mfma_row(a1, qr[1], kt);
+        E[0] = (L[0] + reduce_heads_abs(qr[0], a0)) * sch;
+        mfma_row(a0, qr[2], kt);
+        E[1] = (L[1] + reduce_heads_abs(qr[1], a1)) * sch;
+        mfma_row(a1, qr[3], kt);
+        E[2] = (L[2] + reduce_heads_abs(qr[2], a0)) * sch;
+        E[3] = (L[3] + reduce_heads_abs(qr[3], a1)) * sch;
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i)
+          if (act[i]) finish_row(p, rs[i], E[i], key, key0, sr, i);
       }
       merge_rows(p, rs, sr);
     }
@@ -510,6 +520,9 @@ __device__ __forceinline__ void setup_rows(const FusedParams& p, int b, RowState
   for (int i = 0; i < kRowsPerWave; ++i) {
     RowState& r = rs[i];
     init_row(r, b * kBlockRows + w * kRowsPerWave + i);
+    qr[i].qa[0] = qr[i].qa[1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int v = 0; v < 8; ++v) qr[i].w[v] = 0.f;
     if (r.r >= p.rows) continue;
     row_range(p, r.r, r.s, r.e);
     const int n = r.e - r.s;
@@ -605,7 +618,15 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
     int wx = 0;
     if (hi > lo) {
       if (any_g) gate_block(p, sm, qr, rs, lo, hi);
-      if (!(p.flags & 1u)) scan_rows<false>(p, sm, qr, rs, M_GATED, lo, hi, sr);
+      if (!(p.flags & 1u)) {
+        int frows[kRowsPerWave];
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i)
+          frows[i] = (rs[i].mode == M_ALL || rs[i].mode == M_GATED) ? rs[i].r : -1;
+        FoldOp fo;
+        build_fold(fo, p.q, p.weights, frows);
+        scan_rows<false>(p, sm, qr, fo, rs, M_GATED, lo, hi, sr);
+      }
       // validity check + certified select, per row
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
@@ -667,7 +688,8 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
     int lo, hi, unused;
     block_union(sm, wlo, whi, 0, p.keys, lo, hi, unused);
     if (hi > lo) {
-      scan_rows<true>(p, sm, qr, rs, M_EXACT, lo, hi, sr);
+      FoldOp none;
+      scan_rows<true>(p, sm, qr, none, rs, M_EXACT, lo, hi, sr);
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         RowState& r = rs[i];
