@@ -6,15 +6,21 @@ chunk (row i sees keys [0, 114689 + i), top-2048), inputs resident in HBM.
 Prints ONE JSON line (rank 0):
   value    = visible (row, key) scores per second (sum of the rows' visible
              keys / seconds per step);
-  roofline = FP8 MFMA roofline of the fused kernel: 8192 flop per visible
-             pair (2 * 32 heads * 128 dims) / its average duration, against
-             the MI355X dense FP8 peak (5.0 PFLOP/s); traffic = HBM bytes per
-             launch from the committed rocprofv3 counter summary when it was
-             taken on the current kernel sources, else null;
+  roofline = FP8 MFMA roofline of the scan kernel (the dominant one of the
+             call's three launches): 8192 flop per visible pair (2 * 32 heads *
+             128 dims) over its average duration, timed with HIP events that
+             the library records on the call's stream around that kernel
+             (MQA_FLAG_TIME_SCAN) during the timed steps, against the MI355X
+             dense FP8 peak (5.0 PFLOP/s); traffic = HBM bytes per launch from
+             the committed rocprofv3 counter summary when it was taken on the
+             current kernel sources, else null;
   cpu_baseline = the CPU oracle (exact logits + full sort) timed on this
              host's cores over a bounded sample of the same rows.
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu,
---dense (also time the chunked dense logits + top-k path, for context).
+--dense (also time the chunked dense logits + top-k path, for context),
+--config N (workload 1..5), --copy-calibration MIB (instead of the benchmark,
+run a plain 1-D device copy of MIB MiB five times: the known-size kernel that
+scales rocprofv3's FETCH_SIZE / WRITE_SIZE readings to bytes).
 """
 from __future__ import annotations
 
@@ -140,6 +146,7 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--dense", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this path runs on one GPU; multi-GPU runs are not supported "
@@ -147,6 +154,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
 
     sys.path.insert(0, ROOT)
     import fp8_mqa_logits_amd as mqa
@@ -183,13 +200,14 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(args.steps):
-        step()
+        step(mqa.FLAG_TIME_SCAN)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    scan_ms = mqa.scan_time_ms(args.steps) / args.steps
     pairs = wl.visible_pairs()
     value = pairs / (ms / 1e3)
-    achieved = pairs * FLOP_PER_PAIR / (ms / 1e3) / 1e12
+    achieved = pairs * FLOP_PER_PAIR / (scan_ms / 1e3) / 1e12
     line = {
         "metric": "(row,key) scores/s + % FP8 MFMA peak, top-2048, 16K rows x 128K keys",
         "value": value,
@@ -207,7 +225,8 @@ def main():
                    "visible_pairs": pairs, "parallelism": "1 GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS,
-                     "traffic": traffic_from_counters()},
+                     "traffic": traffic_from_counters(), "kernel": "fused_topk_kernel",
+                     "kernel_ms": scan_ms},
         "path_stats": stats,
     }
     if args.dense:

@@ -23,12 +23,13 @@ FLAG_FORCE_EXACT = 1
 FLAG_FORCE_GATE_MISS = 2
 FLAG_SMALL_CAP = 4
 FLAG_STATS = 8
+FLAG_TIME_SCAN = 16
 
 ERR_NAMES = {0: "MQA_OK", 1: "MQA_ERR_NULL", 2: "MQA_ERR_ALIGN", 3: "MQA_ERR_SHAPE",
              4: "MQA_ERR_WORKSPACE", 5: "MQA_ERR_DEVICE", 6: "MQA_ERR_LAUNCH"}
 
 EXPORTS = ("workspace_size", "mqa_topk_prefill", "mqa_logits_dense", "mqa_topk_dense",
-           "mqa_key_scales", "mqa_strerror")
+           "mqa_key_scales", "mqa_scan_time", "mqa_strerror")
 
 
 class MQAError(RuntimeError):
@@ -64,6 +65,8 @@ def load() -> ctypes.CDLL:
         lib.mqa_topk_dense.restype = I
         lib.mqa_key_scales.argtypes = [P, P, I, P]
         lib.mqa_key_scales.restype = I
+        lib.mqa_scan_time.argtypes = [I, P]
+        lib.mqa_scan_time.restype = I
         lib.mqa_strerror.argtypes = [I]
         lib.mqa_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -203,6 +206,14 @@ def mqa_key_scales(scale_bytes, out=None, stream=None) -> torch.Tensor:
         rc = load().mqa_key_scales(_ptr(scale_bytes), _ptr(out), keys, _stream(dev, stream))
     _check(rc, "mqa_key_scales")
     return out
+
+
+def scan_time_ms(last_n: int) -> float:
+    """Total scan-kernel time (ms) of the last `last_n` calls made with
+    FLAG_TIME_SCAN on the current device (waits for them to finish)."""
+    v = ctypes.c_float(0.0)
+    _check(load().mqa_scan_time(int(last_n), ctypes.byref(v)), "mqa_scan_time")
+    return float(v.value)
 
 
 def read_stats(workspace: torch.Tensor) -> dict:

@@ -109,6 +109,36 @@ const DeviceInfo* current_device() {
 
 bool topk_ok(int topk) { return topk == 512 || topk == 1024 || topk == 2048; }
 
+// Per-device ring of event pairs recorded around the scan kernel by calls made
+// with MQA_FLAG_TIME_SCAN (created on first use, kept until the process ends).
+constexpr int kRing = 256;
+struct TimingRing {
+  bool made = false;
+  hipEvent_t b[kRing], e[kRing];
+  int next = 0, count = 0;
+};
+TimingRing g_ring[64];
+
+// Event pair for the next timed call on `device`; false if events cannot be made.
+bool ring_slot(int device, hipEvent_t* b, hipEvent_t* e) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  TimingRing& r = g_ring[device];
+  if (!r.made) {
+    for (int i = 0; i < kRing; ++i) {
+      if (hipEventCreate(&r.b[i]) != hipSuccess || hipEventCreate(&r.e[i]) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+      }
+    }
+    r.made = true;
+  }
+  *b = r.b[r.next];
+  *e = r.e[r.next];
+  r.next = (r.next + 1) % kRing;
+  r.count = r.count < kRing ? r.count + 1 : kRing;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -158,7 +188,13 @@ int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
   p.tmpE = reinterpret_cast<float*>(ws + L.tmpE);
   p.tmpI = reinterpret_cast<int32_t*>(ws + L.tmpI);
   const int grid = L.grid < L.nblocks ? L.grid : L.nblocks;
-  const int rc = mqa_fused_launch(&p, grid, static_cast<hipStream_t>(stream));
+  hipEvent_t eb = nullptr, ee = nullptr;
+  if (flags & MQA_FLAG_TIME_SCAN) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (!ring_slot(dev, &eb, &ee)) return MQA_ERR_DEVICE;
+  }
+  const int rc = mqa_fused_launch(&p, grid, static_cast<hipStream_t>(stream), eb, ee);
   if (rc != 0) return launch_error(rc);
   return MQA_OK;
 }
@@ -204,6 +240,29 @@ int mqa_key_scales(const uint8_t* scale_bytes, float* scales, int keys, void* st
   if (!current_device()) return MQA_ERR_DEVICE;
   const int rc = mqa_key_scales_launch(scale_bytes, scales, keys, static_cast<hipStream_t>(stream));
   if (rc != 0) return launch_error(rc);
+  return MQA_OK;
+}
+
+int mqa_scan_time(int last_n, float* total_ms) {
+  if (!total_ms) return MQA_ERR_NULL;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return MQA_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(g_mu);
+  const TimingRing& r = g_ring[dev];
+  if (last_n < 1 || last_n > r.count) return MQA_ERR_SHAPE;
+  double sum = 0.0;
+  for (int i = 1; i <= last_n; ++i) {
+    const int s = (r.next - i + kRing) % kRing;
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.e[s]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.b[s], r.e[s]);
+    if (e != hipSuccess) return launch_error((int)e);
+    sum += ms;
+  }
+  *total_ms = (float)sum;
   return MQA_OK;
 }
 

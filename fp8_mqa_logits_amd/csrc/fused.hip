@@ -709,13 +709,16 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
 
 }  // namespace mqa
 
-extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t stream) {
+extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t stream,
+                                hipEvent_t scan_begin, hipEvent_t scan_end) {
   hipLaunchKernelGGL(mqa::fused_plan_kernel, dim3(1), dim3(1024), 0, stream, *p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
+  if (scan_begin && (e = hipEventRecord(scan_begin, stream)) != hipSuccess) return (int)e;
   hipLaunchKernelGGL(mqa::fused_topk_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
   e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
+  if (scan_end && (e = hipEventRecord(scan_end, stream)) != hipSuccess) return (int)e;
   hipLaunchKernelGGL(mqa::fused_exact_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
   return (int)hipGetLastError();
 }

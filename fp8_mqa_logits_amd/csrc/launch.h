@@ -59,7 +59,9 @@ constexpr int kFusedWaves = 8;
 }  // namespace mqa
 
 extern "C" {
-int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t stream);
+// scan_begin/scan_end: optional events recorded around the scan kernel.
+int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t stream,
+                     hipEvent_t scan_begin, hipEvent_t scan_end);
 int mqa_fused_occupancy(int* wg_per_cu);
 int mqa_dense_logits_launch(const mqa::DenseParams* p, hipStream_t stream);
 int mqa_dense_topk_launch(const mqa::DenseTopkParams* p, hipStream_t stream);

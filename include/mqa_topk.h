@@ -16,7 +16,8 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     allocates no device memory and keeps no state between calls.
+ *     allocates no device memory and keeps no state between calls (apart from
+ *     the event ring of MQA_FLAG_TIME_SCAN).
  *   - Every call is asynchronous on `stream` (a hipStream_t; 0 is the null
  *     stream). A return of MQA_OK means the work was queued.
  *   - On any error code nothing has been launched.
@@ -61,6 +62,8 @@ extern "C" {
 #define MQA_FLAG_FORCE_GATE_MISS 2u /* the gate admits nothing: every gated row falls back */
 #define MQA_FLAG_SMALL_CAP 4u       /* per-row candidate slab limited to topk + 128 */
 #define MQA_FLAG_STATS 8u           /* fill the mqa_stats header of the workspace */
+#define MQA_FLAG_TIME_SCAN 16u      /* record HIP events around the scan kernel (see
+                                       mqa_scan_time); a benchmarking aid */
 
 /* Counters written to the first bytes of the workspace when MQA_FLAG_STATS is
  * set (read them after the stream has finished the call). */
@@ -149,6 +152,19 @@ int mqa_topk_dense(const float* logits, int64_t ld, int col0, int ncols,
  *   scale_bytes: [keys,4] uint8, 4-B aligned; scales: [keys] fp32, 4-B aligned.
  */
 int mqa_key_scales(const uint8_t* scale_bytes, float* scales, int keys, void* stream);
+
+/*
+ * Total GPU time, in milliseconds, of the scan kernel (the dominant kernel of
+ * mqa_topk_prefill) over the last `last_n` calls made on the current device
+ * with MQA_FLAG_TIME_SCAN, from HIP events recorded on the call's stream just
+ * before and after that kernel. The library keeps one ring of 256 event pairs
+ * per device, created on the first timed call and kept until the process ends.
+ * Blocks until the last of those calls has finished.
+ *   last_n in [1, number of timed calls so far on this device, at most 256]
+ * Returns MQA_OK, MQA_ERR_NULL (total_ms NULL), MQA_ERR_SHAPE (last_n out of
+ * range), MQA_ERR_DEVICE or MQA_ERR_LAUNCH (an event query failed).
+ */
+int mqa_scan_time(int last_n, float* total_ms);
 
 /* Human-readable text of a return code (for MQA_ERR_LAUNCH it names the HIP
  * error of the failing call on this thread). Never NULL. */

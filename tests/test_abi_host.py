@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert set(names) == {"workspace_size", "mqa_topk_prefill", "mqa_logits_dense",
-                          "mqa_topk_dense", "mqa_key_scales", "mqa_strerror"}
+                          "mqa_topk_dense", "mqa_key_scales", "mqa_scan_time", "mqa_strerror"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -93,6 +93,7 @@ def test_dense_errors():
     assert L.mqa_key_scales(None, P(A16), 10, None) == 1
     assert L.mqa_key_scales(P(0x10001), P(A16), 10, None) == 2
     assert L.mqa_key_scales(P(A16), P(A16), 0, None) == 3
+    assert L.mqa_scan_time(1, None) == 1
 
 
 def test_strerror_covers_every_code():
@@ -111,3 +112,5 @@ def test_device_error_without_gpu():
     # valid arguments on a host with no HIP device: MQA_ERR_DEVICE, nothing launched
     assert _prefill() == 5
     assert mqa.load().workspace_size(64, 0) == 0
+    v = ctypes.c_float(0.0)
+    assert mqa.load().mqa_scan_time(1, ctypes.byref(v)) == 5

@@ -122,6 +122,24 @@ def test_fused_all_rows(cfg):
     assert st["rows_gated"] + st["rows_exact"] + st["rows_short"] == wl.rows
 
 
+def test_scan_timing_flag():
+    # MQA_FLAG_TIME_SCAN leaves the output unchanged and mqa_scan_time sums
+    # the scan kernel's event times of the last calls
+    wl = W.config(1)
+    say("case: scan timing flag, config 1")
+    d = to_device(wl)
+    a = fused(d, wl.topk, flags=mqa.FLAG_TIME_SCAN).cpu().numpy()
+    b = fused(d, wl.topk, flags=mqa.FLAG_TIME_SCAN).cpu().numpy()
+    p = oracle_problem(wl)
+    for o in (a, b):
+        assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, wl.topk)
+        assert not check.check_topk(o, np.arange(wl.rows), p, wl.topk, TOL)
+    t1, t2 = mqa.scan_time_ms(1), mqa.scan_time_ms(2)
+    assert 0.0 < t1 <= t2 < 1e4
+    with pytest.raises(mqa.MQAError):
+        mqa.scan_time_ms(257)
+
+
 @pytest.mark.parametrize("flag", [mqa.FLAG_FORCE_EXACT, mqa.FLAG_FORCE_GATE_MISS,
                                   mqa.FLAG_SMALL_CAP])
 @pytest.mark.parametrize("cfg", [1, 2])
