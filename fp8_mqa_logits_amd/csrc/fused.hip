@@ -145,14 +145,28 @@ __device__ __forceinline__ void init_row(RowState& r, int row) {
   r.vmax = -__builtin_inff();
 }
 
+// Smallest float above a finite x: "score > x" is "score >= next_up(x)".
+__device__ __forceinline__ float next_up(float x) {
+  if (x == 0.f) return __int_as_float(1);
+  const int b = __float_as_int(x);
+  return __int_as_float(b > 0 ? b + 1 : b - 1);
+}
+
+// The row's admission test as one ">=" threshold (+inf admits nothing).
+__device__ __forceinline__ float admit_thr(const RowState& r, bool live) {
+  if (!live) return __builtin_inff();
+  return r.strict ? next_up(r.thr) : r.thr;
+}
+
 // Append the passing lanes of one chunk to a row's slab. A slab row has
 // kSlack records of room past `cap`, so one chunk always fits; a row that
 // went past `cap` is merged down once the whole chunk is scored (merge_rows).
-__device__ __forceinline__ void emit_rec(RowState& rs, float E, bool valid, int key, float* sE,
-                                         int32_t* sI) {
-  const bool pass = valid && (rs.strict ? (E > rs.thr) : (E >= rs.thr));
+// Returns whether any lane passed.
+__device__ __forceinline__ bool emit_rec(RowState& rs, float E, float th, bool valid, int key,
+                                         float* sE, int32_t* sI) {
+  const bool pass = valid && E >= th;
   const uint64_t m = __ballot(pass);
-  if (m == 0) return;
+  if (m == 0) return false;
   if (pass) {
     const unsigned pos = (unsigned)(rs.cnt + rank_in_mask(m));
     sE[pos] = E;
@@ -160,6 +174,7 @@ __device__ __forceinline__ void emit_rec(RowState& rs, float E, bool valid, int 
     rs.vmax = __builtin_fmaxf(rs.vmax, E);
   }
   rs.cnt += __popcll(m);
+  return true;
 }
 
 __device__ __forceinline__ bool row_in_chunk(const RowState& r, int mode, int key0) {
@@ -176,11 +191,11 @@ struct SlabRefs {
   int cap, keep;
 };
 
-__device__ __forceinline__ void finish_row(const FusedParams& p, RowState& r, float E, int key,
-                                           int key0, const SlabRefs& sr, int i) {
+__device__ __forceinline__ bool finish_row(RowState& r, float E, float th, int key, int key0,
+                                           const SlabRefs& sr, int i) {
   const bool full = r.s <= key0 && key0 + kChunk <= r.e;
   const bool valid = full || (key >= r.s && key < r.e);
-  emit_rec(r, E, valid, key, sr.sE[i], sr.sI[i]);
+  return emit_rec(r, E, th, valid, key, sr.sE[i], sr.sI[i]);
 }
 
 // Streaming top-k merge: every row whose slab went past `cap` is cut down to
@@ -229,7 +244,9 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
 // One scan of keys [lo, hi) for the rows of this wave in `mode` (M_ALL and
 // M_GATED rows together, or M_EXACT rows): FP8 MFMA scores, or exact scores
 // for EXACT. FP8 rows are pipelined: the MFMAs of the next row are issued
-// before the epilogue of the current one.
+// before the epilogue of the current one. Chunks that every live row of the
+// wave covers entirely (almost all of them) take a path with no per-row range
+// tests: rows that are not live have an admission threshold of +inf there.
 template <bool EXACT>
 __device__ __forceinline__ void scan_rows(const FusedParams& p, FusedSmem& sm, const QueryRow* qr,
                                           const FoldOp& fo, RowState* rs, int mode, int lo,
@@ -237,6 +254,22 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, FusedSmem& sm, c
   const int tid = threadIdx.x;
   const int l = lane_id();
   const int nch = (hi - lo + kChunk - 1) / kChunk;
+  bool live[kRowsPerWave];
+  float th[kRowsPerWave];
+  int cf = 0, ch = nch, nlive = 0;  // chunks [cf, ch) lie inside every live row
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    live[i] = EXACT ? rs[i].mode == M_EXACT : (rs[i].mode == M_ALL || rs[i].mode == M_GATED);
+    th[i] = admit_thr(rs[i], live[i]);
+    if (live[i]) {
+      ++nlive;
+      const int a = (rs[i].s - lo + kChunk - 1) / kChunk;
+      const int z = (rs[i].e - lo) / kChunk;
+      cf = a > cf ? a : cf;
+      ch = z < ch ? z : ch;
+    }
+  }
+  if (nlive == 0) cf = ch = 0;
   uint4 regs[1];
   float sreg = stage_scale(p.scales, lo, p.keys, tid);
   stage_chunk_regs(regs, p.k, lo, p.keys, tid, kThreads);
@@ -252,29 +285,29 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, FusedSmem& sm, c
     }
     const int key = key0 + l;
     const float sc = sm.sbuf[c & 1][l];
+    const bool fast = c >= cf && c < ch;
     bool act[kRowsPerWave];
-    bool any = false;
+    bool any = fast;
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
-      act[i] = mode == M_EXACT ? row_in_chunk(rs[i], M_EXACT, key0)
-                               : (row_in_chunk(rs[i], M_ALL, key0) ||
-                                  row_in_chunk(rs[i], M_GATED, key0));
+      act[i] = live[i] && rs[i].s < key0 + kChunk && rs[i].e > key0;
       any |= act[i];
     }
     if (any) {
       KeyTile kt;
       load_keys_lds(kt, sm.kbuf[c & 1]);
+      float E[4];
       if (EXACT) {
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i)
-          if (act[i]) finish_row(p, rs[i], score_chunk_exact(qr[i], kt) * sc, key, key0, sr, i);
+          E[i] = act[i] ? score_chunk_exact(qr[i], kt) * sc : 0.f;
       } else {
         // One branch-free block computes the four rows' score vectors (the
         // next row's MFMAs overlap the current row's epilogue); rows that are
-        // not live in this chunk are computed from zeroed operands and never
-        // emit. score = (f.k + sum_h w_h |s_h|) / 2 * scale
+        // not live are computed from zeroed operands and never emit.
+        // score = (f.k + sum_h w_h |s_h|) / 2 * scale
         const float sch = 0.5f * sc;
-        float L[4], E[4];
+        float L[4];
         RowAcc a0, a1;
         fold_linear(L, fo, kt);
         mfma_row(a0, qr[0], kt);
@@ -285,11 +318,22 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, FusedSmem& sm, c
         mfma_row(a1, qr[3], kt);
         E[2] = (L[2] + reduce_heads_abs(qr[2], a0)) * sch;
         E[3] = (L[3] + reduce_heads_abs(qr[3], a1)) * sch;
+      }
+      bool stored = false;
+      if (!EXACT && fast) {
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i)
-          if (act[i]) finish_row(p, rs[i], E[i], key, key0, sr, i);
+          stored |= emit_rec(rs[i], E[i], th[i], true, key, sr.sE[i], sr.sI[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i)
+          if (act[i]) stored |= finish_row(rs[i], E[i], th[i], key, key0, sr, i);
       }
-      merge_rows(p, rs, sr);
+      if (stored) {
+        merge_rows(p, rs, sr);
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) th[i] = admit_thr(rs[i], live[i]);
+      }
     }
     if (more) {
       store_chunk_regs(regs, sm.kbuf[(c + 1) & 1], tid, kThreads);
