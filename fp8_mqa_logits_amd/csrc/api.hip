@@ -65,9 +65,15 @@ struct Layout {
   int grid, nblocks;
 };
 
+// Persistent-grid cap: the kernels address a workgroup's score and key slab
+// rows through one raw buffer whose byte range (the distance between the two
+// slab arrays plus 32 rows) must stay below 2^31; 448 workgroups use 0.95 GB.
+constexpr int kMaxGrid = 448;
+
 Layout layout(int rows, const DeviceInfo& d) {
   Layout L{};
   L.grid = d.cus * d.wg_per_cu;
+  L.grid = L.grid < kMaxGrid ? L.grid : kMaxGrid;
   L.nblocks = (rows + mqa::kFusedBlockRows - 1) / mqa::kFusedBlockRows;
   size_t off = 0;
   L.header = off;

@@ -30,6 +30,9 @@ constexpr int kDim = 128;
 constexpr int kWave = 64;
 constexpr int kChunk = 64;                 // keys per LDS stage
 constexpr int kChunkBytes = kChunk * kDim; // 8 KiB
+// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx950: 32-bit
+// data format; offsets are bytes and stores past num_records are dropped.
+constexpr int kBufferFlags = 0x00020000;
 constexpr int kCap = 16384;                // candidate slab capacity per row
 constexpr int kMaxTopk = 2048;
 

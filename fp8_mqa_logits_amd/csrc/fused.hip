@@ -119,12 +119,29 @@ struct RowState {
   float m0, inv;  // gate: first-tile maximum and inverse bin width
   int have_m0;
   int nsamp;    // gate: sample keys inside the row's range
-  float vmax;   // per lane: largest score this lane appended to the slab
 };
 
+// Keys move through LDS in stages of kStageChunks 64-key chunks, copied by
+// direct global->LDS loads into two stage buffers. Each kernel declares the
+// buffers as separate __shared__ arrays so that the compiler can tell the one
+// being filled from the one being read (and does not wait for the copy in
+// flight before reading the other).
+constexpr int kStageChunks = 2;
+constexpr int kStageKeys = kStageChunks * kChunk;
+
+struct Stages {
+  uint8_t* k[2];
+  float* s[2];
+};
+
+#define MQA_DECLARE_STAGES(name)                                          \
+  __shared__ __align__(16) uint8_t name##_k0[kStageChunks * kChunkBytes]; \
+  __shared__ __align__(16) uint8_t name##_k1[kStageChunks * kChunkBytes]; \
+  __shared__ __align__(16) float name##_s0[kStageKeys];                   \
+  __shared__ __align__(16) float name##_s1[kStageKeys];                   \
+  const Stages name = {{name##_k0, name##_k1}, {name##_s0, name##_s1}}
+
 struct __align__(16) FusedSmem {
-  uint8_t kbuf[2][kChunkBytes];
-  float sbuf[2][kChunk];
   uint32_t hist[kWaves][kHistWords];
   int gath[kChunk];
   int block;
@@ -142,7 +159,28 @@ __device__ __forceinline__ void init_row(RowState& r, int row) {
   r.inv = 1.f;
   r.mode = M_OFF;
   r.s = r.e = 0;
-  r.vmax = -__builtin_inff();
+}
+
+// This wave's slab rows, merge buffers and histogram.
+struct SlabRefs {
+  float* baseE;                // the workgroup's 32 score slab rows
+  int32_t* baseI;              // and key slab rows
+  __amdgpu_buffer_rsrc_t buf;  // raw buffer from the score rows through the key rows
+  int delta;                   // byte distance from the score rows to the key rows
+  int row0;                    // slab row of the wave's row 0
+  uint32_t* hist;
+  int cap, keep;
+  __device__ float* sE(int i) const { return baseE + (row0 + i) * kSlabRow; }
+  __device__ int32_t* sI(int i) const { return baseI + (row0 + i) * kSlabRow; }
+  __device__ int off(int i) const { return (row0 + i) * kSlabRow * 4; }
+};
+
+// This wave's merge buffers.
+__device__ __forceinline__ float* tmp_e(const FusedParams& p) {
+  return p.tmpE + ((int64_t)blockIdx.x * kWaves + wave_id()) * kTmp;
+}
+__device__ __forceinline__ int32_t* tmp_i(const FusedParams& p) {
+  return p.tmpI + ((int64_t)blockIdx.x * kWaves + wave_id()) * kTmp;
 }
 
 // Smallest float above a finite x: "score > x" is "score >= next_up(x)".
@@ -158,20 +196,21 @@ __device__ __forceinline__ float admit_thr(const RowState& r, bool live) {
   return r.strict ? next_up(r.thr) : r.thr;
 }
 
-// Append the passing lanes of one chunk to a row's slab. A slab row has
-// kSlack records of room past `cap`, so one chunk always fits; a row that
-// went past `cap` is merged down once the whole chunk is scored (merge_rows).
-// Returns whether any lane passed.
+// Append the passing lanes of one chunk to slab row i of the wave: score and
+// key at the same record offset of the score and key rows (buffer stores:
+// the per-lane address is one shift). A slab row has room for one more chunk
+// past `cap`; a row that went past `cap` is merged down once the whole chunk
+// is scored (merge_rows). Returns whether any lane passed.
 __device__ __forceinline__ bool emit_rec(RowState& rs, float E, float th, bool valid, int key,
-                                         float* sE, int32_t* sI) {
+                                         const SlabRefs& sr, int i) {
   const bool pass = valid && E >= th;
   const uint64_t m = __ballot(pass);
   if (m == 0) return false;
   if (pass) {
-    const unsigned pos = (unsigned)(rs.cnt + rank_in_mask(m));
-    sE[pos] = E;
-    sI[pos] = key;
-    rs.vmax = __builtin_fmaxf(rs.vmax, E);
+    const int pos = (int)__builtin_amdgcn_mbcnt_hi(
+        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)rs.cnt));
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(E), sr.buf, pos * 4, sr.off(i), 0);
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)key, sr.buf, pos * 4, sr.off(i) + sr.delta, 0);
   }
   rs.cnt += __popcll(m);
   return true;
@@ -181,21 +220,12 @@ __device__ __forceinline__ bool row_in_chunk(const RowState& r, int mode, int ke
   return r.mode == mode && r.s < key0 + kChunk && r.e > key0;
 }
 
-// Emit one active row's scores of a chunk.
-struct SlabRefs {
-  float* sE[4];
-  int32_t* sI[4];
-  float* tE;
-  int32_t* tI;
-  uint32_t* hist;
-  int cap, keep;
-};
 
 __device__ __forceinline__ bool finish_row(RowState& r, float E, float th, int key, int key0,
                                            const SlabRefs& sr, int i) {
   const bool full = r.s <= key0 && key0 + kChunk <= r.e;
   const bool valid = full || (key >= r.s && key < r.e);
-  return emit_rec(r, E, th, valid, key, sr.sE[i], sr.sI[i]);
+  return emit_rec(r, E, th, valid, key, sr, i);
 }
 
 // Streaming top-k merge: every row whose slab went past `cap` is cut down to
@@ -209,25 +239,23 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
   while (todo) {
     const int i = __builtin_ctz(todo);
     todo &= todo - 1;
-    float* sE = sr.sE[0];
-    int32_t* sI = sr.sI[0];
+    float* sE = sr.sE(i);
+    int32_t* sI = sr.sI(i);
+    float* tE = tmp_e(p);
+    int32_t* tI = tmp_i(p);
     int cnt = rs[0].cnt;
 #pragma unroll
     for (int j = 1; j < kRowsPerWave; ++j)
-      if (i == j) {
-        sE = sr.sE[j];
-        sI = sr.sI[j];
-        cnt = rs[j].cnt;
-      }
+      if (i == j) cnt = rs[j].cnt;
     const float kth = wave_select(sE, sI, cnt, sr.keep, sr.hist,
                                   [&](int slot, float e, int idx) {
-                                    sr.tE[slot] = e;
-                                    sr.tI[slot] = idx;
+                                    tE[slot] = e;
+                                    tI[slot] = idx;
                                   });
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     for (int t = lane_id(); t < sr.keep; t += kWave) {
-      sE[t] = sr.tE[t];
-      sI[t] = sr.tI[t];
+      sE[t] = tE[t];
+      sI[t] = tI[t];
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
 #pragma unroll
@@ -241,6 +269,30 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
   }
 }
 
+// Queue direct global->LDS copies of the keys [key0, key0 + kStageKeys)
+// (clamped to the last key) and their scales into a stage buffer. Slot p of
+// the buffer (16 bytes) holds key p / 8, column slice (p % 8) ^ swz(key); each
+// wave fills 64 consecutive slots per copy. The copies are waited for by the
+// barrier that ends the stage before the buffer is read.
+__device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, uint8_t* kdst,
+                                          float* sdst, int tid) {
+#pragma unroll
+  for (int i = 0; i < kStageChunks * kChunk * 8 / kThreads; ++i) {
+    const int slot = tid + i * kThreads;
+    const int j = slot >> 3;
+    const int c = (slot & 7) ^ swz(j);
+    int key = key0 + j;
+    key = key < p.keys ? key : p.keys - 1;
+    __builtin_amdgcn_global_load_lds(p.k + (int64_t)key * kDim + 16 * c, kdst + 16 * (slot & ~63),
+                                     16, 0, 0);
+  }
+  if (tid < kStageKeys) {
+    int key = key0 + tid;
+    key = key < p.keys ? key : p.keys - 1;
+    __builtin_amdgcn_global_load_lds(p.scales + key, sdst + (tid & ~63), 4, 0, 0);
+  }
+}
+
 // One scan of keys [lo, hi) for the rows of this wave in `mode` (M_ALL and
 // M_GATED rows together, or M_EXACT rows): FP8 MFMA scores, or exact scores
 // for EXACT. FP8 rows are pipelined: the MFMAs of the next row are issued
@@ -248,7 +300,7 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
 // wave covers entirely (almost all of them) take a path with no per-row range
 // tests: rows that are not live have an admission threshold of +inf there.
 template <bool EXACT>
-__device__ __forceinline__ void scan_rows(const FusedParams& p, FusedSmem& sm, const QueryRow* qr,
+__device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& stg, const QueryRow* qr,
                                           const FoldOp& fo, RowState* rs, int mode, int lo,
                                           int hi, const SlabRefs& sr) {
   const int tid = threadIdx.x;
@@ -270,21 +322,13 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, FusedSmem& sm, c
     }
   }
   if (nlive == 0) cf = ch = 0;
-  uint4 regs[1];
-  float sreg = stage_scale(p.scales, lo, p.keys, tid);
-  stage_chunk_regs(regs, p.k, lo, p.keys, tid, kThreads);
-  store_chunk_regs(regs, sm.kbuf[0], tid, kThreads);
-  if (tid < kChunk) sm.sbuf[0][tid] = sreg;
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
+  const int nst = (nch + kStageChunks - 1) / kStageChunks;
+  // One chunk of the stage in LDS (keys kc, scales scl): score the wave's
+  // rows and append their candidates.
+  auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
     const int key0 = lo + c * kChunk;
-    const bool more = c + 1 < nch;
-    if (more) {
-      sreg = stage_scale(p.scales, key0 + kChunk, p.keys, tid);
-      stage_chunk_regs(regs, p.k, key0 + kChunk, p.keys, tid, kThreads);
-    }
     const int key = key0 + l;
-    const float sc = sm.sbuf[c & 1][l];
+    const float sc = scl[l];
     const bool fast = c >= cf && c < ch;
     bool act[kRowsPerWave];
     bool any = fast;
@@ -293,61 +337,72 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, FusedSmem& sm, c
       act[i] = live[i] && rs[i].s < key0 + kChunk && rs[i].e > key0;
       any |= act[i];
     }
-    if (any) {
-      KeyTile kt;
-      load_keys_lds(kt, sm.kbuf[c & 1]);
-      float E[4];
-      if (EXACT) {
+    if (!any) return;
+    KeyTile kt;
+    load_keys_lds(kt, kc);
+    float E[4];
+    if (EXACT) {
 #pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i)
-          E[i] = act[i] ? score_chunk_exact(qr[i], kt) * sc : 0.f;
-      } else {
-        // One branch-free block computes the four rows' score vectors (the
-        // next row's MFMAs overlap the current row's epilogue); rows that are
-        // not live are computed from zeroed operands and never emit.
-        // score = (f.k + sum_h w_h |s_h|) / 2 * scale
-        const float sch = 0.5f * sc;
-        float L[4];
-        RowAcc a0, a1;
-        fold_linear(L, fo, kt);
-        mfma_row(a0, qr[0], kt);
-        mfma_row(a1, qr[1], kt);
-        E[0] = (L[0] + reduce_heads_abs(qr[0], a0)) * sch;
-        mfma_row(a0, qr[2], kt);
-        E[1] = (L[1] + reduce_heads_abs(qr[1], a1)) * sch;
-        mfma_row(a1, qr[3], kt);
-        E[2] = (L[2] + reduce_heads_abs(qr[2], a0)) * sch;
-        E[3] = (L[3] + reduce_heads_abs(qr[3], a1)) * sch;
-      }
-      bool stored = false;
-      if (!EXACT && fast) {
-#pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i)
-          stored |= emit_rec(rs[i], E[i], th[i], true, key, sr.sE[i], sr.sI[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i)
-          if (act[i]) stored |= finish_row(rs[i], E[i], th[i], key, key0, sr, i);
-      }
-      if (stored) {
-        merge_rows(p, rs, sr);
-#pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i) th[i] = admit_thr(rs[i], live[i]);
-      }
+      for (int i = 0; i < kRowsPerWave; ++i)
+        E[i] = act[i] ? score_chunk_exact(qr[i], kt) * sc : 0.f;
+    } else {
+      // One branch-free block computes the four rows' score vectors (the
+      // next row's MFMAs overlap the current row's epilogue); rows that are
+      // not live are computed from zeroed operands and never emit.
+      // score = (f.k + sum_h w_h |s_h|) / 2 * scale
+      const float sch = 0.5f * sc;
+      float L[4];
+      RowAcc a0, a1;
+      fold_linear(L, fo, kt);
+      mfma_row(a0, qr[0], kt);
+      mfma_row(a1, qr[1], kt);
+      E[0] = (L[0] + reduce_heads_abs(qr[0], a0)) * sch;
+      mfma_row(a0, qr[2], kt);
+      E[1] = (L[1] + reduce_heads_abs(qr[1], a1)) * sch;
+      mfma_row(a1, qr[3], kt);
+      E[2] = (L[2] + reduce_heads_abs(qr[2], a0)) * sch;
+      E[3] = (L[3] + reduce_heads_abs(qr[3], a1)) * sch;
     }
-    if (more) {
-      store_chunk_regs(regs, sm.kbuf[(c + 1) & 1], tid, kThreads);
-      if (tid < kChunk) sm.sbuf[(c + 1) & 1][tid] = sreg;
+    bool stored = false;
+    if (!EXACT && fast) {
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i)
+        stored |= emit_rec(rs[i], E[i], th[i], true, key, sr, i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i)
+        if (act[i]) stored |= finish_row(rs[i], E[i], th[i], key, key0, sr, i);
+    }
+    if (stored) {
+      merge_rows(p, rs, sr);
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) th[i] = admit_thr(rs[i], live[i]);
+    }
+  };
+  // One stage: queue the copy of the next stage into the other buffer (its
+  // last readers passed the previous barrier), then score this one.
+  auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext, float* snext) {
+    if (st + 1 < nst) dma_stage(p, lo + (st + 1) * kStageKeys, knext, snext, tid);
+#pragma unroll
+    for (int u = 0; u < kStageChunks; ++u) {
+      const int c = st * kStageChunks + u;
+      if (c < nch) chunk(c, kcur + u * kChunkBytes, scur + u * kChunk);
     }
     __syncthreads();
+  };
+  dma_stage(p, lo, stg.k[0], stg.s[0], tid);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    stage(st, stg.k[0], stg.s[0], stg.k[1], stg.s[1]);
+    if (st + 1 < nst) stage(st + 1, stg.k[1], stg.s[1], stg.k[0], stg.s[0]);
   }
 }
 
 // Sampled gate: a strided sample of the block's keys gives each gated row a
 // threshold that should keep about 2k candidates. The sample histogram is
 // binned relative to the row's maximum over the first sample tile.
-__device__ __forceinline__ void gate_block(const FusedParams& p, FusedSmem& sm, const QueryRow* qr,
-                                           RowState* rs, int lo, int hi) {
+__device__ __forceinline__ void gate_block(const FusedParams& p, FusedSmem& sm, const Stages& stg,
+                                           const QueryRow* qr, RowState* rs, int lo, int hi) {
   const int tid = threadIdx.x;
   const int w = wave_id();
   const int l = lane_id();
@@ -362,12 +417,12 @@ __device__ __forceinline__ void gate_block(const FusedParams& p, FusedSmem& sm, 
     if (tid < kChunk) sm.gath[tid] = lo + (int)(((int64_t)(c * kChunk + tid) * span) / S);
     __syncthreads();
     stage_chunk_regs(regs, p.k, 0, p.keys, tid, kThreads, sm.gath);
-    store_chunk_regs(regs, sm.kbuf[0], tid, kThreads);
+    store_chunk_regs(regs, stg.k[0], tid, kThreads);
     __syncthreads();
     const int key = sm.gath[l];
     const float sc = p.scales[key];
     KeyTile kt;
-    load_keys_lds(kt, sm.kbuf[0]);
+    load_keys_lds(kt, stg.k[0]);
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       RowState& r = rs[i];
@@ -439,25 +494,27 @@ __device__ __forceinline__ void gate_block(const FusedParams& p, FusedSmem& sm, 
 // Returns false when the certificate fails (the caller rescans the row).
 template <class Emit>
 __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int n, int k, float T,
-                              float vmax, const QueryRow& qr, uint32_t* hist,
+                              const QueryRow& qr, uint32_t* hist,
                               unsigned* band_count, Emit emit) {
   const int l = lane_id();
   constexpr int kBins = kHistWords;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   const float4* e4 = reinterpret_cast<const float4*>(sE);  // slab rows are 64 KiB aligned
   const int n4 = n >> 2;
-  const float mx = wave_max(vmax);
-  float mn = T;
-  if (!(mn > -__builtin_inff())) {
-    float m = __builtin_inff();
+  float m = __builtin_inff(), x = -__builtin_inff();
 #pragma unroll 4
-    for (int i = l; i < n4; i += kWave) {
-      const float4 v = e4[i];
-      m = __builtin_fminf(m, __builtin_fminf(__builtin_fminf(v.x, v.y), __builtin_fminf(v.z, v.w)));
-    }
-    for (int i = 4 * n4 + l; i < n; i += kWave) m = __builtin_fminf(m, sE[i]);
-    mn = wave_min(m);
+  for (int i = l; i < n4; i += kWave) {
+    const float4 v = e4[i];
+    m = __builtin_fminf(m, __builtin_fminf(__builtin_fminf(v.x, v.y), __builtin_fminf(v.z, v.w)));
+    x = __builtin_fmaxf(x, __builtin_fmaxf(__builtin_fmaxf(v.x, v.y), __builtin_fmaxf(v.z, v.w)));
   }
+  for (int i = 4 * n4 + l; i < n; i += kWave) {
+    m = __builtin_fminf(m, sE[i]);
+    x = __builtin_fmaxf(x, sE[i]);
+  }
+  const float mx = wave_max(x);
+  // every candidate scored >= T; the lower end of the range is T when T is finite
+  const float mn = T > -__builtin_inff() ? T : wave_min(m);
   const float span = mx - mn;
   const float inv = span > 0.f ? (float)(kBins - 1) / span : 0.f;
   auto bin_of = [&](float e) {
@@ -597,14 +654,14 @@ __device__ __forceinline__ void setup_rows(const FusedParams& p, int b, RowState
 __device__ __forceinline__ SlabRefs slab_refs(const FusedParams& p, FusedSmem& sm, int cap) {
   const int w = wave_id();
   SlabRefs sr;
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int64_t slot = (int64_t)blockIdx.x * kBlockRows + w * kRowsPerWave + i;
-    sr.sE[i] = p.slabE + slot * kSlabRow;
-    sr.sI[i] = p.slabI + slot * kSlabRow;
-  }
-  sr.tE = p.tmpE + ((int64_t)blockIdx.x * kWaves + w) * kTmp;
-  sr.tI = p.tmpI + ((int64_t)blockIdx.x * kWaves + w) * kTmp;
+  sr.baseE = p.slabE + (int64_t)blockIdx.x * kBlockRows * kSlabRow;
+  sr.baseI = p.slabI + (int64_t)blockIdx.x * kBlockRows * kSlabRow;
+  sr.row0 = w * kRowsPerWave;
+  // one raw buffer from the workgroup's score rows to the end of its key rows
+  // (the host keeps the distance below 2^31 bytes)
+  sr.delta = (int)(reinterpret_cast<const char*>(sr.baseI) - reinterpret_cast<const char*>(sr.baseE));
+  sr.buf = __builtin_amdgcn_make_buffer_rsrc(sr.baseE, 0, sr.delta + kBlockRows * kSlabRow * 4,
+                                             kBufferFlags);
   sr.hist = sm.hist[w];
   sr.cap = cap;
   const int keep = 2 * p.topk;
@@ -635,6 +692,7 @@ __device__ __forceinline__ void block_union(FusedSmem& sm, int wlo, int whi, int
 
 __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
   __shared__ FusedSmem sm;
+  MQA_DECLARE_STAGES(stg);
   const int tid = threadIdx.x;
   const int w = wave_id();
   const int l = lane_id();
@@ -661,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
     block_union(sm, wlo, whi, wgated, p.keys, lo, hi, any_g);
     int wx = 0;
     if (hi > lo) {
-      if (any_g) gate_block(p, sm, qr, rs, lo, hi);
+      if (any_g) gate_block(p, sm, stg, qr, rs, lo, hi);
       if (!(p.flags & 1u)) {
         int frows[kRowsPerWave];
 #pragma unroll
@@ -669,7 +727,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
           frows[i] = (rs[i].mode == M_ALL || rs[i].mode == M_GATED) ? rs[i].r : -1;
         FoldOp fo;
         build_fold(fo, p.q, p.weights, frows);
-        scan_rows<false>(p, sm, qr, fo, rs, M_GATED, lo, hi, sr);
+        scan_rows<false>(p, stg, qr, fo, rs, M_GATED, lo, hi, sr);
       }
       // validity check + certified select, per row
 #pragma unroll
@@ -681,7 +739,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
           if (r.cnt >= k) {
             int32_t* o = p.out + (int64_t)r.r * k;
             const int base = r.s;
-            ok = select_banded(p, sr.sE[i], sr.sI[i], r.cnt, k, r.thr, r.vmax, qr[i], sr.hist,
+            ok = select_banded(p, sr.sE(i), sr.sI(i), r.cnt, k, r.thr, qr[i], sr.hist,
                                stats ? &p.header[H_BAND_LO] : nullptr,
                                [&](int sl, int idx) { o[sl] = idx - base; });
             if (stats && l == 0) {
@@ -712,6 +770,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
 // the flagged rows with a streaming top-k merge, then an exact select.
 __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
   __shared__ FusedSmem sm;
+  MQA_DECLARE_STAGES(stg);
   const int tid = threadIdx.x;
   const int l = lane_id();
   const int k = p.topk;
@@ -733,7 +792,7 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
     block_union(sm, wlo, whi, 0, p.keys, lo, hi, unused);
     if (hi > lo) {
       FoldOp none;
-      scan_rows<true>(p, sm, qr, none, rs, M_EXACT, lo, hi, sr);
+      scan_rows<true>(p, stg, qr, none, rs, M_EXACT, lo, hi, sr);
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         RowState& r = rs[i];
@@ -741,7 +800,7 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
         int32_t* o = p.out + (int64_t)r.r * k;
         const int base = r.s;
         const int have = r.cnt;
-        wave_select(sr.sE[i], sr.sI[i], have, k, sr.hist,
+        wave_select(sr.sE(i), sr.sI(i), have, k, sr.hist,
                     [&](int sl, float, int idx) { o[sl] = idx - base; });
         for (int j = have + l; j < k; j += kWave) o[j] = -1;
         if ((p.flags & 8u) && l == 0) atomicAdd(&p.header[H_EXACT], 1u);
