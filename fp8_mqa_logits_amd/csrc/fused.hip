@@ -165,14 +165,13 @@ __device__ __forceinline__ void init_row(RowState& r, int row) {
 struct SlabRefs {
   float* baseE;                // the workgroup's 32 score slab rows
   int32_t* baseI;              // and key slab rows
-  __amdgpu_buffer_rsrc_t buf;  // raw buffer from the score rows through the key rows
+  __amdgpu_buffer_rsrc_t buf;  // raw buffer from this wave's score rows through its key rows
   int delta;                   // byte distance from the score rows to the key rows
   int row0;                    // slab row of the wave's row 0
   uint32_t* hist;
   int cap, keep;
   __device__ float* sE(int i) const { return baseE + (row0 + i) * kSlabRow; }
   __device__ int32_t* sI(int i) const { return baseI + (row0 + i) * kSlabRow; }
-  __device__ int off(int i) const { return (row0 + i) * kSlabRow * 4; }
 };
 
 // This wave's merge buffers.
@@ -197,23 +196,23 @@ __device__ __forceinline__ float admit_thr(const RowState& r, bool live) {
 }
 
 // Append the passing lanes of one chunk to slab row i of the wave: score and
-// key at the same record offset of the score and key rows (buffer stores:
-// the per-lane address is one shift). A slab row has room for one more chunk
-// past `cap`; a row that went past `cap` is merged down once the whole chunk
-// is scored (merge_rows). Returns whether any lane passed.
-__device__ __forceinline__ bool emit_rec(RowState& rs, float E, float th, bool valid, int key,
+// key at the same record offset of the score and key rows (buffer stores
+// whose lane offset, record (i * kSlabRow + cnt + rank) of the wave's rows,
+// comes from one mbcnt). A slab row has room for one more chunk past `cap`;
+// a row that went past `cap` is merged down once the whole chunk is scored
+// (merge_rows).
+__device__ __forceinline__ void emit_rec(RowState& rs, float E, float th, bool valid, int key,
                                          const SlabRefs& sr, int i) {
   const bool pass = valid && E >= th;
   const uint64_t m = __ballot(pass);
-  if (m == 0) return false;
   if (pass) {
     const int pos = (int)__builtin_amdgcn_mbcnt_hi(
-        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)rs.cnt));
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(E), sr.buf, pos * 4, sr.off(i), 0);
-    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)key, sr.buf, pos * 4, sr.off(i) + sr.delta, 0);
+        (uint32_t)(m >> 32),
+        __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)(rs.cnt + i * kSlabRow)));
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(E), sr.buf, pos * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)key, sr.buf, pos * 4, sr.delta, 0);
   }
   rs.cnt += __popcll(m);
-  return true;
 }
 
 __device__ __forceinline__ bool row_in_chunk(const RowState& r, int mode, int key0) {
@@ -221,18 +220,19 @@ __device__ __forceinline__ bool row_in_chunk(const RowState& r, int mode, int ke
 }
 
 
-__device__ __forceinline__ bool finish_row(RowState& r, float E, float th, int key, int key0,
+__device__ __forceinline__ void finish_row(RowState& r, float E, float th, int key, int key0,
                                            const SlabRefs& sr, int i) {
   const bool full = r.s <= key0 && key0 + kChunk <= r.e;
   const bool valid = full || (key >= r.s && key < r.e);
-  return emit_rec(r, E, th, valid, key, sr, i);
+  emit_rec(r, E, th, valid, key, sr, i);
 }
 
 // Streaming top-k merge: every row whose slab went past `cap` is cut down to
 // its `keep` best records by score, and its admission threshold rises to the
 // smallest of them (later records must beat it strictly). One merge site for
 // the wave's rows, so the select code appears once in the scan loop.
-__device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, const SlabRefs& sr) {
+__device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, const SlabRefs& sr,
+                                           float* th) {
   unsigned todo = 0;
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) todo |= (rs[i].cnt > sr.cap ? 1u : 0u) << i;
@@ -264,6 +264,7 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
         rs[j].cnt = sr.keep;
         rs[j].thr = kth;
         rs[j].strict = 1;
+        th[j] = next_up(kth);
       }
     if ((p.flags & 8u) && lane_id() == 0) atomicAdd(&p.header[H_COMPACT], 1u);
   }
@@ -363,21 +364,18 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
       E[2] = (L[2] + reduce_heads_abs(qr[2], a0)) * sch;
       E[3] = (L[3] + reduce_heads_abs(qr[3], a1)) * sch;
     }
-    bool stored = false;
     if (!EXACT && fast) {
 #pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i)
-        stored |= emit_rec(rs[i], E[i], th[i], true, key, sr, i);
+      for (int i = 0; i < kRowsPerWave; ++i) emit_rec(rs[i], E[i], th[i], true, key, sr, i);
     } else {
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i)
-        if (act[i]) stored |= finish_row(rs[i], E[i], th[i], key, key0, sr, i);
+        if (act[i]) finish_row(rs[i], E[i], th[i], key, key0, sr, i);
     }
-    if (stored) {
-      merge_rows(p, rs, sr);
+    bool over = false;
 #pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i) th[i] = admit_thr(rs[i], live[i]);
-    }
+    for (int i = 0; i < kRowsPerWave; ++i) over |= rs[i].cnt > sr.cap;
+    if (over) merge_rows(p, rs, sr, th);
   };
   // One stage: queue the copy of the next stage into the other buffer (its
   // last readers passed the previous barrier), then score this one.
@@ -657,10 +655,10 @@ __device__ __forceinline__ SlabRefs slab_refs(const FusedParams& p, FusedSmem& s
   sr.baseE = p.slabE + (int64_t)blockIdx.x * kBlockRows * kSlabRow;
   sr.baseI = p.slabI + (int64_t)blockIdx.x * kBlockRows * kSlabRow;
   sr.row0 = w * kRowsPerWave;
-  // one raw buffer from the workgroup's score rows to the end of its key rows
-  // (the host keeps the distance below 2^31 bytes)
+  // one raw buffer from the wave's score rows to the end of its key rows (the
+  // host keeps the distance between the two slab arrays below 2^31 bytes)
   sr.delta = (int)(reinterpret_cast<const char*>(sr.baseI) - reinterpret_cast<const char*>(sr.baseE));
-  sr.buf = __builtin_amdgcn_make_buffer_rsrc(sr.baseE, 0, sr.delta + kBlockRows * kSlabRow * 4,
+  sr.buf = __builtin_amdgcn_make_buffer_rsrc(sr.sE(0), 0, sr.delta + kRowsPerWave * kSlabRow * 4,
                                              kBufferFlags);
   sr.hist = sm.hist[w];
   sr.cap = cap;
