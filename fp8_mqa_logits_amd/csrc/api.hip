@@ -61,30 +61,37 @@ const DeviceInfo* device_info(int device) {
 }
 
 struct Layout {
-  size_t header, order, xrow, xqueue, slabE, slabI, tmpE, tmpI, total;
+  size_t header, order, xrow, xqueue, xflag, rowinfo, slabE, slabI, tmpE, tmpI, total;
   int grid, nblocks;
 };
 
-// Persistent-grid cap: the kernels address a workgroup's score and key slab
-// rows through one raw buffer whose byte range (the distance between the two
-// slab arrays plus 32 rows) must stay below 2^31; 448 workgroups use 0.95 GB.
-constexpr int kMaxGrid = 448;
+// The kernels address a wave's score and key slab rows through one raw
+// buffer whose byte range (the distance between the two slab arrays plus four
+// rows) must stay below 2^31: a batch of kMaxBatchRows rows uses 1.09 GB.
+static_assert((size_t)mqa::kMaxBatchRows * mqa::kSlabRow * 4 + 4 * mqa::kSlabRow * 4 + kAlign <
+                  ((size_t)1 << 31),
+              "slab range");
 
+// Workspace of one batch of `rows` rows (rows <= kMaxBatchRows).
 Layout layout(int rows, const DeviceInfo& d) {
   Layout L{};
   L.grid = d.cus * d.wg_per_cu;
-  L.grid = L.grid < kMaxGrid ? L.grid : kMaxGrid;
   L.nblocks = (rows + mqa::kFusedBlockRows - 1) / mqa::kFusedBlockRows;
+  const size_t rows_pad = (size_t)L.nblocks * mqa::kFusedBlockRows;
   size_t off = 0;
   L.header = off;
   off = align_up(off + kHeaderWords * 4);
   L.order = off;
   off = align_up(off + (size_t)L.nblocks * 4);
   L.xrow = off;
-  off = align_up(off + (size_t)rows);
+  off = align_up(off + rows_pad);
   L.xqueue = off;
   off = align_up(off + (size_t)L.nblocks * 4);
-  const size_t slab = (size_t)L.grid * mqa::kFusedBlockRows * mqa::kSlabRow * 4;
+  L.xflag = off;
+  off = align_up(off + (size_t)L.nblocks * 4);
+  L.rowinfo = off;
+  off = align_up(off + rows_pad * sizeof(mqa::RowInfo));
+  const size_t slab = rows_pad * mqa::kSlabRow * 4;
   L.slabE = off;
   off = align_up(off + slab);
   L.slabI = off;
@@ -97,6 +104,8 @@ Layout layout(int rows, const DeviceInfo& d) {
   L.total = off;
   return L;
 }
+
+int batch_rows(int rows) { return rows < mqa::kMaxBatchRows ? rows : mqa::kMaxBatchRows; }
 
 int launch_error(int hip_code) {
   std::snprintf(g_err, sizeof(g_err), "HIP launch failed: %s",
@@ -153,7 +162,7 @@ size_t workspace_size(int rows, int device) {
   if (rows < 1 || rows > MQA_MAX_ROWS) return 0;
   const DeviceInfo* d = device_info(device);
   if (!d) return 0;
-  return layout(rows, *d).total;
+  return layout(batch_rows(rows), *d).total;
 }
 
 int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
@@ -169,39 +178,49 @@ int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
     return MQA_ERR_SHAPE;
   const DeviceInfo* d = current_device();
   if (!d) return MQA_ERR_DEVICE;
-  const Layout L = layout(rows, *d);
+  const int batch = batch_rows(rows);
+  const Layout L = layout(batch, *d);
   if (workspace_bytes < L.total) return MQA_ERR_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  mqa::FusedParams p;
-  p.q = q;
-  p.k = k;
-  p.scales = scales;
-  p.weights = weights;
-  p.starts = starts;
-  p.ends = ends;
-  p.out = out;
-  p.rows = rows;
-  p.keys = keys;
-  p.topk = topk;
-  p.nblocks = L.nblocks;
-  p.flags = flags;
-  p.header = reinterpret_cast<uint32_t*>(ws + L.header);
-  p.order = reinterpret_cast<int32_t*>(ws + L.order);
-  p.xrow = ws + L.xrow;
-  p.xqueue = reinterpret_cast<int32_t*>(ws + L.xqueue);
-  p.slabE = reinterpret_cast<float*>(ws + L.slabE);
-  p.slabI = reinterpret_cast<int32_t*>(ws + L.slabI);
-  p.tmpE = reinterpret_cast<float*>(ws + L.tmpE);
-  p.tmpI = reinterpret_cast<int32_t*>(ws + L.tmpI);
-  const int grid = L.grid < L.nblocks ? L.grid : L.nblocks;
   hipEvent_t eb = nullptr, ee = nullptr;
   if (flags & MQA_FLAG_TIME_SCAN) {
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (!ring_slot(dev, &eb, &ee)) return MQA_ERR_DEVICE;
   }
-  const int rc = mqa_fused_launch(&p, grid, static_cast<hipStream_t>(stream), eb, ee);
-  if (rc != 0) return launch_error(rc);
+  // Rows run in batches of `batch` rows, one launch sequence each, in order
+  // on the stream (they share the workspace).
+  for (int r0 = 0; r0 < rows; r0 += batch) {
+    const int nr = rows - r0 < batch ? rows - r0 : batch;
+    mqa::FusedParams p;
+    p.q = q + (size_t)r0 * MQA_HEADS * MQA_HEAD_DIM;
+    p.k = k;
+    p.scales = scales;
+    p.weights = weights + (size_t)r0 * MQA_HEADS;
+    p.starts = starts + r0;
+    p.ends = ends + r0;
+    p.out = out + (size_t)r0 * topk;
+    p.rows = nr;
+    p.keys = keys;
+    p.topk = topk;
+    p.nblocks = (nr + mqa::kFusedBlockRows - 1) / mqa::kFusedBlockRows;
+    p.flags = flags;
+    p.header = reinterpret_cast<uint32_t*>(ws + L.header);
+    p.order = reinterpret_cast<int32_t*>(ws + L.order);
+    p.xrow = ws + L.xrow;
+    p.xqueue = reinterpret_cast<int32_t*>(ws + L.xqueue);
+    p.xflag = reinterpret_cast<uint32_t*>(ws + L.xflag);
+    p.rowinfo = reinterpret_cast<mqa::RowInfo*>(ws + L.rowinfo);
+    p.slabE = reinterpret_cast<float*>(ws + L.slabE);
+    p.slabI = reinterpret_cast<int32_t*>(ws + L.slabI);
+    p.tmpE = reinterpret_cast<float*>(ws + L.tmpE);
+    p.tmpI = reinterpret_cast<int32_t*>(ws + L.tmpI);
+    const int grid = L.grid < p.nblocks ? L.grid : p.nblocks;
+    // timing events: from the first batch's scan to the end of the last one
+    const int rc = mqa_fused_launch(&p, grid, static_cast<hipStream_t>(stream),
+                                    r0 == 0 ? eb : nullptr, r0 + nr >= rows ? ee : nullptr);
+    if (rc != 0) return launch_error(rc);
+  }
   return MQA_OK;
 }
 

@@ -3,26 +3,27 @@
 // Follows vLLM PR #60618, "What this PR does" (scoring, sampled gate,
 // candidate emission, per-row selection, exact rescan, heaviest-first block
 // claims) and the API page "fused_mqa_topk" (contract and output convention),
-// laid out for gfx950:
-//   * a workgroup is 8 waves (512 threads); a block is 32 consecutive query
-//     rows, 4 per wave, whose q and weights stay in VGPRs for the whole scan;
-//   * keys stream through a double-buffered 8 KiB LDS stage (64 keys) loaded
-//     with coalesced 16-byte global loads; every wave reads the stage as FP8
-//     MFMA B operands and scores its 4 rows, issuing the next row's MFMAs
-//     before the current row's relu/weight epilogue (common.h);
-//   * each wave owns its rows, so the gate threshold, the candidate count and
-//     the slab cursor of a row are wave-uniform values: emission is a ballot,
-//     a popcount and one 8-byte store per passing lane, with no atomics;
-//   * the scan ranks with FP8 MFMA scores, which are approximate on gfx950
-//     (common.h); the select finds each row's k-th approximate score,
-//     recomputes the scores of a band of keys around it exactly (bf16 MFMA)
-//     and accepts the row only when the band's largest measured error, times
-//     a safety factor, cannot move any key across the cut;
-//   * rows whose gate misses, whose slab overflows or whose band cannot be
-//     certified are queued; a second persistent kernel rescans their blocks
-//     with exact scores and a streaming top-k merge;
-//   * blocks are claimed heaviest first from a global counter; no workgroup
-//     ever waits for another one.
+// laid out for gfx950 as five launches on the caller's stream:
+//   * plan: heaviest-first order of the 32-row blocks, counters cleared;
+//   * gate (persistent): per block, a strided sample of the keys gives each
+//     row an admission threshold meant to keep about 2k candidates; rows
+//     with n <= k get their output here;
+//   * scan (persistent, 8 waves of 4 rows per workgroup): keys stream through
+//     LDS in 128-key stages filled by direct global->LDS loads; each wave
+//     scores its 4 rows with FP8 MFMAs (the rows' q and weights stay in
+//     VGPRs) and appends the keys that reach a row's threshold to that row's
+//     candidate slab (a ballot, an mbcnt and two buffer stores per row and
+//     chunk, no atomics: a row belongs to one wave);
+//   * select (one wave per row): the row's k-th approximate score is found in
+//     its slab, a band of keys around it is rescored exactly (bf16 MFMA) and
+//     the row is accepted only when the band's measured error, times a safety
+//     factor, cannot move any key across the cut (FP8 MFMA scores are
+//     approximate on gfx950, see common.h);
+//   * exact (persistent): rows whose gate admitted fewer than k keys or whose
+//     band could not be certified are rescanned with exact scores and a
+//     streaming top-k merge.
+// Each phase is its own kernel so that each gets the registers it needs (the
+// scan loop in particular holds no state of the other phases).
 #include "common.h"
 #include "launch.h"
 
@@ -38,13 +39,15 @@ constexpr int kGateOff = 16;  // bins above the first-tile maximum
 constexpr int kHistWords = 2048;
 constexpr int kBand = 32;           // keys on each side of rank k that are rescored exactly
 constexpr float kBandSafety = 8.f;  // certificate margin, in units of the band's largest error
+constexpr int kSelWaves = 4;        // rows (waves) per select workgroup
 
 // Header words (the first 12 mirror struct mqa_stats in mqa_topk.h).
 enum : int {
   H_CLAIM = 0, H_SHORT = 1, H_GATED = 2, H_EXACT = 3, H_OVERFLOW = 4, H_UNDER = 5,
   H_COMPACT = 6, H_UNCERT = 7, H_CAND_LO = 8, H_CAND_HI = 9, H_BAND_LO = 10, H_BAND_HI = 11,
-  H_XQ = 16,     // blocks queued for the exact rescan
-  H_XCLAIM = 17  // exact-rescan claim counter
+  H_XQ = 16,      // blocks queued for the exact rescan
+  H_XCLAIM = 17,  // exact-rescan claim counter
+  H_GCLAIM = 18   // gate claim counter
 };
 
 enum RowMode : int { M_OFF = 0, M_SHORT = 1, M_ALL = 2, M_GATED = 3, M_EXACT = 4 };
@@ -80,13 +83,15 @@ __device__ __forceinline__ int block_cost(const FusedParams& p, int b) {
 }
 
 // Heaviest-first block order (counting sort by cost, 1024 buckets of 1024
-// keys, descending) and the reset of the header. One workgroup.
+// keys, descending), the reset of the header and of the per-block exact
+// flags. One workgroup.
 __global__ __launch_bounds__(1024) void fused_plan_kernel(FusedParams p) {
   __shared__ int cnt[1024];
   __shared__ int off[1024];
   const int tid = threadIdx.x;
   cnt[tid] = 0;
   if (tid < 64) p.header[tid] = 0;
+  for (int b = tid; b < p.nblocks; b += 1024) p.xflag[b] = 0;
   __syncthreads();
   for (int b = tid; b < p.nblocks; b += 1024) {
     const int c = block_cost(p, b) >> 10;
@@ -110,16 +115,57 @@ __global__ __launch_bounds__(1024) void fused_plan_kernel(FusedParams p) {
 }
 
 struct RowState {
-  int r;        // global row id
+  int r;        // row id
   int s, e;     // clamped visible range
   int mode;     // RowMode
   float thr;    // admission threshold
   int strict;   // admit score > thr (1) or >= thr (0)
   int cnt;      // records appended to the slab
-  float m0, inv;  // gate: first-tile maximum and inverse bin width
-  int have_m0;
-  int nsamp;    // gate: sample keys inside the row's range
 };
+
+// Rows of block b owned by the calling wave (modes off, thresholds open).
+__device__ __forceinline__ void wave_rows(const FusedParams& p, int b, RowState* rs) {
+  const int w = wave_id();
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    RowState& r = rs[i];
+    r.r = b * kBlockRows + w * kRowsPerWave + i;
+    r.cnt = 0;
+    r.strict = 0;
+    r.thr = -__builtin_inff();
+    r.mode = M_OFF;
+    r.s = r.e = 0;
+    if (r.r < p.rows) row_range(p, r.r, r.s, r.e);
+  }
+}
+
+__device__ __forceinline__ void zero_query(QueryRow& qr) {
+  qr.qa[0] = qr.qa[1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int v = 0; v < 8; ++v) qr.w[v] = 0.f;
+}
+
+// The union range of the live rows over the workgroup's waves (wlo/whi: this
+// wave's) and the OR of a per-wave flag. All threads call it.
+__device__ __forceinline__ void block_union(int* wlo_s, int* whi_s, int* wf_s, int wlo, int whi,
+                                            int flag, int keys, int& lo, int& hi, int& any) {
+  const int w = wave_id();
+  if (lane_id() == 0) {
+    wlo_s[w] = wlo;
+    whi_s[w] = whi;
+    wf_s[w] = flag;
+  }
+  __syncthreads();
+  lo = keys;
+  hi = 0;
+  any = 0;
+  for (int i = 0; i < kWaves; ++i) {
+    lo = wlo_s[i] < lo ? wlo_s[i] : lo;
+    hi = whi_s[i] > hi ? whi_s[i] : hi;
+    any |= wf_s[i];
+  }
+  __syncthreads();
+}
 
 // Keys move through LDS in stages of kStageChunks 64-key chunks, copied by
 // direct global->LDS loads into two stage buffers. Each kernel declares the
@@ -141,47 +187,6 @@ struct Stages {
   __shared__ __align__(16) float name##_s1[kStageKeys];                   \
   const Stages name = {{name##_k0, name##_k1}, {name##_s0, name##_s1}}
 
-struct __align__(16) FusedSmem {
-  uint32_t hist[kWaves][kHistWords];
-  int gath[kChunk];
-  int block;
-  int wlo[kWaves], whi[kWaves], wg[kWaves], wx[kWaves];
-};
-
-__device__ __forceinline__ void init_row(RowState& r, int row) {
-  r.r = row;
-  r.cnt = 0;
-  r.strict = 0;
-  r.thr = -__builtin_inff();
-  r.have_m0 = 0;
-  r.nsamp = 0;
-  r.m0 = 0.f;
-  r.inv = 1.f;
-  r.mode = M_OFF;
-  r.s = r.e = 0;
-}
-
-// This wave's slab rows, merge buffers and histogram.
-struct SlabRefs {
-  float* baseE;                // the workgroup's 32 score slab rows
-  int32_t* baseI;              // and key slab rows
-  __amdgpu_buffer_rsrc_t buf;  // raw buffer from this wave's score rows through its key rows
-  int delta;                   // byte distance from the score rows to the key rows
-  int row0;                    // slab row of the wave's row 0
-  uint32_t* hist;
-  int cap, keep;
-  __device__ float* sE(int i) const { return baseE + (row0 + i) * kSlabRow; }
-  __device__ int32_t* sI(int i) const { return baseI + (row0 + i) * kSlabRow; }
-};
-
-// This wave's merge buffers.
-__device__ __forceinline__ float* tmp_e(const FusedParams& p) {
-  return p.tmpE + ((int64_t)blockIdx.x * kWaves + wave_id()) * kTmp;
-}
-__device__ __forceinline__ int32_t* tmp_i(const FusedParams& p) {
-  return p.tmpI + ((int64_t)blockIdx.x * kWaves + wave_id()) * kTmp;
-}
-
 // Smallest float above a finite x: "score > x" is "score >= next_up(x)".
 __device__ __forceinline__ float next_up(float x) {
   if (x == 0.f) return __int_as_float(1);
@@ -193,6 +198,45 @@ __device__ __forceinline__ float next_up(float x) {
 __device__ __forceinline__ float admit_thr(const RowState& r, bool live) {
   if (!live) return __builtin_inff();
   return r.strict ? next_up(r.thr) : r.thr;
+}
+
+// The calling wave's 4 slab rows of block b, its merge buffers and its LDS
+// histogram. Slab row r (a row id) holds kSlabRow (score, key) records in two
+// arrays; the scan appends with buffer stores through one raw buffer that
+// spans the wave's score rows through its key rows (the host keeps the
+// distance between the two arrays below 2^31 bytes).
+struct SlabRefs {
+  float* sE0;                  // score slab row of the wave's row 0 (row i at + i * kSlabRow)
+  int32_t* sI0;                // key slab row of the wave's row 0
+  __amdgpu_buffer_rsrc_t buf;  // raw buffer from sE0 through the end of the wave's key rows
+  int delta;                   // byte distance from the score rows to the key rows
+  uint32_t* hist;
+  int cap, keep;
+  __device__ float* sE(int i) const { return sE0 + i * kSlabRow; }
+  __device__ int32_t* sI(int i) const { return sI0 + i * kSlabRow; }
+};
+
+__device__ __forceinline__ SlabRefs slab_refs(const FusedParams& p, int b, uint32_t* hist) {
+  SlabRefs sr;
+  const int64_t row0 = (int64_t)b * kBlockRows + wave_id() * kRowsPerWave;
+  sr.sE0 = p.slabE + row0 * kSlabRow;
+  sr.sI0 = p.slabI + row0 * kSlabRow;
+  sr.delta = (int)(reinterpret_cast<const char*>(p.slabI) - reinterpret_cast<const char*>(p.slabE));
+  sr.buf = __builtin_amdgcn_make_buffer_rsrc(sr.sE0, 0, sr.delta + kRowsPerWave * kSlabRow * 4,
+                                             kBufferFlags);
+  sr.hist = hist;
+  sr.cap = slab_cap(p);
+  const int keep = 2 * p.topk;
+  sr.keep = keep < sr.cap - kWave ? keep : sr.cap - kWave;
+  return sr;
+}
+
+// This wave's merge buffers (persistent workgroup blockIdx.x).
+__device__ __forceinline__ float* tmp_e(const FusedParams& p) {
+  return p.tmpE + ((int64_t)blockIdx.x * kWaves + wave_id()) * kTmp;
+}
+__device__ __forceinline__ int32_t* tmp_i(const FusedParams& p) {
+  return p.tmpI + ((int64_t)blockIdx.x * kWaves + wave_id()) * kTmp;
 }
 
 // Append the passing lanes of one chunk to slab row i of the wave: score and
@@ -214,11 +258,6 @@ __device__ __forceinline__ void emit_rec(RowState& rs, float E, float th, bool v
   }
   rs.cnt += __popcll(m);
 }
-
-__device__ __forceinline__ bool row_in_chunk(const RowState& r, int mode, int key0) {
-  return r.mode == mode && r.s < key0 + kChunk && r.e > key0;
-}
-
 
 __device__ __forceinline__ void finish_row(RowState& r, float E, float th, int key, int key0,
                                            const SlabRefs& sr, int i) {
@@ -294,6 +333,26 @@ __device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, uint8_
   }
 }
 
+// Approximate scores of the wave's 4 rows for a 64-key chunk, lane l <->
+// key l: (f.k + sum_h w_h |s_h|) / 2 * scale (relu fold, common.h). One
+// branch-free block: the next row's MFMAs are issued before the current
+// row's epilogue; rows with zeroed operands score 0.
+__device__ __forceinline__ void score4(float E[4], const QueryRow* qr, const FoldOp& fo,
+                                       const KeyTile& kt, float sc) {
+  const float sch = 0.5f * sc;
+  float L[4];
+  RowAcc a0, a1;
+  fold_linear(L, fo, kt);
+  mfma_row(a0, qr[0], kt);
+  mfma_row(a1, qr[1], kt);
+  E[0] = (L[0] + reduce_heads_abs(qr[0], a0)) * sch;
+  mfma_row(a0, qr[2], kt);
+  E[1] = (L[1] + reduce_heads_abs(qr[1], a1)) * sch;
+  mfma_row(a1, qr[3], kt);
+  E[2] = (L[2] + reduce_heads_abs(qr[2], a0)) * sch;
+  E[3] = (L[3] + reduce_heads_abs(qr[3], a1)) * sch;
+}
+
 // One scan of keys [lo, hi) for the rows of this wave in `mode` (M_ALL and
 // M_GATED rows together, or M_EXACT rows): FP8 MFMA scores, or exact scores
 // for EXACT. FP8 rows are pipelined: the MFMAs of the next row are issued
@@ -347,22 +406,8 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
       for (int i = 0; i < kRowsPerWave; ++i)
         E[i] = act[i] ? score_chunk_exact(qr[i], kt) * sc : 0.f;
     } else {
-      // One branch-free block computes the four rows' score vectors (the
-      // next row's MFMAs overlap the current row's epilogue); rows that are
-      // not live are computed from zeroed operands and never emit.
-      // score = (f.k + sum_h w_h |s_h|) / 2 * scale
-      const float sch = 0.5f * sc;
-      float L[4];
-      RowAcc a0, a1;
-      fold_linear(L, fo, kt);
-      mfma_row(a0, qr[0], kt);
-      mfma_row(a1, qr[1], kt);
-      E[0] = (L[0] + reduce_heads_abs(qr[0], a0)) * sch;
-      mfma_row(a0, qr[2], kt);
-      E[1] = (L[1] + reduce_heads_abs(qr[1], a1)) * sch;
-      mfma_row(a1, qr[3], kt);
-      E[2] = (L[2] + reduce_heads_abs(qr[2], a0)) * sch;
-      E[3] = (L[3] + reduce_heads_abs(qr[3], a1)) * sch;
+      // rows that are not live have zeroed operands and never emit
+      score4(E, qr, fo, kt, sc);
     }
     if (!EXACT && fast) {
 #pragma unroll
@@ -396,82 +441,219 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
   }
 }
 
-// Sampled gate: a strided sample of the block's keys gives each gated row a
-// threshold that should keep about 2k candidates. The sample histogram is
-// binned relative to the row's maximum over the first sample tile.
-__device__ __forceinline__ void gate_block(const FusedParams& p, FusedSmem& sm, const Stages& stg,
-                                           const QueryRow* qr, RowState* rs, int lo, int hi) {
+// ---------------------------------------------------------------------------
+// Gate. A strided sample of the block's keys (1024..4096 keys, span / 16)
+// is scored like the scan scores; each gated row bins (first-tile maximum -
+// score) in kGateBins bins of 1/64 of the first sample tile's score range and
+// takes as threshold the bin edge whose sample count, scaled by n / sample,
+// reaches 2k. Rows with n <= k are answered here (keys 0..n-1, -1 padding).
+struct __align__(16) GateSmem {
+  uint8_t kbuf[kChunkBytes];
+  uint32_t hist[kWaves][kRowsPerWave * kGateBins];
+  int gath[kChunk];
+  int block;
+  int wlo[kWaves], whi[kWaves], wf[kWaves];
+};
+
+__global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
+  __shared__ GateSmem sm;
   const int tid = threadIdx.x;
   const int w = wave_id();
   const int l = lane_id();
-  const int span = hi - lo;
-  int S = (span / 16) & ~(kChunk - 1);
-  S = S < 1024 ? 1024 : (S > 4096 ? 4096 : S);
-  const int nch = S / kChunk;
-  uint32_t* hist = sm.hist[w];
-  for (int i = l; i < kRowsPerWave * kGateBins; i += kWave) hist[i] = 0;
-  uint4 regs[1];
-  for (int c = 0; c < nch; ++c) {
-    if (tid < kChunk) sm.gath[tid] = lo + (int)(((int64_t)(c * kChunk + tid) * span) / S);
+  const int k = p.topk;
+  const int cap = slab_cap(p);
+  const bool stats = p.flags & 8u;
+  for (;;) {
+    if (tid == 0) sm.block = (int)atomicAdd(&p.header[H_GCLAIM], 1u);
     __syncthreads();
-    stage_chunk_regs(regs, p.k, 0, p.keys, tid, kThreads, sm.gath);
-    store_chunk_regs(regs, stg.k[0], tid, kThreads);
-    __syncthreads();
-    const int key = sm.gath[l];
-    const float sc = p.scales[key];
-    KeyTile kt;
-    load_keys_lds(kt, stg.k[0]);
+    const int bi = sm.block;
+    if (bi >= p.nblocks) break;
+    const int b = p.order[bi];
+    RowState rs[kRowsPerWave];
+    QueryRow qr[kRowsPerWave];
+    wave_rows(p, b, rs);
+    int wlo = p.keys, whi = 0, wg = 0;
+    int frows[kRowsPerWave];
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       RowState& r = rs[i];
-      if (r.mode != M_GATED) continue;
-      const float E = score_chunk(qr[i], kt) * sc;
-      const bool valid = key >= r.s && key < r.e;
-      const uint64_t vm = __ballot(valid);
-      if (vm == 0) continue;
-      if (!r.have_m0) {
-        const float mx = wave_max(valid ? E : -__builtin_inff());
-        const float mn = wave_min(valid ? E : __builtin_inff());
-        float width = (mx - mn) / 64.f;
-        if (!(width > 0.f) || !__builtin_isfinite(width))
-          width = __builtin_fmaxf(__builtin_fabsf(mx), 1e-30f) * (1.f / 128.f);
-        r.m0 = mx;
-        r.inv = 1.f / width;
-        r.have_m0 = 1;
+      zero_query(qr[i]);
+      frows[i] = -1;
+      if (r.r >= p.rows) continue;
+      const int n = r.e - r.s;
+      if (n <= k) {
+        r.mode = M_SHORT;
+        int32_t* o = p.out + (int64_t)r.r * k;
+        for (int j = l; j < k; j += kWave) o[j] = j < n ? j : -1;
+        if (stats && l == 0) atomicAdd(&p.header[H_SHORT], 1u);
+      } else if (p.flags & 1u) {
+        r.mode = M_EXACT;  // forced: straight to the exact rescan
+      } else if (n <= 4 * k && n <= cap) {
+        r.mode = M_ALL;  // every visible key is a candidate
+      } else {
+        r.mode = M_GATED;
+        load_query(qr[i], p.q, p.weights, r.r);
+        frows[i] = r.r;
+        wlo = r.s < wlo ? r.s : wlo;
+        whi = r.e > whi ? r.e : whi;
+        wg = 1;
       }
-      r.nsamp += __popcll(vm);
-      if (valid) {
-        const float fb = (r.m0 - E) * r.inv;
-        int bin = fb < -1e6f ? 0
-                             : (fb > 1e6f ? kGateBins - 1 : (int)__builtin_floorf(fb) + kGateOff);
-        bin = bin < 0 ? 0 : (bin > kGateBins - 1 ? kGateBins - 1 : bin);
-        atomicAdd(&hist[i * kGateBins + bin], 1u);
+    }
+    int lo, hi, any_g;
+    block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, wg, p.keys, lo, hi, any_g);
+    if (any_g && hi > lo) {
+      FoldOp fo;
+      build_fold(fo, p.q, p.weights, frows);
+      const int span = hi - lo;
+      int S = (span / 16) & ~(kChunk - 1);
+      S = S < 1024 ? 1024 : (S > 4096 ? 4096 : S);
+      const int nch = S / kChunk;
+      uint32_t* hist = sm.hist[w];
+      for (int i = l; i < kRowsPerWave * kGateBins; i += kWave) hist[i] = 0;
+      float m0[kRowsPerWave], inv[kRowsPerWave];
+      int have_m0[kRowsPerWave], nsamp[kRowsPerWave];
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        m0[i] = 0.f;
+        inv[i] = 1.f;
+        have_m0[i] = 0;
+        nsamp[i] = 0;
+      }
+      uint4 regs[1];
+      for (int c = 0; c < nch; ++c) {
+        if (tid < kChunk) sm.gath[tid] = lo + (int)(((int64_t)(c * kChunk + tid) * span) / S);
+        __syncthreads();
+        stage_chunk_regs(regs, p.k, 0, p.keys, tid, kThreads, sm.gath);
+        store_chunk_regs(regs, sm.kbuf, tid, kThreads);
+        __syncthreads();
+        const int key = sm.gath[l];
+        KeyTile kt;
+        load_keys_lds(kt, sm.kbuf);
+        float E[4];
+        score4(E, qr, fo, kt, p.scales[key]);
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+          const RowState& r = rs[i];
+          if (r.mode != M_GATED) continue;
+          const bool valid = key >= r.s && key < r.e;
+          const uint64_t vm = __ballot(valid);
+          if (vm == 0) continue;
+          if (!have_m0[i]) {
+            const float mx = wave_max(valid ? E[i] : -__builtin_inff());
+            const float mn = wave_min(valid ? E[i] : __builtin_inff());
+            float width = (mx - mn) / 64.f;
+            if (!(width > 0.f) || !__builtin_isfinite(width))
+              width = __builtin_fmaxf(__builtin_fabsf(mx), 1e-30f) * (1.f / 128.f);
+            m0[i] = mx;
+            inv[i] = 1.f / width;
+            have_m0[i] = 1;
+          }
+          nsamp[i] += __popcll(vm);
+          if (valid) {
+            const float fb = (m0[i] - E[i]) * inv[i];
+            int bin = fb < -1e6f ? 0
+                                 : (fb > 1e6f ? kGateBins - 1 : (int)__builtin_floorf(fb) + kGateOff);
+            bin = bin < 0 ? 0 : (bin > kGateBins - 1 ? kGateBins - 1 : bin);
+            atomicAdd(&hist[i * kGateBins + bin], 1u);
+          }
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        RowState& r = rs[i];
+        if (r.mode != M_GATED) continue;
+        const int n = r.e - r.s;
+        const int64_t target = 2 * (int64_t)k;
+        const int ks = (int)((target * nsamp[i] + n - 1) / n);
+        float thr = -__builtin_inff();
+        if (have_m0[i] && ks >= 1 && ks <= nsamp[i]) {
+          // bins 2l, 2l+1 per lane, cumulative from bin 0 (the top)
+          const int h0 = (int)hist[i * kGateBins + 2 * l];
+          const int h1 = (int)hist[i * kGateBins + 2 * l + 1];
+          const int incl = wave_incl_scan(h0 + h1);
+          const uint64_t hit = __ballot(incl >= ks);
+          const int src = hit ? __builtin_ctzll(hit) : 63;
+          int bstar = 2 * l + ((incl - h1) >= ks ? 0 : 1);
+          bstar = __shfl(bstar, src, 64);
+          if (bstar < kGateBins - 1) thr = m0[i] - (float)(bstar - kGateOff + 1) / inv[i];
+        }
+        if (p.flags & 2u) thr = __builtin_inff();  // forced gate miss
+        r.thr = thr;
+      }
+    }
+    if (l == 0) {
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        const RowState& r = rs[i];
+        if (r.r >= p.rows) continue;
+        p.rowinfo[r.r] = RowInfo{r.thr, 0, r.mode, 0};
+        p.xrow[r.r] = 0;
       }
     }
     __syncthreads();
   }
-  // thresholds
+}
+
+// ---------------------------------------------------------------------------
+// Scan: every visible key of every live row of a block, candidates to the
+// rows' slabs.
+struct __align__(16) ScanSmem {
+  uint32_t hist[kWaves][kHistWords];
+  int block;
+  int wlo[kWaves], whi[kWaves], wf[kWaves];
+};
+
+__global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
+  __shared__ ScanSmem sm;
+  MQA_DECLARE_STAGES(stg);
+  const int tid = threadIdx.x;
+  const int w = wave_id();
+  const int l = lane_id();
+  for (;;) {
+    if (tid == 0) sm.block = (int)atomicAdd(&p.header[H_CLAIM], 1u);
+    __syncthreads();
+    const int bi = sm.block;
+    if (bi >= p.nblocks) break;
+    const int b = p.order[bi];
+    RowState rs[kRowsPerWave];
+    QueryRow qr[kRowsPerWave];
+    wave_rows(p, b, rs);
+    int wlo = p.keys, whi = 0;
+    int frows[kRowsPerWave];
 #pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    RowState& r = rs[i];
-    if (r.mode != M_GATED) continue;
-    const int n = r.e - r.s;
-    const int64_t target = 2 * (int64_t)p.topk;
-    const int ks = (int)((target * r.nsamp + n - 1) / n);
-    float thr = -__builtin_inff();
-    if (r.have_m0 && ks >= 1 && ks <= r.nsamp) {
-      // bins 2l, 2l+1 per lane, cumulative from bin 0 (the top)
-      const int h0 = (int)hist[i * kGateBins + 2 * l];
-      const int h1 = (int)hist[i * kGateBins + 2 * l + 1];
-      const int incl = wave_incl_scan(h0 + h1);
-      const uint64_t hit = __ballot(incl >= ks);
-      const int src = hit ? __builtin_ctzll(hit) : 63;
-      int bstar = 2 * l + ((incl - h1) >= ks ? 0 : 1);
-      bstar = __shfl(bstar, src, 64);
-      if (bstar < kGateBins - 1) thr = r.m0 - (float)(bstar - kGateOff + 1) / r.inv;
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      RowState& r = rs[i];
+      zero_query(qr[i]);
+      frows[i] = -1;
+      if (r.r >= p.rows) continue;
+      const RowInfo ri = p.rowinfo[r.r];
+      r.mode = ri.mode;
+      r.thr = ri.thr;
+      if (r.mode == M_ALL || r.mode == M_GATED) {
+        load_query(qr[i], p.q, p.weights, r.r);
+        frows[i] = r.r;
+        wlo = r.s < wlo ? r.s : wlo;
+        whi = r.e > whi ? r.e : whi;
+      }
     }
-    if (p.flags & 2u) thr = __builtin_inff();  // forced gate miss
-    r.thr = thr;
+    int lo, hi, unused;
+    block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, 0, p.keys, lo, hi, unused);
+    if (hi > lo) {
+      FoldOp fo;
+      build_fold(fo, p.q, p.weights, frows);
+      const SlabRefs sr = slab_refs(p, b, sm.hist[w]);
+      scan_rows<false>(p, stg, qr, fo, rs, M_GATED, lo, hi, sr);
+      if (l == 0) {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+          const RowState& r = rs[i];
+          if (r.mode == M_ALL || r.mode == M_GATED)
+            p.rowinfo[r.r] = RowInfo{r.thr, r.cnt, r.mode, r.strict};
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -604,178 +786,62 @@ __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int 
   return ok_above && ok_below;
 }
 
-// Per-wave setup of a block's rows; writes the output of short rows (n <= k:
-// keys 0..n-1 then -1) in the main pass. Returns the wave's union range of
-// the rows it will scan.
-__device__ __forceinline__ void setup_rows(const FusedParams& p, int b, RowState* rs, QueryRow* qr,
-                                           bool exact_pass, int& wlo, int& whi) {
+// Queue row r (of block r / 32) for the exact rescan; each block is queued
+// once.
+__device__ __forceinline__ void queue_exact(const FusedParams& p, int r) {
+  if (lane_id() != 0) return;
+  p.xrow[r] = 1;
+  const int b = r / kBlockRows;
+  if (atomicExch(&p.xflag[b], 1u) == 0u) p.xqueue[atomicAdd(&p.header[H_XQ], 1u)] = b;
+}
+
+// Select: one wave per row.
+__global__ __launch_bounds__(kSelWaves * kWave) void fused_select_kernel(FusedParams p) {
+  __shared__ uint32_t hist[kSelWaves][kHistWords];
   const int w = wave_id();
   const int l = lane_id();
   const int k = p.topk;
-  const int cap = slab_cap(p);
-  wlo = p.keys;
-  whi = 0;
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    RowState& r = rs[i];
-    init_row(r, b * kBlockRows + w * kRowsPerWave + i);
-    qr[i].qa[0] = qr[i].qa[1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int v = 0; v < 8; ++v) qr[i].w[v] = 0.f;
-    if (r.r >= p.rows) continue;
-    row_range(p, r.r, r.s, r.e);
-    const int n = r.e - r.s;
-    if (exact_pass) {
-      if (n <= k || !p.xrow[r.r]) continue;
-      r.mode = M_EXACT;
-    } else if (n <= k) {
-      r.mode = M_SHORT;
-      int32_t* o = p.out + (int64_t)r.r * k;
-      for (int j = l; j < k; j += kWave) o[j] = j < n ? j : -1;
-      if ((p.flags & 8u) && l == 0) atomicAdd(&p.header[H_SHORT], 1u);
-      if (l == 0) p.xrow[r.r] = 0;
-      continue;
-    } else if (p.flags & 1u) {
-      r.mode = M_EXACT;  // forced: straight to the exact rescan
-    } else if (n <= 4 * k && n <= cap) {
-      r.mode = M_ALL;  // every visible key is a candidate
-    } else {
-      r.mode = M_GATED;
-    }
-    load_query(qr[i], p.q, p.weights, r.r);
-    wlo = r.s < wlo ? r.s : wlo;
-    whi = r.e > whi ? r.e : whi;
-  }
-}
-
-// Slab, merge buffers and histogram of this wave.
-__device__ __forceinline__ SlabRefs slab_refs(const FusedParams& p, FusedSmem& sm, int cap) {
-  const int w = wave_id();
-  SlabRefs sr;
-  sr.baseE = p.slabE + (int64_t)blockIdx.x * kBlockRows * kSlabRow;
-  sr.baseI = p.slabI + (int64_t)blockIdx.x * kBlockRows * kSlabRow;
-  sr.row0 = w * kRowsPerWave;
-  // one raw buffer from the wave's score rows to the end of its key rows (the
-  // host keeps the distance between the two slab arrays below 2^31 bytes)
-  sr.delta = (int)(reinterpret_cast<const char*>(sr.baseI) - reinterpret_cast<const char*>(sr.baseE));
-  sr.buf = __builtin_amdgcn_make_buffer_rsrc(sr.sE(0), 0, sr.delta + kRowsPerWave * kSlabRow * 4,
-                                             kBufferFlags);
-  sr.hist = sm.hist[w];
-  sr.cap = cap;
-  const int keep = 2 * p.topk;
-  sr.keep = keep < cap - kWave ? keep : cap - kWave;
-  return sr;
-}
-
-// The block's union range over the waves' rows and the OR of a per-wave flag.
-__device__ __forceinline__ void block_union(FusedSmem& sm, int wlo, int whi, int flag, int keys,
-                                            int& lo, int& hi, int& any) {
-  const int w = wave_id();
-  if (lane_id() == 0) {
-    sm.wlo[w] = wlo;
-    sm.whi[w] = whi;
-    sm.wg[w] = flag;
-  }
-  __syncthreads();
-  lo = keys;
-  hi = 0;
-  any = 0;
-  for (int i = 0; i < kWaves; ++i) {
-    lo = sm.wlo[i] < lo ? sm.wlo[i] : lo;
-    hi = sm.whi[i] > hi ? sm.whi[i] : hi;
-    any |= sm.wg[i];
-  }
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
-  __shared__ FusedSmem sm;
-  MQA_DECLARE_STAGES(stg);
-  const int tid = threadIdx.x;
-  const int w = wave_id();
-  const int l = lane_id();
-  const int k = p.topk;
-  const int cap = slab_cap(p);
+  const int r = blockIdx.x * kSelWaves + w;
+  if (r >= p.rows) return;
   const bool stats = p.flags & 8u;
-  const SlabRefs sr = slab_refs(p, sm, cap);
-
-  for (;;) {
-    if (tid == 0) sm.block = (int)atomicAdd(&p.header[H_CLAIM], 1u);
-    __syncthreads();
-    const int bi = sm.block;
-    if (bi >= p.nblocks) break;
-    const int b = p.order[bi];
-
-    RowState rs[kRowsPerWave];
-    QueryRow qr[kRowsPerWave];
-    int wlo, whi;
-    setup_rows(p, b, rs, qr, false, wlo, whi);
-    int wgated = 0;
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) wgated |= rs[i].mode == M_GATED;
-    int lo, hi, any_g;
-    block_union(sm, wlo, whi, wgated, p.keys, lo, hi, any_g);
-    int wx = 0;
-    if (hi > lo) {
-      if (any_g) gate_block(p, sm, stg, qr, rs, lo, hi);
-      if (!(p.flags & 1u)) {
-        int frows[kRowsPerWave];
-#pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i)
-          frows[i] = (rs[i].mode == M_ALL || rs[i].mode == M_GATED) ? rs[i].r : -1;
-        FoldOp fo;
-        build_fold(fo, p.q, p.weights, frows);
-        scan_rows<false>(p, stg, qr, fo, rs, M_GATED, lo, hi, sr);
+  const RowInfo ri = p.rowinfo[r];
+  if (ri.mode == M_SHORT || ri.mode == M_OFF) return;
+  bool ok = false;
+  if (ri.mode != M_EXACT) {
+    if (ri.cnt >= k) {
+      int s, e;
+      row_range(p, r, s, e);
+      QueryRow qr;
+      load_query(qr, p.q, p.weights, r);
+      int32_t* o = p.out + (int64_t)r * k;
+      float* sE = p.slabE + (int64_t)r * kSlabRow;
+      int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
+      ok = select_banded(p, sE, sI, ri.cnt, k, ri.thr, qr, hist[w],
+                         stats ? &p.header[H_BAND_LO] : nullptr,
+                         [&](int sl, int idx) { o[sl] = idx - s; });
+      if (stats && l == 0) {
+        atomicAdd(&p.header[ok ? H_GATED : H_UNCERT], 1u);
+        atomicAdd(reinterpret_cast<unsigned long long*>(&p.header[H_CAND_LO]),
+                  (unsigned long long)ri.cnt);
       }
-      // validity check + certified select, per row
-#pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i) {
-        RowState& r = rs[i];
-        if (r.mode == M_OFF || r.mode == M_SHORT) continue;
-        bool ok = false;
-        if (r.mode != M_EXACT) {
-          if (r.cnt >= k) {
-            int32_t* o = p.out + (int64_t)r.r * k;
-            const int base = r.s;
-            ok = select_banded(p, sr.sE(i), sr.sI(i), r.cnt, k, r.thr, qr[i], sr.hist,
-                               stats ? &p.header[H_BAND_LO] : nullptr,
-                               [&](int sl, int idx) { o[sl] = idx - base; });
-            if (stats && l == 0) {
-              atomicAdd(&p.header[ok ? H_GATED : H_UNCERT], 1u);
-              atomicAdd(reinterpret_cast<unsigned long long*>(&p.header[H_CAND_LO]),
-                        (unsigned long long)r.cnt);
-            }
-          } else if (stats && l == 0) {
-            atomicAdd(&p.header[H_UNDER], 1u);
-          }
-        }
-        if (l == 0) p.xrow[r.r] = ok ? 0 : 1;
-        wx |= !ok;
-      }
+    } else if (stats && l == 0) {
+      atomicAdd(&p.header[H_UNDER], 1u);
     }
-    if (l == 0) sm.wx[w] = wx;
-    __syncthreads();
-    if (tid == 0) {
-      int any_x = 0;
-      for (int i = 0; i < kWaves; ++i) any_x |= sm.wx[i];
-      if (any_x) p.xqueue[atomicAdd(&p.header[H_XQ], 1u)] = b;
-    }
-    __syncthreads();
   }
+  if (!ok) queue_exact(p, r);
 }
 
+// ---------------------------------------------------------------------------
 // Exact rescan of the queued blocks: exact (bf16 MFMA) scores of every key of
 // the flagged rows with a streaming top-k merge, then an exact select.
 __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
-  __shared__ FusedSmem sm;
+  __shared__ ScanSmem sm;
   MQA_DECLARE_STAGES(stg);
   const int tid = threadIdx.x;
+  const int w = wave_id();
   const int l = lane_id();
   const int k = p.topk;
-  const int cap = slab_cap(p);
   const int nq = (int)p.header[H_XQ];
-  SlabRefs sr = slab_refs(p, sm, cap);
-  sr.keep = k;
   for (;;) {
     if (tid == 0) sm.block = (int)atomicAdd(&p.header[H_XCLAIM], 1u);
     __syncthreads();
@@ -784,11 +850,23 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
     const int b = p.xqueue[qi];
     RowState rs[kRowsPerWave];
     QueryRow qr[kRowsPerWave];
-    int wlo, whi;
-    setup_rows(p, b, rs, qr, true, wlo, whi);
+    wave_rows(p, b, rs);
+    int wlo = p.keys, whi = 0;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      RowState& r = rs[i];
+      zero_query(qr[i]);
+      if (r.r >= p.rows || r.e - r.s <= k || !p.xrow[r.r]) continue;
+      r.mode = M_EXACT;
+      load_query(qr[i], p.q, p.weights, r.r);
+      wlo = r.s < wlo ? r.s : wlo;
+      whi = r.e > whi ? r.e : whi;
+    }
     int lo, hi, unused;
-    block_union(sm, wlo, whi, 0, p.keys, lo, hi, unused);
+    block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, 0, p.keys, lo, hi, unused);
     if (hi > lo) {
+      SlabRefs sr = slab_refs(p, b, sm.hist[w]);
+      sr.keep = k;
       FoldOp none;
       scan_rows<true>(p, stg, qr, none, rs, M_EXACT, lo, hi, sr);
 #pragma unroll
@@ -812,25 +890,33 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
 
 extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t stream,
                                 hipEvent_t scan_begin, hipEvent_t scan_end) {
+  hipError_t e;
   hipLaunchKernelGGL(mqa::fused_plan_kernel, dim3(1), dim3(1024), 0, stream, *p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
+  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  hipLaunchKernelGGL(mqa::fused_gate_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
+  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (scan_begin && (e = hipEventRecord(scan_begin, stream)) != hipSuccess) return (int)e;
   hipLaunchKernelGGL(mqa::fused_topk_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
+  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (scan_end && (e = hipEventRecord(scan_end, stream)) != hipSuccess) return (int)e;
+  const int sel = (p->rows + mqa::kSelWaves - 1) / mqa::kSelWaves;
+  hipLaunchKernelGGL(mqa::fused_select_kernel, dim3(sel), dim3(mqa::kSelWaves * mqa::kWave), 0,
+                     stream, *p);
+  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   hipLaunchKernelGGL(mqa::fused_exact_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
   return (int)hipGetLastError();
 }
 
 extern "C" int mqa_fused_occupancy(int* wg_per_cu) {
-  int a = 0, b = 0;
+  int a = 0, b = 0, c = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, mqa::fused_topk_kernel,
                                                               mqa::kThreads, 0);
   if (e != hipSuccess) return (int)e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, mqa::fused_exact_kernel, mqa::kThreads, 0);
   if (e != hipSuccess) return (int)e;
-  *wg_per_cu = a < b ? a : b;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, mqa::fused_gate_kernel, mqa::kThreads, 0);
+  if (e != hipSuccess) return (int)e;
+  a = a < b ? a : b;
+  *wg_per_cu = a < c ? a : c;
   return 0;
 }

@@ -7,6 +7,15 @@
 
 namespace mqa {
 
+// Per-row state handed from the gate to the scan and from the scan to the
+// select kernel.
+struct RowInfo {
+  float thr;   // admission threshold
+  int cnt;     // candidates in the row's slab
+  int mode;    // how the row is served (fused.hip RowMode)
+  int strict;  // 1: later candidates had to beat thr strictly (after a merge)
+};
+
 struct FusedParams {
   const uint8_t* q;
   const uint8_t* k;
@@ -21,8 +30,10 @@ struct FusedParams {
   int32_t* order;    // [nblocks] heaviest-first block order
   uint8_t* xrow;     // [rows] 1 = the row needs the exact rescan
   int32_t* xqueue;   // [nblocks] blocks queued for the exact rescan
-  float* slabE;      // [grid][32 rows][kSlabRow] candidate scores
-  int32_t* slabI;    // [grid][32 rows][kSlabRow] candidate keys
+  uint32_t* xflag;   // [nblocks] 1 = the block is queued
+  RowInfo* rowinfo;  // [rows]
+  float* slabE;      // [nblocks * 32 rows][kSlabRow] candidate scores
+  int32_t* slabI;    // [nblocks * 32 rows][kSlabRow] candidate keys
   float* tmpE;       // [grid][8 waves][kTmp] merge buffers
   int32_t* tmpI;
 };
@@ -55,6 +66,9 @@ constexpr int kTmp = 4096;  // merge-buffer records per wave
 // 64 records past it (rows stay 1 KiB aligned).
 constexpr int kSlabRow = 16384 + 256;
 constexpr int kFusedWaves = 8;
+// Rows per launch sequence: larger calls run in batches of this many rows
+// (the workspace holds one batch's candidate slabs, 1.09 GB).
+constexpr int kMaxBatchRows = 16384;
 
 }  // namespace mqa
 
