@@ -66,52 +66,56 @@ __device__ __forceinline__ void row_range(const FusedParams& p, int r, int& s, i
   e = b;
 }
 
-// Cost of a block: the union range its non-short rows scan.
-__device__ __forceinline__ int block_cost(const FusedParams& p, int b) {
-  int lo = p.keys, hi = 0;
-  for (int i = 0; i < kBlockRows; ++i) {
-    const int r = b * kBlockRows + i;
-    if (r >= p.rows) break;
-    int s, e;
-    row_range(p, r, s, e);
-    if (e - s > p.topk) {
-      lo = s < lo ? s : lo;
-      hi = e > hi ? e : hi;
-    }
-  }
-  return hi > lo ? hi - lo : 0;
-}
+// Heaviest-first block order and the reset of the header and of the
+// per-block exact flags. One workgroup. A block's cost is the union range its
+// non-short rows scan (one thread per row, LDS min/max per block); blocks are
+// counting-sorted by cost in 1024 buckets of 1024 keys, descending.
+constexpr int kMaxBlocks = kMaxBatchRows / kBlockRows;
 
-// Heaviest-first block order (counting sort by cost, 1024 buckets of 1024
-// keys, descending), the reset of the header and of the per-block exact
-// flags. One workgroup.
 __global__ __launch_bounds__(1024) void fused_plan_kernel(FusedParams p) {
   __shared__ int cnt[1024];
   __shared__ int off[1024];
+  __shared__ int blo[kMaxBlocks], bhi[kMaxBlocks];
   const int tid = threadIdx.x;
   cnt[tid] = 0;
   if (tid < 64) p.header[tid] = 0;
-  for (int b = tid; b < p.nblocks; b += 1024) p.xflag[b] = 0;
-  __syncthreads();
   for (int b = tid; b < p.nblocks; b += 1024) {
-    const int c = block_cost(p, b) >> 10;
-    atomicAdd(&cnt[c > 1023 ? 1023 : c], 1);
+    p.xflag[b] = 0;
+    blo[b] = p.keys;
+    bhi[b] = 0;
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int c = 1023; c >= 0; --c) {
-      off[c] = acc;
-      acc += cnt[c];
+#pragma unroll 4
+  for (int r = tid; r < p.rows; r += 1024) {
+    int s, e;
+    row_range(p, r, s, e);
+    if (e - s > p.topk) {
+      atomicMin(&blo[r / kBlockRows], s);
+      atomicMax(&bhi[r / kBlockRows], e);
     }
   }
   __syncthreads();
   for (int b = tid; b < p.nblocks; b += 1024) {
-    int c = block_cost(p, b) >> 10;
-    c = c > 1023 ? 1023 : c;
-    const int pos = atomicAdd(&off[c], 1);
-    p.order[pos] = b;
+    const int c = (bhi[b] > blo[b] ? bhi[b] - blo[b] : 0) >> 10;
+    bhi[b] = c > 1023 ? 1023 : c;  // bucket
+    atomicAdd(&cnt[bhi[b]], 1);
   }
+  __syncthreads();
+  // off[c] = number of blocks in buckets above c: a suffix sum over the 1024
+  // buckets (thread t holds bucket 1023 - t; wave scans, then the 16 wave
+  // totals)
+  {
+    const int v = cnt[1023 - tid];
+    const int incl = wave_incl_scan(v);
+    if (lane_id() == kWave - 1) off[tid >> 6] = incl;  // wave totals (off[0..15] reused below)
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < (tid >> 6); ++i) before += off[i];
+    __syncthreads();
+    off[1023 - tid] = before + incl - v;
+  }
+  __syncthreads();
+  for (int b = tid; b < p.nblocks; b += 1024) p.order[atomicAdd(&off[bhi[b]], 1)] = b;
 }
 
 struct RowState {
@@ -309,25 +313,25 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
   }
 }
 
-// Queue direct global->LDS copies of the keys [key0, key0 + kStageKeys)
-// (clamped to the last key) and their scales into a stage buffer. Slot p of
-// the buffer (16 bytes) holds key p / 8, column slice (p % 8) ^ swz(key); each
-// wave fills 64 consecutive slots per copy. The copies are waited for by the
-// barrier that ends the stage before the buffer is read.
-__device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, uint8_t* kdst,
-                                          float* sdst, int tid) {
+// Queue direct global->LDS copies of the keys key0 + j * stride, j <
+// kStageKeys (clamped to the last key), and their scales into a stage buffer.
+// Slot p of the buffer (16 bytes) holds key j = p / 8, column slice (p % 8) ^
+// swz(j); each wave fills 64 consecutive slots per copy. The copies are
+// waited for by the barrier that ends the stage before the buffer is read.
+__device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, int stride,
+                                          uint8_t* kdst, float* sdst, int tid) {
 #pragma unroll
   for (int i = 0; i < kStageChunks * kChunk * 8 / kThreads; ++i) {
     const int slot = tid + i * kThreads;
     const int j = slot >> 3;
     const int c = (slot & 7) ^ swz(j);
-    int key = key0 + j;
+    int key = key0 + j * stride;
     key = key < p.keys ? key : p.keys - 1;
     __builtin_amdgcn_global_load_lds(p.k + (int64_t)key * kDim + 16 * c, kdst + 16 * (slot & ~63),
                                      16, 0, 0);
   }
   if (tid < kStageKeys) {
-    int key = key0 + tid;
+    int key = key0 + tid * stride;
     key = key < p.keys ? key : p.keys - 1;
     __builtin_amdgcn_global_load_lds(p.scales + key, sdst + (tid & ~63), 4, 0, 0);
   }
@@ -425,7 +429,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
   // One stage: queue the copy of the next stage into the other buffer (its
   // last readers passed the previous barrier), then score this one.
   auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext, float* snext) {
-    if (st + 1 < nst) dma_stage(p, lo + (st + 1) * kStageKeys, knext, snext, tid);
+    if (st + 1 < nst) dma_stage(p, lo + (st + 1) * kStageKeys, 1, knext, snext, tid);
 #pragma unroll
     for (int u = 0; u < kStageChunks; ++u) {
       const int c = st * kStageChunks + u;
@@ -433,7 +437,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
     }
     __syncthreads();
   };
-  dma_stage(p, lo, stg.k[0], stg.s[0], tid);
+  dma_stage(p, lo, 1, stg.k[0], stg.s[0], tid);
   __syncthreads();
   for (int st = 0; st < nst; st += 2) {
     stage(st, stg.k[0], stg.s[0], stg.k[1], stg.s[1]);
@@ -442,21 +446,21 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
 }
 
 // ---------------------------------------------------------------------------
-// Gate. A strided sample of the block's keys (1024..4096 keys, span / 16)
-// is scored like the scan scores; each gated row bins (first-tile maximum -
+// Gate. A strided sample of the block's keys (1024..4096 keys, about span /
+// 16, at a fixed integer stride from the start of the block's range) is
+// scored like the scan scores; each gated row bins (first-tile maximum -
 // score) in kGateBins bins of 1/64 of the first sample tile's score range and
 // takes as threshold the bin edge whose sample count, scaled by n / sample,
 // reaches 2k. Rows with n <= k are answered here (keys 0..n-1, -1 padding).
 struct __align__(16) GateSmem {
-  uint8_t kbuf[kChunkBytes];
   uint32_t hist[kWaves][kRowsPerWave * kGateBins];
-  int gath[kChunk];
   int block;
   int wlo[kWaves], whi[kWaves], wf[kWaves];
 };
 
 __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
   __shared__ GateSmem sm;
+  MQA_DECLARE_STAGES(stg);
   const int tid = threadIdx.x;
   const int w = wave_id();
   const int l = lane_id();
@@ -504,10 +508,12 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
     if (any_g && hi > lo) {
       FoldOp fo;
       build_fold(fo, p.q, p.weights, frows);
+      // S sample keys lo + j * stride, j < S (S a multiple of the stage size)
       const int span = hi - lo;
-      int S = (span / 16) & ~(kChunk - 1);
+      int S = (span / 16) & ~(kStageKeys - 1);
       S = S < 1024 ? 1024 : (S > 4096 ? 4096 : S);
-      const int nch = S / kChunk;
+      const int stride = span / S > 1 ? span / S : 1;
+      const int nst = S / kStageKeys;
       uint32_t* hist = sm.hist[w];
       for (int i = l; i < kRowsPerWave * kGateBins; i += kWave) hist[i] = 0;
       float m0[kRowsPerWave], inv[kRowsPerWave];
@@ -519,18 +525,12 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
         have_m0[i] = 0;
         nsamp[i] = 0;
       }
-      uint4 regs[1];
-      for (int c = 0; c < nch; ++c) {
-        if (tid < kChunk) sm.gath[tid] = lo + (int)(((int64_t)(c * kChunk + tid) * span) / S);
-        __syncthreads();
-        stage_chunk_regs(regs, p.k, 0, p.keys, tid, kThreads, sm.gath);
-        store_chunk_regs(regs, sm.kbuf, tid, kThreads);
-        __syncthreads();
-        const int key = sm.gath[l];
+      auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
+        const int key = lo + (c * kChunk + l) * stride;
         KeyTile kt;
-        load_keys_lds(kt, sm.kbuf);
+        load_keys_lds(kt, kc);
         float E[4];
-        score4(E, qr, fo, kt, p.scales[key]);
+        score4(E, qr, fo, kt, scl[l]);
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) {
           const RowState& r = rs[i];
@@ -557,7 +557,21 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
             atomicAdd(&hist[i * kGateBins + bin], 1u);
           }
         }
+      };
+      auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext,
+                       float* snext) {
+        if (st + 1 < nst)
+          dma_stage(p, lo + (st + 1) * kStageKeys * stride, stride, knext, snext, tid);
+#pragma unroll
+        for (int u = 0; u < kStageChunks; ++u)
+          chunk(st * kStageChunks + u, kcur + u * kChunkBytes, scur + u * kChunk);
         __syncthreads();
+      };
+      dma_stage(p, lo, stride, stg.k[0], stg.s[0], tid);
+      __syncthreads();
+      for (int st = 0; st < nst; st += 2) {
+        stage(st, stg.k[0], stg.s[0], stg.k[1], stg.s[1]);
+        if (st + 1 < nst) stage(st + 1, stg.k[1], stg.s[1], stg.k[0], stg.s[0]);
       }
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
