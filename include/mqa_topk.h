@@ -66,7 +66,9 @@ extern "C" {
                                        mqa_scan_time); a benchmarking aid */
 
 /* Counters written to the first bytes of the workspace when MQA_FLAG_STATS is
- * set (read them after the stream has finished the call). */
+ * set (read them after the stream has finished the call). A call over more
+ * than 16384 rows runs in batches of 16384 rows that share the workspace; the
+ * counters then describe the last batch. */
 typedef struct mqa_stats {
   uint32_t claim_counter;   /* internal: blocks claimed (== number of blocks) */
   uint32_t rows_short;      /* rows with n <= k (no scoring) */

@@ -120,6 +120,8 @@ def test_fused_all_rows(cfg):
     fails = check.check_topk(o, np.arange(wl.rows), oracle_problem(wl), wl.topk, TOL)
     assert not fails, fails[:5]
     assert st["rows_gated"] + st["rows_exact"] + st["rows_short"] == wl.rows
+    # the fused path (gate + certified select) serves every scored row
+    assert st["rows_exact"] == 0 and st["rows_uncertified"] == 0 and st["rows_undercount"] == 0
 
 
 def test_scan_timing_flag():
@@ -192,4 +194,61 @@ def test_fused_large_sampled(cfg):
     assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, wl.topk)
     rows = W.sample_rows(wl, 256)
     fails = check.check_topk(o[rows], rows, oracle_problem(wl), wl.topk, TOL)
+    assert not fails, fails[:5]
+    scored = wl.rows - st["rows_short"]
+    assert st["rows_gated"] + st["rows_exact"] == scored
+    if cfg in (3, 4):
+        # i.i.d. keys: the fused path serves every row, none falls back
+        assert st["rows_gated"] == scored and st["rows_exact"] == 0
+
+
+@pytest.mark.parametrize("which", ["x1_common_offset", "x2_elementwise_ties"])
+def test_fused_extra_cases(which):
+    wl = (W.extra_common_offset() if which == "x1_common_offset"
+          else W.extra_elementwise_ties())
+    say(f"case: fused {wl.name}; validity all rows, set rule on 64 rows")
+    d = to_device(wl)
+    ws = mqa.alloc_workspace(wl.rows)
+    out = fused(d, wl.topk, flags=mqa.FLAG_STATS, workspace=ws)
+    st = mqa.read_stats(ws)
+    say("stats", st)
+    o = out.cpu().numpy()
+    del d
+    assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, wl.topk)
+    rows = W.sample_rows(wl, 64)
+    fails = check.check_topk(o[rows], rows, oracle_problem(wl), wl.topk, TOL)
+    assert not fails, fails[:5]
+
+
+@pytest.mark.parametrize("keys,topk", [(32768, 512), (262144, 2048)])
+def test_fused_sweep_points(keys, topk):
+    wl = W.sweep(keys, topk)
+    say(f"case: fused {wl.name}; validity all rows, set rule on 64 rows")
+    d = to_device(wl)
+    out = fused(d, wl.topk)
+    o = out.cpu().numpy()
+    del d
+    assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, wl.topk)
+    rows = W.sample_rows(wl, 64)
+    fails = check.check_topk(o[rows], rows, oracle_problem(wl), wl.topk, TOL)
+    assert not fails, fails[:5]
+
+
+def test_fused_row_batches():
+    # more rows than one launch sequence takes: the call runs in two batches
+    rows, keys, topk = 16384 + 96, 4096, 512
+    i = np.arange(rows, dtype=np.int64)
+    st = np.zeros(rows, np.int32)
+    en = (keys - 1 - (i % 1024)).astype(np.int32)
+    wl = W.custom(rows, keys, topk, st, en, seed=21, name="batches_16480x4096_k512")
+    say(f"case: fused {wl.name} (two row batches); all rows checked")
+    d = to_device(wl)
+    ws = mqa.alloc_workspace(wl.rows)
+    out = fused(d, topk, flags=mqa.FLAG_STATS, workspace=ws)
+    st_ = mqa.read_stats(ws)
+    say("stats (last batch)", st_)
+    o = out.cpu().numpy()
+    assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, topk)
+    rows_all = np.arange(rows)
+    fails = check.check_topk(o, rows_all, oracle_problem(wl), topk, TOL)
     assert not fails, fails[:5]
