@@ -18,7 +18,9 @@ Prints ONE JSON line (rank 0):
              host's cores over a bounded sample of the same rows.
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu,
 --dense (also time the chunked dense logits + top-k path, for context),
---config N (workload 1..5), --copy-calibration MIB (instead of the benchmark,
+--config N (workload 1..5), --sweep (instead of the benchmark: fused and
+dense times on the causal-tail sweep, 16384 rows x 16K..1M keys, one JSON line
+per point), --copy-calibration MIB (instead of the benchmark,
 run a plain 1-D device copy of MIB MiB five times: the known-size kernel that
 scales rocprofv3's FETCH_SIZE / WRITE_SIZE readings to bytes).
 """
@@ -138,6 +140,73 @@ def time_dense(d, wl, steps: int, warmup: int):
     return ev0.elapsed_time(ev1) / steps, len(chunks)
 
 
+def to_device(wl, dev):
+    import torch
+
+    import fp8_mqa_logits_amd as mqa
+    d = {
+        "q": torch.from_numpy(wl.q).to(dev),
+        "k": torch.from_numpy(wl.k).to(dev),
+        "weights": torch.from_numpy(wl.weights).to(dev),
+        "starts": torch.from_numpy(wl.starts).to(dev),
+        "ends": torch.from_numpy(wl.ends).to(dev),
+    }
+    d["scales"] = mqa.mqa_key_scales(torch.from_numpy(wl.scale_bytes).to(dev))
+    return d
+
+
+def time_fused(d, wl, steps: int, warmup: int):
+    import torch
+
+    import fp8_mqa_logits_amd as mqa
+    ws = mqa.alloc_workspace(wl.rows)
+    out = torch.empty((wl.rows, wl.topk), dtype=torch.int32, device="cuda")
+
+    def step():
+        mqa.mqa_topk_prefill(d["q"], d["k"], d["scales"], d["weights"], d["starts"], d["ends"],
+                             wl.topk, out=out, workspace=ws)
+    mqa.mqa_topk_prefill(d["q"], d["k"], d["scales"], d["weights"], d["starts"], d["ends"],
+                         wl.topk, out=out, workspace=ws, flags=mqa.FLAG_STATS)
+    stats = mqa.read_stats(ws)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps, stats
+
+
+def sweep(args):
+    """Fused vs dense on the causal tail of K-key contexts (16384 rows)."""
+    import gc
+
+    import torch
+
+    import mqa_workloads as W
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    for topk in (2048, 512):
+        for keys in (16384, 32768, 65536, 131072, 262144, 524288, 1048576):
+            wl = W.sweep(keys, topk)
+            d = to_device(wl, dev)
+            fms, stats = time_fused(d, wl, 5, 2)
+            dms, ncalls = time_dense(d, wl, 2 if keys >= 262144 else 3, 1)
+            pairs = wl.visible_pairs()
+            print(json.dumps({"sweep": wl.name, "keys": keys, "topk": topk, "rows": wl.rows,
+                              "visible_pairs": pairs, "fused_ms": fms, "dense_ms": dms,
+                              "dense_call_pairs": ncalls, "fused_over_dense": dms / fms,
+                              "fused_tflops": pairs * FLOP_PER_PAIR / (fms / 1e3) / 1e12,
+                              "path_stats": stats}),
+                  flush=True)
+            del d
+            gc.collect()
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +216,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--dense", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--sweep", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this path runs on one GPU; multi-GPU runs are not supported "
@@ -168,6 +238,10 @@ def main():
     sys.path.insert(0, ROOT)
     import fp8_mqa_logits_amd as mqa
     import mqa_workloads as W
+
+    if args.sweep:
+        sweep(args)
+        return
 
     wl = W.config(args.config)
     print(f"[bench] workload {wl.name}: {wl.visible_pairs()} visible pairs, hashes "

@@ -450,8 +450,8 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
 // 16, at a fixed integer stride from the start of the block's range) is
 // scored like the scan scores; each gated row bins (first-tile maximum -
 // score) in kGateBins bins of 1/64 of the first sample tile's score range and
-// takes as threshold the bin edge whose sample count, scaled by n / sample,
-// reaches 2k. Rows with n <= k are answered here (keys 0..n-1, -1 padding).
+// takes as threshold the lower score edge of the bin where the count of sample keys
+// above reaches a safe margin over the k-th key's expected sample rank. Rows with n <= k are answered here (keys 0..n-1, -1 padding).
 struct __align__(16) GateSmem {
   uint32_t hist[kWaves][kRowsPerWave * kGateBins];
   int block;
@@ -577,9 +577,14 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
       for (int i = 0; i < kRowsPerWave; ++i) {
         RowState& r = rs[i];
         if (r.mode != M_GATED) continue;
+        // The sample keys above the row's true k-th score are about
+        // Poisson(lam), lam = k * nsamp / n. The threshold is put at the
+        // ks-th best sample, ks = lam + 5 sqrt(lam) + 5, so that fewer than k
+        // keys pass it with probability below ~1e-6 (about 1.5k candidates
+        // at lam ~ 150, more when the sample is thin).
         const int n = r.e - r.s;
-        const int64_t target = 2 * (int64_t)k;
-        const int ks = (int)((target * nsamp[i] + n - 1) / n);
+        const float lam = (float)k * (float)nsamp[i] / (float)n;
+        const int ks = (int)__builtin_ceilf(lam + 5.f * __builtin_sqrtf(lam) + 5.f);
         float thr = -__builtin_inff();
         if (have_m0[i] && ks >= 1 && ks <= nsamp[i]) {
           // bins 2l, 2l+1 per lane, cumulative from bin 0 (the top)
