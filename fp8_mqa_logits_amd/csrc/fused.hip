@@ -34,8 +34,8 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kRowsPerWave = 4;
 constexpr int kBlockRows = kWaves * kRowsPerWave;  // 32
 static_assert(kBlockRows == kFusedBlockRows, "block rows");
-constexpr int kGateBins = 128;
-constexpr int kGateOff = 16;  // bins above the first-tile maximum
+constexpr int kGateBins = 512;
+constexpr int kGateOff = 64;  // bins above the first-tile maximum
 constexpr int kHistWords = 2048;
 constexpr int kBand = 32;           // keys on each side of rank k that are rescored exactly
 constexpr float kBandSafety = 8.f;  // certificate margin, in units of the band's largest error
@@ -449,7 +449,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
 // Gate. A strided sample of the block's keys (1024..4096 keys, about span /
 // 16, at a fixed integer stride from the start of the block's range) is
 // scored like the scan scores; each gated row bins (first-tile maximum -
-// score) in kGateBins bins of 1/64 of the first sample tile's score range and
+// score) in kGateBins bins of 1/256 of the first sample tile's score range and
 // takes as threshold the lower score edge of the bin where the count of sample keys
 // above reaches a safe margin over the k-th key's expected sample rank. Rows with n <= k are answered here (keys 0..n-1, -1 padding).
 struct __align__(16) GateSmem {
@@ -541,9 +541,9 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
           if (!have_m0[i]) {
             const float mx = wave_max(valid ? E[i] : -__builtin_inff());
             const float mn = wave_min(valid ? E[i] : __builtin_inff());
-            float width = (mx - mn) / 64.f;
+            float width = (mx - mn) / 256.f;
             if (!(width > 0.f) || !__builtin_isfinite(width))
-              width = __builtin_fmaxf(__builtin_fabsf(mx), 1e-30f) * (1.f / 128.f);
+              width = __builtin_fmaxf(__builtin_fabsf(mx), 1e-30f) * (1.f / 512.f);
             m0[i] = mx;
             inv[i] = 1.f / width;
             have_m0[i] = 1;
@@ -587,15 +587,28 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
         const int ks = (int)__builtin_ceilf(lam + 5.f * __builtin_sqrtf(lam) + 5.f);
         float thr = -__builtin_inff();
         if (have_m0[i] && ks >= 1 && ks <= nsamp[i]) {
-          // bins 2l, 2l+1 per lane, cumulative from bin 0 (the top)
-          const int h0 = (int)hist[i * kGateBins + 2 * l];
-          const int h1 = (int)hist[i * kGateBins + 2 * l + 1];
-          const int incl = wave_incl_scan(h0 + h1);
+          // bins kPer*l .. kPer*l + kPer-1 per lane, cumulative from bin 0 (the top)
+          constexpr int kPer = kGateBins / kWave;
+          int hv[kPer], hsum = 0;
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) {
+            hv[j] = (int)hist[i * kGateBins + kPer * l + j];
+            hsum += hv[j];
+          }
+          const int incl = wave_incl_scan(hsum);
           const uint64_t hit = __ballot(incl >= ks);
-          const int src = hit ? __builtin_ctzll(hit) : 63;
-          int bstar = 2 * l + ((incl - h1) >= ks ? 0 : 1);
-          bstar = __shfl(bstar, src, 64);
-          if (bstar < kGateBins - 1) thr = m0[i] - (float)(bstar - kGateOff + 1) / inv[i];
+          int c = incl - hsum, bstar = kPer * l + kPer - 1;
+          // first bin of this lane where the running count reaches ks
+          bool found = false;
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) {
+            const bool here = !found && c + hv[j] >= ks;
+            bstar = here ? kPer * l + j : bstar;
+            found = found || here;
+            c += hv[j];
+          }
+          bstar = __shfl(bstar, hit ? __builtin_ctzll(hit) : 0, 64);
+          if (hit && bstar < kGateBins - 1) thr = m0[i] - (float)(bstar - kGateOff + 1) / inv[i];
         }
         if (p.flags & 2u) thr = __builtin_inff();  // forced gate miss
         r.thr = thr;
