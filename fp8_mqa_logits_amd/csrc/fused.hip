@@ -754,11 +754,8 @@ __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int 
   __builtin_amdgcn_wave_barrier();
   int na = 0, nb = 0;
   float min_above = __builtin_inff(), max_below = -__builtin_inff();
-  for (int i0 = 0; i0 < n; i0 += kWave) {
-    const int i = i0 + l;
-    const bool in = i < n;
-    const float e = in ? sE[i] : 0.f;
-    const int32_t idx = in ? sI[i] : 0;
+  // One record: taken (above the band), compacted into the band, or below.
+  auto visit = [&](bool in, float e, int32_t idx) {
     const int b = bin_of(e);
     const bool up = in && b < b_hi;
     const bool band = in && b >= b_hi && b <= b_lo;
@@ -770,7 +767,7 @@ __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int 
       min_above = __builtin_fminf(min_above, e);
     }
     if (in && b > b_lo) max_below = __builtin_fmaxf(max_below, e);
-    // in-place compaction: targets lie at or before this chunk, already read
+    // in-place compaction: the targets lie in records already loaded
     if (band) {
       const int pos = nb + rank_in_mask(mb);
       sE[pos] = e;
@@ -778,6 +775,28 @@ __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int 
     }
     na += __popcll(mu);
     nb += __popcll(mb);
+  };
+  // groups of 4 consecutive records per lane (256 per wave step), the next
+  // group's loads issued before the current group is visited
+  const int4* i4 = reinterpret_cast<const int4*>(sI);
+  float4 ev = l < n4 ? e4[l] : float4{0.f, 0.f, 0.f, 0.f};
+  int4 iv = l < n4 ? i4[l] : int4{0, 0, 0, 0};
+  for (int g0 = 0; g0 < n4; g0 += kWave) {
+    const bool in = g0 + l < n4;
+    const int gn = g0 + kWave + l;
+    const float4 en = gn < n4 ? e4[gn] : float4{0.f, 0.f, 0.f, 0.f};
+    const int4 inx = gn < n4 ? i4[gn] : int4{0, 0, 0, 0};
+    visit(in, ev.x, iv.x);
+    visit(in, ev.y, iv.y);
+    visit(in, ev.z, iv.z);
+    visit(in, ev.w, iv.w);
+    ev = en;
+    iv = inx;
+  }
+  {
+    const int i = 4 * n4 + l;
+    const bool in = i < n;
+    visit(in, in ? sE[i] : 0.f, in ? sI[i] : 0);
   }
   min_above = wave_min(min_above);
   max_below = wave_max(max_below);
