@@ -608,7 +608,20 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
             c += hv[j];
           }
           bstar = __shfl(bstar, hit ? __builtin_ctzll(hit) : 0, 64);
-          if (hit && bstar < kGateBins - 1) thr = m0[i] - (float)(bstar - kGateOff + 1) / inv[i];
+          // The threshold goes halfway down the run of empty bins below bstar
+          // (to the next sampled score), not at bstar's lower edge: when the
+          // scores are heavily tied the k-th key's score sits at the top of a
+          // wide gap, and the select's certificate needs that gap as margin.
+          int b2 = kGateBins;
+#pragma unroll
+          for (int j = kPer - 1; j >= 0; --j)
+            b2 = (kPer * l + j > bstar && hv[j] > 0) ? kPer * l + j : b2;
+          b2 = -wave_max_i(-b2);
+          if (hit && bstar < kGateBins - 1) {
+            const float lower = (float)(bstar - kGateOff + 1);  // bstar's lower score edge
+            const float next = (float)(b2 - kGateOff);           // upper edge of the next sample
+            thr = m0[i] - (b2 < kGateBins ? 0.5f * (lower + next) : lower) / inv[i];
+          }
         }
         if (p.flags & 2u) thr = __builtin_inff();  // forced gate miss
         r.thr = thr;
