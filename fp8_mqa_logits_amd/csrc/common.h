@@ -587,32 +587,19 @@ __device__ __forceinline__ int first_bin_reaching(const uint32_t* hist, int nb, 
 }
 
 // ---------------------------------------------------------------------------
-// Wave-level exact top-k select over n (score, key) records held in global
-// memory (E[i], I[i]). Radix select on the order-preserving uint32 of the
-// score with digits of 11, 11 and 10 bits, counted in an LDS histogram of
-// 2048 words private to the wave; then one output pass. Records strictly
-// above the selected prefix are all taken; records equal to it fill the
-// remaining slots in slab order (any subset of ties at the k-th score is a
-// correct answer). `emit(slot, score, key)` is called once per selected
-// record with distinct slots in [0, min(n, k)). Returns the smallest selected
-// score (or +inf when nothing is selected).
-template <class Emit>
-__device__ float wave_select(const float* __restrict__ E, const int* __restrict__ I, int n,
-                             int k, uint32_t* hist, Emit emit) {
-  const int l = lane_id();
-  // the records were stored by this wave: make them visible to all its lanes
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  if (n <= k) {
-    float mn = __builtin_inff();
-    for (int i = l; i < n; i += kWave) {
-      const float e = E[i];
-      emit(i, e, I[i]);
-      mn = __builtin_fminf(mn, e);
-    }
-    return wave_min(mn);
-  }
-  uint32_t prefix = 0, pmask = 0;
-  int need = k;
+// Radix search of the wave-level selects below: the order-preserving key of
+// the k-th best of E[0..n) (n > k) is found 11, 11 and 10 bits at a time in
+// an LDS histogram of 2048 words private to the wave. On return the records
+// whose key matches `prefix` under `pmask` are the ties of the k-th best
+// (pmask stops short of all 32 bits when every record matching the prefix so
+// far belongs to the best k), records above the prefix are all among the best
+// k, and `need` of the ties complete them.
+__device__ __forceinline__ void radix_search(const float* __restrict__ E, int n, int k,
+                                             uint32_t* hist, uint32_t& prefix, uint32_t& pmask,
+                                             int& need) {
+  prefix = 0;
+  pmask = 0;
+  need = k;
   bool done = false;
   const int shifts[3] = {21, 10, 0};
   const int widths[3] = {11, 11, 10};
@@ -629,6 +616,33 @@ __device__ float wave_select(const float* __restrict__ E, const int* __restrict_
     if (cnt == need) done = true;
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// Wave-level exact top-k select over n (score, key) records held in global
+// memory (E[i], I[i]), then one output pass. Records strictly above the
+// selected prefix are all taken; records equal to it fill the remaining slots
+// in slab order (any subset of ties at the k-th score is a correct answer).
+// `emit(slot, score, key)` is called once per selected record with distinct
+// slots in [0, min(n, k)). Returns the smallest selected score (or +inf when
+// nothing is selected).
+template <class Emit>
+__device__ float wave_select(const float* __restrict__ E, const int* __restrict__ I, int n,
+                             int k, uint32_t* hist, Emit emit) {
+  const int l = lane_id();
+  // the records were stored by this wave: make them visible to all its lanes
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  if (n <= k) {
+    float mn = __builtin_inff();
+    for (int i = l; i < n; i += kWave) {
+      const float e = E[i];
+      emit(i, e, I[i]);
+      mn = __builtin_fminf(mn, e);
+    }
+    return wave_min(mn);
+  }
+  uint32_t prefix, pmask;
+  int need;
+  radix_search(E, n, k, hist, prefix, pmask, need);
   // output: strictly-above records fill slots [0, k - need), ties the rest
   const int n_above = k - need;
   int taken_above = 0, taken_tie = 0;
@@ -664,6 +678,55 @@ __device__ float wave_select(const float* __restrict__ E, const int* __restrict_
     taken_tie += __popcll(mt);
   }
   return wave_min(mn);
+}
+
+// The best k of n > k records as wave_select picks them, widened by every
+// record tied with the k-th best while no more than `room` (>= k) records
+// are taken in all. emit(slot, score, key) fills slots [0, taken); returns
+// taken. `bound` receives a score that every record left out is at most
+// (and every taken record beats): the best left-out score when all ties were
+// taken, else the k-th best score itself (then exactly k are taken).
+template <class Emit>
+__device__ int wave_select_ties(const float* __restrict__ E, const int* __restrict__ I, int n,
+                                int k, int room, uint32_t* hist, float& bound, Emit emit) {
+  const int l = lane_id();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  uint32_t prefix, pmask;
+  int need;
+  radix_search(E, n, k, hist, prefix, pmask, need);
+  const int n_above = k - need;
+  const int tie_room = room - n_above;
+  int taken_above = 0, taken_tie = 0;
+  float below = -__builtin_inff();
+  for (int i0 = 0; i0 < n; i0 += kWave) {
+    const int i = i0 + l;
+    uint32_t key = 0;
+    float e = 0.f;
+    if (i < n) {
+      e = E[i];
+      key = fkey(e);
+    }
+    const bool in = i < n;
+    const bool up = in && (key & pmask) > prefix;
+    const bool tie = in && (key & pmask) == prefix;
+    const uint64_t mu = __ballot(up);
+    const uint64_t mt = __ballot(tie);
+    if (up) emit(taken_above + rank_in_mask(mu), e, I[i]);
+    if (tie) {
+      const int rk = taken_tie + rank_in_mask(mt);
+      if (rk < tie_room) emit(n_above + rk, e, I[i]);
+    }
+    if (in && !up && !tie) below = __builtin_fmaxf(below, e);
+    taken_above += __popcll(mu);
+    taken_tie += __popcll(mt);
+  }
+  if (taken_tie <= tie_room) {
+    bound = wave_max(below);
+    return n_above + taken_tie;
+  }
+  // more ties than room: the prefix is the whole key of the k-th best score
+  bound = kfloat(prefix);
+  return k;
 }
 
 }  // namespace mqa

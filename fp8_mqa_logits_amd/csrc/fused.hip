@@ -215,12 +215,14 @@ struct SlabRefs {
   __amdgpu_buffer_rsrc_t buf;  // raw buffer from sE0 through the end of the wave's key rows
   int delta;                   // byte distance from the score rows to the key rows
   uint32_t* hist;
-  int cap, keep;
+  int cap;   // a row merges once it holds more records than this
+  int keep;  // records a merge keeps (ties of the last one aside)
   __device__ float* sE(int i) const { return sE0 + i * kSlabRow; }
   __device__ int32_t* sI(int i) const { return sI0 + i * kSlabRow; }
 };
 
-__device__ __forceinline__ SlabRefs slab_refs(const FusedParams& p, int b, uint32_t* hist) {
+__device__ __forceinline__ SlabRefs slab_refs(const FusedParams& p, int b, uint32_t* hist,
+                                              int keep) {
   SlabRefs sr;
   const int64_t row0 = (int64_t)b * kBlockRows + wave_id() * kRowsPerWave;
   sr.sE0 = p.slabE + row0 * kSlabRow;
@@ -230,7 +232,6 @@ __device__ __forceinline__ SlabRefs slab_refs(const FusedParams& p, int b, uint3
                                              kBufferFlags);
   sr.hist = hist;
   sr.cap = slab_cap(p);
-  const int keep = 2 * p.topk;
   sr.keep = keep < sr.cap - kWave ? keep : sr.cap - kWave;
   return sr;
 }
@@ -271,9 +272,16 @@ __device__ __forceinline__ void finish_row(RowState& r, float E, float th, int k
 }
 
 // Streaming top-k merge: every row whose slab went past `cap` is cut down to
-// its `keep` best records by score, and its admission threshold rises to the
-// smallest of them (later records must beat it strictly). One merge site for
-// the wave's rows, so the select code appears once in the scan loop.
+// its `keep` best records, widened by the records tied with the keep-th best
+// while they fit in `room`; the admission threshold rises to a score that
+// every dropped record is at most (later records must beat it strictly):
+// the best dropped score when every tie stayed, so that rows of heavily tied
+// scores keep a gap between the threshold and their k-th score, else the
+// keep-th best score. One merge site for the wave's rows, so the select code
+// appears once in the scan loop.
+// The gated scan records the new threshold in the row's RowInfo at once
+// (the row state keeps only the admission bound th).
+template <bool EXACT>
 __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, const SlabRefs& sr,
                                            float* th) {
   unsigned todo = 0;
@@ -290,13 +298,16 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
 #pragma unroll
     for (int j = 1; j < kRowsPerWave; ++j)
       if (i == j) cnt = rs[j].cnt;
-    const float kth = wave_select(sE, sI, cnt, sr.keep, sr.hist,
-                                  [&](int slot, float e, int idx) {
-                                    tE[slot] = e;
-                                    tI[slot] = idx;
-                                  });
+    // the ties may fill half the room above `keep` (and the merge buffers)
+    const int half = (sr.cap + sr.keep) >> 1;
+    float bound;
+    const int kept = wave_select_ties(sE, sI, cnt, sr.keep, half < kTmp ? half : kTmp, sr.hist, bound,
+                                      [&](int slot, float e, int idx) {
+                                        tE[slot] = e;
+                                        tI[slot] = idx;
+                                      });
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    for (int t = lane_id(); t < sr.keep; t += kWave) {
+    for (int t = lane_id(); t < kept; t += kWave) {
       sE[t] = tE[t];
       sI[t] = tI[t];
     }
@@ -304,10 +315,12 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
 #pragma unroll
     for (int j = 0; j < kRowsPerWave; ++j)
       if (i == j) {
-        rs[j].cnt = sr.keep;
-        rs[j].thr = kth;
-        rs[j].strict = 1;
-        th[j] = next_up(kth);
+        rs[j].cnt = kept;
+        th[j] = next_up(bound);
+        if (!EXACT && lane_id() == 0) {
+          p.rowinfo[rs[j].r].thr = bound;
+          p.rowinfo[rs[j].r].strict = 1;
+        }
       }
     if ((p.flags & 8u) && lane_id() == 0) atomicAdd(&p.header[H_COMPACT], 1u);
   }
@@ -392,31 +405,36 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
   auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
     const int key0 = lo + c * kChunk;
     const int key = key0 + l;
-    const float sc = scl[l];
-    const bool fast = c >= cf && c < ch;
-    bool act[kRowsPerWave];
-    bool any = fast;
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      act[i] = live[i] && rs[i].s < key0 + kChunk && rs[i].e > key0;
-      any |= act[i];
-    }
-    if (!any) return;
-    KeyTile kt;
-    load_keys_lds(kt, kc);
-    float E[4];
-    if (EXACT) {
-#pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i)
-        E[i] = act[i] ? score_chunk_exact(qr[i], kt) * sc : 0.f;
-    } else {
-      // rows that are not live have zeroed operands and never emit
+    if (!EXACT && c >= cf && c < ch) {
+      // interior chunk: no per-row range tests
+      const float sc = scl[l];
+      KeyTile kt;
+      load_keys_lds(kt, kc);
+      float E[4];
       score4(E, qr, fo, kt, sc);
-    }
-    if (!EXACT && fast) {
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) emit_rec(rs[i], E[i], th[i], true, key, sr, i);
     } else {
+      bool act[kRowsPerWave];
+      bool any = false;
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        act[i] = live[i] && rs[i].s < key0 + kChunk && rs[i].e > key0;
+        any |= act[i];
+      }
+      if (!any) return;
+      const float sc = scl[l];
+      KeyTile kt;
+      load_keys_lds(kt, kc);
+      float E[4];
+      if (EXACT) {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i)
+          E[i] = act[i] ? score_chunk_exact(qr[i], kt) * sc : 0.f;
+      } else {
+        // rows that are not live have zeroed operands and never emit
+        score4(E, qr, fo, kt, sc);
+      }
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i)
         if (act[i]) finish_row(rs[i], E[i], th[i], key, key0, sr, i);
@@ -424,7 +442,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
     bool over = false;
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) over |= rs[i].cnt > sr.cap;
-    if (over) merge_rows(p, rs, sr, th);
+    if (over) merge_rows<EXACT>(p, rs, sr, th);
   };
   // One stage: queue the copy of the next stage into the other buffer (its
   // last readers passed the previous barrier), then score this one.
@@ -687,14 +705,13 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
     if (hi > lo) {
       FoldOp fo;
       build_fold(fo, p.q, p.weights, frows);
-      const SlabRefs sr = slab_refs(p, b, sm.hist[w]);
+      const SlabRefs sr = slab_refs(p, b, sm.hist[w], 2 * p.topk);
       scan_rows<false>(p, stg, qr, fo, rs, M_GATED, lo, hi, sr);
       if (l == 0) {
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) {
           const RowState& r = rs[i];
-          if (r.mode == M_ALL || r.mode == M_GATED)
-            p.rowinfo[r.r] = RowInfo{r.thr, r.cnt, r.mode, r.strict};
+          if (r.mode == M_ALL || r.mode == M_GATED) p.rowinfo[r.r].cnt = r.cnt;
         }
       }
     }
@@ -929,8 +946,7 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
     int lo, hi, unused;
     block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, 0, p.keys, lo, hi, unused);
     if (hi > lo) {
-      SlabRefs sr = slab_refs(p, b, sm.hist[w]);
-      sr.keep = k;
+      SlabRefs sr = slab_refs(p, b, sm.hist[w], k);
       FoldOp none;
       scan_rows<true>(p, stg, qr, none, rs, M_EXACT, lo, hi, sr);
 #pragma unroll

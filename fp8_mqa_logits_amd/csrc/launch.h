@@ -61,7 +61,7 @@ struct DenseTopkParams {
 };
 
 constexpr int kFusedBlockRows = 32;
-constexpr int kTmp = 4096;  // merge-buffer records per wave
+constexpr int kTmp = 10240;  // merge-buffer records per wave
 // Records per slab row: a capacity of 16384 plus room for one more chunk of
 // 64 records past it (rows stay 1 KiB aligned).
 constexpr int kSlabRow = 16384 + 256;
