@@ -24,6 +24,7 @@ FLAG_FORCE_GATE_MISS = 2
 FLAG_SMALL_CAP = 4
 FLAG_STATS = 8
 FLAG_TIME_SCAN = 16
+FLAG_FORCE_RESCAN = 32
 
 ERR_NAMES = {0: "MQA_OK", 1: "MQA_ERR_NULL", 2: "MQA_ERR_ALIGN", 3: "MQA_ERR_SHAPE",
              4: "MQA_ERR_WORKSPACE", 5: "MQA_ERR_DEVICE", 6: "MQA_ERR_LAUNCH"}
@@ -220,7 +221,7 @@ def read_stats(workspace: torch.Tensor) -> dict:
     """The mqa_stats header of a workspace used with FLAG_STATS (synchronizes)."""
     h = workspace[:64].cpu().numpy().view("<u4")
     return {"rows_short": int(h[1]), "rows_gated": int(h[2]), "rows_exact": int(h[3]),
-            "rows_overflow": int(h[4]), "rows_undercount": int(h[5]),
+            "rows_rescanned": int(h[4]), "rows_undercount": int(h[5]),
             "compactions": int(h[6]), "rows_uncertified": int(h[7]),
             "candidates": int(h[8]) | (int(h[9]) << 32),
             "band_keys": int(h[10]) | (int(h[11]) << 32)}

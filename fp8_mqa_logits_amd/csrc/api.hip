@@ -61,7 +61,7 @@ const DeviceInfo* device_info(int device) {
 }
 
 struct Layout {
-  size_t header, order, xrow, xqueue, xflag, rowinfo, slabE, slabI, tmpE, tmpI, total;
+  size_t header, order, xrow, xqueue, xflag, rqueue, rowinfo, slabE, slabI, tmpE, tmpI, total;
   int grid, nblocks;
 };
 
@@ -89,6 +89,8 @@ Layout layout(int rows, const DeviceInfo& d) {
   off = align_up(off + (size_t)L.nblocks * 4);
   L.xflag = off;
   off = align_up(off + (size_t)L.nblocks * 4);
+  L.rqueue = off;
+  off = align_up(off + 2 * rows_pad * 4);
   L.rowinfo = off;
   off = align_up(off + rows_pad * sizeof(mqa::RowInfo));
   const size_t slab = rows_pad * mqa::kSlabRow * 4;
@@ -210,6 +212,7 @@ int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
     p.xrow = ws + L.xrow;
     p.xqueue = reinterpret_cast<int32_t*>(ws + L.xqueue);
     p.xflag = reinterpret_cast<uint32_t*>(ws + L.xflag);
+    p.rqueue = reinterpret_cast<int32_t*>(ws + L.rqueue);
     p.rowinfo = reinterpret_cast<mqa::RowInfo*>(ws + L.rowinfo);
     p.slabE = reinterpret_cast<float*>(ws + L.slabE);
     p.slabI = reinterpret_cast<int32_t*>(ws + L.slabI);

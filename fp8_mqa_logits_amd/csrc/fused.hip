@@ -43,14 +43,18 @@ constexpr int kSelWaves = 4;        // rows (waves) per select workgroup
 
 // Header words (the first 12 mirror struct mqa_stats in mqa_topk.h).
 enum : int {
-  H_CLAIM = 0, H_SHORT = 1, H_GATED = 2, H_EXACT = 3, H_OVERFLOW = 4, H_UNDER = 5,
+  H_CLAIM = 0, H_SHORT = 1, H_GATED = 2, H_EXACT = 3, H_RESCAN = 4, H_UNDER = 5,
   H_COMPACT = 6, H_UNCERT = 7, H_CAND_LO = 8, H_CAND_HI = 9, H_BAND_LO = 10, H_BAND_HI = 11,
   H_XQ = 16,      // blocks queued for the exact rescan
   H_XCLAIM = 17,  // exact-rescan claim counter
-  H_GCLAIM = 18   // gate claim counter
+  H_GCLAIM = 18,  // gate claim counter
+  H_RQ = 19,      // rows queued for the bounded rescan (then 21 for its second round)
+  H_RCLAIM = 20   // work-item claim counter of the bounded rescan (then 22)
 };
 
 enum RowMode : int { M_OFF = 0, M_SHORT = 1, M_ALL = 2, M_GATED = 3, M_EXACT = 4 };
+
+constexpr int kRescanKeys = 8192;  // keys per bounded-rescan work item
 
 // Candidate capacity of a slab row (SMALL_CAP: just above k, to exercise the
 // merges in tests).
@@ -733,11 +737,13 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
 //      result is exact when every record above the band scores >= tau + D and
 //      every record below it (and every non-candidate, < T) <= tau - D, tau
 //      being the k-th exact score.
-// Returns false when the certificate fails (the caller rescans the row).
+// Returns false when the certificate fails (the caller rescans the row); `low`
+// then receives a lower bound of the row's k-th exact score (the k records
+// taken score at least min(tau, smallest above-band score - D)), or -inf.
 template <class Emit>
 __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int n, int k, float T,
                               const QueryRow& qr, uint32_t* hist,
-                              unsigned* band_count, Emit emit) {
+                              unsigned* band_count, float& low, Emit emit) {
   const int l = lane_id();
   constexpr int kBins = kHistWords;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -832,6 +838,7 @@ __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int 
   max_below = wave_max(max_below);
   const float maxabs = __builtin_fmaxf(__builtin_fabsf(mx), __builtin_fabsf(mn));
   const int need = k - na;
+  low = -__builtin_inff();
   if (na >= k || nb < need) return false;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   // exact scores of the band, 64 records at a time
@@ -864,6 +871,7 @@ __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int 
   const float below = __builtin_fmaxf(max_below, T);
   const bool ok_above = na == 0 || min_above - d >= tau;
   const bool ok_below = below + d <= tau;
+  low = na == 0 ? tau : __builtin_fminf(tau, min_above - d);
   return ok_above && ok_below;
 }
 
@@ -874,6 +882,16 @@ __device__ __forceinline__ void queue_exact(const FusedParams& p, int r) {
   p.xrow[r] = 1;
   const int b = r / kBlockRows;
   if (atomicExch(&p.xflag[b], 1u) == 0u) p.xqueue[atomicAdd(&p.header[H_XQ], 1u)] = b;
+}
+
+// Queue row r for the bounded rescan: every visible key is scored exactly and
+// the keys scoring >= low (a lower bound of the row's k-th exact score) are
+// appended to the row's slab.
+__device__ __forceinline__ void queue_rescan(const FusedParams& p, int r, float low) {
+  if (lane_id() != 0) return;
+  p.rowinfo[r].thr = low;
+  p.rowinfo[r].cnt = 0;
+  p.rqueue[atomicAdd(&p.header[H_RQ], 1u)] = r;
 }
 
 // Select: one wave per row.
@@ -888,7 +906,9 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_select_kernel(FusedPa
   const RowInfo ri = p.rowinfo[r];
   if (ri.mode == M_SHORT || ri.mode == M_OFF) return;
   bool ok = false;
-  if (ri.mode != M_EXACT) {
+  float low = -__builtin_inff();
+  const bool forced = ri.mode != M_EXACT && (p.flags & 32u);  // rescan from an open bound
+  if (ri.mode != M_EXACT && !forced) {
     if (ri.cnt >= k) {
       int s, e;
       row_range(p, r, s, e);
@@ -898,7 +918,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_select_kernel(FusedPa
       float* sE = p.slabE + (int64_t)r * kSlabRow;
       int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
       ok = select_banded(p, sE, sI, ri.cnt, k, ri.thr, qr, hist[w],
-                         stats ? &p.header[H_BAND_LO] : nullptr,
+                         stats ? &p.header[H_BAND_LO] : nullptr, low,
                          [&](int sl, int idx) { o[sl] = idx - s; });
       if (stats && l == 0) {
         atomicAdd(&p.header[ok ? H_GATED : H_UNCERT], 1u);
@@ -909,7 +929,112 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_select_kernel(FusedPa
       atomicAdd(&p.header[H_UNDER], 1u);
     }
   }
-  if (!ok) queue_exact(p, r);
+  if (!ok) {
+    if (forced || low > -__builtin_inff())
+      queue_rescan(p, r, low);
+    else
+      queue_exact(p, r);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Bounded rescan of the queued rows, in up to two rounds. Work item i of a
+// round covers keys [kRescanKeys * (i / nq), kRescanKeys * (i / nq + 1)) of
+// queued row i % nq (slice-major, so that the waves working at one time share
+// their keys in L2); one wave per item, claimed from the round's counter.
+// Exact scores (the band rescoring's bf16 MFMA) of 64 keys at a time; keys
+// scoring >= the row's bound get slab slots from the row's counter (slots past
+// the slab are counted, not written).
+__global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, int round) {
+  const int l = lane_id();
+  const int nq = (int)p.header[H_RQ + 2 * round];
+  const int32_t* queue = p.rqueue + (int64_t)round * p.nblocks * kBlockRows;
+  const int nsl = (p.keys + kRescanKeys - 1) / kRescanKeys;
+  const int items = nq * nsl;
+  if (items == 0) return;  // no claims (one contended counter) when nothing is queued
+  for (;;) {
+    int it = 0;
+    if (l == 0) it = (int)atomicAdd(&p.header[H_RCLAIM + 2 * round], 1u);
+    it = __shfl(it, 0, 64);
+    if (it >= items) break;
+    const int r = queue[it % nq];
+    const int slice = it / nq;
+    int s, e;
+    row_range(p, r, s, e);
+    const int a = s > slice * kRescanKeys ? s : slice * kRescanKeys;
+    const int b = e < (slice + 1) * kRescanKeys ? e : (slice + 1) * kRescanKeys;
+    if (a >= b) continue;
+    QueryRow qr;
+    load_query(qr, p.q, p.weights, r);
+    const float low = p.rowinfo[r].thr;
+    float* sE = p.slabE + (int64_t)r * kSlabRow;
+    int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
+    for (int k0 = a; k0 < b; k0 += kWave) {
+      int keyidx[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int j = k0 + 16 * t + (l & 15);
+        keyidx[t] = j < b ? j : b - 1;
+      }
+      KeyTile kt;
+      load_keys_gather(kt, p.k, keyidx);
+      const int key = k0 + l;
+      const bool valid = key < b;
+      const float E = score_chunk_exact(qr, kt) * p.scales[valid ? key : b - 1];
+      const bool pass = valid && E >= low;
+      const uint64_t m = __ballot(pass);
+      if (m == 0) continue;
+      int base = 0;
+      if (l == 0) base = atomicAdd(&p.rowinfo[r].cnt, __popcll(m));
+      base = __shfl(base, 0, 64);
+      const int pos = base + rank_in_mask(m);
+      if (pass && pos < kSlabRow) {
+        sE[pos] = E;
+        sI[pos] = key;
+      }
+    }
+  }
+}
+
+// Top-k of each row of a bounded-rescan round from its slab (one wave per
+// row). A row whose keys at or above its bound overfilled the slab gets, in
+// the first round, the k-th best exact score among the slab's records as a
+// new (higher) bound and a second round; a row with fewer than k such keys,
+// or still too many, goes on to the exact streaming rescan.
+__global__ __launch_bounds__(kSelWaves * kWave) void fused_finish_kernel(FusedParams p,
+                                                                         int round) {
+  __shared__ uint32_t hist[kSelWaves][kHistWords];
+  const int w = wave_id();
+  const int l = lane_id();
+  const int k = p.topk;
+  const int nq = (int)p.header[H_RQ + 2 * round];
+  const int64_t qrows = (int64_t)p.nblocks * kBlockRows;
+  for (int qi = blockIdx.x * kSelWaves + w; qi < nq; qi += gridDim.x * kSelWaves) {
+    const int r = p.rqueue[round * qrows + qi];
+    const int cnt = p.rowinfo[r].cnt;
+    float* sE = p.slabE + (int64_t)r * kSlabRow;
+    int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
+    if (cnt >= k && cnt <= kSlabRow) {
+      int s, e;
+      row_range(p, r, s, e);
+      int32_t* o = p.out + (int64_t)r * k;
+      wave_select(sE, sI, cnt, k, hist[w], [&](int sl, float, int idx) { o[sl] = idx - s; });
+      if ((p.flags & 8u) && l == 0) atomicAdd(&p.header[H_RESCAN], 1u);
+      continue;
+    }
+    if (round == 0 && cnt > kSlabRow) {
+      const float low = wave_kth_value(sE, kSlabRow, k, hist[w]);
+      if (low > p.rowinfo[r].thr) {
+        if (l == 0) {
+          p.rowinfo[r].thr = low;
+          p.rowinfo[r].cnt = 0;
+          p.rqueue[qrows + atomicAdd(&p.header[H_RQ + 2], 1u)] = r;
+        }
+        continue;
+      }
+    }
+    queue_exact(p, r);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -983,6 +1108,15 @@ extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t
   hipLaunchKernelGGL(mqa::fused_select_kernel, dim3(sel), dim3(mqa::kSelWaves * mqa::kWave), 0,
                      stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  const int fin = sel < 256 ? sel : 256;
+  for (int round = 0; round < 2; ++round) {
+    hipLaunchKernelGGL(mqa::fused_rescan_kernel, dim3(2 * grid), dim3(mqa::kThreads), 0, stream,
+                       *p, round);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(mqa::fused_finish_kernel, dim3(fin), dim3(mqa::kSelWaves * mqa::kWave), 0,
+                       stream, *p, round);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  }
   hipLaunchKernelGGL(mqa::fused_exact_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
   return (int)hipGetLastError();
 }

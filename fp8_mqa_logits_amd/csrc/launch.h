@@ -30,6 +30,7 @@ struct FusedParams {
   int32_t* order;    // [nblocks] heaviest-first block order
   uint8_t* xrow;     // [rows] 1 = the row needs the exact rescan
   int32_t* xqueue;   // [nblocks] blocks queued for the exact rescan
+  int32_t* rqueue;   // [2][nblocks * 32] rows queued for the two bounded-rescan rounds
   uint32_t* xflag;   // [nblocks] 1 = the block is queued
   RowInfo* rowinfo;  // [rows]
   float* slabE;      // [nblocks * 32 rows][kSlabRow] candidate scores

@@ -64,6 +64,9 @@ extern "C" {
 #define MQA_FLAG_STATS 8u           /* fill the mqa_stats header of the workspace */
 #define MQA_FLAG_TIME_SCAN 16u      /* record HIP events around the scan kernel (see
                                        mqa_scan_time); a benchmarking aid */
+#define MQA_FLAG_FORCE_RESCAN 32u   /* every gated row skips the certified select and
+                                       is redone by the bounded rescan from an open
+                                       bound */
 
 /* Counters written to the first bytes of the workspace when MQA_FLAG_STATS is
  * set (read them after the stream has finished the call). A call over more
@@ -74,7 +77,7 @@ typedef struct mqa_stats {
   uint32_t rows_short;      /* rows with n <= k (no scoring) */
   uint32_t rows_gated;      /* rows served by the gate + certified select */
   uint32_t rows_exact;      /* rows served by the exact streaming rescan */
-  uint32_t rows_overflow;   /* unused (a full slab is merged in place) */
+  uint32_t rows_rescanned;  /* uncertified rows redone by the bounded rescan */
   uint32_t rows_undercount; /* gated rows with fewer than k candidates */
   uint32_t compactions;     /* slab merges (keep the best records, raise the threshold) */
   uint32_t rows_uncertified;/* gated rows whose exact band could not certify the cut */
@@ -85,12 +88,12 @@ typedef struct mqa_stats {
 /*
  * Bytes of device workspace one mqa_topk_prefill call over `rows` query rows
  * needs on HIP device `device` (the pages' get_fused_mqa_topk_workspaces, API
- * page "fused_mqa_topk"). It holds the block queue, one candidate slab of
- * 16384 (score, key) records per row of every block a persistent workgroup can
- * hold at once, and per-wave compaction buffers; it grows with the device's
- * compute-unit count, and with rows only through a 4-byte-per-block queue.
- * Returns 0 if the device does not exist or is not gfx950, or rows is out of
- * range.
+ * page "fused_mqa_topk"). It holds the block order, per-row state and queues,
+ * one candidate slab of 16640 (score, key) records per row of a batch of up
+ * to 16384 rows (1.09 GB for a full batch), and per-wave merge buffers of
+ * 10240 records for every workgroup the device runs at once; it grows with
+ * rows up to 16384 and with the device's compute-unit count. Returns 0 if the
+ * device does not exist or is not gfx950, or rows is out of range.
  */
 size_t workspace_size(int rows, int device);
 

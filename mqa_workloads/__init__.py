@@ -233,6 +233,39 @@ def extra_elementwise_ties(rows: int = 16384, keys: int = 1048576, topk: int = 2
                     ends, seed)
 
 
+def extra_near_tie_groups(rows: int = 64, keys: int = 65536, topk: int = 2048,
+                          group: int = 9000) -> Workload:
+    """Two groups of `group` identical keys each, at random positions, whose
+    scores differ by about 2e-5 of their size (above the checker's tolerance,
+    below the certified select's margin), every other key far below them.
+    Head 0 of every query is (0.0390625, 1, ..., 1) and the other heads are
+    zero; group A keys are all ones, group B keys are all ones except 0.9375 in
+    dim 0, the remaining keys are e4m3(N(0,1) / 4); every scale is 1.0 and
+    head 0's weight is uniform in [0.5, 2) (the other weights, N(0,1)/sqrt(32),
+    multiply zero dots). The two groups together overfill a candidate slab,
+    so the scan must drop group B by merging."""
+    seed = SEED_BASE + 13
+    rng = np.random.Generator(np.random.PCG64(seed))
+    qf = np.zeros((rows, HEADS, DIM), np.float32)
+    qf[:, 0, :] = 1.0
+    qf[:, 0, 0] = 0.0390625
+    q = encode_e4m3(qf)
+    kf = _normal(rng, (keys, DIM)) / np.float32(4.0)
+    perm = rng.permutation(keys)
+    kf[perm[:group]] = 1.0
+    kf[perm[group:2 * group]] = 1.0
+    kf[perm[group:2 * group], 0] = 0.9375
+    k = encode_e4m3(kf)
+    sb = ue8m0_bytes(np.zeros(keys, np.int64))
+    w = _weights(rng, rows)
+    w[:, 0] = rng.uniform(0.5, 2.0, size=rows).astype(np.float32)
+    starts = np.zeros(rows, np.int32)
+    ends = np.full(rows, keys, np.int32)
+    return Workload(f"x3_neartie_{rows}x{keys}_k{topk}", rows, keys, topk, q, k, sb, w, starts,
+                    ends, seed, groups={"group_a": np.sort(perm[:group]).astype(np.int32),
+                                        "group_b": np.sort(perm[group:2 * group]).astype(np.int32)})
+
+
 def custom(rows: int, keys: int, topk: int, starts, ends, seed: int = 1,
            q_offset: float = 0.0, weight_scale: float = 1.0, name: str = "custom") -> Workload:
     """Small hand-shaped inputs for edge-case tests (ragged ranges, empty rows)."""

@@ -83,3 +83,27 @@ def test_dense_checker():
     g = ref.copy()
     g[1, 1] += 100.0 * 5e-6
     assert check.check_dense(g, ref) == []
+
+
+def test_near_tie_workload_separates_groups_beyond_tolerance():
+    # the near-tie workload is only a discriminating GPU case if the oracle
+    # puts group A strictly above group B by more than the checker's tolerance
+    # (yet less than 8 * 2^-18 of the row's size, the select's margin floor),
+    # every other key well below, and the checker rejects a B key in place of
+    # an A key
+    wl = W.extra_near_tie_groups()
+    p = oracle.Problem(wl.q, wl.k, oracle.key_scales(wl.scale_bytes), wl.weights, wl.starts,
+                       wl.ends)
+    a, b = wl.groups["group_a"], wl.groups["group_b"]
+    rest = np.setdiff1d(np.arange(wl.keys), np.concatenate([a, b]))
+    lg = oracle.logits(p, [0, 1]).astype(np.float64)
+    for r in range(2):
+        la, lb, lr = lg[r, a], lg[r, b], lg[r, rest]
+        assert la.min() == la.max() and lb.min() == lb.max()
+        gap = (la[0] - lb[0]) / la[0]
+        assert check.REL_TOL < gap < 8 * 2.0 ** -18, gap
+        assert lr.max() < 0.5 * lb[0]
+        sel = a[:wl.topk].copy()
+        assert check.check_topk_row(sel, lg[r].astype(np.float32), wl.topk) is None
+        sel[0] = b[0]
+        assert check.check_topk_row(sel, lg[r].astype(np.float32), wl.topk) is not None

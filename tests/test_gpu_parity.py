@@ -119,7 +119,8 @@ def test_fused_all_rows(cfg):
     assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, wl.topk)
     fails = check.check_topk(o, np.arange(wl.rows), oracle_problem(wl), wl.topk, TOL)
     assert not fails, fails[:5]
-    assert st["rows_gated"] + st["rows_exact"] + st["rows_short"] == wl.rows
+    assert (st["rows_gated"] + st["rows_rescanned"] + st["rows_exact"] + st["rows_short"]
+            == wl.rows)
     # the fused path (gate + certified select) serves every scored row
     assert st["rows_exact"] == 0 and st["rows_uncertified"] == 0 and st["rows_undercount"] == 0
 
@@ -143,7 +144,7 @@ def test_scan_timing_flag():
 
 
 @pytest.mark.parametrize("flag", [mqa.FLAG_FORCE_EXACT, mqa.FLAG_FORCE_GATE_MISS,
-                                  mqa.FLAG_SMALL_CAP])
+                                  mqa.FLAG_SMALL_CAP, mqa.FLAG_FORCE_RESCAN])
 @pytest.mark.parametrize("cfg", [1, 2])
 def test_fused_forced_fallback(cfg, flag):
     wl = W.config(cfg)
@@ -158,8 +159,12 @@ def test_fused_forced_fallback(cfg, flag):
     rows = np.arange(wl.rows) if cfg == 1 else W.sample_rows(wl, 128)
     fails = check.check_topk(o[rows], rows, oracle_problem(wl), wl.topk, TOL)
     assert not fails, fails[:5]
-    if flag != mqa.FLAG_SMALL_CAP:
-        assert st["rows_exact"] == wl.rows - st["rows_short"]
+    scored = wl.rows - st["rows_short"]
+    if flag in (mqa.FLAG_FORCE_EXACT, mqa.FLAG_FORCE_GATE_MISS):
+        assert st["rows_exact"] == scored
+    if flag == mqa.FLAG_FORCE_RESCAN:
+        # every gated row is redone by the bounded rescan, none needs more
+        assert st["rows_rescanned"] == scored and st["rows_exact"] == 0
 
 
 def test_fused_edge_ranges():
@@ -172,7 +177,7 @@ def test_fused_edge_ranges():
     wl = W.custom(rows, keys, topk, st, en, seed=9)
     say("case: fused edge ranges (empty, n<k, n==k, n==k+1, clamped, start>end), 77 rows")
     d = to_device(wl)
-    for flags in (0, mqa.FLAG_FORCE_EXACT, mqa.FLAG_SMALL_CAP):
+    for flags in (0, mqa.FLAG_FORCE_EXACT, mqa.FLAG_SMALL_CAP, mqa.FLAG_FORCE_RESCAN):
         out = fused(d, topk, flags=flags)
         o = out.cpu().numpy()
         assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, topk), flags
@@ -196,16 +201,20 @@ def test_fused_large_sampled(cfg):
     fails = check.check_topk(o[rows], rows, oracle_problem(wl), wl.topk, TOL)
     assert not fails, fails[:5]
     scored = wl.rows - st["rows_short"]
-    assert st["rows_gated"] + st["rows_exact"] == scored
+    assert st["rows_gated"] + st["rows_rescanned"] + st["rows_exact"] == scored
     if cfg in (3, 4):
         # i.i.d. keys: the fused path serves every row, none falls back
         assert st["rows_gated"] == scored and st["rows_exact"] == 0
+    else:
+        # heavy ties: the few uncertified rows are redone by the bounded rescan
+        assert st["rows_exact"] == 0
 
 
-@pytest.mark.parametrize("which", ["x1_common_offset", "x2_elementwise_ties"])
+@pytest.mark.parametrize("which", ["x1_common_offset", "x2_elementwise_ties",
+                                   "x3_near_tie_groups"])
 def test_fused_extra_cases(which):
-    wl = (W.extra_common_offset() if which == "x1_common_offset"
-          else W.extra_elementwise_ties())
+    wl = {"x1_common_offset": W.extra_common_offset, "x2_elementwise_ties": W.extra_elementwise_ties,
+          "x3_near_tie_groups": W.extra_near_tie_groups}[which]()
     say(f"case: fused {wl.name}; validity all rows, set rule on 64 rows")
     d = to_device(wl)
     ws = mqa.alloc_workspace(wl.rows)
@@ -218,6 +227,31 @@ def test_fused_extra_cases(which):
     rows = W.sample_rows(wl, 64)
     fails = check.check_topk(o[rows], rows, oracle_problem(wl), wl.topk, TOL)
     assert not fails, fails[:5]
+    if which == "x3_near_tie_groups":
+        # group B scores within the certificate's margin of group A and is
+        # dropped by a merge: every row is redone by the bounded rescan, which
+        # takes group A only
+        assert st["rows_rescanned"] == wl.rows and st["rows_exact"] == 0
+        a = set(wl.groups["group_a"].tolist())
+        assert all(set(o[r].tolist()) <= a for r in range(wl.rows))
+
+
+def test_fused_rescan_second_round():
+    # the bounded rescan from an open bound overfills every row's slab in its
+    # first round (65536 keys); the k-th best exact score among the stored
+    # records bounds the second round, which keeps group A (9000 keys) alone
+    wl = W.extra_near_tie_groups()
+    say(f"case: fused {wl.name} forced bounded rescan; all rows checked")
+    d = to_device(wl)
+    ws = mqa.alloc_workspace(wl.rows)
+    out = fused(d, wl.topk, flags=mqa.FLAG_FORCE_RESCAN | mqa.FLAG_STATS, workspace=ws)
+    st = mqa.read_stats(ws)
+    say("stats", st)
+    o = out.cpu().numpy()
+    assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, wl.topk)
+    fails = check.check_topk(o, np.arange(wl.rows), oracle_problem(wl), wl.topk, TOL)
+    assert not fails, fails[:5]
+    assert st["rows_rescanned"] + st["rows_exact"] == wl.rows and st["rows_rescanned"] > 0
 
 
 @pytest.mark.parametrize("keys,topk", [(32768, 512), (262144, 2048)])
