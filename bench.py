@@ -50,15 +50,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_counters():
+def traffic_from_counters(workload: str):
     """HBM bytes per fused-kernel launch from the committed counter summary,
-    or None when the summary is missing or was taken on other sources."""
+    or None when the summary is missing, was taken on other sources or on
+    another workload."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_hash") != kernel_source_hash():
+    if c.get("kernel_source_hash") != kernel_source_hash() or c.get("workload") != workload:
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -211,7 +212,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--dense", action="store_true")
@@ -299,7 +300,7 @@ def main():
                    "visible_pairs": pairs, "parallelism": "1 GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS,
-                     "traffic": traffic_from_counters(), "kernel": "fused_topk_kernel",
+                     "traffic": traffic_from_counters(wl.name), "kernel": "fused_topk_kernel",
                      "kernel_ms": scan_ms},
         "path_stats": stats,
     }

@@ -54,7 +54,7 @@ enum : int {
 
 enum RowMode : int { M_OFF = 0, M_SHORT = 1, M_ALL = 2, M_GATED = 3, M_EXACT = 4 };
 
-constexpr int kRescanKeys = 8192;  // keys per bounded-rescan work item
+constexpr int kRescanKeys = 2048;  // keys per bounded-rescan work item
 
 // Candidate capacity of a slab row (SMALL_CAP: just above k, to exercise the
 // merges in tests).
