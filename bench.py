@@ -221,7 +221,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this path runs on one GPU; multi-GPU runs are not supported "
-              "(the row-sharded design is described in DESIGN.md)", file=sys.stderr)
+              "(rows would shard across GPUs, each running the one-GPU path on its share)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
