@@ -266,6 +266,26 @@ def extra_near_tie_groups(rows: int = 64, keys: int = 65536, topk: int = 2048,
                                         "group_b": np.sort(perm[group:2 * group]).astype(np.int32)})
 
 
+def extra_repeated_keys(rows: int = 64, keys: int = 8192, topk: int = 512,
+                        distinct: int = 256) -> Workload:
+    """Keys drawn from `distinct` e4m3 vectors (each (vector, scale) pair
+    repeats about keys / (distinct * 5) times), config-3 q, scale and weight
+    distributions; row i sees [0, 6000 + 32 i). Small groups of tied scores
+    sit everywhere, also at the rank where a full candidate slab is cut."""
+    seed = SEED_BASE + 14
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = encode_e4m3(_normal(rng, (rows, HEADS, DIM)))
+    vecs = encode_e4m3(_normal(rng, (distinct, DIM)))
+    k = vecs[rng.integers(0, distinct, size=keys)]
+    sb = _scales(rng, keys)
+    w = _weights(rng, rows)
+    starts = np.zeros(rows, np.int32)
+    ends = (6000 + 32 * np.arange(rows)).astype(np.int32)
+    assert int(ends[-1]) <= keys
+    return Workload(f"x4_repkeys_{rows}x{keys}_k{topk}", rows, keys, topk, q, k, sb, w, starts,
+                    ends, seed)
+
+
 def custom(rows: int, keys: int, topk: int, starts, ends, seed: int = 1,
            q_offset: float = 0.0, weight_scale: float = 1.0, name: str = "custom") -> Workload:
     """Small hand-shaped inputs for edge-case tests (ragged ranges, empty rows)."""

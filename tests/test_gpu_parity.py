@@ -236,6 +236,26 @@ def test_fused_extra_cases(which):
         assert all(set(o[r].tolist()) <= a for r in range(wl.rows))
 
 
+def test_fused_merges_with_ties():
+    # a slab capped just above k (SMALL_CAP) merges every few chunks; with
+    # keys repeated from 256 vectors the merge cut often falls inside a group
+    # of tied scores, whose members the merge keeps while they fit
+    wl = W.extra_repeated_keys()
+    say(f"case: fused {wl.name} with the small slab cap; all rows checked")
+    d = to_device(wl)
+    for flags in (0, mqa.FLAG_SMALL_CAP):
+        ws = mqa.alloc_workspace(wl.rows)
+        out = fused(d, wl.topk, flags=flags | mqa.FLAG_STATS, workspace=ws)
+        st = mqa.read_stats(ws)
+        say("flags", flags, "stats", st)
+        o = out.cpu().numpy()
+        assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, wl.topk)
+        fails = check.check_topk(o, np.arange(wl.rows), oracle_problem(wl), wl.topk, TOL)
+        assert not fails, (flags, fails[:5])
+        if flags:
+            assert st["compactions"] > 0
+
+
 def test_fused_rescan_second_round():
     # the bounded rescan from an open bound overfills every row's slab in its
     # first round (65536 keys); the k-th best exact score among the stored
