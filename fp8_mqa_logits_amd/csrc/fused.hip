@@ -3,25 +3,30 @@
 // Follows vLLM PR #60618, "What this PR does" (scoring, sampled gate,
 // candidate emission, per-row selection, exact rescan, heaviest-first block
 // claims) and the API page "fused_mqa_topk" (contract and output convention),
-// laid out for gfx950 as five launches on the caller's stream:
+// laid out for gfx950 as nine launches on the caller's stream:
 //   * plan: heaviest-first order of the 32-row blocks, counters cleared;
 //   * gate (persistent): per block, a strided sample of the keys gives each
-//     row an admission threshold meant to keep about 2k candidates; rows
-//     with n <= k get their output here;
+//     row an admission threshold with a safe margin over its k-th key's
+//     expected sample rank; rows with n <= k get their output here;
 //   * scan (persistent, 8 waves of 4 rows per workgroup): keys stream through
 //     LDS in 128-key stages filled by direct global->LDS loads; each wave
 //     scores its 4 rows with FP8 MFMAs (the rows' q and weights stay in
 //     VGPRs) and appends the keys that reach a row's threshold to that row's
 //     candidate slab (a ballot, an mbcnt and two buffer stores per row and
-//     chunk, no atomics: a row belongs to one wave);
+//     chunk, no atomics: a row belongs to one wave); a full slab is merged in
+//     place (the best records and their ties stay, the threshold rises);
 //   * select (one wave per row): the row's k-th approximate score is found in
 //     its slab, a band of keys around it is rescored exactly (bf16 MFMA) and
 //     the row is accepted only when the band's measured error, times a safety
 //     factor, cannot move any key across the cut (FP8 MFMA scores are
 //     approximate on gfx950, see common.h);
-//   * exact (persistent): rows whose gate admitted fewer than k keys or whose
-//     band could not be certified are rescanned with exact scores and a
-//     streaming top-k merge.
+//   * bounded rescan and finish, two rounds: a row whose band could not be
+//     certified has every visible key scored exactly, in key slices spread
+//     over all waves, against a lower bound of its k-th score, and its top k
+//     selected from the keys above the bound;
+//   * exact (persistent): rows with fewer than k candidates, or whose
+//     bounded rescan overfilled the slab twice, are rescanned with exact
+//     scores and a streaming top-k merge.
 // Each phase is its own kernel so that each gets the registers it needs (the
 // scan loop in particular holds no state of the other phases).
 #include "common.h"

@@ -13,7 +13,7 @@ struct RowInfo {
   float thr;   // admission threshold
   int cnt;     // candidates in the row's slab
   int mode;    // how the row is served (fused.hip RowMode)
-  int strict;  // 1: later candidates had to beat thr strictly (after a merge)
+  int strict;  // 1: a merge raised thr; later candidates had to beat it strictly
 };
 
 struct FusedParams {
