@@ -181,7 +181,10 @@ __device__ __forceinline__ float reduce_heads(const QueryRow& qr, const RowAcc& 
 // term t encodes what terms 0..t-1 left over, so the sum of the terms
 // matches f to about 2^-16 of each block's largest magnitude. The 4 terms of
 // the wave's 4 rows are the 16 A rows of one extra MFMA per 16 keys: M row
-// 4r + t = term t of row r. The head epilogue then only accumulates |s|.
+// 4t + r = term t of row r, so that lane group g receives term g of every
+// row (output register r: row r). Each row's head epilogue starts its
+// lane's |s| accumulation from that term, and the cross-lane head reduction
+// sums the 4 terms together with the 4 head groups.
 
 struct FoldOp {
   v8i fa;      // this lane's 32 e4m3 codes: M row (l%16), dims 32*(l/16) ..
@@ -198,14 +201,14 @@ __device__ __forceinline__ float e4m3_to_f32(int word, int byte) {
 }
 
 // Builds this lane's fold operand for the wave's rows rows[0..3] (-1: unused
-// row, zero terms). Lane l covers row (l%16)/4, term (l%16)%4, dims
+// row, zero terms). Lane l covers row (l%16)%4, term (l%16)/4, dims
 // 32*(l/16) .. +31.
 __device__ __forceinline__ void build_fold(FoldOp& fo, const uint8_t* __restrict__ q,
                                            const float* __restrict__ weights, const int* rows) {
   const int l = lane_id();
   const int m = l & 15;
-  const int rr = m >> 2;
-  const int term = m & 3;
+  const int rr = m & 3;
+  const int term = m >> 2;
   const int g = l >> 4;
   int row = rows[0];
 #pragma unroll
@@ -280,37 +283,31 @@ __device__ __forceinline__ void build_fold(FoldOp& fo, const uint8_t* __restrict
   fo.fscale = 127 + es;
 }
 
-// Linear halves L = f . k of the wave's 4 rows for a 64-key chunk: 4 scaled
-// MFMAs (one per 16-key sub-tile), the 4 terms summed per lane, then a 4x4
-// transpose of lane groups so that L[r] holds row r with lane l <-> key l.
-__device__ __forceinline__ void fold_linear(float L[4], const FoldOp& fo, const KeyTile& kt) {
-  float x[4];
+// The fold terms of the wave's 4 rows for a 64-key chunk: 4 scaled MFMAs
+// (one per 16-key sub-tile); ft[t][r] in lane group g is term g of row r for
+// key 16t + l%16.
+struct FoldTerms {
+  v4f ft[4];
+};
+
+__device__ __forceinline__ void fold_terms(FoldTerms& f, const FoldOp& fo, const KeyTile& kt) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const v4f z = {0.f, 0.f, 0.f, 0.f};
-    const v4f c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fo.fa, kt.kb[t], z, 0, 0, 0,
-                                                                    fo.fscale, 0, 127);
-    x[t] = (c[0] + c[1]) + (c[2] + c[3]);  // lane group g: row g, sub-tile t
+    f.ft[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fo.fa, kt.kb[t], z, 0, 0, 0,
+                                                               fo.fscale, 0, 127);
   }
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[0]), __float_as_uint(x[2]),
-                                                  false, false);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[1]), __float_as_uint(x[3]),
-                                                  false, false);
-  const auto c01 = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  const auto c23 = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  L[0] = __uint_as_float(c01[0]);
-  L[1] = __uint_as_float(c01[1]);
-  L[2] = __uint_as_float(c23[0]);
-  L[3] = __uint_as_float(c23[1]);
 }
 
-// Weighted |s| sum over the lane's 8 heads of each sub-tile (one abs-modified
-// FMA per head), reduced across lane groups like reduce_heads.
-__device__ __forceinline__ float reduce_heads_abs(const QueryRow& qr, const RowAcc& acc) {
+// Linear half plus weighted |s| sum of row r: per sub-tile, the lane's fold
+// term of row r plus its 8 heads (one abs-modified FMA per head), reduced
+// across lane groups like reduce_heads (4 terms + 32 heads).
+__device__ __forceinline__ float reduce_heads_abs(const QueryRow& qr, const RowAcc& acc,
+                                                  const FoldTerms& f, int r) {
   float part[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    float s = 0.f;
+    float s = f.ft[t][r];
 #pragma unroll
     for (int v = 0; v < 4; ++v) s = __builtin_fmaf(qr.w[v], __builtin_fabsf(acc.a[t][0][v]), s);
 #pragma unroll

@@ -333,6 +333,10 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
       }
     if ((p.flags & 8u) && lane_id() == 0) atomicAdd(&p.header[H_COMPACT], 1u);
   }
+  // The counts are wave-uniform; stating it keeps them, and the scan's
+  // per-chunk count updates and capacity tests, in scalar registers.
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) rs[j].cnt = __builtin_amdgcn_readfirstlane(rs[j].cnt);
 }
 
 // Queue direct global->LDS copies of the keys key0 + j * stride, j <
@@ -366,17 +370,17 @@ __device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, int st
 __device__ __forceinline__ void score4(float E[4], const QueryRow* qr, const FoldOp& fo,
                                        const KeyTile& kt, float sc) {
   const float sch = 0.5f * sc;
-  float L[4];
+  FoldTerms f;
   RowAcc a0, a1;
-  fold_linear(L, fo, kt);
+  fold_terms(f, fo, kt);
   mfma_row(a0, qr[0], kt);
   mfma_row(a1, qr[1], kt);
-  E[0] = (L[0] + reduce_heads_abs(qr[0], a0)) * sch;
+  E[0] = reduce_heads_abs(qr[0], a0, f, 0) * sch;
   mfma_row(a0, qr[2], kt);
-  E[1] = (L[1] + reduce_heads_abs(qr[1], a1)) * sch;
+  E[1] = reduce_heads_abs(qr[1], a1, f, 1) * sch;
   mfma_row(a1, qr[3], kt);
-  E[2] = (L[2] + reduce_heads_abs(qr[2], a0)) * sch;
-  E[3] = (L[3] + reduce_heads_abs(qr[3], a1)) * sch;
+  E[2] = reduce_heads_abs(qr[2], a0, f, 2) * sch;
+  E[3] = reduce_heads_abs(qr[3], a1, f, 3) * sch;
 }
 
 // One scan of keys [lo, hi) for the rows of this wave in `mode` (M_ALL and
@@ -414,15 +418,33 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
   auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
     const int key0 = lo + c * kChunk;
     const int key = key0 + l;
-    if (!EXACT && c >= cf && c < ch) {
-      // interior chunk: no per-row range tests
+    if constexpr (!EXACT) {
+      // Each row's admission test as one per-lane threshold: the row's own on
+      // interior chunks, +inf for keys outside the row's range on the others,
+      // so that scoring and emission are the same code for both (no range
+      // tests behind the scores).
+      float thl[kRowsPerWave];
+      if (c >= cf && c < ch) {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) thl[i] = th[i];
+      } else {
+        bool any = false;
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+          const bool act = live[i] && rs[i].s < key0 + kChunk && rs[i].e > key0;
+          any |= act;
+          thl[i] = act && key >= rs[i].s && key < rs[i].e ? th[i] : __builtin_inff();
+        }
+        if (!any) return;
+      }
       const float sc = scl[l];
       KeyTile kt;
       load_keys_lds(kt, kc);
       float E[4];
+      // rows that are not live have zeroed operands and a +inf threshold
       score4(E, qr, fo, kt, sc);
 #pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i) emit_rec(rs[i], E[i], th[i], true, key, sr, i);
+      for (int i = 0; i < kRowsPerWave; ++i) emit_rec(rs[i], E[i], thl[i], true, key, sr, i);
     } else {
       bool act[kRowsPerWave];
       bool any = false;
@@ -436,14 +458,9 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
       KeyTile kt;
       load_keys_lds(kt, kc);
       float E[4];
-      if (EXACT) {
 #pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i)
-          E[i] = act[i] ? score_chunk_exact(qr[i], kt) * sc : 0.f;
-      } else {
-        // rows that are not live have zeroed operands and never emit
-        score4(E, qr, fo, kt, sc);
-      }
+      for (int i = 0; i < kRowsPerWave; ++i)
+        E[i] = act[i] ? score_chunk_exact(qr[i], kt) * sc : 0.f;
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i)
         if (act[i]) finish_row(rs[i], E[i], th[i], key, key0, sr, i);
