@@ -30,9 +30,17 @@ constexpr int kDim = 128;
 constexpr int kWave = 64;
 constexpr int kChunk = 64;                 // keys per LDS stage
 constexpr int kChunkBytes = kChunk * kDim; // 8 KiB
-// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx950: 32-bit
-// data format; offsets are bytes and stores past num_records are dropped.
+// Word 3 of an unswizzled buffer resource on gfx950: 32-bit data format.
+// Raw (stride 0): offsets are bytes and stores past num_records bytes are
+// dropped; structured (stride > 0): a store addresses record `vindex` and
+// records past num_records are dropped.
 constexpr int kBufferFlags = 0x00020000;
+
+// Structured-buffer dword store (the LLVM intrinsic has no clang builtin):
+// writes v at base + soffset + voffset + stride * vindex.
+__device__ void struct_buffer_store_b32(uint32_t v, __amdgpu_buffer_rsrc_t rsrc, int vindex,
+                                        int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.struct.ptr.buffer.store.i32");
 constexpr int kCap = 16384;                // candidate slab capacity per row
 constexpr int kMaxTopk = 2048;
 
@@ -42,8 +50,10 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b, v4f c) {
-  // cbsz = blgp = 0: both operands OCP e4m3; scale bytes 127 = 2^0.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  // cbsz = blgp = 0: both operands OCP e4m3. Scale operands 0 make the
+  // compiler emit the unscaled v_mfma_f32_16x16x128_f8f6f4 (no scale-load
+  // prefix instruction); the scaled form is only needed for the fold terms.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
@@ -87,8 +97,11 @@ struct QueryRow {
   float w[8];  // w[r, 16*hh + 4*(l/16) + v] at index 4*hh + v
 };
 
+// wmul scales the weights as they are loaded (the FP8 scorers take w / 2, the
+// relu fold's factor 1/2; exact scorers take w).
 __device__ __forceinline__ void load_query(QueryRow& qr, const uint8_t* __restrict__ q,
-                                           const float* __restrict__ weights, int64_t r) {
+                                           const float* __restrict__ weights, int64_t r,
+                                           float wmul = 1.f) {
   const int l = lane_id();
   const int g = l >> 4;
 #pragma unroll
@@ -99,10 +112,10 @@ __device__ __forceinline__ void load_query(QueryRow& qr, const uint8_t* __restri
     qr.qa[hh] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     const float4 wv = *reinterpret_cast<const float4*>(weights + r * kHeads + 16 * hh + 4 * g);
-    qr.w[4 * hh + 0] = wv.x;
-    qr.w[4 * hh + 1] = wv.y;
-    qr.w[4 * hh + 2] = wv.z;
-    qr.w[4 * hh + 3] = wv.w;
+    qr.w[4 * hh + 0] = wv.x * wmul;
+    qr.w[4 * hh + 1] = wv.y * wmul;
+    qr.w[4 * hh + 2] = wv.z * wmul;
+    qr.w[4 * hh + 3] = wv.w * wmul;
   }
 }
 
@@ -175,7 +188,8 @@ __device__ __forceinline__ float reduce_heads(const QueryRow& qr, const RowAcc& 
 // relu fold (vLLM PR #60618, "What this PR does"): relu(s) = (s + |s|) / 2, so
 //   sum_h w_h relu(s_h) = ( sum_h w_h s_h + sum_h w_h |s_h| ) / 2
 // and the linear half is one dot product of the key with the folded query
-// f = sum_h w_h q_h. f (fp32) is carried as 4 e4m3 terms, each with a
+// f = sum_h w_h q_h. The factor 1/2 is exact and is carried by the operands:
+// the weights are loaded halved and the fold terms' MFMA scale is halved. f (fp32) is carried as 4 e4m3 terms, each with a
 // power-of-two scale per 32-element block of the MFMA's K order (its E8M0 A
 // scales):
 // term t encodes what terms 0..t-1 left over, so the sum of the terms
@@ -280,7 +294,7 @@ __device__ __forceinline__ void build_fold(FoldOp& fo, const uint8_t* __restrict
   const int from_g0 = __shfl(e_kept[1], m, 64);       // block 2: half 1 of group 0
   const int es = g == 0 ? e_kept[0] : (g == 1 ? from_g2 : (g == 2 ? from_g0 : e_kept[1]));
   fo.fa = v8i{codes[0], codes[1], codes[2], codes[3], codes[4], codes[5], codes[6], codes[7]};
-  fo.fscale = 127 + es;
+  fo.fscale = 126 + es;  // the MFMA applies f / 2: the relu fold's factor 1/2
 }
 
 // The fold terms of the wave's 4 rows for a 64-key chunk: 4 scaled MFMAs
@@ -301,7 +315,8 @@ __device__ __forceinline__ void fold_terms(FoldTerms& f, const FoldOp& fo, const
 
 // Linear half plus weighted |s| sum of row r: per sub-tile, the lane's fold
 // term of row r plus its 8 heads (one abs-modified FMA per head), reduced
-// across lane groups like reduce_heads (4 terms + 32 heads).
+// across lane groups like reduce_heads (4 terms + 32 heads). With halved
+// weights and fold terms this is the unscaled score itself.
 __device__ __forceinline__ float reduce_heads_abs(const QueryRow& qr, const RowAcc& acc,
                                                   const FoldTerms& f, int r) {
   float part[4];

@@ -221,7 +221,7 @@ __device__ __forceinline__ float admit_thr(const RowState& r, bool live) {
 struct SlabRefs {
   float* sE0;                  // score slab row of the wave's row 0 (row i at + i * kSlabRow)
   int32_t* sI0;                // key slab row of the wave's row 0
-  __amdgpu_buffer_rsrc_t buf;  // raw buffer from sE0 through the end of the wave's key rows
+  __amdgpu_buffer_rsrc_t buf;  // 4-byte records from sE0 through the end of the wave's key rows
   int delta;                   // byte distance from the score rows to the key rows
   uint32_t* hist;
   int cap;   // a row merges once it holds more records than this
@@ -237,7 +237,7 @@ __device__ __forceinline__ SlabRefs slab_refs(const FusedParams& p, int b, uint3
   sr.sE0 = p.slabE + row0 * kSlabRow;
   sr.sI0 = p.slabI + row0 * kSlabRow;
   sr.delta = (int)(reinterpret_cast<const char*>(p.slabI) - reinterpret_cast<const char*>(p.slabE));
-  sr.buf = __builtin_amdgcn_make_buffer_rsrc(sr.sE0, 0, sr.delta + kRowsPerWave * kSlabRow * 4,
+  sr.buf = __builtin_amdgcn_make_buffer_rsrc(sr.sE0, 4, sr.delta / 4 + kRowsPerWave * kSlabRow,
                                              kBufferFlags);
   sr.hist = hist;
   sr.cap = slab_cap(p);
@@ -267,8 +267,8 @@ __device__ __forceinline__ void emit_rec(RowState& rs, float E, float th, bool v
     const int pos = (int)__builtin_amdgcn_mbcnt_hi(
         (uint32_t)(m >> 32),
         __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)(rs.cnt + i * kSlabRow)));
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(E), sr.buf, pos * 4, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)key, sr.buf, pos * 4, sr.delta, 0);
+    struct_buffer_store_b32(__float_as_uint(E), sr.buf, pos, 0, 0, 0);
+    struct_buffer_store_b32((uint32_t)key, sr.buf, pos, 0, sr.delta, 0);
   }
   rs.cnt += __popcll(m);
 }
@@ -364,23 +364,23 @@ __device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, int st
 }
 
 // Approximate scores of the wave's 4 rows for a 64-key chunk, lane l <->
-// key l: (f.k + sum_h w_h |s_h|) / 2 * scale (relu fold, common.h). One
+// key l: (f.k + sum_h w_h |s_h|) / 2 * scale (relu fold, common.h; the rows'
+// weights are loaded halved and the fold operand carries f / 2). One
 // branch-free block: the next row's MFMAs are issued before the current
 // row's epilogue; rows with zeroed operands score 0.
 __device__ __forceinline__ void score4(float E[4], const QueryRow* qr, const FoldOp& fo,
                                        const KeyTile& kt, float sc) {
-  const float sch = 0.5f * sc;
   FoldTerms f;
   RowAcc a0, a1;
   fold_terms(f, fo, kt);
   mfma_row(a0, qr[0], kt);
   mfma_row(a1, qr[1], kt);
-  E[0] = reduce_heads_abs(qr[0], a0, f, 0) * sch;
+  E[0] = reduce_heads_abs(qr[0], a0, f, 0) * sc;
   mfma_row(a0, qr[2], kt);
-  E[1] = reduce_heads_abs(qr[1], a1, f, 1) * sch;
+  E[1] = reduce_heads_abs(qr[1], a1, f, 1) * sc;
   mfma_row(a1, qr[3], kt);
-  E[2] = reduce_heads_abs(qr[2], a0, f, 2) * sch;
-  E[3] = reduce_heads_abs(qr[3], a1, f, 3) * sch;
+  E[2] = reduce_heads_abs(qr[2], a0, f, 2) * sc;
+  E[3] = reduce_heads_abs(qr[3], a1, f, 3) * sc;
 }
 
 // One scan of keys [lo, hi) for the rows of this wave in `mode` (M_ALL and
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
         r.mode = M_ALL;  // every visible key is a candidate
       } else {
         r.mode = M_GATED;
-        load_query(qr[i], p.q, p.weights, r.r);
+        load_query(qr[i], p.q, p.weights, r.r, 0.5f);
         frows[i] = r.r;
         wlo = r.s < wlo ? r.s : wlo;
         whi = r.e > whi ? r.e : whi;
@@ -720,7 +720,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
       r.mode = ri.mode;
       r.thr = ri.thr;
       if (r.mode == M_ALL || r.mode == M_GATED) {
-        load_query(qr[i], p.q, p.weights, r.r);
+        load_query(qr[i], p.q, p.weights, r.r, 0.5f);
         frows[i] = r.r;
         wlo = r.s < wlo ? r.s : wlo;
         whi = r.e > whi ? r.e : whi;
