@@ -64,7 +64,7 @@ def traffic_from_counters(workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, target_s: float = 12.0):
+def cpu_baseline(wl, target_s: float = 15.0):
     """Time the oracle (as it stands) on a bounded sample of the workload."""
     import numpy as np
 
@@ -77,8 +77,9 @@ def cpu_baseline(wl, target_s: float = 12.0):
     rows = np.sort(rng.choice(wl.rows, size=wl.rows, replace=False))
     s = np.clip(wl.starts.astype(np.int64), 0, wl.keys)
     e = np.clip(wl.ends.astype(np.int64), s, wl.keys)
-    # calibrate on a few rows, then size the sample to about target_s seconds
-    probe = rows[:threads]
+    # calibrate on a few rows per thread, then size the sample to about
+    # target_s seconds
+    probe = rows[:4 * threads]
     t0 = time.perf_counter()
     oracle.topk(p, probe, wl.topk, threads=threads)
     dt = time.perf_counter() - t0
@@ -86,7 +87,7 @@ def cpu_baseline(wl, target_s: float = 12.0):
     per_row = float((e - s).mean())
     nrows = int(max(threads, min(wl.rows, target_s * rate / per_row)))
     nrows = (nrows + threads - 1) // threads * threads
-    sample = rows[threads:threads + nrows]
+    sample = rows[4 * threads:4 * threads + nrows]
     t0 = time.perf_counter()
     oracle.topk(p, sample, wl.topk, threads=threads)
     dt = time.perf_counter() - t0

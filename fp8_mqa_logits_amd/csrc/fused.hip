@@ -491,7 +491,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
 
 // ---------------------------------------------------------------------------
 // Gate. A strided sample of the block's keys (1024..16384 keys, about span /
-// 16, at a fixed integer stride from the start of the block's range) is
+// 24, at a fixed integer stride from the start of the block's range) is
 // scored like the scan scores; each gated row bins (first-tile maximum -
 // score) in kGateBins bins of 1/256 of the first sample tile's score range and
 // takes as threshold the lower score edge of the bin where the count of sample keys
@@ -554,7 +554,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
       build_fold(fo, p.q, p.weights, frows);
       // S sample keys lo + j * stride, j < S (S a multiple of the stage size)
       const int span = hi - lo;
-      int S = (span / 16) & ~(kStageKeys - 1);
+      int S = (span / 24) & ~(kStageKeys - 1);
       S = S < 1024 ? 1024 : (S > 16384 ? 16384 : S);
       const int stride = span / S > 1 ? span / S : 1;
       const int nst = S / kStageKeys;
