@@ -7,13 +7,18 @@ Prints ONE JSON line (rank 0):
   value    = visible (row, key) scores per second (sum of the rows' visible
              keys / seconds per step);
   roofline = FP8 MFMA roofline of the scan kernel (the dominant one of the
-             call's three launches): 8192 flop per visible pair (2 * 32 heads *
+             call's nine launches): 8192 flop per visible pair (2 * 32 heads *
              128 dims) over its average duration, timed with HIP events that
              the library records on the call's stream around that kernel
              (MQA_FLAG_TIME_SCAN) during the timed steps, against the MI355X
              dense FP8 peak (5.0 PFLOP/s); traffic = HBM bytes per launch from
              the committed rocprofv3 counter summary when it was taken on the
-             current kernel sources, else null;
+             current kernel sources, else null; measured_peak = the FP8 MFMA
+             rate this GPU sustains on the scan's head-tile instruction (the
+             mqa_mfma_peak probe, best of 3 launches) and measured_frac =
+             achieved / measured_peak;
+  timing   = per-call medians and minima of 10 single calls, warm and with a
+             512 MiB buffer written before each call (flushed caches);
   cpu_baseline = the CPU oracle (exact logits + full sort) timed on this
              host's cores over a bounded sample of the same rows.
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu,
@@ -96,6 +101,35 @@ def cpu_baseline(wl, target_s: float = 15.0):
             "sample": f"{len(sample)} seeded random rows of the same workload "
                       f"({int(pairs)} visible pairs), exact logits + full sort per row, "
                       f"{dt:.1f} s"}
+
+
+def per_call_times(step, stream, dev, n: int = 10):
+    """Whole-call times (ms) of n single calls each, warm (inputs and the
+    previous call's data in the caches) and flushed (512 MiB written by another
+    kernel before each call); medians and minima."""
+    import statistics
+
+    import torch
+
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+
+    def run(flushed):
+        t = []
+        for _ in range(n):
+            if flushed:
+                flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return t
+
+    warm, flushed = run(False), run(True)
+    return {"calls": n, "warm_median_ms": statistics.median(warm), "warm_min_ms": min(warm),
+            "flushed_median_ms": statistics.median(flushed), "flushed_min_ms": min(flushed),
+            "flush_bytes": flush.numel() * 4}
 
 
 def time_dense(d, wl, steps: int, warmup: int):
@@ -282,6 +316,8 @@ def main():
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
     scan_ms = mqa.scan_time_ms(args.steps) / args.steps
+    timing = per_call_times(step, stream, dev)
+    measured_peak = mqa.mfma_peak_tflops()
     pairs = wl.visible_pairs()
     value = pairs / (ms / 1e3)
     achieved = pairs * FLOP_PER_PAIR / (scan_ms / 1e3) / 1e12
@@ -303,7 +339,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS,
                      "traffic": traffic_from_counters(wl.name), "kernel": "fused_topk_kernel",
-                     "kernel_ms": scan_ms},
+                     "kernel_ms": scan_ms, "measured_peak": measured_peak,
+                     "measured_frac": achieved / measured_peak},
+        "timing": timing,
         "path_stats": stats,
     }
     if args.dense:

@@ -30,7 +30,7 @@ ERR_NAMES = {0: "MQA_OK", 1: "MQA_ERR_NULL", 2: "MQA_ERR_ALIGN", 3: "MQA_ERR_SHA
              4: "MQA_ERR_WORKSPACE", 5: "MQA_ERR_DEVICE", 6: "MQA_ERR_LAUNCH"}
 
 EXPORTS = ("workspace_size", "mqa_topk_prefill", "mqa_logits_dense", "mqa_topk_dense",
-           "mqa_key_scales", "mqa_scan_time", "mqa_strerror")
+           "mqa_key_scales", "mqa_scan_time", "mqa_mfma_peak", "mqa_strerror")
 
 
 class MQAError(RuntimeError):
@@ -68,6 +68,8 @@ def load() -> ctypes.CDLL:
         lib.mqa_key_scales.restype = I
         lib.mqa_scan_time.argtypes = [I, P]
         lib.mqa_scan_time.restype = I
+        lib.mqa_mfma_peak.argtypes = [P, I64, I, I, P]
+        lib.mqa_mfma_peak.restype = I
         lib.mqa_strerror.argtypes = [I]
         lib.mqa_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -215,6 +217,34 @@ def scan_time_ms(last_n: int) -> float:
     v = ctypes.c_float(0.0)
     _check(load().mqa_scan_time(int(last_n), ctypes.byref(v)), "mqa_scan_time")
     return float(v.value)
+
+
+def mfma_peak_tflops(workgroups: int = 2048, iters: int = 4096, repeats: int = 3) -> float:
+    """FP8 MFMA rate (TFLOP/s) this GPU sustains on the scan's head-tile
+    instruction: the best of `repeats` timed launches of the mqa_mfma_peak
+    probe (after one untimed launch), timed with events on the current stream."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    out = torch.empty(workgroups * 512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    lib = load()
+
+    def launch():
+        _check(lib.mqa_mfma_peak(_ptr(out), out.numel(), workgroups, iters, stream.cuda_stream),
+               "mqa_mfma_peak")
+
+    launch()
+    best = 0.0
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        e1.synchronize()
+        flop = workgroups * 8.0 * iters * 8 * 65536
+        best = max(best, flop / (e0.elapsed_time(e1) / 1e3) / 1e12)
+    if not torch.isfinite(out).all():
+        raise RuntimeError("mqa_mfma_peak: non-finite probe sums")
+    return best
 
 
 def read_stats(workspace: torch.Tensor) -> dict:

@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libmqa_topk.so")
-SOURCES = ["fused.hip", "dense.hip", "api.hip"]
+SOURCES = ["fused.hip", "dense.hip", "probe.hip", "api.hip"]
 HEADERS = ["common.h", "launch.h"]
 
 

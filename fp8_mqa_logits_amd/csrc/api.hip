@@ -271,6 +271,21 @@ int mqa_key_scales(const uint8_t* scale_bytes, float* scales, int keys, void* st
   return MQA_OK;
 }
 
+// The probe's launcher (probe.hip).
+extern "C" int mqa_mfma_peak_launch(float* out, int workgroups, int iters, hipStream_t stream);
+
+int mqa_mfma_peak(float* out, int64_t out_len, int workgroups, int iters, void* stream) {
+  if (!out) return MQA_ERR_NULL;
+  if (!aligned(out, 4)) return MQA_ERR_ALIGN;
+  if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 20) ||
+      out_len < (int64_t)workgroups * 512)
+    return MQA_ERR_SHAPE;
+  if (!current_device()) return MQA_ERR_DEVICE;
+  const int rc = mqa_mfma_peak_launch(out, workgroups, iters, static_cast<hipStream_t>(stream));
+  if (rc != 0) return launch_error(rc);
+  return MQA_OK;
+}
+
 int mqa_scan_time(int last_n, float* total_ms) {
   if (!total_ms) return MQA_ERR_NULL;
   int dev = -1;

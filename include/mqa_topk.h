@@ -171,6 +171,23 @@ int mqa_key_scales(const uint8_t* scale_bytes, float* scales, int keys, void* st
  */
 int mqa_scan_time(int last_n, float* total_ms);
 
+/*
+ * FP8 MFMA throughput probe (a benchmarking aid; the pages give no peak for the
+ * part they measure on, so the scan's MFMA fraction is also read against the
+ * rate this machine sustains). Launches `workgroups` workgroups of 512 threads
+ * on `stream`; each of their 8 waves issues `iters` rounds of 8 independent
+ * v_mfma_f32_16x16x128_f8f6f4 (the instruction of the scan's head tiles) on
+ * register operands and writes one float per thread to `out` (the sums, so that
+ * nothing is optimised away). FP8 flop per launch: workgroups * 8 * iters * 8 *
+ * 65536. The caller times the launch (events on `stream`).
+ *   out: device, caller-owned, >= workgroups * 512 floats (out_len), 4-B aligned;
+ *   workgroups in [1, 65536]; iters in [1, 2^20].
+ * Returns MQA_OK, MQA_ERR_NULL, MQA_ERR_ALIGN, MQA_ERR_SHAPE (sizes out of range
+ * or out_len too small), MQA_ERR_DEVICE or MQA_ERR_LAUNCH; nothing is launched
+ * on an error.
+ */
+int mqa_mfma_peak(float* out, int64_t out_len, int workgroups, int iters, void* stream);
+
 /* Human-readable text of a return code (for MQA_ERR_LAUNCH it names the HIP
  * error of the failing call on this thread). Never NULL. */
 const char* mqa_strerror(int code);

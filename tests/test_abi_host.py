@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert set(names) == {"workspace_size", "mqa_topk_prefill", "mqa_logits_dense",
-                          "mqa_topk_dense", "mqa_key_scales", "mqa_scan_time", "mqa_strerror"}
+                          "mqa_topk_dense", "mqa_key_scales", "mqa_scan_time", "mqa_mfma_peak",
+                          "mqa_strerror"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -96,6 +97,20 @@ def test_dense_errors():
     assert L.mqa_scan_time(1, None) == 1
 
 
+def _peak(out=A16, out_len=512 * 4, workgroups=4, iters=16):
+    return mqa.load().mqa_mfma_peak(ctypes.c_void_p(out), out_len, workgroups, iters, None)
+
+
+def test_mfma_peak_errors():
+    assert _peak(out=0) == 1
+    assert _peak(out=0x10002) == 2
+    assert _peak(workgroups=0) == 3
+    assert _peak(workgroups=65537, out_len=1 << 40) == 3
+    assert _peak(iters=0) == 3
+    assert _peak(iters=(1 << 20) + 1) == 3
+    assert _peak(out_len=4 * 512 - 1) == 3
+
+
 def test_strerror_covers_every_code():
     for c in range(0, 7):
         assert mqa.strerror(c)
@@ -114,3 +129,4 @@ def test_device_error_without_gpu():
     assert mqa.load().workspace_size(64, 0) == 0
     v = ctypes.c_float(0.0)
     assert mqa.load().mqa_scan_time(1, ctypes.byref(v)) == 5
+    assert _peak() == 5
