@@ -25,6 +25,7 @@ FLAG_SMALL_CAP = 4
 FLAG_STATS = 8
 FLAG_TIME_SCAN = 16
 FLAG_FORCE_RESCAN = 32
+FLAG_DETERMINISTIC = 64
 
 ERR_NAMES = {0: "MQA_OK", 1: "MQA_ERR_NULL", 2: "MQA_ERR_ALIGN", 3: "MQA_ERR_SHAPE",
              4: "MQA_ERR_WORKSPACE", 5: "MQA_ERR_DEVICE", 6: "MQA_ERR_LAUNCH"}

@@ -692,6 +692,73 @@ __device__ float wave_select(const float* __restrict__ E, const int* __restrict_
   return wave_min(mn);
 }
 
+// The k best of n records by (score descending, key ascending): every record
+// scoring above the k-th best score tau, then the ties of tau with the
+// smallest keys (keys are distinct and below 2^20). tau is found by
+// wave_kth_value; the cut among the ties by a two-level radix select over the
+// key bits (10 + 10) in the same LDS histogram. emit(slot, score, key) fills
+// slots [0, min(n, k)): above-tau records first, then the ties. Returns tau
+// (+inf when n == 0). Score comparisons are float comparisons (-0 == +0).
+template <class Emit>
+__device__ float wave_select_lowkey(const float* __restrict__ E, const int* __restrict__ I, int n,
+                                    int k, uint32_t* hist, Emit emit) {
+  const int l = lane_id();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  if (n <= k) {
+    float mn = __builtin_inff();
+    for (int i = l; i < n; i += kWave) {
+      const float e = E[i];
+      emit(i, e, I[i]);
+      mn = __builtin_fminf(mn, e);
+    }
+    return wave_min(mn);
+  }
+  const float tau = wave_kth_value(E, n, k, hist);
+  int gt = 0;
+  for (int i = l; i < n; i += kWave) gt += E[i] > tau ? 1 : 0;
+  gt = wave_sum(gt);
+  // the need-th smallest key among the records scoring tau
+  int rem = k - gt;
+  uint32_t kpre = 0, kmask = 0;
+  for (int lev = 0; lev < 2; ++lev) {
+    const int sh = lev == 0 ? 10 : 0;
+    constexpr uint32_t dmask = 1023u;
+    constexpr int nb = 1024;
+    for (int b = l; b < nb; b += kWave) hist[b] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    for (int i = l; i < n; i += kWave) {
+      const uint32_t key = (uint32_t)I[i];
+      if (E[i] == tau && (key & kmask) == kpre) atomicAdd(&hist[(key >> sh) & dmask], 1u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    int before;
+    const int bin = first_bin_reaching(hist, nb, rem, before);
+    rem -= before;
+    kpre |= (uint32_t)bin << sh;
+    kmask |= dmask << sh;
+    __builtin_amdgcn_wave_barrier();
+  }
+  const uint32_t kcut = kpre;  // the last tie taken
+  int taken_above = 0, taken_tie = 0;
+  for (int i0 = 0; i0 < n; i0 += kWave) {
+    const int i = i0 + l;
+    const bool in = i < n;
+    const float e = in ? E[i] : 0.f;
+    const int key = in ? I[i] : 0;
+    const bool up = in && e > tau;
+    const bool tie = in && e == tau && (uint32_t)key <= kcut;
+    const uint64_t mu = __ballot(up);
+    const uint64_t mt = __ballot(tie);
+    if (up) emit(taken_above + rank_in_mask(mu), e, key);
+    if (tie) emit(gt + taken_tie + rank_in_mask(mt), e, key);
+    taken_above += __popcll(mu);
+    taken_tie += __popcll(mt);
+  }
+  return tau;
+}
+
 // The best k of n > k records as wave_select picks them, widened by every
 // record tied with the k-th best while no more than `room` (>= k) records
 // are taken in all. emit(slot, score, key) fills slots [0, taken); returns

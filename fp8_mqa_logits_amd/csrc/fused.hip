@@ -67,6 +67,11 @@ __device__ __forceinline__ int slab_cap(const FusedParams& p) {
   return (p.flags & 4u) ? p.topk + 2 * kWave : kCap;
 }
 
+// Deterministic mode (MQA_FLAG_DETERMINISTIC): ties at a row's k-th exact
+// score go to the smallest keys, certificates are strict, and each row's
+// output is sorted by key.
+__device__ __forceinline__ bool det_mode(const FusedParams& p) { return (p.flags & 64u) != 0u; }
+
 __device__ __forceinline__ void row_range(const FusedParams& p, int r, int& s, int& e) {
   int a = p.starts[r], b = p.ends[r];
   a = a < 0 ? 0 : (a > p.keys ? p.keys : a);
@@ -886,13 +891,15 @@ __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int 
   if (l == 0 && band_count)
     atomicAdd(reinterpret_cast<unsigned long long*>(band_count), (unsigned long long)nb);
   auto take = [&](int slot, float, int idx) { emit(na + slot, idx); };
-  const float tau = nb <= 256
-      ? small_select(sE, sI, nb, need, reinterpret_cast<float*>(hist), take)
-      : wave_select(sE, sI, nb, need, hist, take);
+  const bool det = det_mode(p);
+  const float tau = det ? wave_select_lowkey(sE, sI, nb, need, hist, take)
+      : nb <= 256 ? small_select(sE, sI, nb, need, reinterpret_cast<float*>(hist), take)
+                  : wave_select(sE, sI, nb, need, hist, take);
   const float d = kBandSafety * __builtin_fmaxf(err, maxabs * 0x1p-18f);
   const float below = __builtin_fmaxf(max_below, T);
-  const bool ok_above = na == 0 || min_above - d >= tau;
-  const bool ok_below = below + d <= tau;
+  // deterministic mode: no record outside the band may tie with tau either
+  const bool ok_above = na == 0 || (det ? min_above - d > tau : min_above - d >= tau);
+  const bool ok_below = det ? below + d < tau : below + d <= tau;
   low = na == 0 ? tau : __builtin_fminf(tau, min_above - d);
   return ok_above && ok_below;
 }
@@ -1040,7 +1047,11 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_finish_kernel(FusedPa
       int s, e;
       row_range(p, r, s, e);
       int32_t* o = p.out + (int64_t)r * k;
-      wave_select(sE, sI, cnt, k, hist[w], [&](int sl, float, int idx) { o[sl] = idx - s; });
+      auto put = [&](int sl, float, int idx) { o[sl] = idx - s; };
+      if (det_mode(p))
+        wave_select_lowkey(sE, sI, cnt, k, hist[w], put);
+      else
+        wave_select(sE, sI, cnt, k, hist[w], put);
       if ((p.flags & 8u) && l == 0) atomicAdd(&p.header[H_RESCAN], 1u);
       continue;
     }
@@ -1103,14 +1114,59 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
         int32_t* o = p.out + (int64_t)r.r * k;
         const int base = r.s;
         const int have = r.cnt;
-        wave_select(sr.sE(i), sr.sI(i), have, k, sr.hist,
-                    [&](int sl, float, int idx) { o[sl] = idx - base; });
+        auto put = [&](int sl, float, int idx) { o[sl] = idx - base; };
+        if (det_mode(p))
+          wave_select_lowkey(sr.sE(i), sr.sI(i), have, k, sr.hist, put);
+        else
+          wave_select(sr.sE(i), sr.sI(i), have, k, sr.hist, put);
         for (int j = have + l; j < k; j += kWave) o[j] = -1;
         if ((p.flags & 8u) && l == 0) atomicAdd(&p.header[H_EXACT], 1u);
       }
     }
     __syncthreads();
   }
+}
+
+}  // namespace mqa
+
+namespace mqa {
+
+// Deterministic mode, last launch: each row with more than k visible keys has
+// its k output keys sorted ascending (one wave per row, a bitonic sort of the
+// k <= 2048 values in the wave's LDS; k is a power of two). Rows with n <= k
+// already hold 0..n-1 and their -1 padding.
+__global__ __launch_bounds__(kSelWaves * kWave) void fused_sort_kernel(FusedParams p) {
+  __shared__ int32_t buf[kSelWaves][kMaxTopk];
+  const int w = wave_id();
+  const int l = lane_id();
+  const int k = p.topk;
+  const int r = blockIdx.x * kSelWaves + w;
+  if (r >= p.rows) return;
+  int s, e;
+  row_range(p, r, s, e);
+  if (e - s <= k) return;
+  int32_t* o = p.out + (int64_t)r * k;
+  int32_t* v = buf[w];
+  for (int i = l; i < k; i += kWave) v[i] = o[i];
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  for (int size = 2; size <= k; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = l; t < (k >> 1); t += kWave) {
+        const int i = (t / stride) * 2 * stride + (t % stride);
+        const int j = i + stride;
+        const bool up = (i & size) == 0;
+        const int a = v[i], b = v[j];
+        if ((a > b) == up) {
+          v[i] = b;
+          v[j] = a;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  for (int i = l; i < k; i += kWave) o[i] = v[i];
 }
 
 }  // namespace mqa
@@ -1140,6 +1196,11 @@ extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   hipLaunchKernelGGL(mqa::fused_exact_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
+  if (p->flags & 64u) {
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(mqa::fused_sort_kernel, dim3(sel), dim3(mqa::kSelWaves * mqa::kWave), 0,
+                       stream, *p);
+  }
   return (int)hipGetLastError();
 }
 

@@ -67,6 +67,15 @@ extern "C" {
 #define MQA_FLAG_FORCE_RESCAN 32u   /* every gated row skips the certified select and
                                        is redone by the bounded rescan from an open
                                        bound */
+#define MQA_FLAG_DETERMINISTIC 64u  /* deterministic, batch-invariant selection (API
+                                       page, use_fused_mqa_topk: batch-invariant serving
+                                       stays on the dense path there because the fused
+                                       op resolves k-th-score ties in atomic order): a
+                                       row's output is the k keys of largest
+                                       exact score, ties at the k-th score going to the
+                                       smallest keys, listed in ascending key order
+                                       (then the -1 padding); certificates are strict,
+                                       and one more launch sorts the rows */
 
 /* Counters written to the first bytes of the workspace when MQA_FLAG_STATS is
  * set (read them after the stream has finished the call). A call over more

@@ -84,6 +84,55 @@ def check_topk_row(sel_idx: np.ndarray, row_logits: np.ndarray, topk: int,
     return None
 
 
+def check_lowkey_row(sel_row: np.ndarray, row_logits: np.ndarray, topk: int):
+    """The deterministic tie rule for one row, on the oracle's logits of its
+    visible keys (position = key - start): valid entries in ascending order,
+    then -1; and no key left out scores exactly the smallest selected logit
+    while being smaller than a selected key of that score (ties at the cut go
+    to the smallest keys). Returns None when it holds, else a message."""
+    sel_row = np.asarray(sel_row)
+    n = row_logits.shape[0]
+    m = min(n, topk)
+    lead = sel_row[:m]
+    if np.any(sel_row[m:] != -1):
+        return "padding is not trailing -1"
+    if m > 1 and np.any(np.diff(lead) <= 0):
+        return "valid entries not in ascending key order"
+    if n <= topk:
+        return None
+    chosen = np.zeros(n, bool)
+    chosen[lead] = True
+    cut = row_logits[chosen].min()
+    at_cut = row_logits == cut
+    taken = np.nonzero(at_cut & chosen)[0]
+    left = np.nonzero(at_cut & ~chosen)[0]
+    if left.size and taken.size and left.min() < taken.max():
+        return (f"tie at the cut {cut!r}: key {int(left.min())} left out, "
+                f"key {int(taken.max())} taken")
+    return None
+
+
+def check_lowkey(out_rows: np.ndarray, rows, oracle_problem, topk: int, batch: int = 16,
+                 threads: int = 0):
+    """check_lowkey_row on the given rows (oracle logits a batch at a time)."""
+    import oracle  # test infrastructure: this module lives beside it
+
+    rows = np.asarray(rows, np.int32)
+    fails = []
+    for lo in range(0, rows.shape[0], batch):
+        rb = rows[lo:lo + batch]
+        rng = [oracle_problem.visible(int(r)) for r in rb]
+        c0 = min(s for s, _ in rng)
+        c1 = max(e for _, e in rng)
+        lg = oracle.logits(oracle_problem, rb, col0=c0, ncols=max(c1 - c0, 1), threads=threads)
+        for i, r in enumerate(rb):
+            s, e = rng[i]
+            msg = check_lowkey_row(np.asarray(out_rows[lo + i]), lg[i, s - c0:e - c0], topk)
+            if msg:
+                fails.append((int(r), msg))
+    return fails
+
+
 def check_topk(out_rows: np.ndarray, rows, oracle_problem, topk: int,
                rel_tol: float = REL_TOL, batch: int = 16, threads: int = 0):
     """Rule (ii) on the given rows. out_rows: [len(rows), topk] result rows.

@@ -63,6 +63,39 @@ def test_checker_accepts_any_tie_resolution():
     assert check.check_topk_row(np.array([1, 2]), lg, 2) is not None
 
 
+def test_lowkey_checker_pins():
+    # ties at the cut go to the smallest keys; valid entries ascending
+    lg = np.array([5, 3, 3, 3, 1, 0], np.float32)
+    assert check.check_lowkey_row(np.array([0, 1]), lg, 2) is None
+    assert check.check_lowkey_row(np.array([0, 3]), lg, 2) is not None  # key 1 left out
+    assert check.check_lowkey_row(np.array([1, 0]), lg, 2) is not None  # not ascending
+    assert check.check_lowkey_row(np.array([0, 1, 2]), lg, 3) is None
+    assert check.check_lowkey_row(np.array([0, 2, 3]), lg, 3) is not None
+    # short rows: 0..n-1 then -1
+    assert check.check_lowkey_row(np.array([0, 1, -1]), lg[:2], 3) is None
+    assert check.check_lowkey_row(np.array([0, -1, 1]), lg[:2], 3) is not None
+    # against brute force: the (value desc, key asc) choice, sorted, passes both
+    # rules; every other correct tie resolution fails the tie rule only
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        n, k = int(rng.integers(2, 12)), int(rng.integers(1, 6))
+        k = min(k, n - 1)
+        v = rng.integers(0, 4, size=n).astype(np.float32)
+        order = sorted(range(n), key=lambda j: (-v[j], j))
+        want = np.sort(np.array(order[:k], np.int32))
+        assert np.array_equal(np.sort(oracle.select(v, k)), want)
+        assert check.check_lowkey_row(want, v, k) is None
+        assert check.check_topk_row(want, v, k) is None
+        tau = v[order[k - 1]]
+        ties = [j for j in range(n) if v[j] == tau]
+        taken = [j for j in want if v[j] == tau]
+        if len(ties) > len(taken):
+            alt = sorted(set(want.tolist()) - {max(taken)} | {max(ties)})
+            alt = np.array(alt, np.int32)
+            assert check.check_topk_row(alt, v, k) is None
+            assert check.check_lowkey_row(alt, v, k) is not None
+
+
 def test_checker_tolerance_is_relative_to_row_max():
     lg = np.array([1000.0, 10.0, 10.0 - 5e-3, 9.0], np.float32)
     # tol = 1e-5 * 1000 = 1e-2: keys within 1e-2 of the k-th score may swap
