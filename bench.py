@@ -23,7 +23,8 @@ Prints ONE JSON line (rank 0):
              host's cores over a bounded sample of the same rows.
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu,
 --dense (also time the chunked dense logits + top-k path, for context),
---config N (workload 1..5), --sweep (instead of the benchmark: fused and
+--config N (workload 1..5), --deterministic (MQA_FLAG_DETERMINISTIC: ties at
+the k-th score to the smallest keys, outputs sorted), --sweep (instead of the benchmark: fused and
 dense times on the causal-tail sweep, 16384 rows x 16K..1M keys, one JSON line
 per point), --copy-calibration MIB (instead of the benchmark,
 run a plain 1-D device copy of MIB MiB five times: the known-size kernel that
@@ -253,6 +254,7 @@ def main():
     ap.add_argument("--dense", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--deterministic", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this path runs on one GPU; multi-GPU runs are not supported "
@@ -296,9 +298,11 @@ def main():
     ws = mqa.alloc_workspace(wl.rows)
     out = torch.empty((wl.rows, wl.topk), dtype=torch.int32, device=dev)
 
+    mode = mqa.FLAG_DETERMINISTIC if args.deterministic else 0
+
     def step(flags=0):
         mqa.mqa_topk_prefill(d["q"], d["k"], d["scales"], d["weights"], d["starts"], d["ends"],
-                             wl.topk, out=out, workspace=ws, flags=flags)
+                             wl.topk, out=out, workspace=ws, flags=flags | mode)
 
     # path statistics (one extra call outside the timed region)
     step(mqa.FLAG_STATS)
@@ -335,7 +339,8 @@ def main():
         "dtype": "fp8e4m3 MFMA, fp32 scores",
         "data": "synthetic (seeded N(0,1) e4m3 q/k, UE8M0 scales 2^[-4,0], N(0,1)/sqrt(32) weights)",
         "config": {"workload": wl.name, "rows": wl.rows, "keys": wl.keys, "topk": wl.topk,
-                   "visible_pairs": pairs, "parallelism": "1 GPU"},
+                   "visible_pairs": pairs, "parallelism": "1 GPU",
+                   "ties": "lowest key, sorted output" if args.deterministic else "any"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS,
                      "traffic": traffic_from_counters(wl.name), "kernel": "fused_topk_kernel",

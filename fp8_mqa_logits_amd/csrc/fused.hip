@@ -1131,42 +1131,73 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
 
 namespace mqa {
 
-// Deterministic mode, last launch: each row with more than k visible keys has
-// its k output keys sorted ascending (one wave per row, a bitonic sort of the
-// k <= 2048 values in the wave's LDS; k is a power of two). Rows with n <= k
-// already hold 0..n-1 and their -1 padding.
-__global__ __launch_bounds__(kSelWaves * kWave) void fused_sort_kernel(FusedParams p) {
-  __shared__ int32_t buf[kSelWaves][kMaxTopk];
-  const int w = wave_id();
+// Ascending bitonic sort of the 64 * E ints at o (16-byte aligned), one wave,
+// in registers: lane l holds elements l * E .. l * E + E - 1; stages whose
+// stride is below E compare within a lane, the others with lane l ^ (stride /
+// E) through a lane-xor shuffle.
+template <int E>
+__device__ __forceinline__ void wave_sort_asc(int32_t* o) {
   const int l = lane_id();
-  const int k = p.topk;
-  const int r = blockIdx.x * kSelWaves + w;
+  int v[E];
+  int4* o4 = reinterpret_cast<int4*>(o + l * E);
+#pragma unroll
+  for (int j = 0; j < E / 4; ++j) {
+    const int4 x = o4[j];
+    v[4 * j] = x.x;
+    v[4 * j + 1] = x.y;
+    v[4 * j + 2] = x.z;
+    v[4 * j + 3] = x.w;
+  }
+  for (int size = 2; size <= kWave * E; size <<= 1) {
+    // cross-lane stages (stride >= E)
+    for (int stride = size >> 1; stride >= E; stride >>= 1) {
+      const int lm = stride / E;
+      const bool lower = (l & lm) == 0;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const int p = __shfl_xor(v[j], lm, 64);
+        const bool up = ((l * E + j) & size) == 0;
+        v[j] = lower == up ? (v[j] < p ? v[j] : p) : (v[j] > p ? v[j] : p);
+      }
+    }
+    // in-lane stages (stride < E, compile-time strides: constant register
+    // indices)
+#pragma unroll
+    for (int stride = E / 2; stride > 0; stride >>= 1) {
+      if (stride >= size) continue;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        if (j & stride) continue;  // the pair (j, j + stride)
+        const bool up = ((l * E + j) & size) == 0;
+        const int a = v[j], b = v[j + stride];
+        const int mn = a < b ? a : b, mx = a < b ? b : a;
+        v[j] = up ? mn : mx;
+        v[j + stride] = up ? mx : mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < E / 4; ++j) o4[j] = int4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+}
+
+// Deterministic mode, last launch: each row with more than k visible keys has
+// its k output keys sorted ascending (one wave per row, wave_sort_asc; k is
+// 512, 1024 or 2048). Rows with n <= k already hold 0..n-1 and their -1
+// padding.
+__global__ __launch_bounds__(kSelWaves * kWave) void fused_sort_kernel(FusedParams p) {
+  const int r = blockIdx.x * kSelWaves + wave_id();
   if (r >= p.rows) return;
+  const int k = p.topk;
   int s, e;
   row_range(p, r, s, e);
   if (e - s <= k) return;
   int32_t* o = p.out + (int64_t)r * k;
-  int32_t* v = buf[w];
-  for (int i = l; i < k; i += kWave) v[i] = o[i];
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  for (int size = 2; size <= k; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = l; t < (k >> 1); t += kWave) {
-        const int i = (t / stride) * 2 * stride + (t % stride);
-        const int j = i + stride;
-        const bool up = (i & size) == 0;
-        const int a = v[i], b = v[j];
-        if ((a > b) == up) {
-          v[i] = b;
-          v[j] = a;
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
-  for (int i = l; i < k; i += kWave) o[i] = v[i];
+  if (k == 2048)
+    wave_sort_asc<32>(o);
+  else if (k == 1024)
+    wave_sort_asc<16>(o);
+  else
+    wave_sort_asc<8>(o);
 }
 
 }  // namespace mqa
