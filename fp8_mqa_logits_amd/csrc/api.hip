@@ -61,7 +61,8 @@ const DeviceInfo* device_info(int device) {
 }
 
 struct Layout {
-  size_t header, order, xrow, xqueue, xflag, rqueue, rowinfo, slabE, slabI, tmpE, tmpI, total;
+  size_t header, order, xrow, xqueue, xflag, rqueue, rowinfo, seg, slabE, slabI, tmpE, tmpI,
+      total;
   int grid, nblocks;
 };
 
@@ -93,6 +94,8 @@ Layout layout(int rows, const DeviceInfo& d) {
   off = align_up(off + 2 * rows_pad * 4);
   L.rowinfo = off;
   off = align_up(off + rows_pad * sizeof(mqa::RowInfo));
+  L.seg = off;
+  off = align_up(off + rows_pad * mqa::kMaxSeg * sizeof(mqa::SegInfo));
   const size_t slab = rows_pad * mqa::kSlabRow * 4;
   L.slabE = off;
   off = align_up(off + slab);
@@ -108,6 +111,18 @@ Layout layout(int rows, const DeviceInfo& d) {
 }
 
 int batch_rows(int rows) { return rows < mqa::kMaxBatchRows ? rows : mqa::kMaxBatchRows; }
+
+// Key segments per block (FusedParams.nseg): a power of two that gives about
+// two work items per persistent workgroup when blocks are fewer, bounded so
+// that a segment's part of a slab row (kSlabRow / nseg records) holds a merge
+// of 2 * topk records plus two chunks.
+int key_segments(int nblocks, int grid, int topk) {
+  int s = 1;
+  while (s < mqa::kMaxSeg && (size_t)nblocks * s < (size_t)2 * grid &&
+         mqa::kSlabRow / (2 * s) >= 2 * topk + 128)
+    s *= 2;
+  return s;
+}
 
 int launch_error(int hip_code) {
   std::snprintf(g_err, sizeof(g_err), "HIP launch failed: %s",
@@ -214,11 +229,14 @@ int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
     p.xflag = reinterpret_cast<uint32_t*>(ws + L.xflag);
     p.rqueue = reinterpret_cast<int32_t*>(ws + L.rqueue);
     p.rowinfo = reinterpret_cast<mqa::RowInfo*>(ws + L.rowinfo);
+    p.seg = reinterpret_cast<mqa::SegInfo*>(ws + L.seg);
     p.slabE = reinterpret_cast<float*>(ws + L.slabE);
     p.slabI = reinterpret_cast<int32_t*>(ws + L.slabI);
     p.tmpE = reinterpret_cast<float*>(ws + L.tmpE);
     p.tmpI = reinterpret_cast<int32_t*>(ws + L.tmpI);
     const int grid = L.grid < p.nblocks ? L.grid : p.nblocks;
+    p.nseg = key_segments(p.nblocks, L.grid, topk);
+    p.scan_grid = L.grid < p.nblocks * p.nseg ? L.grid : p.nblocks * p.nseg;
     // timing events: from the first batch's scan to the end of the last one
     const int rc = mqa_fused_launch(&p, grid, static_cast<hipStream_t>(stream),
                                     r0 == 0 ? eb : nullptr, r0 + nr >= rows ? ee : nullptr);

@@ -235,17 +235,28 @@ struct SlabRefs {
   __device__ int32_t* sI(int i) const { return sI0 + i * kSlabRow; }
 };
 
+// seg >= 0: key segment seg of a split scan (p.nseg > 1), whose records go to
+// records [seg * R, (seg + 1) * R) of each slab row, R = kSlabRow / nseg, with
+// a capacity of R - 64 (one more chunk fits past it); seg < 0: the whole row.
 __device__ __forceinline__ SlabRefs slab_refs(const FusedParams& p, int b, uint32_t* hist,
-                                              int keep) {
+                                              int keep, int seg = -1) {
   SlabRefs sr;
   const int64_t row0 = (int64_t)b * kBlockRows + wave_id() * kRowsPerWave;
-  sr.sE0 = p.slabE + row0 * kSlabRow;
-  sr.sI0 = p.slabI + row0 * kSlabRow;
+  const int region = kSlabRow / p.nseg;
+  const int64_t off = seg > 0 ? (int64_t)seg * region : 0;
+  sr.sE0 = p.slabE + row0 * kSlabRow + off;
+  sr.sI0 = p.slabI + row0 * kSlabRow + off;
   sr.delta = (int)(reinterpret_cast<const char*>(p.slabI) - reinterpret_cast<const char*>(p.slabE));
   sr.buf = __builtin_amdgcn_make_buffer_rsrc(sr.sE0, 4, sr.delta / 4 + kRowsPerWave * kSlabRow,
                                              kBufferFlags);
   sr.hist = hist;
   sr.cap = slab_cap(p);
+  if (seg >= 0 && p.nseg > 1) {
+    // SMALL_CAP: a segment's part of the row merges past topk / (2 nseg) + 64
+    // records (segments of i.i.d. rows hold about topk / nseg candidates)
+    const int c = (p.flags & 4u) ? p.topk / (2 * p.nseg) + kWave : region - kWave;
+    sr.cap = c < region - kWave ? c : region - kWave;
+  }
   sr.keep = keep < sr.cap - kWave ? keep : sr.cap - kWave;
   return sr;
 }
@@ -330,8 +341,9 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
     for (int j = 0; j < kRowsPerWave; ++j)
       if (i == j) {
         rs[j].cnt = kept;
+        rs[j].thr = bound;
         th[j] = next_up(bound);
-        if (!EXACT && lane_id() == 0) {
+        if (!EXACT && p.nseg == 1 && lane_id() == 0) {
           p.rowinfo[rs[j].r].thr = bound;
           p.rowinfo[rs[j].r].strict = 1;
         }
@@ -698,18 +710,25 @@ struct __align__(16) ScanSmem {
   int wlo[kWaves], whi[kWaves], wf[kWaves];
 };
 
+// SPLIT: the launch uses key segments (p.nseg > 1); the instance without
+// them keeps no segment state.
+template <bool SPLIT>
 __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
   __shared__ ScanSmem sm;
   MQA_DECLARE_STAGES(stg);
   const int tid = threadIdx.x;
   const int w = wave_id();
   const int l = lane_id();
+  // work items: (block, key segment), the block order major
+  const int nseg = SPLIT ? p.nseg : 1;
+  const int items = p.nblocks * nseg;
   for (;;) {
     if (tid == 0) sm.block = (int)atomicAdd(&p.header[H_CLAIM], 1u);
     __syncthreads();
     const int bi = sm.block;
-    if (bi >= p.nblocks) break;
-    const int b = p.order[bi];
+    if (bi >= items) break;
+    const int b = p.order[SPLIT ? bi / nseg : bi];
+    const int seg = SPLIT ? bi % nseg : 0;
     RowState rs[kRowsPerWave];
     QueryRow qr[kRowsPerWave];
     wave_rows(p, b, rs);
@@ -733,17 +752,28 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
     }
     int lo, hi, unused;
     block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, 0, p.keys, lo, hi, unused);
+    if (SPLIT && hi > lo) {
+      // segment seg of the block's key range, in whole chunks
+      const int len = ((hi - lo + nseg - 1) / nseg + kChunk - 1) / kChunk * kChunk;
+      const int a = lo + seg * len;
+      hi = a + len < hi ? a + len : hi;
+      lo = a;
+    }
     if (hi > lo) {
       FoldOp fo;
       build_fold(fo, p.q, p.weights, frows);
-      const SlabRefs sr = slab_refs(p, b, sm.hist[w], 2 * p.topk);
+      const SlabRefs sr = slab_refs(p, b, sm.hist[w], 2 * p.topk, SPLIT ? seg : -1);
       scan_rows<false>(p, stg, qr, fo, rs, M_GATED, lo, hi, sr);
-      if (l == 0) {
+    }
+    if (l == 0) {
 #pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i) {
-          const RowState& r = rs[i];
-          if (r.mode == M_ALL || r.mode == M_GATED) p.rowinfo[r.r].cnt = r.cnt;
-        }
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        const RowState& r = rs[i];
+        if (r.mode != M_ALL && r.mode != M_GATED) continue;
+        if (!SPLIT)
+          p.rowinfo[r.r].cnt = r.cnt;
+        else
+          p.seg[(int64_t)r.r * kMaxSeg + seg] = SegInfo{r.thr, r.cnt};
       }
     }
     __syncthreads();
@@ -751,7 +781,9 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
 }
 
 // Top-k of a row from its FP8-scored candidates (sE, sI)[0..n), n >= k, all
-// with approximate score >= T (non-candidates score below T):
+// with approximate score >= Tlo, every non-candidate scoring <= Thi (Tlo =
+// Thi: the row's admission bound; a row scanned in key segments has one bound
+// per segment, Tlo their minimum and Thi their maximum):
 //   1. one pass for the candidates' score range, one histogram pass over
 //      2048 equal-width bins of that range (descending scores);
 //   2. the bins holding ranks k-kBand and k+kBand bound the band: records in
@@ -762,14 +794,14 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
 //   4. certificate: with D = kBandSafety * (largest |exact - approximate| in
 //      the band, floored at 2^-18 of the row's largest score magnitude), the
 //      result is exact when every record above the band scores >= tau + D and
-//      every record below it (and every non-candidate, < T) <= tau - D, tau
+//      every record below it (and every non-candidate, <= Thi) <= tau - D, tau
 //      being the k-th exact score.
 // Returns false when the certificate fails (the caller rescans the row); `low`
 // then receives a lower bound of the row's k-th exact score (the k records
 // taken score at least min(tau, smallest above-band score - D)), or -inf.
 template <class Emit>
-__device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int n, int k, float T,
-                              const QueryRow& qr, uint32_t* hist,
+__device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int n, int k,
+                              float Tlo, float Thi, const QueryRow& qr, uint32_t* hist,
                               unsigned* band_count, float& low, Emit emit) {
   const int l = lane_id();
   constexpr int kBins = kHistWords;
@@ -788,8 +820,8 @@ __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int 
     x = __builtin_fmaxf(x, sE[i]);
   }
   const float mx = wave_max(x);
-  // every candidate scored >= T; the lower end of the range is T when T is finite
-  const float mn = T > -__builtin_inff() ? T : wave_min(m);
+  // every candidate scored >= Tlo; the lower end of the range is Tlo when finite
+  const float mn = Tlo > -__builtin_inff() ? Tlo : wave_min(m);
   const float span = mx - mn;
   const float inv = span > 0.f ? (float)(kBins - 1) / span : 0.f;
   auto bin_of = [&](float e) {
@@ -896,7 +928,7 @@ __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int 
       : nb <= 256 ? small_select(sE, sI, nb, need, reinterpret_cast<float*>(hist), take)
                   : wave_select(sE, sI, nb, need, hist, take);
   const float d = kBandSafety * __builtin_fmaxf(err, maxabs * 0x1p-18f);
-  const float below = __builtin_fmaxf(max_below, T);
+  const float below = __builtin_fmaxf(max_below, Thi);
   // deterministic mode: no record outside the band may tie with tau either
   const bool ok_above = na == 0 || (det ? min_above - d > tau : min_above - d >= tau);
   const bool ok_below = det ? below + d < tau : below + d <= tau;
@@ -937,22 +969,49 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_select_kernel(FusedPa
   bool ok = false;
   float low = -__builtin_inff();
   const bool forced = ri.mode != M_EXACT && (p.flags & 32u);  // rescan from an open bound
+  float* sE = p.slabE + (int64_t)r * kSlabRow;
+  int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
+  // candidates and admission bounds: the row's, or the union of its key
+  // segments' (moved down to one run at the start of the slab row; tlo bounds
+  // every candidate from below, thi every other key from above)
+  int cnt = ri.cnt;
+  float tlo = ri.thr, thi = ri.thr;
+  if (p.nseg > 1 && ri.mode != M_EXACT) {
+    const int region = kSlabRow / p.nseg;
+    cnt = 0;
+    tlo = __builtin_inff();
+    thi = -__builtin_inff();
+    for (int sg = 0; sg < p.nseg; ++sg) {
+      const SegInfo si = p.seg[(int64_t)r * kMaxSeg + sg];
+      tlo = __builtin_fminf(tlo, si.thr);
+      thi = __builtin_fmaxf(thi, si.thr);
+      const int src = sg * region;
+      // forward copy to a lower offset: no lane reads a record already written
+      if (sg > 0 && src != cnt) {
+        for (int i = l; i < si.cnt; i += kWave) {
+          const float e = sE[src + i];
+          const int32_t x = sI[src + i];
+          sE[cnt + i] = e;
+          sI[cnt + i] = x;
+        }
+      }
+      cnt += si.cnt;
+    }
+  }
   if (ri.mode != M_EXACT && !forced) {
-    if (ri.cnt >= k) {
+    if (cnt >= k) {
       int s, e;
       row_range(p, r, s, e);
       QueryRow qr;
       load_query(qr, p.q, p.weights, r);
       int32_t* o = p.out + (int64_t)r * k;
-      float* sE = p.slabE + (int64_t)r * kSlabRow;
-      int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
-      ok = select_banded(p, sE, sI, ri.cnt, k, ri.thr, qr, hist[w],
+      ok = select_banded(p, sE, sI, cnt, k, tlo, thi, qr, hist[w],
                          stats ? &p.header[H_BAND_LO] : nullptr, low,
                          [&](int sl, int idx) { o[sl] = idx - s; });
       if (stats && l == 0) {
         atomicAdd(&p.header[ok ? H_GATED : H_UNCERT], 1u);
         atomicAdd(reinterpret_cast<unsigned long long*>(&p.header[H_CAND_LO]),
-                  (unsigned long long)ri.cnt);
+                  (unsigned long long)cnt);
       }
     } else if (stats && l == 0) {
       atomicAdd(&p.header[H_UNDER], 1u);
@@ -1210,7 +1269,12 @@ extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t
   hipLaunchKernelGGL(mqa::fused_gate_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (scan_begin && (e = hipEventRecord(scan_begin, stream)) != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(mqa::fused_topk_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
+  if (p->nseg > 1)
+    hipLaunchKernelGGL(mqa::fused_topk_kernel<true>, dim3(p->scan_grid), dim3(mqa::kThreads), 0,
+                       stream, *p);
+  else
+    hipLaunchKernelGGL(mqa::fused_topk_kernel<false>, dim3(p->scan_grid), dim3(mqa::kThreads), 0,
+                       stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (scan_end && (e = hipEventRecord(scan_end, stream)) != hipSuccess) return (int)e;
   const int sel = (p->rows + mqa::kSelWaves - 1) / mqa::kSelWaves;
@@ -1237,7 +1301,7 @@ extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t
 
 extern "C" int mqa_fused_occupancy(int* wg_per_cu) {
   int a = 0, b = 0, c = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, mqa::fused_topk_kernel,
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, mqa::fused_topk_kernel<false>,
                                                               mqa::kThreads, 0);
   if (e != hipSuccess) return (int)e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, mqa::fused_exact_kernel, mqa::kThreads, 0);

@@ -16,6 +16,14 @@ struct RowInfo {
   int strict;  // 1: a merge raised thr; later candidates had to beat it strictly
 };
 
+// Per-(row, key segment) state of a split scan (nseg > 1): the segment's
+// final admission bound and its candidate count in the segment's part of the
+// row's slab.
+struct SegInfo {
+  float thr;  // every candidate of the segment scores >= thr, every other key <= thr
+  int cnt;
+};
+
 struct FusedParams {
   const uint8_t* q;
   const uint8_t* k;
@@ -25,6 +33,11 @@ struct FusedParams {
   const int32_t* ends;
   int32_t* out;
   int rows, keys, topk, nblocks;
+  // Key segments per block: with few blocks each block's key range is split
+  // into nseg segments scanned as separate work items (nblocks * nseg items
+  // over scan_grid persistent workgroups), each into its own part of the
+  // rows' slabs; 1 otherwise.
+  int nseg, scan_grid;
   unsigned flags;
   uint32_t* header;  // 64 words: stats + claim counter
   int32_t* order;    // [nblocks] heaviest-first block order
@@ -33,6 +46,7 @@ struct FusedParams {
   int32_t* rqueue;   // [2][nblocks * 32] rows queued for the two bounded-rescan rounds
   uint32_t* xflag;   // [nblocks] 1 = the block is queued
   RowInfo* rowinfo;  // [rows]
+  SegInfo* seg;      // [nblocks * 32 rows][kMaxSeg] (nseg > 1)
   float* slabE;      // [nblocks * 32 rows][kSlabRow] candidate scores
   int32_t* slabI;    // [nblocks * 32 rows][kSlabRow] candidate keys
   float* tmpE;       // [grid][8 waves][kTmp] merge buffers
@@ -67,6 +81,7 @@ constexpr int kTmp = 10240;  // merge-buffer records per wave
 // 64 records past it (rows stay 1 KiB aligned).
 constexpr int kSlabRow = 16384 + 256;
 constexpr int kFusedWaves = 8;
+constexpr int kMaxSeg = 8;
 // Rows per launch sequence: larger calls run in batches of this many rows
 // (the workspace holds one batch's candidate slabs, 1.09 GB).
 constexpr int kMaxBatchRows = 16384;

@@ -60,7 +60,10 @@ extern "C" {
  * does": exact rescan) so that tests can reach it. */
 #define MQA_FLAG_FORCE_EXACT 1u     /* every row takes the exact streaming rescan */
 #define MQA_FLAG_FORCE_GATE_MISS 2u /* the gate admits nothing: every gated row falls back */
-#define MQA_FLAG_SMALL_CAP 4u       /* per-row candidate slab limited to topk + 128 */
+#define MQA_FLAG_SMALL_CAP 4u       /* per-row candidate slab limited to topk + 128
+                                       (a merge past topk / (2 S) + 64 records per key
+                                       segment when a call with few rows splits each
+                                       block's keys into S segments) */
 #define MQA_FLAG_STATS 8u           /* fill the mqa_stats header of the workspace */
 #define MQA_FLAG_TIME_SCAN 16u      /* record HIP events around the scan kernel (see
                                        mqa_scan_time); a benchmarking aid */
