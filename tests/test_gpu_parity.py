@@ -306,3 +306,29 @@ def test_fused_row_batches():
     rows_all = np.arange(rows)
     fails = check.check_topk(o, rows_all, oracle_problem(wl), topk, TOL)
     assert not fails, fails[:5]
+
+
+@pytest.mark.parametrize("cfg,nrows", [(3, 4096), (4, 2048)])
+def test_fused_key_split_long_rows(cfg, nrows):
+    # a call with few rows splits each block's keys into segments (top-2048:
+    # 2 segments here); the first nrows rows of config 3 / config 4 (the
+    # latter includes the biased request's first rows) as a call of their own
+    wl = W.config(cfg)
+    say(f"case: fused key-split scan, first {nrows} rows of {wl.name}; validity all, "
+        f"set rule on 64 rows")
+    d = to_device(wl)
+    sub = {n: (t[:nrows].contiguous() if n in ("q", "weights", "starts", "ends") else t)
+           for n, t in d.items()}
+    ws = mqa.alloc_workspace(nrows)
+    out = fused(sub, wl.topk, flags=mqa.FLAG_STATS, workspace=ws)
+    st = mqa.read_stats(ws)
+    say("stats", st)
+    o = out.cpu().numpy()
+    del d, sub
+    p = oracle.Problem(wl.q[:nrows], wl.k, oracle.key_scales(wl.scale_bytes), wl.weights[:nrows],
+                       wl.starts[:nrows], wl.ends[:nrows])
+    assert not check.check_valid(o, wl.starts[:nrows], wl.ends[:nrows], wl.keys, wl.topk)
+    rows = np.sort(np.random.default_rng(5).choice(nrows, 64, replace=False)).astype(np.int32)
+    fails = check.check_topk(o[rows], rows, p, wl.topk, TOL)
+    assert not fails, fails[:5]
+    assert st["rows_exact"] == 0
