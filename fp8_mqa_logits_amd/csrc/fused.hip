@@ -528,12 +528,19 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
   const int k = p.topk;
   const int cap = slab_cap(p);
   const bool stats = p.flags & 8u;
+  // Work items (block, part): with key segments (p.nseg > 1, few blocks) a
+  // block's rows are shared by p.nseg workgroups, part t serving the rows of
+  // waves [t * 8 / nseg, (t + 1) * 8 / nseg); every part samples the whole
+  // block's union range, so the thresholds do not depend on the split.
+  const int parts = p.nseg;
+  const int items = p.nblocks * parts;
   for (;;) {
     if (tid == 0) sm.block = (int)atomicAdd(&p.header[H_GCLAIM], 1u);
     __syncthreads();
     const int bi = sm.block;
-    if (bi >= p.nblocks) break;
-    const int b = p.order[bi];
+    if (bi >= items) break;
+    const int b = p.order[bi / parts];
+    const bool mine = w * parts / kWaves == bi % parts;
     RowState rs[kRowsPerWave];
     QueryRow qr[kRowsPerWave];
     wave_rows(p, b, rs);
@@ -548,20 +555,25 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
       const int n = r.e - r.s;
       if (n <= k) {
         r.mode = M_SHORT;
-        int32_t* o = p.out + (int64_t)r.r * k;
-        for (int j = l; j < k; j += kWave) o[j] = j < n ? j : -1;
-        if (stats && l == 0) atomicAdd(&p.header[H_SHORT], 1u);
+        if (mine) {
+          int32_t* o = p.out + (int64_t)r.r * k;
+          for (int j = l; j < k; j += kWave) o[j] = j < n ? j : -1;
+          if (stats && l == 0) atomicAdd(&p.header[H_SHORT], 1u);
+        }
       } else if (p.flags & 1u) {
         r.mode = M_EXACT;  // forced: straight to the exact rescan
       } else if (n <= 4 * k && n <= cap) {
         r.mode = M_ALL;  // every visible key is a candidate
       } else {
-        r.mode = M_GATED;
-        load_query(qr[i], p.q, p.weights, r.r, 0.5f);
-        frows[i] = r.r;
+        // rows of other parts count for the union range only
+        r.mode = mine ? M_GATED : M_OFF;
+        if (mine) {
+          load_query(qr[i], p.q, p.weights, r.r, 0.5f);
+          frows[i] = r.r;
+        }
         wlo = r.s < wlo ? r.s : wlo;
         whi = r.e > whi ? r.e : whi;
-        wg = 1;
+        wg |= mine ? 1 : 0;  // the part samples only when it serves a gated row
       }
     }
     int lo, hi, any_g;
@@ -587,6 +599,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
         nsamp[i] = 0;
       }
       auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
+        if (!mine) return;
         const int key = lo + (c * kChunk + l) * stride;
         KeyTile kt;
         load_keys_lds(kt, kc);
@@ -688,7 +701,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
         r.thr = thr;
       }
     }
-    if (l == 0) {
+    if (mine && l == 0) {
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         const RowState& r = rs[i];
@@ -1266,7 +1279,8 @@ extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t
   hipError_t e;
   hipLaunchKernelGGL(mqa::fused_plan_kernel, dim3(1), dim3(1024), 0, stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(mqa::fused_gate_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
+  hipLaunchKernelGGL(mqa::fused_gate_kernel, dim3(p->scan_grid), dim3(mqa::kThreads), 0, stream,
+                     *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (scan_begin && (e = hipEventRecord(scan_begin, stream)) != hipSuccess) return (int)e;
   if (p->nseg > 1)
