@@ -61,8 +61,8 @@ const DeviceInfo* device_info(int device) {
 }
 
 struct Layout {
-  size_t header, order, xrow, xqueue, xflag, rqueue, rowinfo, seg, slabE, slabI, tmpE, tmpI,
-      total;
+  size_t header, order, xrow, xqueue, xflag, fqueue, fflag, rinfo, rqueue, rowinfo, seg, slabE,
+      slabI, tmpE, tmpI, total;
   int grid, nblocks;
 };
 
@@ -90,6 +90,12 @@ Layout layout(int rows, const DeviceInfo& d) {
   off = align_up(off + (size_t)L.nblocks * 4);
   L.xflag = off;
   off = align_up(off + (size_t)L.nblocks * 4);
+  L.fqueue = off;
+  off = align_up(off + (size_t)L.nblocks * 4);
+  L.fflag = off;
+  off = align_up(off + (size_t)L.nblocks * 4);
+  L.rinfo = off;
+  off = align_up(off + rows_pad * sizeof(mqa::RefineInfo));
   L.rqueue = off;
   off = align_up(off + 2 * rows_pad * 4);
   L.rowinfo = off;
@@ -227,6 +233,9 @@ int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
     p.xrow = ws + L.xrow;
     p.xqueue = reinterpret_cast<int32_t*>(ws + L.xqueue);
     p.xflag = reinterpret_cast<uint32_t*>(ws + L.xflag);
+    p.fqueue = reinterpret_cast<int32_t*>(ws + L.fqueue);
+    p.fflag = reinterpret_cast<uint32_t*>(ws + L.fflag);
+    p.rinfo = reinterpret_cast<mqa::RefineInfo*>(ws + L.rinfo);
     p.rqueue = reinterpret_cast<int32_t*>(ws + L.rqueue);
     p.rowinfo = reinterpret_cast<mqa::RowInfo*>(ws + L.rowinfo);
     p.seg = reinterpret_cast<mqa::SegInfo*>(ws + L.seg);

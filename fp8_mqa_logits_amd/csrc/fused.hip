@@ -41,6 +41,9 @@ constexpr int kBlockRows = kWaves * kRowsPerWave;  // 32
 static_assert(kBlockRows == kFusedBlockRows, "block rows");
 constexpr int kGateBins = 512;
 constexpr int kGateOff = 64;  // bins above the first-tile maximum
+// A row's threshold bin that holds more sample keys than this and than the ks
+// the threshold is placed at is binned again, finer (fused_refine_kernel).
+constexpr int kGateCrowded = 48;
 constexpr int kHistWords = 2048;
 constexpr int kBand = 32;           // keys on each side of rank k that are rescored exactly
 constexpr float kBandSafety = 8.f;  // certificate margin, in units of the band's largest error
@@ -54,7 +57,9 @@ enum : int {
   H_XCLAIM = 17,  // exact-rescan claim counter
   H_GCLAIM = 18,  // gate claim counter
   H_RQ = 19,      // rows queued for the bounded rescan (then 21 for its second round)
-  H_RCLAIM = 20   // work-item claim counter of the bounded rescan (then 22)
+  H_RCLAIM = 20,  // work-item claim counter of the bounded rescan (then 22)
+  H_FQ = 24,      // blocks queued for the gate's fine pass
+  H_FCLAIM = 25   // claim counter of the fine pass
 };
 
 enum RowMode : int { M_OFF = 0, M_SHORT = 1, M_ALL = 2, M_GATED = 3, M_EXACT = 4 };
@@ -95,6 +100,7 @@ __global__ __launch_bounds__(1024) void fused_plan_kernel(FusedParams p) {
   if (tid < 64) p.header[tid] = 0;
   for (int b = tid; b < p.nblocks; b += 1024) {
     p.xflag[b] = 0;
+    p.fflag[b] = 0;
     blo[b] = p.keys;
     bhi[b] = 0;
   }
@@ -513,6 +519,16 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
 // score) in kGateBins bins of 1/256 of the first sample tile's score range and
 // takes as threshold the lower score edge of the bin where the count of sample keys
 // above reaches a safe margin over the k-th key's expected sample rank. Rows with n <= k are answered here (keys 0..n-1, -1 padding).
+// The gate's sample of a block whose union range spans `span` keys: S keys
+// (about span / 24, a multiple of the stage size, 1024..16384) at an integer
+// stride from the start of the range. Returns the number of stages.
+__device__ __forceinline__ int gate_sample(int span, int& stride) {
+  int S = (span / 24) & ~(kStageKeys - 1);
+  S = S < 1024 ? 1024 : (S > 16384 ? 16384 : S);
+  stride = span / S > 1 ? span / S : 1;
+  return S / kStageKeys;
+}
+
 struct __align__(16) GateSmem {
   uint32_t hist[kWaves][kRowsPerWave * kGateBins];
   int block;
@@ -578,15 +594,22 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
     }
     int lo, hi, any_g;
     block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, wg, p.keys, lo, hi, any_g);
+    // the fine pass's hand-over (rbin -1: none)
+    int rbin[kRowsPerWave], rneed[kRowsPerWave], rnext[kRowsPerWave];
+    float rm0[kRowsPerWave], rinv[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      rbin[i] = -1;
+      rneed[i] = rnext[i] = 0;
+      rm0[i] = 0.f;
+      rinv[i] = 1.f;
+    }
     if (any_g && hi > lo) {
       FoldOp fo;
       build_fold(fo, p.q, p.weights, frows);
-      // S sample keys lo + j * stride, j < S (S a multiple of the stage size)
-      const int span = hi - lo;
-      int S = (span / 24) & ~(kStageKeys - 1);
-      S = S < 1024 ? 1024 : (S > 16384 ? 16384 : S);
-      const int stride = span / S > 1 ? span / S : 1;
-      const int nst = S / kStageKeys;
+      // the sample keys lo + j * stride, j < nst * kStageKeys
+      int stride;
+      const int nst = gate_sample(hi - lo, stride);
       uint32_t* hist = sm.hist[w];
       for (int i = l; i < kRowsPerWave * kGateBins; i += kWave) hist[i] = 0;
       float m0[kRowsPerWave], inv[kRowsPerWave];
@@ -650,6 +673,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         RowState& r = rs[i];
+        rbin[i] = -1;
         if (r.mode != M_GATED) continue;
         // The sample keys above the row's true k-th score are about
         // Poisson(lam), lam = k * nsamp / n. The threshold is put at the
@@ -695,20 +719,48 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
             const float lower = (float)(bstar - kGateOff + 1);  // bstar's lower score edge
             const float next = (float)(b2 - kGateOff);           // upper edge of the next sample
             thr = m0[i] - (b2 < kGateBins ? 0.5f * (lower + next) : lower) / inv[i];
+            // A crowded bin (the first tile's range can be far wider than the
+            // spread of scores around the k-th, e.g. with a large common score
+            // offset) would admit every key of it: the fine pass bins its
+            // samples again.
+            int hb = 0, before = 0, cc = incl - hsum;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+              if (kPer * l + j == bstar) {
+                hb = hv[j];
+                before = cc;
+              }
+              cc += hv[j];
+            }
+            hb = __shfl(hb, bstar / kPer, 64);
+            before = __shfl(before, bstar / kPer, 64);
+            if (bstar >= 1 && hb > kGateCrowded && hb > ks && !(p.flags & 2u)) {
+              rbin[i] = bstar;
+              rneed[i] = ks - before;
+              rnext[i] = b2;
+            }
           }
         }
         if (p.flags & 2u) thr = __builtin_inff();  // forced gate miss
         r.thr = thr;
+        rm0[i] = m0[i];
+        rinv[i] = inv[i];
       }
     }
     if (mine && l == 0) {
+      bool fine = false;
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         const RowState& r = rs[i];
         if (r.r >= p.rows) continue;
         p.rowinfo[r.r] = RowInfo{r.thr, 0, r.mode, 0};
         p.xrow[r.r] = 0;
+        if (r.mode == M_GATED) p.rinfo[r.r] = RefineInfo{rm0[i], rinv[i], rbin[i], rneed[i], rnext[i]};
+        fine = fine || rbin[i] >= 0;
       }
+      // queue the block for the fine pass, once
+      if (fine && atomicExch(&p.fflag[b], 1u) == 0u)
+        p.fqueue[atomicAdd(&p.header[H_FQ], 1u)] = b;
     }
     __syncthreads();
   }
@@ -717,6 +769,147 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
 // ---------------------------------------------------------------------------
 // Scan: every visible key of every live row of a block, candidates to the
 // rows' slabs.
+// The gate's fine pass, for the blocks the gate queued (a row whose threshold
+// bin was crowded). The block's sample is drawn again as the gate drew it
+// (the union range of its gated rows, gate_sample), the queued rows score it
+// again (the same arithmetic as the gate, so the same scores) and bin the
+// samples of their crowded coarse bin in kGateBins fine bins across it; the
+// threshold goes into the first fine bin that completes the row's count, with
+// the gate's gap rule (halfway down to the next sampled score). Returns at
+// once when nothing is queued.
+__global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
+  __shared__ GateSmem sm;
+  MQA_DECLARE_STAGES(stg);
+  const int tid = threadIdx.x;
+  const int w = wave_id();
+  const int l = lane_id();
+  const int nq = (int)p.header[H_FQ];
+  if (nq == 0) return;
+  for (;;) {
+    if (tid == 0) sm.block = (int)atomicAdd(&p.header[H_FCLAIM], 1u);
+    __syncthreads();
+    const int qi = sm.block;
+    if (qi >= nq) break;
+    const int b = p.fqueue[qi];
+    RowState rs[kRowsPerWave];
+    QueryRow qr[kRowsPerWave];
+    wave_rows(p, b, rs);
+    int wlo = p.keys, whi = 0, wfine = 0;
+    int frows[kRowsPerWave], rbin[kRowsPerWave], rneed[kRowsPerWave], rnext[kRowsPerWave];
+    float m0[kRowsPerWave], inv[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      RowState& r = rs[i];
+      zero_query(qr[i]);
+      frows[i] = rbin[i] = -1;
+      rneed[i] = rnext[i] = 0;
+      m0[i] = 0.f;
+      inv[i] = 1.f;
+      if (r.r >= p.rows || p.rowinfo[r.r].mode != M_GATED) continue;
+      wlo = r.s < wlo ? r.s : wlo;  // the gate's union: every gated row
+      whi = r.e > whi ? r.e : whi;
+      const RefineInfo f = p.rinfo[r.r];
+      if (f.bin < 0) continue;
+      rbin[i] = f.bin;
+      rneed[i] = f.need;
+      rnext[i] = f.next;
+      m0[i] = f.m0;
+      inv[i] = f.inv;
+      load_query(qr[i], p.q, p.weights, r.r, 0.5f);
+      frows[i] = r.r;
+      wfine = 1;
+    }
+    int lo, hi, unused;
+    block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, 0, p.keys, lo, hi, unused);
+    if (hi > lo) {
+      int stride;
+      const int nst = gate_sample(hi - lo, stride);
+      FoldOp fo;
+      build_fold(fo, p.q, p.weights, frows);
+      uint32_t* hist = sm.hist[w];
+      for (int j = l; j < kRowsPerWave * kGateBins; j += kWave) hist[j] = 0;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
+        if (!wfine) return;
+        const int key = lo + (c * kChunk + l) * stride;
+        KeyTile kt;
+        load_keys_lds(kt, kc);
+        float E[4];
+        score4(E, qr, fo, kt, scl[l]);
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+          const RowState& r = rs[i];
+          if (rbin[i] < 0 || key < r.s || key >= r.e) continue;
+          // the gate's coarse bin, by the gate's expression
+          const float fb = (m0[i] - E[i]) * inv[i];
+          if (fb < -1e6f || fb > 1e6f) continue;
+          const float fl = __builtin_floorf(fb);
+          if ((int)fl + kGateOff != rbin[i]) continue;
+          int f = (int)((fb - fl) * (float)kGateBins);
+          f = f < 0 ? 0 : (f > kGateBins - 1 ? kGateBins - 1 : f);
+          atomicAdd(&hist[i * kGateBins + f], 1u);
+        }
+      };
+      auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext,
+                       float* snext) {
+        if (st + 1 < nst)
+          dma_stage(p, lo + (st + 1) * kStageKeys * stride, stride, knext, snext, tid);
+#pragma unroll
+        for (int u = 0; u < kStageChunks; ++u)
+          chunk(st * kStageChunks + u, kcur + u * kChunkBytes, scur + u * kChunk);
+        __syncthreads();
+      };
+      dma_stage(p, lo, stride, stg.k[0], stg.s[0], tid);
+      __syncthreads();
+      for (int st = 0; st < nst; st += 2) {
+        stage(st, stg.k[0], stg.s[0], stg.k[1], stg.s[1]);
+        if (st + 1 < nst) stage(st + 1, stg.k[1], stg.s[1], stg.k[0], stg.s[0]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        if (rbin[i] < 0) continue;
+        constexpr int kPer = kGateBins / kWave;
+        int hv[kPer], hsum = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          hv[j] = (int)hist[i * kGateBins + kPer * l + j];
+          hsum += hv[j];
+        }
+        const int incl = wave_incl_scan(hsum);
+        const uint64_t hit = __ballot(incl >= rneed[i]);
+        if (!hit) continue;  // keep the gate's threshold
+        int c = incl - hsum, fstar = kPer * l + kPer - 1;
+        bool found = false;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const bool here = !found && c + hv[j] >= rneed[i];
+          fstar = here ? kPer * l + j : fstar;
+          found = found || here;
+          c += hv[j];
+        }
+        fstar = __shfl(fstar, __builtin_ctzll(hit), 64);
+        int f2 = kGateBins;
+#pragma unroll
+        for (int j = kPer - 1; j >= 0; --j)
+          f2 = (kPer * l + j > fstar && hv[j] > 0) ? kPer * l + j : f2;
+        f2 = -wave_max_i(-f2);
+        const float base = (float)(rbin[i] - kGateOff);
+        const float lower = base + (float)(fstar + 1) / (float)kGateBins;
+        float pos = lower;
+        if (f2 < kGateBins)
+          pos = 0.5f * (lower + base + (float)f2 / (float)kGateBins);
+        else if (rnext[i] < kGateBins)
+          pos = 0.5f * (lower + (float)(rnext[i] - kGateOff));
+        if (l == 0) p.rowinfo[rs[i].r].thr = m0[i] - pos / inv[i];
+      }
+    }
+    __syncthreads();
+  }
+}
+
 struct __align__(16) ScanSmem {
   uint32_t hist[kWaves][kHistWords];
   int block;
@@ -1281,6 +1474,8 @@ extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   hipLaunchKernelGGL(mqa::fused_gate_kernel, dim3(p->scan_grid), dim3(mqa::kThreads), 0, stream,
                      *p);
+  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  hipLaunchKernelGGL(mqa::fused_refine_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (scan_begin && (e = hipEventRecord(scan_begin, stream)) != hipSuccess) return (int)e;
   if (p->nseg > 1)

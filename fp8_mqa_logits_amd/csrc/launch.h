@@ -24,6 +24,15 @@ struct SegInfo {
   int cnt;
 };
 
+// Per-row hand-over from the gate to its fine pass (fused_refine_kernel):
+// the coarse histogram's reference and scale, the crowded threshold bin (-1:
+// the row needs no fine pass), the sample count still needed inside it and
+// the next sampled coarse bin below it.
+struct RefineInfo {
+  float m0, inv;
+  int bin, need, next;
+};
+
 struct FusedParams {
   const uint8_t* q;
   const uint8_t* k;
@@ -43,6 +52,9 @@ struct FusedParams {
   int32_t* order;    // [nblocks] heaviest-first block order
   uint8_t* xrow;     // [rows] 1 = the row needs the exact rescan
   int32_t* xqueue;   // [nblocks] blocks queued for the exact rescan
+  int32_t* fqueue;   // [nblocks] blocks queued for the gate's fine pass
+  uint32_t* fflag;   // [nblocks] 1 = the block is queued for the fine pass
+  RefineInfo* rinfo; // [rows]
   int32_t* rqueue;   // [2][nblocks * 32] rows queued for the two bounded-rescan rounds
   uint32_t* xflag;   // [nblocks] 1 = the block is queued
   RowInfo* rowinfo;  // [rows]
