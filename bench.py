@@ -7,7 +7,7 @@ Prints ONE JSON line (rank 0):
   value    = visible (row, key) scores per second (sum of the rows' visible
              keys / seconds per step);
   roofline = FP8 MFMA roofline of the scan kernel (the dominant one of the
-             call's nine launches): 8192 flop per visible pair (2 * 32 heads *
+             call's ten launches): 8192 flop per visible pair (2 * 32 heads *
              128 dims) over its average duration, timed with HIP events that
              the library records on the call's stream around that kernel
              (MQA_FLAG_TIME_SCAN) during the timed steps, against the MI355X

@@ -3,11 +3,14 @@
 // Follows vLLM PR #60618, "What this PR does" (scoring, sampled gate,
 // candidate emission, per-row selection, exact rescan, heaviest-first block
 // claims) and the API page "fused_mqa_topk" (contract and output convention),
-// laid out for gfx950 as nine launches on the caller's stream:
+// laid out for gfx950 as ten launches on the caller's stream (eleven in the
+// deterministic mode):
 //   * plan: heaviest-first order of the 32-row blocks, counters cleared;
 //   * gate (persistent): per block, a strided sample of the keys gives each
 //     row an admission threshold with a safe margin over its k-th key's
 //     expected sample rank; rows with n <= k get their output here;
+//   * refine (persistent, usually empty): rows whose threshold bin was
+//     crowded have their sample binned again, finer;
 //   * scan (persistent, 8 waves of 4 rows per workgroup): keys stream through
 //     LDS in 128-key stages filled by direct global->LDS loads; each wave
 //     scores its 4 rows with FP8 MFMAs (the rows' q and weights stay in
@@ -26,7 +29,8 @@
 //     selected from the keys above the bound;
 //   * exact (persistent): rows with fewer than k candidates, or whose
 //     bounded rescan overfilled the slab twice, are rescanned with exact
-//     scores and a streaming top-k merge.
+//     scores and a streaming top-k merge;
+//   * sort (deterministic mode only): each row's keys in ascending order.
 // Each phase is its own kernel so that each gets the registers it needs (the
 // scan loop in particular holds no state of the other phases).
 #include "common.h"
