@@ -1166,7 +1166,7 @@ __device__ __forceinline__ void queue_rescan(const FusedParams& p, int r, float 
 }
 
 // Select: one wave per row.
-__global__ __launch_bounds__(kSelWaves * kWave) void fused_select_kernel(FusedParams p) {
+__global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_eu(4))) void fused_select_kernel(FusedParams p) {
   __shared__ uint32_t hist[kSelWaves][kHistWords];
   const int w = wave_id();
   const int l = lane_id();
