@@ -1110,24 +1110,39 @@ __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int 
   low = -__builtin_inff();
   if (na >= k || nb < need) return false;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  // exact scores of the band, 64 records at a time
+  // exact scores of the band, 64 records at a time; the next group's key
+  // indices, scales and approximate scores are loaded one group ahead
   float err = 0.f;
-  for (int b0 = 0; b0 < nb; b0 += kWave) {
-    int keyidx[4];
+  int keyidx[4];
+  float sc = 0.f, eo = 0.f;
+  auto group_refs = [&](int b0, int* ki, float& s_, float& e_) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int j = b0 + 16 * t + (l & 15);
-      keyidx[t] = sI[j < nb ? j : nb - 1];
+      ki[t] = sI[j < nb ? j : nb - 1];
     }
-    KeyTile kt;
-    load_keys_gather(kt, p.k, keyidx);
     const int j = b0 + l;
     const int jj = j < nb ? j : nb - 1;
-    const float E = score_chunk_exact(qr, kt) * p.scales[sI[jj]];
+    s_ = p.scales[sI[jj]];
+    e_ = sE[jj];
+  };
+  if (nb > 0) group_refs(0, keyidx, sc, eo);
+  for (int b0 = 0; b0 < nb; b0 += kWave) {
+    KeyTile kt;
+    load_keys_gather(kt, p.k, keyidx);
+    int kn[4] = {0, 0, 0, 0};
+    float scn = 0.f, eon = 0.f;
+    if (b0 + kWave < nb) group_refs(b0 + kWave, kn, scn, eon);
+    const int j = b0 + l;
+    const float E = score_chunk_exact(qr, kt) * sc;
     if (j < nb) {
-      err = __builtin_fmaxf(err, __builtin_fabsf(E - sE[j]));
+      err = __builtin_fmaxf(err, __builtin_fabsf(E - eo));
       sE[j] = E;
     }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) keyidx[t] = kn[t];
+    sc = scn;
+    eo = eon;
   }
   err = wave_max(err);
   if (l == 0 && band_count)
