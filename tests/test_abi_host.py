@@ -30,6 +30,16 @@ def test_header_declares_the_abi():
                           "mqa_strerror"}
 
 
+def test_binding_flags_match_the_header():
+    text = open(HEADER).read()
+    defs = {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"#define MQA_FLAG_(\w+) (\d+)u", text)}
+    assert defs, "no MQA_FLAG_ defines found"
+    for name, value in defs.items():
+        assert getattr(mqa, "FLAG_" + name) == value, name
+    assert len(set(defs.values())) == len(defs)
+
+
 def test_library_exports_every_declared_symbol():
     lib = mqa.load()
     for n in declared_functions():
