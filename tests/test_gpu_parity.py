@@ -332,3 +332,45 @@ def test_fused_key_split_long_rows(cfg, nrows):
     fails = check.check_topk(o[rows], rows, p, wl.topk, TOL)
     assert not fails, fails[:5]
     assert st["rows_exact"] == 0
+
+
+# Mixed shapes through the whole fused path: row counts that are not a
+# multiple of the 32-row block (1 to 8 key segments), key ranges of mixed
+# lengths (short, empty, long, offset starts), every topk, a common query
+# offset on some cases (the gate's fine pass), and the deterministic mode.
+# (rows, keys, topk, q_offset, flags) per case; every row against the oracle.
+MIXED = [
+    (37, 5000, 512, 0.0, 0),
+    (100, 20000, 1024, 2.0, 0),
+    (333, 70000, 2048, 0.0, 0),
+    (333, 70000, 2048, 3.0, 0),
+    (1000, 20000, 512, 0.0, 64),
+    (257, 40000, 1024, 3.0, 64),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MIXED)))
+def test_fused_mixed_shapes(case):
+    rows, keys, topk, q_off, flags = MIXED[case]
+    rng = np.random.default_rng(100 + case)
+    n = rng.integers(0, keys + 1, size=rows)
+    short = rng.random(rows) < 0.1
+    n[short] = rng.integers(0, topk + 2, size=int(short.sum()))
+    st = rng.integers(0, keys + 1, size=rows)
+    st = np.minimum(st, keys - n)
+    en = st + n
+    wl = W.custom(rows, keys, topk, st.astype(np.int32), en.astype(np.int32), seed=200 + case,
+                  q_offset=q_off, name=f"mixed{case}_{rows}x{keys}_k{topk}")
+    say(f"case: fused {wl.name} q_offset={q_off} flags={flags}; all rows checked")
+    d = to_device(wl)
+    ws = mqa.alloc_workspace(rows)
+    out = fused(d, topk, flags=flags | mqa.FLAG_STATS, workspace=ws)
+    say("stats", mqa.read_stats(ws))
+    o = out.cpu().numpy()
+    assert not check.check_valid(o, wl.starts, wl.ends, wl.keys, topk)
+    p = oracle_problem(wl)
+    fails = check.check_topk(o, np.arange(rows), p, topk, TOL)
+    assert not fails, fails[:5]
+    if flags & mqa.FLAG_DETERMINISTIC:
+        fails = check.check_lowkey(o, np.arange(rows), p, topk)
+        assert not fails, fails[:5]
