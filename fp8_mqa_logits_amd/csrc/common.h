@@ -45,6 +45,7 @@ constexpr int kCap = 16384;                // candidate slab capacity per row
 constexpr int kMaxTopk = 2048;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -124,17 +125,21 @@ struct KeyTile {
   v8i kb[4];
 };
 
+// Each 16-byte slice is read as one vector from a single byte offset off the
+// chunk base. The shallow address chain matters: the compiler tags an LDS
+// access with its variable's alias scope only when it can trace the address
+// back to the variable in a few steps, and an untagged read waits for every
+// direct global->LDS copy in flight, the next stage's included.
 __device__ __forceinline__ void load_keys_lds(KeyTile& kt, const uint8_t* lds_chunk) {
   const int l = lane_id();
   const int g = l >> 4;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int j = 16 * t + (l & 15);
-    const uint8_t* row = lds_chunk + j * kDim;
-    const uint4 x0 = *reinterpret_cast<const uint4*>(row + 16 * ((2 * g) ^ swz(j)));
-    const uint4 x1 = *reinterpret_cast<const uint4*>(row + 16 * ((2 * g + 1) ^ swz(j)));
-    kt.kb[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                   (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    const v4i x0 = *reinterpret_cast<const v4i*>(lds_chunk + (j * kDim + 16 * ((2 * g) ^ swz(j))));
+    const v4i x1 =
+        *reinterpret_cast<const v4i*>(lds_chunk + (j * kDim + 16 * ((2 * g + 1) ^ swz(j))));
+    kt.kb[t] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 }
 
