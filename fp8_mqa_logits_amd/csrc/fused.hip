@@ -517,18 +517,18 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
 }
 
 // ---------------------------------------------------------------------------
-// Gate. A strided sample of the block's keys (1024..16384 keys, about span /
+// Gate. A strided sample of the block's keys (512..16384 keys, about span /
 // 24, at a fixed integer stride from the start of the block's range) is
 // scored like the scan scores; each gated row bins (first-tile maximum -
 // score) in kGateBins bins of 1/256 of the first sample tile's score range and
 // takes as threshold the lower score edge of the bin where the count of sample keys
 // above reaches a safe margin over the k-th key's expected sample rank. Rows with n <= k are answered here (keys 0..n-1, -1 padding).
 // The gate's sample of a block whose union range spans `span` keys: S keys
-// (about span / 24, a multiple of the stage size, 1024..16384) at an integer
+// (about span / 24, a multiple of the stage size, 512..16384) at an integer
 // stride from the start of the range. Returns the number of stages.
 __device__ __forceinline__ int gate_sample(int span, int& stride) {
   int S = (span / 24) & ~(kStageKeys - 1);
-  S = S < 1024 ? 1024 : (S > 16384 ? 16384 : S);
+  S = S < 512 ? 512 : (S > 16384 ? 16384 : S);
   stride = span / S > 1 ? span / S : 1;
   return S / kStageKeys;
 }
