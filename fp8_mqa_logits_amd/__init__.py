@@ -31,7 +31,8 @@ ERR_NAMES = {0: "MQA_OK", 1: "MQA_ERR_NULL", 2: "MQA_ERR_ALIGN", 3: "MQA_ERR_SHA
              4: "MQA_ERR_WORKSPACE", 5: "MQA_ERR_DEVICE", 6: "MQA_ERR_LAUNCH"}
 
 EXPORTS = ("workspace_size", "mqa_topk_prefill", "mqa_logits_dense", "mqa_topk_dense",
-           "mqa_key_scales", "mqa_scan_time", "mqa_mfma_peak", "mqa_strerror")
+           "mqa_key_scales", "mqa_scan_time", "mqa_mfma_peak", "mqa_fp8_mfma_probe",
+           "mqa_strerror")
 
 
 class MQAError(RuntimeError):
@@ -71,6 +72,8 @@ def load() -> ctypes.CDLL:
         lib.mqa_scan_time.restype = I
         lib.mqa_mfma_peak.argtypes = [P, I64, I, I, P]
         lib.mqa_mfma_peak.restype = I
+        lib.mqa_fp8_mfma_probe.argtypes = [P, P, P, P, I, P]
+        lib.mqa_fp8_mfma_probe.restype = I
         lib.mqa_strerror.argtypes = [I]
         lib.mqa_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -106,6 +109,19 @@ def _need(t: torch.Tensor, name: str, dtypes, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _tensors(**named):
+    for name, t in named.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a tensor")
+
+
+def _shape(t: torch.Tensor, shape: tuple, name: str):
+    # the C ABI takes sizes, not tensors: a short tensor would be read or
+    # written out of bounds on the device, so every shape is checked here
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 FP8 = (torch.float8_e4m3fn, torch.uint8)
 
 
@@ -129,6 +145,19 @@ def mqa_topk_prefill(q, k, scales, weights, starts, ends, topk: int, out=None, w
     """Fused scores + per-row top-k. q [rows,32,128] e4m3 (or its uint8 bytes),
     k [keys,128] e4m3, scales [keys] fp32, weights [rows,32] fp32, starts/ends
     [rows] int32; returns out [rows, topk] int32 (key - start, -1 padded)."""
+    _tensors(q=q, k=k, scales=scales, weights=weights, starts=starts, ends=ends)
+    if q.dim() != 3 or k.dim() != 2:
+        raise ValueError("q must be [rows,32,128] and k [keys,128]")
+    rows, keys = q.shape[0], k.shape[0]
+    _shape(q, (rows, HEADS, HEAD_DIM), "q")
+    _shape(k, (keys, HEAD_DIM), "k")
+    _shape(scales, (keys,), "scales")
+    _shape(weights, (rows, HEADS), "weights")
+    _shape(starts, (rows,), "starts")
+    _shape(ends, (rows,), "ends")
+    if out is not None:
+        _tensors(out=out)
+        _shape(out, (rows, topk), "out")
     dev = q.device
     _need(q, "q", FP8, dev)
     _need(k, "k", FP8, dev)
@@ -136,12 +165,10 @@ def mqa_topk_prefill(q, k, scales, weights, starts, ends, topk: int, out=None, w
     _need(weights, "weights", (torch.float32,), dev)
     _need(starts, "starts", (torch.int32,), dev)
     _need(ends, "ends", (torch.int32,), dev)
-    rows, keys = q.shape[0], k.shape[0]
-    if q.shape[1:] != (HEADS, HEAD_DIM) or k.shape[1:] != (HEAD_DIM,):
-        raise ValueError("q must be [rows,32,128] and k [keys,128]")
     if out is None:
         out = torch.empty((rows, topk), dtype=torch.int32, device=dev)
     _need(out, "out", (torch.int32,), dev)
+    _shape(out, (rows, topk), "out")
     if workspace is None:
         workspace = alloc_workspace(rows, dev.index)
     _need(workspace, "workspace", (torch.uint8,), dev)
@@ -157,20 +184,32 @@ def mqa_topk_prefill(q, k, scales, weights, starts, ends, topk: int, out=None, w
 def mqa_logits_dense(q, k, scales, weights, starts, ends, col0: int = 0, ncols: int | None = None,
                      logits=None, stream=None) -> torch.Tensor:
     """fp32 logits [rows, ncols] for keys col0 .. col0+ncols-1 (-inf where not visible)."""
+    _tensors(q=q, k=k, scales=scales, weights=weights, starts=starts, ends=ends)
+    if q.dim() != 3 or k.dim() != 2:
+        raise ValueError("q must be [rows,32,128] and k [keys,128]")
+    rows, keys = q.shape[0], k.shape[0]
+    _shape(q, (rows, HEADS, HEAD_DIM), "q")
+    _shape(k, (keys, HEAD_DIM), "k")
+    _shape(scales, (keys,), "scales")
+    _shape(weights, (rows, HEADS), "weights")
+    _shape(starts, (rows,), "starts")
+    _shape(ends, (rows,), "ends")
     dev = q.device
     for t, n, d in ((q, "q", FP8), (k, "k", FP8), (scales, "scales", (torch.float32,)),
                     (weights, "weights", (torch.float32,)), (starts, "starts", (torch.int32,)),
                     (ends, "ends", (torch.int32,))):
         _need(t, n, d, dev)
-    rows, keys = q.shape[0], k.shape[0]
     if ncols is None:
         ncols = keys - col0
     if logits is None:
         ld = (ncols + 3) // 4 * 4
         logits = torch.empty((rows, ld), dtype=torch.float32, device=dev)[:, :ncols]
+    if not isinstance(logits, torch.Tensor) or logits.device != dev:
+        raise ValueError(f"logits must be a tensor on {dev}")
     ld = logits.stride(0)
     if logits.dtype != torch.float32 or logits.stride(1) != 1:
         raise ValueError("logits must be fp32 with unit column stride")
+    _shape(logits, (rows, ncols), "logits")
     with torch.cuda.device(dev):
         rc = load().mqa_logits_dense(_ptr(q), _ptr(k), _ptr(scales), _ptr(weights), _ptr(starts),
                                      _ptr(ends), _ptr(logits), ld, rows, keys, int(col0),
@@ -182,12 +221,18 @@ def mqa_logits_dense(q, k, scales, weights, starts, ends, col0: int = 0, ncols: 
 def mqa_topk_dense(logits, starts, ends, topk: int, keys: int, col0: int = 0, out=None,
                    stream=None) -> torch.Tensor:
     """Per-row top-k of a logits window [rows, ncols] (columns = keys col0 ..)."""
+    _tensors(logits=logits, starts=starts, ends=ends)
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be 2-D fp32 with unit column stride")
+    rows, ncols = logits.shape
+    _shape(starts, (rows,), "starts")
+    _shape(ends, (rows,), "ends")
+    if out is not None:
+        _tensors(out=out)
+        _shape(out, (rows, topk), "out")
     dev = logits.device
     _need(starts, "starts", (torch.int32,), dev)
     _need(ends, "ends", (torch.int32,), dev)
-    if logits.dtype != torch.float32 or logits.stride(1) != 1:
-        raise ValueError("logits must be fp32 with unit column stride")
-    rows, ncols = logits.shape
     if out is None:
         out = torch.empty((rows, topk), dtype=torch.int32, device=dev)
     _need(out, "out", (torch.int32,), dev)
@@ -201,11 +246,19 @@ def mqa_topk_dense(logits, starts, ends, topk: int, keys: int, col0: int = 0, ou
 
 def mqa_key_scales(scale_bytes, out=None, stream=None) -> torch.Tensor:
     """UE8M0 [keys,4] uint8 -> fp32 [keys] (bit pattern e << 23), on the GPU."""
+    _tensors(scale_bytes=scale_bytes)
+    if scale_bytes.dim() != 2:
+        raise ValueError("scale_bytes must be [keys,4] uint8")
+    keys = scale_bytes.shape[0]
+    _shape(scale_bytes, (keys, 4), "scale_bytes")
+    if out is not None:
+        _tensors(out=out)
+        _shape(out, (keys,), "out")
     dev = scale_bytes.device
     _need(scale_bytes, "scale_bytes", (torch.uint8,), dev)
-    keys = scale_bytes.shape[0]
     if out is None:
         out = torch.empty(keys, dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), dev)
     with torch.cuda.device(dev):
         rc = load().mqa_key_scales(_ptr(scale_bytes), _ptr(out), keys, _stream(dev, stream))
     _check(rc, "mqa_key_scales")
@@ -248,11 +301,43 @@ def mfma_peak_tflops(workgroups: int = 2048, iters: int = 4096, repeats: int = 3
     return best
 
 
+def fp8_mfma_probe(a: torch.Tensor, b: torch.Tensor, ascale: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """The FP8 MFMA's dot products of a [n,16,128] and b [n,16,128] e4m3 codes
+    (uint8), out [n,16,16] fp32, with the A-scaled form when ascale [n,16,4]
+    (E8M0 bytes per row and K block) is given."""
+    _tensors(a=a, b=b)
+    if a.dim() != 3:
+        raise ValueError("a must be [n,16,128]")
+    n = a.shape[0]
+    _shape(a, (n, 16, HEAD_DIM), "a")
+    _shape(b, (n, 16, HEAD_DIM), "b")
+    if ascale is not None:
+        _tensors(ascale=ascale)
+        _shape(ascale, (n, 16, 4), "ascale")
+    dev = a.device
+    _need(a, "a", FP8, dev)
+    _need(b, "b", FP8, dev)
+    if ascale is not None:
+        _need(ascale, "ascale", (torch.uint8,), dev)
+    out = torch.empty((n, 16, 16), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        rc = load().mqa_fp8_mfma_probe(_ptr(a), _ptr(b), _ptr(ascale), _ptr(out), n,
+                                       _stream(dev, stream))
+    _check(rc, "mqa_fp8_mfma_probe")
+    return out
+
+
 def read_stats(workspace: torch.Tensor) -> dict:
     """The mqa_stats header of a workspace used with FLAG_STATS (synchronizes)."""
-    h = workspace[:64].cpu().numpy().view("<u4")
+    h = workspace[:256].cpu().numpy().view("<u4")
     return {"rows_short": int(h[1]), "rows_gated": int(h[2]), "rows_exact": int(h[3]),
             "rows_rescanned": int(h[4]), "rows_undercount": int(h[5]),
             "compactions": int(h[6]), "rows_uncertified": int(h[7]),
             "candidates": int(h[8]) | (int(h[9]) << 32),
-            "band_keys": int(h[10]) | (int(h[11]) << 32)}
+            "band_keys": int(h[10]) | (int(h[11]) << 32),
+            "bound_ratio_max": float(h[12:13].view("<f4")[0]),
+            # rows the select could not certify, by reason (counts, window
+            # too far off, taken / dropped record reaching the k-th score,
+            # admission bound reaching it)
+            "fail_reasons": [int(h[26]), int(h[27]), int(h[28]), int(h[29])]}

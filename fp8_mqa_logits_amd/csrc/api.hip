@@ -61,8 +61,8 @@ const DeviceInfo* device_info(int device) {
 }
 
 struct Layout {
-  size_t header, order, xrow, xqueue, xflag, fqueue, fflag, rinfo, rqueue, rowinfo, seg, slabE,
-      slabI, tmpE, tmpI, total;
+  size_t header, order, xrow, xqueue, xflag, fqueue, fflag, rinfo, rqueue, rowinfo, seg, keyinfo,
+      beta, slabE, slabI, tmpE, tmpI, total;
   int grid, nblocks;
 };
 
@@ -97,11 +97,15 @@ Layout layout(int rows, const DeviceInfo& d) {
   L.rinfo = off;
   off = align_up(off + rows_pad * sizeof(mqa::RefineInfo));
   L.rqueue = off;
-  off = align_up(off + 2 * rows_pad * 4);
+  off = align_up(off + 3 * rows_pad * 4);
   L.rowinfo = off;
   off = align_up(off + rows_pad * sizeof(mqa::RowInfo));
   L.seg = off;
   off = align_up(off + rows_pad * mqa::kMaxSeg * sizeof(mqa::SegInfo));
+  L.keyinfo = off;  // per key, for the largest key count a call may have
+  off = align_up(off + (size_t)MQA_MAX_KEYS * 8);
+  L.beta = off;
+  off = align_up(off + rows_pad * 4);
   const size_t slab = rows_pad * mqa::kSlabRow * 4;
   L.slabE = off;
   off = align_up(off + slab);
@@ -239,6 +243,8 @@ int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
     p.rqueue = reinterpret_cast<int32_t*>(ws + L.rqueue);
     p.rowinfo = reinterpret_cast<mqa::RowInfo*>(ws + L.rowinfo);
     p.seg = reinterpret_cast<mqa::SegInfo*>(ws + L.seg);
+    p.keyinfo = reinterpret_cast<float*>(ws + L.keyinfo);
+    p.beta = reinterpret_cast<float*>(ws + L.beta);
     p.slabE = reinterpret_cast<float*>(ws + L.slabE);
     p.slabI = reinterpret_cast<int32_t*>(ws + L.slabI);
     p.tmpE = reinterpret_cast<float*>(ws + L.tmpE);
@@ -309,6 +315,21 @@ int mqa_mfma_peak(float* out, int64_t out_len, int workgroups, int iters, void* 
     return MQA_ERR_SHAPE;
   if (!current_device()) return MQA_ERR_DEVICE;
   const int rc = mqa_mfma_peak_launch(out, workgroups, iters, static_cast<hipStream_t>(stream));
+  if (rc != 0) return launch_error(rc);
+  return MQA_OK;
+}
+
+extern "C" int mqa_fp8_mfma_probe_launch(const uint8_t* a, const uint8_t* b, const uint8_t* sa,
+                                         float* out, int ncases, hipStream_t stream);
+
+int mqa_fp8_mfma_probe(const uint8_t* a, const uint8_t* b, const uint8_t* ascale, float* out,
+                       int ncases, void* stream) {
+  if (!a || !b || !out) return MQA_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 4)) return MQA_ERR_ALIGN;
+  if (ncases < 1 || ncases > (1 << 20)) return MQA_ERR_SHAPE;
+  if (!current_device()) return MQA_ERR_DEVICE;
+  const int rc = mqa_fp8_mfma_probe_launch(a, b, ascale, out, ncases,
+                                           static_cast<hipStream_t>(stream));
   if (rc != 0) return launch_error(rc);
   return MQA_OK;
 }

@@ -5,7 +5,9 @@
 // claims) and the API page "fused_mqa_topk" (contract and output convention),
 // laid out for gfx950 as ten launches on the caller's stream (eleven in the
 // deterministic mode):
-//   * plan: heaviest-first order of the 32-row blocks, counters cleared;
+//   * prologue: heaviest-first order of the 32-row blocks, counters cleared
+//     (one workgroup), and the FP8 score error bounds of every key and row
+//     (the other workgroups);
 //   * gate (persistent): per block, a strided sample of the keys gives each
 //     row an admission threshold with a safe margin over its k-th key's
 //     expected sample rank; rows with n <= k get their output here;
@@ -18,18 +20,20 @@
 //     candidate slab (a ballot, an mbcnt and two buffer stores per row and
 //     chunk, no atomics: a row belongs to one wave); a full slab is merged in
 //     place (the best records and their ties stay, the threshold rises);
-//   * select (one wave per row): the row's k-th approximate score is found in
-//     its slab, a band of keys around it is rescored exactly (bf16 MFMA) and
-//     the row is accepted only when the band's measured error, times a safety
-//     factor, cannot move any key across the cut (FP8 MFMA scores are
-//     approximate on gfx950, see common.h);
-//   * bounded rescan and finish, two rounds: a row whose band could not be
+//   * select (one wave per row): every candidate's exact score lies within a
+//     proven bound of its FP8 score (FP8 MFMA scores are approximate on
+//     gfx950, see common.h); the keys whose interval can reach the row's k-th
+//     score are rescored exactly (bf16 MFMA), the keys wholly above it are
+//     taken, and the row is accepted only when no other key's interval, and
+//     no key left out by the admission bound, can reach the k-th exact score;
+//   * bounded rescan and finish, up to three rounds: a row that could not be
 //     certified has every visible key scored exactly, in key slices spread
 //     over all waves, against a lower bound of its k-th score, and its top k
-//     selected from the keys above the bound;
+//     selected from the keys above the bound (an overfull round raises the
+//     bound for the next);
 //   * exact (persistent): rows with fewer than k candidates, or whose
-//     bounded rescan overfilled the slab twice, are rescanned with exact
-//     scores and a streaming top-k merge;
+//     bounded rescan overfilled the slab in every round, are rescanned with
+//     exact scores and a streaming top-k merge;
 //   * sort (deterministic mode only): each row's keys in ascending order.
 // Each phase is its own kernel so that each gets the registers it needs (the
 // scan loop in particular holds no state of the other phases).
@@ -49,26 +53,34 @@ constexpr int kGateOff = 64;  // bins above the first-tile maximum
 // the threshold is placed at is binned again, finer (fused_refine_kernel).
 constexpr int kGateCrowded = 48;
 constexpr int kHistWords = 2048;
-constexpr int kBand = 32;           // keys on each side of rank k that are rescored exactly
-constexpr float kBandSafety = 8.f;  // certificate margin, in units of the band's largest error
 constexpr int kSelWaves = 4;        // rows (waves) per select workgroup
+// The select's window around the estimated k-th FP8 score, in histogram bins
+// beyond the one bin of binning slack on each side.
+constexpr int kWinBins = 1;
 
 // Header words (the first 12 mirror struct mqa_stats in mqa_topk.h).
 enum : int {
   H_CLAIM = 0, H_SHORT = 1, H_GATED = 2, H_EXACT = 3, H_RESCAN = 4, H_UNDER = 5,
   H_COMPACT = 6, H_UNCERT = 7, H_CAND_LO = 8, H_CAND_HI = 9, H_BAND_LO = 10, H_BAND_HI = 11,
+  H_ERRMAX = 12,  // largest |exact - FP8| / bound seen in a band (fp32 bits, >= 0)
   H_XQ = 16,      // blocks queued for the exact rescan
   H_XCLAIM = 17,  // exact-rescan claim counter
   H_GCLAIM = 18,  // gate claim counter
-  H_RQ = 19,      // rows queued for the bounded rescan (then 21 for its second round)
-  H_RCLAIM = 20,  // work-item claim counter of the bounded rescan (then 22)
-  H_FQ = 24,      // blocks queued for the gate's fine pass
-  H_FCLAIM = 25   // claim counter of the fine pass
+  H_RQ = 19,      // rows queued for the bounded rescan (then 21, 23 for rounds 1, 2)
+  H_RCLAIM = 20,  // work-item claim counter of the bounded rescan (then 22, 24)
+  H_FQ = 30,      // blocks queued for the gate's fine pass
+  H_FCLAIM = 31,  // claim counter of the fine pass
+  // rows the select could not certify, by the first reason (statistics): too
+  // many keys above the window or too few around it, a taken record's
+  // interval reaching tau, a dropped record's reaching tau, the admission
+  // bound reaching tau
+  H_FAIL_COUNT = 26, H_FAIL_ABOVE = 27, H_FAIL_BELOW = 28, H_FAIL_ADMIT = 29
 };
 
 enum RowMode : int { M_OFF = 0, M_SHORT = 1, M_ALL = 2, M_GATED = 3, M_EXACT = 4 };
 
 constexpr int kRescanKeys = 2048;  // keys per bounded-rescan work item
+constexpr int kRescanRounds = 3;    // bounded-rescan rounds before the exact rescan
 
 // Candidate capacity of a slab row (SMALL_CAP: just above k, to exercise the
 // merges in tests).
@@ -89,16 +101,137 @@ __device__ __forceinline__ void row_range(const FusedParams& p, int r, int& s, i
   e = b;
 }
 
-// Heaviest-first block order and the reset of the header and of the
-// per-block exact flags. One workgroup. A block's cost is the union range its
-// non-short rows scan (one thread per row, LDS min/max per block); blocks are
-// counting-sorted by cost in 1024 buckets of 1024 keys, descending.
-constexpr int kMaxBlocks = kMaxBatchRows / kBlockRows;
+// ---------------------------------------------------------------------------
+// FP8 score error bounds.
+//
+// The FP8 MFMA (16x16x128; measured on gfx950) splits a 128-term dot product
+// into 16 groups of 8 consecutive dimensions. In each group it truncates every
+// product toward zero to a multiple of 2^(E - 13), E being the largest
+// exponent sum e(a) + e(b) over the group's nonzero products (e: the unbiased
+// exponent of an e4m3 code, -6 for subnormals), and it adds the 16 group sums
+// one after another in fp32, each addition within one ulp. The product that
+// sets E is exact, so a group loses less than
+// 7 * 2^(E - 13) <= 7 * 2^-13 * max_d x(a_d) * max_d x(b_d), with x(v) =
+// 2^e(v) for v != 0 and x(0) = 0, and the additions lose at most 2^-19 of the
+// dot's sum of |products|. Summed over heads (with |w|), groups, and the relu
+// fold's terms, the FP8 score of key j in row r is within beta_r * nhat_j of
+// its exact score, where
+//   nhat_j  = scale_j * sum_g max_{d in g} x(k_jd), rounded up to 12 bits;
+//   beta_r  = 2^-13 * (4.5 alpha + 3.5 phi + 2 fmax) * (1 + 2^-10);
+//   alpha   = max_g sum_h |w_rh| * max_{d in g} x(q_rhd);
+//   fmax    = max_d |f_rd|, f_r = sum_h w_rh q_rh (the fold vector);
+//   phi     = the power of two at or below 1.0625 * fmax.
+// The head MFMAs' truncation contributes 3.5 alpha (the relu fold halves
+// every term) and their fp32 additions 0.25 alpha; the fold-term MFMAs
+// 3.5 phi plus 0.4 fmax; the fold's four-term residual and the fp32 rounding
+// of f 1.0 fmax + 0.25 alpha; the fp32 epilogue and the record arithmetic
+// 0.15 alpha + 0.1 fmax (|q_d| < 2 x(q_d), sum_d |k_d| < 16 sum_g max x).
 
-__global__ __launch_bounds__(1024) void fused_plan_kernel(FusedParams p) {
+// x(v) of the largest e4m3 magnitude among the 8 codes of (lo, hi): x is
+// nondecreasing in the code's magnitude bits, so it is x of their maximum.
+__device__ __forceinline__ float xhat8(uint32_t lo, uint32_t hi) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t c0 = (lo >> (8 * b)) & 0x7Fu, c1 = (hi >> (8 * b)) & 0x7Fu;
+    m = c0 > m ? c0 : m;
+    m = c1 > m ? c1 : m;
+  }
+  if (m == 0) return 0.f;
+  const uint32_t f = m >> 3;  // exponent field; 0 for subnormals (exponent -6 as field 1)
+  return __uint_as_float(((f > 1u ? f : 1u) + 120u) << 23);
+}
+
+__device__ __forceinline__ float row_beta(float alpha, float fmax) {
+  const float fm = fmax * 1.0625f * (1.f + 0x1p-12f);
+  const uint32_t ex = __float_as_uint(fm) & 0x7F800000u;
+  const float phi = ex ? __uint_as_float(ex) : fm;  // fm itself when subnormal
+  return 0x1p-13f * (4.5f * alpha + 3.5f * phi + 2.f * fmax) * (1.f + 0x1p-10f);
+}
+
+// nhat of a key from its unscaled group-maximum sum x (exact: a sum of 16
+// powers of two) and its scale: rounded up, and kept to its top 12 bits.
+__device__ __forceinline__ float key_nhat(float x, float scale) {
+  float v = x * scale;  // a power-of-two scale: exact unless tiny
+  if (v == 0.f) return 0.f;
+  v = v < 0x1p-100f ? 0x1p-100f : v;
+  return __uint_as_float((__float_as_uint(v) + 0xFFFFFu) & ~kKeyMask);
+}
+
+// Workgroup 0: heaviest-first block order and the reset of the header and of
+// the per-block flags. A block's cost is the union range its non-short rows
+// scan (one thread per row, LDS min/max per block); blocks are counting-sorted
+// by cost in 1024 buckets of 1024 keys, descending.
+// Workgroups 1..: nhat of every key (4 keys per wave) and beta of every row (a
+// wave per row).
+constexpr int kMaxBlocks = kMaxBatchRows / kBlockRows;
+constexpr int kPrologueThreads = 1024;
+
+__device__ __forceinline__ void prologue_bounds(const FusedParams& p) {
+  const int l = lane_id();
+  const int nwaves = (gridDim.x - 1) * (kPrologueThreads / kWave);
+  const int kunits = (p.keys + 3) / 4;
+  const int units = kunits + p.rows;
+  for (int u = (blockIdx.x - 1) * (kPrologueThreads / kWave) + wave_id(); u < units;
+       u += nwaves) {
+    const int g = l & 15;  // dimension group: dims 8g .. 8g + 7
+    if (u < kunits) {
+      const int key = 4 * u + (l >> 4);
+      float x = 0.f;
+      if (key < p.keys) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p.k + (int64_t)key * kDim + 8 * g);
+        x = xhat8(v.x, v.y);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+      if (g == 0 && key < p.keys) {
+        const float sc = p.scales[key];
+        *reinterpret_cast<float2*>(p.keyinfo + 2 * (int64_t)key) = float2{sc, key_nhat(x, sc)};
+      }
+    } else {
+      // lane (g, quarter): heads quarter, quarter + 4, ... of dim group g
+      const int64_t r = u - kunits;
+      const int hq = l >> 4;
+      float a = 0.f;
+      float f[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) f[d] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int h = hq + 4 * i;
+        const float w = p.weights[r * kHeads + h];
+        const uint2 v = *reinterpret_cast<const uint2*>(p.q + (r * kHeads + h) * kDim + 8 * g);
+        a = __builtin_fmaf(__builtin_fabsf(w), xhat8(v.x, v.y), a);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          f[b] = __builtin_fmaf(w, e4m3_to_f32((int)v.x, b), f[b]);
+          f[4 + b] = __builtin_fmaf(w, e4m3_to_f32((int)v.y, b), f[4 + b]);
+        }
+      }
+      a += __shfl_xor(a, 16, 64);
+      a += __shfl_xor(a, 32, 64);
+      float fm = 0.f;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        float t = f[d] + __shfl_xor(f[d], 16, 64);
+        t += __shfl_xor(t, 32, 64);
+        fm = __builtin_fmaxf(fm, __builtin_fabsf(t));
+      }
+      const float alpha = wave_max(a);
+      const float fmax = wave_max(fm);
+      if (l == 0) p.beta[r] = row_beta(alpha, fmax);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kPrologueThreads) void fused_prologue_kernel(FusedParams p) {
   __shared__ int cnt[1024];
   __shared__ int off[1024];
   __shared__ int blo[kMaxBlocks], bhi[kMaxBlocks];
+  if (blockIdx.x > 0) {
+    prologue_bounds(p);
+    return;
+  }
   const int tid = threadIdx.x;
   cnt[tid] = 0;
   if (tid < 64) p.header[tid] = 0;
@@ -149,6 +282,7 @@ struct RowState {
   float thr;    // admission threshold
   int strict;   // admit score > thr (1) or >= thr (0)
   int cnt;      // records appended to the slab
+  float beta;   // the row's FP8 error bound factor (0: not scored)
 };
 
 // Rows of block b owned by the calling wave (modes off, thresholds open).
@@ -162,9 +296,16 @@ __device__ __forceinline__ void wave_rows(const FusedParams& p, int b, RowState*
     r.strict = 0;
     r.thr = -__builtin_inff();
     r.mode = M_OFF;
+    r.beta = 0.f;
     r.s = r.e = 0;
     if (r.r < p.rows) row_range(p, r.r, r.s, r.e);
   }
+}
+
+// A row's error bound factor as a wave-uniform (scalar) value: in the scan
+// loop it is an SGPR operand of the admission FMA, not one of the VGPRs.
+__device__ __forceinline__ float row_beta_of(const FusedParams& p, int r) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(p.beta[r])));
 }
 
 __device__ __forceinline__ void zero_query(QueryRow& qr) {
@@ -203,6 +344,8 @@ __device__ __forceinline__ void block_union(int* wlo_s, int* whi_s, int* wf_s, i
 constexpr int kStageChunks = 2;
 constexpr int kStageKeys = kStageChunks * kChunk;
 
+// A stage's per-key floats: the scales, then (kStageKeys floats further, so
+// that one LDS address serves both reads) the error bound factors nhat.
 struct Stages {
   uint8_t* k[2];
   float* s[2];
@@ -211,8 +354,8 @@ struct Stages {
 #define MQA_DECLARE_STAGES(name)                                          \
   __shared__ __align__(16) uint8_t name##_k0[kStageChunks * kChunkBytes]; \
   __shared__ __align__(16) uint8_t name##_k1[kStageChunks * kChunkBytes]; \
-  __shared__ __align__(16) float name##_s0[kStageKeys];                   \
-  __shared__ __align__(16) float name##_s1[kStageKeys];                   \
+  __shared__ __align__(16) float name##_s0[2 * kStageKeys];               \
+  __shared__ __align__(16) float name##_s1[2 * kStageKeys];               \
   const Stages name = {{name##_k0, name##_k1}, {name##_s0, name##_s1}}
 
 // Smallest float above a finite x: "score > x" is "score >= next_up(x)".
@@ -367,12 +510,27 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
 }
 
 // Queue direct global->LDS copies of the keys key0 + j * stride, j <
-// kStageKeys (clamped to the last key), and their scales into a stage buffer.
+// kStageKeys (clamped to the last key), their scales and their nhat into a
+// stage buffer.
 // Slot p of the buffer (16 bytes) holds key j = p / 8, column slice (p % 8) ^
 // swz(j); each wave fills 64 consecutive slots per copy. The copies are
 // waited for by the barrier that ends the stage before the buffer is read.
 __device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, int stride,
                                           uint8_t* kdst, float* sdst, int tid) {
+  // threads [0, kStageKeys): scales; [kStageKeys, 2 kStageKeys): nhat (the
+  // two halves of each key's keyinfo pair). Issued before the key tiles, so
+  // that anything the compiler reloads for it is waited for before the tile
+  // copies are in flight.
+  if (tid < 2 * kStageKeys) {
+    const int t = tid & (kStageKeys - 1);
+    const int half = tid / kStageKeys;
+    int key = key0 + t * stride;
+    key = key < p.keys ? key : p.keys - 1;
+    // a 32-bit byte offset from the uniform base (keys < 2^20): one VGPR
+    const uint32_t off = (uint32_t)(2 * key + half) * 4u;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(p.keyinfo) + off,
+                                     sdst + (tid & ~63), 4, 0, 0);
+  }
 #pragma unroll
   for (int i = 0; i < kStageChunks * kChunk * 8 / kThreads; ++i) {
     const int slot = tid + i * kThreads;
@@ -382,11 +540,6 @@ __device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, int st
     key = key < p.keys ? key : p.keys - 1;
     __builtin_amdgcn_global_load_lds(p.k + (int64_t)key * kDim + 16 * c, kdst + 16 * (slot & ~63),
                                      16, 0, 0);
-  }
-  if (tid < kStageKeys) {
-    int key = key0 + tid * stride;
-    key = key < p.keys ? key : p.keys - 1;
-    __builtin_amdgcn_global_load_lds(p.scales + key, sdst + (tid & ~63), 4, 0, 0);
   }
 }
 
@@ -440,8 +593,8 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
   }
   if (nlive == 0) cf = ch = 0;
   const int nst = (nch + kStageChunks - 1) / kStageChunks;
-  // One chunk of the stage in LDS (keys kc, scales scl): score the wave's
-  // rows and append their candidates.
+  // One chunk of the stage in LDS (keys kc, scales scl, error bound factors
+  // nrm): score the wave's rows and append their candidates.
   auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
     const int key0 = lo + c * kChunk;
     const int key = key0 + l;
@@ -465,13 +618,19 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
         if (!any) return;
       }
       const float sc = scl[l];
+      const float nh = scl[kStageKeys + l];
+      // the record's key word: the key and its nhat bits
+      const int kw = key | __float_as_int(nh);
       KeyTile kt;
       load_keys_lds(kt, kc);
       float E[4];
       // rows that are not live have zeroed operands and a +inf threshold
       score4(E, qr, fo, kt, sc);
+      // admission and records by U = E + beta * nhat, an upper bound of the
+      // key's exact score
 #pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i) emit_rec(rs[i], E[i], thl[i], true, key, sr, i);
+      for (int i = 0; i < kRowsPerWave; ++i)
+        emit_rec(rs[i], __builtin_fmaf(rs[i].beta, nh, E[i]), thl[i], true, kw, sr, i);
     } else {
       bool act[kRowsPerWave];
       bool any = false;
@@ -499,7 +658,8 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
   };
   // One stage: queue the copy of the next stage into the other buffer (its
   // last readers passed the previous barrier), then score this one.
-  auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext, float* snext) {
+  auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext,
+                   float* snext) {
     if (st + 1 < nst) dma_stage(p, lo + (st + 1) * kStageKeys, 1, knext, snext, tid);
 #pragma unroll
     for (int u = 0; u < kStageChunks; ++u) {
@@ -590,6 +750,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
         if (mine) {
           load_query(qr[i], p.q, p.weights, r.r, 0.5f);
           frows[i] = r.r;
+          r.beta = row_beta_of(p, r.r);
         }
         wlo = r.s < wlo ? r.s : wlo;
         whi = r.e > whi ? r.e : whi;
@@ -625,13 +786,18 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
         have_m0[i] = 0;
         nsamp[i] = 0;
       }
+      // The sample is scored as the scan will admit it: by U = E + beta * nhat
+      // (E the FP8 score), so that its counts predict the scan's candidates.
       auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
         if (!mine) return;
         const int key = lo + (c * kChunk + l) * stride;
+        const float nh = scl[kStageKeys + l];
         KeyTile kt;
         load_keys_lds(kt, kc);
         float E[4];
         score4(E, qr, fo, kt, scl[l]);
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) E[i] = __builtin_fmaf(rs[i].beta, nh, E[i]);
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) {
           const RowState& r = rs[i];
@@ -710,10 +876,12 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
             c += hv[j];
           }
           bstar = __shfl(bstar, hit ? __builtin_ctzll(hit) : 0, 64);
-          // The threshold goes halfway down the run of empty bins below bstar
-          // (to the next sampled score), not at bstar's lower edge: when the
-          // scores are heavily tied the k-th key's score sits at the top of a
-          // wide gap, and the select's certificate needs that gap as margin.
+          // The threshold goes down the run of empty bins below bstar to the
+          // next sampled score, not to bstar's lower edge: when the scores are
+          // heavily tied the k-th key's score sits at the top of a wide gap,
+          // and the select's certificate needs that gap as margin (every key
+          // left out must score below the k-th exact score, about one error
+          // bound under its U).
           int b2 = kGateBins;
 #pragma unroll
           for (int j = kPer - 1; j >= 0; --j)
@@ -722,7 +890,9 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
           if (hit && bstar < kGateBins - 1) {
             const float lower = (float)(bstar - kGateOff + 1);  // bstar's lower score edge
             const float next = (float)(b2 - kGateOff);           // upper edge of the next sample
-            thr = m0[i] - (b2 < kGateBins ? 0.5f * (lower + next) : lower) / inv[i];
+            // (a quarter bin above the next sampled bin, so that its scores
+            // stay out under rounding; never above bstar's lower edge)
+            thr = m0[i] - (b2 < kGateBins ? __builtin_fmaxf(lower, next - 0.25f) : lower) / inv[i];
             // A crowded bin (the first tile's range can be far wider than the
             // spread of scores around the k-th, e.g. with a large common score
             // offset) would admit every key of it: the fine pass bins its
@@ -757,7 +927,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
       for (int i = 0; i < kRowsPerWave; ++i) {
         const RowState& r = rs[i];
         if (r.r >= p.rows) continue;
-        p.rowinfo[r.r] = RowInfo{r.thr, 0, r.mode, 0};
+        p.rowinfo[r.r] = RowInfo{r.thr, 0, r.mode, 0, 0, 0};
         p.xrow[r.r] = 0;
         if (r.mode == M_GATED) p.rinfo[r.r] = RefineInfo{rm0[i], rinv[i], rbin[i], rneed[i], rnext[i]};
         fine = fine || rbin[i] >= 0;
@@ -779,7 +949,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
 // again (the same arithmetic as the gate, so the same scores) and bin the
 // samples of their crowded coarse bin in kGateBins fine bins across it; the
 // threshold goes into the first fine bin that completes the row's count, with
-// the gate's gap rule (halfway down to the next sampled score). Returns at
+// the gate's gap rule (down to the next sampled score). Returns at
 // once when nothing is queued.
 __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
   __shared__ GateSmem sm;
@@ -821,6 +991,7 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
       inv[i] = f.inv;
       load_query(qr[i], p.q, p.weights, r.r, 0.5f);
       frows[i] = r.r;
+      r.beta = row_beta_of(p, r.r);
       wfine = 1;
     }
     int lo, hi, unused;
@@ -837,10 +1008,13 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
       auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
         if (!wfine) return;
         const int key = lo + (c * kChunk + l) * stride;
+        const float nh = scl[kStageKeys + l];
         KeyTile kt;
         load_keys_lds(kt, kc);
         float E[4];
         score4(E, qr, fo, kt, scl[l]);
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) E[i] = __builtin_fmaf(rs[i].beta, nh, E[i]);
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) {
           const RowState& r = rs[i];
@@ -904,9 +1078,9 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
         const float lower = base + (float)(fstar + 1) / (float)kGateBins;
         float pos = lower;
         if (f2 < kGateBins)
-          pos = 0.5f * (lower + base + (float)f2 / (float)kGateBins);
+          pos = __builtin_fmaxf(lower, base + ((float)f2 - 0.25f) / (float)kGateBins);
         else if (rnext[i] < kGateBins)
-          pos = 0.5f * (lower + (float)(rnext[i] - kGateOff));
+          pos = __builtin_fmaxf(lower, (float)(rnext[i] - kGateOff) - 0.25f);
         if (l == 0) p.rowinfo[rs[i].r].thr = m0[i] - pos / inv[i];
       }
     }
@@ -956,6 +1130,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
       if (r.mode == M_ALL || r.mode == M_GATED) {
         load_query(qr[i], p.q, p.weights, r.r, 0.5f);
         frows[i] = r.r;
+        r.beta = row_beta_of(p, r.r);
         wlo = r.s < wlo ? r.s : wlo;
         whi = r.e > whi ? r.e : whi;
       }
@@ -990,100 +1165,141 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
   }
 }
 
-// Top-k of a row from its FP8-scored candidates (sE, sI)[0..n), n >= k, all
-// with approximate score >= Tlo, every non-candidate scoring <= Thi (Tlo =
-// Thi: the row's admission bound; a row scanned in key segments has one bound
-// per segment, Tlo their minimum and Thi their maximum):
-//   1. one pass for the candidates' score range, one histogram pass over
-//      2048 equal-width bins of that range (descending scores);
-//   2. the bins holding ranks k-kBand and k+kBand bound the band: records in
-//      better bins are taken, band records are compacted to the front of the
-//      slab, and the smallest score above / largest below the band are kept;
-//   3. the band's scores are recomputed exactly and its best k - |above|
-//      records are taken by exact score;
-//   4. certificate: with D = kBandSafety * (largest |exact - approximate| in
-//      the band, floored at 2^-18 of the row's largest score magnitude), the
-//      result is exact when every record above the band scores >= tau + D and
-//      every record below it (and every non-candidate, <= Thi) <= tau - D, tau
-//      being the k-th exact score.
-// Returns false when the certificate fails (the caller rescans the row); `low`
-// then receives a lower bound of the row's k-th exact score (the k records
-// taken score at least min(tau, smallest above-band score - D)), or -inf.
+// Top-k of a row from its FP8-scored candidates (sE, sI)[0..n), n >= k. A
+// record holds U = E + B, E the key's FP8 score and B = beta * nhat its error
+// bound, and the key word (key | nhat bits), so that the key's exact score
+// lies in [U - 2B, U]. Every key without a record scores at most Thi exactly
+// (strictly less when thi_lt: the admission bound of a row whose threshold
+// never rose; a row scanned in key segments has one per segment, Thi their
+// maximum).
+//   1. one pass for the range of the FP8 scores E (and the mean bound) and
+//      one histogram pass over 2048 equal-width bins of it find the bin of
+//      the k-th best E; the window [t_lo, t_hi] is that bin widened by
+//      1 + kWinBins bins and a sixteenth of the mean bound on each side;
+//   2. records whose whole interval lies above t_hi are taken; records whose
+//      interval meets the window form the band, compacted to the front of the
+//      slab; the others lie wholly below t_lo;
+//   3. the band is rescored exactly (bf16 MFMA) and its best need = k - taken
+//      records complete the row; tau is the need-th best exact band score;
+//   4. the result is exact when every taken record's interval lies above tau,
+//      every other record's below it and Thi does not exceed it (strictly, in
+//      the deterministic mode, so that every key scoring tau is in the band).
+// Returns false when step 4 fails; `low` then receives a lower bound of the
+// row's k-th exact score (the k records found score at least min(tau, the
+// lowest taken interval); more than k taken records bound it by t_hi), or
+// -inf.
 template <class Emit>
-__device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int n, int k,
-                              float Tlo, float Thi, const QueryRow& qr, uint32_t* hist,
-                              unsigned* band_count, float& low, Emit emit) {
+__device__ bool select_interval(const FusedParams& p, float* sE, int32_t* sI, int n, int k,
+                                float beta, float Thi, bool thi_lt, float hint_lo, float hint_hi,
+                                const QueryRow& qr, uint32_t* hist, float& low, Emit emit) {
   const int l = lane_id();
   constexpr int kBins = kHistWords;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  const float4* e4 = reinterpret_cast<const float4*>(sE);  // slab rows are 64 KiB aligned
+  // slab rows start on 1 KiB boundaries: 16-byte groups of 4 records
+  const float4* e4 = reinterpret_cast<const float4*>(sE);
+  const int4* i4 = reinterpret_cast<const int4*>(sI);
   const int n4 = n >> 2;
-  float m = __builtin_inff(), x = -__builtin_inff();
-#pragma unroll 4
-  for (int i = l; i < n4; i += kWave) {
-    const float4 v = e4[i];
-    m = __builtin_fminf(m, __builtin_fminf(__builtin_fminf(v.x, v.y), __builtin_fminf(v.z, v.w)));
-    x = __builtin_fmaxf(x, __builtin_fmaxf(__builtin_fmaxf(v.x, v.y), __builtin_fmaxf(v.z, v.w)));
+  auto bnd = [&](int kw) { return beta * __uint_as_float((uint32_t)kw & ~kKeyMask); };
+  // The histogram's range: the gate's hint (from its threshold up to twice
+  // its first-tile maximum's distance above it; scores outside fall into the
+  // end bins) when the row has one, else the records' own range (one pass);
+  // also when the k-th best lands in an end bin of the hinted range.
+  float mx = hint_hi, mn = hint_lo;
+  bool hinted = hint_hi > hint_lo && __builtin_isfinite(hint_hi - hint_lo);
+  float bs = 0.f;
+  int bk = 0;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    if (!hinted) {
+      float m = __builtin_inff(), x = -__builtin_inff();
+#pragma unroll 2
+      for (int i = l; i < n4; i += kWave) {
+        const float4 u = e4[i];
+        const int4 w4 = i4[i];
+        const float a0 = u.x - bnd(w4.x), a1 = u.y - bnd(w4.y), a2 = u.z - bnd(w4.z),
+                    a3 = u.w - bnd(w4.w);
+        m = __builtin_fminf(m, __builtin_fminf(__builtin_fminf(a0, a1), __builtin_fminf(a2, a3)));
+        x = __builtin_fmaxf(x, __builtin_fmaxf(__builtin_fmaxf(a0, a1), __builtin_fmaxf(a2, a3)));
+      }
+      for (int i = 4 * n4 + l; i < n; i += kWave) {
+        const float a0 = sE[i] - bnd(sI[i]);
+        m = __builtin_fminf(m, a0);
+        x = __builtin_fmaxf(x, a0);
+      }
+      mx = wave_max(x);
+      mn = wave_min(m);
+    }
+    const float span = mx - mn;
+    const float inv = span > 0.f ? (float)(kBins - 1) / span : 0.f;
+    auto bin_of = [&](float e) {
+      const float f = (mx - e) * inv;
+      int b = f < (float)(kBins - 1) ? (int)f : kBins - 1;
+      return b < 0 ? 0 : b;
+    };
+    for (int b = l; b < kBins; b += kWave) hist[b] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    bs = 0.f;
+#pragma unroll 2
+    for (int i = l; i < n4; i += kWave) {
+      const float4 u = e4[i];
+      const int4 w4 = i4[i];
+      const float b0 = bnd(w4.x), b1 = bnd(w4.y), b2 = bnd(w4.z), b3 = bnd(w4.w);
+      atomicAdd(&hist[bin_of(u.x - b0)], 1u);
+      atomicAdd(&hist[bin_of(u.y - b1)], 1u);
+      atomicAdd(&hist[bin_of(u.z - b2)], 1u);
+      atomicAdd(&hist[bin_of(u.w - b3)], 1u);
+      bs += (b0 + b1) + (b2 + b3);
+    }
+    for (int i = 4 * n4 + l; i < n; i += kWave) {
+      const float b0 = bnd(sI[i]);
+      atomicAdd(&hist[bin_of(sE[i] - b0)], 1u);
+      bs += b0;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    int before;
+    bk = first_bin_reaching(hist, kBins, k, before);
+    __builtin_amdgcn_wave_barrier();
+    if (!(hinted && (bk == 0 || bk == kBins - 1))) break;
+    hinted = false;  // the k-th best lies outside the hinted range
   }
-  for (int i = 4 * n4 + l; i < n; i += kWave) {
-    m = __builtin_fminf(m, sE[i]);
-    x = __builtin_fmaxf(x, sE[i]);
-  }
-  const float mx = wave_max(x);
-  // every candidate scored >= Tlo; the lower end of the range is Tlo when finite
-  const float mn = Tlo > -__builtin_inff() ? Tlo : wave_min(m);
-  const float span = mx - mn;
-  const float inv = span > 0.f ? (float)(kBins - 1) / span : 0.f;
-  auto bin_of = [&](float e) {
-    const float f = (mx - e) * inv;
-    int b = f < (float)(kBins - 1) ? (int)f : kBins - 1;
-    return b < 0 ? 0 : b;
-  };
-  for (int b = l; b < kBins; b += kWave) hist[b] = 0;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
-  for (int i = l; i < n4; i += kWave) {
-    const float4 v = e4[i];
-    atomicAdd(&hist[bin_of(v.x)], 1u);
-    atomicAdd(&hist[bin_of(v.y)], 1u);
-    atomicAdd(&hist[bin_of(v.z)], 1u);
-    atomicAdd(&hist[bin_of(v.w)], 1u);
-  }
-  for (int i = 4 * n4 + l; i < n; i += kWave) atomicAdd(&hist[bin_of(sE[i])], 1u);
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  int before_hi, before_lo;
-  const int b_hi = first_bin_reaching(hist, kBins, k - kBand, before_hi);
-  const int b_lo = first_bin_reaching(hist, kBins, k + kBand, before_lo);
-  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) bs += __shfl_xor(bs, o, 64);
+  const float margin = bs / (16.f * (float)n);  // a sixteenth of the mean bound
+  const float wbin = mx > mn ? (mx - mn) / (float)(kBins - 1) : 0.f;
+  // the k-th best E lies in bin bk, up to one bin of rounding in bin_of
+  const float t_lo = mx - (float)(bk + 2 + kWinBins) * wbin - margin;
+  const float t_hi = mx - (float)(bk - 1 - kWinBins) * wbin + margin;
   int na = 0, nb = 0;
-  float min_above = __builtin_inff(), max_below = -__builtin_inff();
-  // One record: taken (above the band), compacted into the band, or below.
-  auto visit = [&](bool in, float e, int32_t idx) {
-    const int b = bin_of(e);
-    const bool up = in && b < b_hi;
-    const bool band = in && b >= b_hi && b <= b_lo;
+  // the lowest interval end among the taken records and the highest among
+  // the dropped ones
+  float a_lo = __builtin_inff(), z_hi = -__builtin_inff();
+  // One record: taken (wholly above t_hi), compacted into the band (meets the
+  // window), or dropped (wholly below t_lo).
+  auto visit = [&](bool in, float u, int32_t kw) {
+    const float lo = u - 2.f * bnd(kw);
+    const bool up = in && lo > t_hi;
+    const bool band = in && !up && u >= t_lo;
     const uint64_t mu = __ballot(up);
     const uint64_t mb = __ballot(band);
+    const int key = kw & (int)kKeyMask;
     if (up) {
       const int slot = na + rank_in_mask(mu);
-      if (slot < k) emit(slot, idx);
-      min_above = __builtin_fminf(min_above, e);
+      if (slot < k) emit(slot, key);
+      a_lo = __builtin_fminf(a_lo, lo);
     }
-    if (in && b > b_lo) max_below = __builtin_fmaxf(max_below, e);
+    if (in && !up && !band) z_hi = __builtin_fmaxf(z_hi, u);
     // in-place compaction: the targets lie in records already loaded
     if (band) {
       const int pos = nb + rank_in_mask(mb);
-      sE[pos] = e;
-      sI[pos] = idx;
+      sE[pos] = u;
+      sI[pos] = kw;
     }
     na += __popcll(mu);
     nb += __popcll(mb);
   };
   // groups of 4 consecutive records per lane (256 per wave step), the next
   // group's loads issued before the current group is visited
-  const int4* i4 = reinterpret_cast<const int4*>(sI);
   float4 ev = l < n4 ? e4[l] : float4{0.f, 0.f, 0.f, 0.f};
   int4 iv = l < n4 ? i4[l] : int4{0, 0, 0, 0};
   for (int g0 = 0; g0 < n4; g0 += kWave) {
@@ -1103,62 +1319,77 @@ __device__ bool select_banded(const FusedParams& p, float* sE, int32_t* sI, int 
     const bool in = i < n;
     visit(in, in ? sE[i] : 0.f, in ? sI[i] : 0);
   }
-  min_above = wave_min(min_above);
-  max_below = wave_max(max_below);
-  const float maxabs = __builtin_fmaxf(__builtin_fabsf(mx), __builtin_fabsf(mn));
+  a_lo = wave_min(a_lo);
+  z_hi = wave_max(z_hi);
   const int need = k - na;
+  const bool stats = p.flags & 8u;
   low = -__builtin_inff();
-  if (na >= k || nb < need) return false;
+  if (need < 1 || nb < need) {
+    if (need < 1) low = t_hi;  // k or more keys score above t_hi
+    if (stats && l == 0) atomicAdd(&p.header[H_FAIL_COUNT], 1u);
+    return false;
+  }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   // exact scores of the band, 64 records at a time; the next group's key
-  // indices, scales and approximate scores are loaded one group ahead
-  float err = 0.f;
+  // indices and scales are loaded one group ahead. With MQA_FLAG_STATS the
+  // largest |exact - FP8| / bound of the band goes to the header (a check of
+  // the bound on the hardware that runs it).
+  float ratio = 0.f;
   int keyidx[4];
-  float sc = 0.f, eo = 0.f;
-  auto group_refs = [&](int b0, int* ki, float& s_, float& e_) {
+  float sc = 0.f;
+  auto group_refs = [&](int b0, int* ki, float& s_) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int j = b0 + 16 * t + (l & 15);
-      ki[t] = sI[j < nb ? j : nb - 1];
+      ki[t] = sI[j < nb ? j : nb - 1] & (int)kKeyMask;
     }
     const int j = b0 + l;
-    const int jj = j < nb ? j : nb - 1;
-    s_ = p.scales[sI[jj]];
-    e_ = sE[jj];
+    s_ = p.scales[sI[j < nb ? j : nb - 1] & (int)kKeyMask];
   };
-  if (nb > 0) group_refs(0, keyidx, sc, eo);
+  group_refs(0, keyidx, sc);
   for (int b0 = 0; b0 < nb; b0 += kWave) {
     KeyTile kt;
     load_keys_gather(kt, p.k, keyidx);
     int kn[4] = {0, 0, 0, 0};
-    float scn = 0.f, eon = 0.f;
-    if (b0 + kWave < nb) group_refs(b0 + kWave, kn, scn, eon);
+    float scn = 0.f;
+    if (b0 + kWave < nb) group_refs(b0 + kWave, kn, scn);
     const int j = b0 + l;
     const float E = score_chunk_exact(qr, kt) * sc;
     if (j < nb) {
-      err = __builtin_fmaxf(err, __builtin_fabsf(E - eo));
+      const int kw = sI[j];
+      if (stats) {
+        const float bb = bnd(kw);
+        const float dev = __builtin_fabsf(E - (sE[j] - bb));
+        ratio = __builtin_fmaxf(ratio, bb > 0.f ? dev / bb : (dev > 0.f ? 1e30f : 0.f));
+      }
       sE[j] = E;
+      sI[j] = kw & (int)kKeyMask;
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) keyidx[t] = kn[t];
     sc = scn;
-    eo = eon;
   }
-  err = wave_max(err);
-  if (l == 0 && band_count)
-    atomicAdd(reinterpret_cast<unsigned long long*>(band_count), (unsigned long long)nb);
+  if (stats) {
+    ratio = wave_max(ratio);
+    if (l == 0) atomicMax(&p.header[H_ERRMAX], __float_as_uint(ratio));
+  }
+  if (l == 0 && stats)
+    atomicAdd(reinterpret_cast<unsigned long long*>(&p.header[H_BAND_LO]), (unsigned long long)nb);
   auto take = [&](int slot, float, int idx) { emit(na + slot, idx); };
   const bool det = det_mode(p);
   const float tau = det ? wave_select_lowkey(sE, sI, nb, need, hist, take)
       : nb <= 256 ? small_select(sE, sI, nb, need, reinterpret_cast<float*>(hist), take)
                   : wave_select(sE, sI, nb, need, hist, take);
-  const float d = kBandSafety * __builtin_fmaxf(err, maxabs * 0x1p-18f);
-  const float below = __builtin_fmaxf(max_below, Thi);
-  // deterministic mode: no record outside the band may tie with tau either
-  const bool ok_above = na == 0 || (det ? min_above - d > tau : min_above - d >= tau);
-  const bool ok_below = det ? below + d < tau : below + d <= tau;
-  low = na == 0 ? tau : __builtin_fminf(tau, min_above - d);
-  return ok_above && ok_below;
+  low = __builtin_fminf(tau, a_lo);
+  // taken records above tau, dropped ones and non-candidates below it
+  // (ties at tau are allowed outside the band unless the mode is
+  // deterministic)
+  const bool ok_a = det ? a_lo > tau : a_lo >= tau;
+  const bool ok_z = det ? z_hi < tau : z_hi <= tau;
+  const bool ok_nc = (thi_lt || !det) ? Thi <= tau : Thi < tau;
+  if (stats && l == 0 && !(ok_a && ok_z && ok_nc))
+    atomicAdd(&p.header[!ok_a ? H_FAIL_ABOVE : (!ok_z ? H_FAIL_BELOW : H_FAIL_ADMIT)], 1u);
+  return ok_a && ok_z && ok_nc;
 }
 
 // Queue row r (of block r / 32) for the exact rescan; each block is queued
@@ -1177,6 +1408,9 @@ __device__ __forceinline__ void queue_rescan(const FusedParams& p, int r, float 
   if (lane_id() != 0) return;
   p.rowinfo[r].thr = low;
   p.rowinfo[r].cnt = 0;
+  p.rowinfo[r].strict = 0;
+  p.rowinfo[r].above = 0;
+  p.rowinfo[r].filled = 0;
   p.rqueue[atomicAdd(&p.header[H_RQ], 1u)] = r;
 }
 
@@ -1196,19 +1430,17 @@ __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_
   const bool forced = ri.mode != M_EXACT && (p.flags & 32u);  // rescan from an open bound
   float* sE = p.slabE + (int64_t)r * kSlabRow;
   int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
-  // candidates and admission bounds: the row's, or the union of its key
-  // segments' (moved down to one run at the start of the slab row; tlo bounds
-  // every candidate from below, thi every other key from above)
+  // candidates and admission bound: the row's, or the union of its key
+  // segments' (moved down to one run at the start of the slab row; thi bounds
+  // every other key's exact score from above)
   int cnt = ri.cnt;
-  float tlo = ri.thr, thi = ri.thr;
+  float thi = ri.thr;
   if (p.nseg > 1 && ri.mode != M_EXACT) {
     const int region = kSlabRow / p.nseg;
     cnt = 0;
-    tlo = __builtin_inff();
     thi = -__builtin_inff();
     for (int sg = 0; sg < p.nseg; ++sg) {
       const SegInfo si = p.seg[(int64_t)r * kMaxSeg + sg];
-      tlo = __builtin_fminf(tlo, si.thr);
       thi = __builtin_fmaxf(thi, si.thr);
       const int src = sg * region;
       // forward copy to a lower offset: no lane reads a record already written
@@ -1230,9 +1462,19 @@ __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_
       QueryRow qr;
       load_query(qr, p.q, p.weights, r);
       int32_t* o = p.out + (int64_t)r * k;
-      ok = select_banded(p, sE, sI, cnt, k, tlo, thi, qr, hist[w],
-                         stats ? &p.header[H_BAND_LO] : nullptr, low,
-                         [&](int sl, int idx) { o[sl] = idx - s; });
+      // non-candidates score below the bound unless a merge raised it (then
+      // at most it); split rows are taken as raised
+      const bool thi_lt = p.nseg == 1 && ri.strict == 0;
+      // the histogram's range from the gate: [thr, m0 + (m0 - thr)], m0 the
+      // maximum U of the gate's first sample tile
+      float hlo = 0.f, hhi = 0.f;
+      if (ri.mode == M_GATED && p.nseg == 1 && ri.strict == 0) {
+        const float m0 = p.rinfo[r].m0;
+        hlo = ri.thr;
+        hhi = m0 + (m0 - ri.thr);
+      }
+      ok = select_interval(p, sE, sI, cnt, k, p.beta[r], thi, thi_lt, hlo, hhi, qr, hist[w], low,
+                           [&](int sl, int idx) { o[sl] = idx - s; });
       if (stats && l == 0) {
         atomicAdd(&p.header[ok ? H_GATED : H_UNCERT], 1u);
         atomicAdd(reinterpret_cast<unsigned long long*>(&p.header[H_CAND_LO]),
@@ -1251,13 +1493,14 @@ __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_
 }
 
 // ---------------------------------------------------------------------------
-// Bounded rescan of the queued rows, in up to two rounds. Work item i of a
+// Bounded rescan of the queued rows, in up to three rounds. Work item i of a
 // round covers keys [kRescanKeys * (i / nq), kRescanKeys * (i / nq + 1)) of
 // queued row i % nq (slice-major, so that the waves working at one time share
 // their keys in L2); one wave per item, claimed from the round's counter.
 // Exact scores (the band rescoring's bf16 MFMA) of 64 keys at a time; keys
-// scoring >= the row's bound get slab slots from the row's counter (slots past
-// the slab are counted, not written).
+// scoring >= the row's bound (> in a strict round) get slab slots from the
+// row's counter (slots past the slab are counted, not written), and the keys
+// strictly above it are counted apart.
 __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, int round) {
   const int l = lane_id();
   const int nq = (int)p.header[H_RQ + 2 * round];
@@ -1280,6 +1523,7 @@ __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, i
     QueryRow qr;
     load_query(qr, p.q, p.weights, r);
     const float low = p.rowinfo[r].thr;
+    const bool strict = p.rowinfo[r].strict != 0;
     float* sE = p.slabE + (int64_t)r * kSlabRow;
     int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
     for (int k0 = a; k0 < b; k0 += kWave) {
@@ -1294,11 +1538,15 @@ __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, i
       const int key = k0 + l;
       const bool valid = key < b;
       const float E = score_chunk_exact(qr, kt) * p.scales[valid ? key : b - 1];
-      const bool pass = valid && E >= low;
+      const bool pass = valid && (strict ? E > low : E >= low);
       const uint64_t m = __ballot(pass);
       if (m == 0) continue;
+      const uint64_t ma = __ballot(valid && E > low);
       int base = 0;
-      if (l == 0) base = atomicAdd(&p.rowinfo[r].cnt, __popcll(m));
+      if (l == 0) {
+        base = atomicAdd(&p.rowinfo[r].cnt, __popcll(m));
+        if (!strict && ma) atomicAdd(&p.rowinfo[r].above, __popcll(ma));
+      }
       base = __shfl(base, 0, 64);
       const int pos = base + rank_in_mask(m);
       if (pass && pos < kSlabRow) {
@@ -1311,9 +1559,10 @@ __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, i
 
 // Top-k of each row of a bounded-rescan round from its slab (one wave per
 // row). A row whose keys at or above its bound overfilled the slab gets, in
-// the first round, the k-th best exact score among the slab's records as a
-// new (higher) bound and a second round; a row with fewer than k such keys,
-// or still too many, goes on to the exact streaming rescan.
+// the first two rounds, another round: over the keys at or above the k-th best
+// exact score among the slab's records when that is a higher bound, else over
+// the keys strictly above the bound when k of them are; a row with fewer than
+// k such keys, or still too many, goes on to the exact streaming rescan.
 __global__ __launch_bounds__(kSelWaves * kWave) void fused_finish_kernel(FusedParams p,
                                                                          int round) {
   __shared__ uint32_t hist[kSelWaves][kHistWords];
@@ -1325,27 +1574,60 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_finish_kernel(FusedPa
   for (int qi = blockIdx.x * kSelWaves + w; qi < nq; qi += gridDim.x * kSelWaves) {
     const int r = p.rqueue[round * qrows + qi];
     const int cnt = p.rowinfo[r].cnt;
+    const int filled = p.rowinfo[r].filled;
+    const int need = k - filled;  // slots [need, k) were filled by round 0
     float* sE = p.slabE + (int64_t)r * kSlabRow;
     int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
-    if (cnt >= k && cnt <= kSlabRow) {
-      int s, e;
-      row_range(p, r, s, e);
-      int32_t* o = p.out + (int64_t)r * k;
+    int s, e;
+    row_range(p, r, s, e);
+    int32_t* o = p.out + (int64_t)r * k;
+    if (cnt >= need && cnt <= kSlabRow) {
       auto put = [&](int sl, float, int idx) { o[sl] = idx - s; };
       if (det_mode(p))
-        wave_select_lowkey(sE, sI, cnt, k, hist[w], put);
+        wave_select_lowkey(sE, sI, cnt, need, hist[w], put);
       else
-        wave_select(sE, sI, cnt, k, hist[w], put);
+        wave_select(sE, sI, cnt, need, hist[w], put);
       if ((p.flags & 8u) && l == 0) atomicAdd(&p.header[H_RESCAN], 1u);
       continue;
     }
-    if (round == 0 && cnt > kSlabRow) {
+    if (round + 1 < kRescanRounds && cnt > kSlabRow) {
+      // Too many keys at or above the bound. The k-th best stored score is a
+      // higher bound when it exceeds it (the second round then takes the keys
+      // at or above it); else, when k keys score strictly above the bound
+      // (the rest tie with it, e.g. relu's exact zeros), the second round
+      // takes those; else the k-th score is the bound itself: stored ties of
+      // it fill the last k - above slots and the second round takes the
+      // `above` keys strictly above it (not in the deterministic mode, whose
+      // ties go to the smallest keys, not to the stored ones).
+      const int above = p.rowinfo[r].above;
+      const float thr = p.rowinfo[r].thr;
       const float low = wave_kth_value(sE, kSlabRow, k, hist[w]);
-      if (low > p.rowinfo[r].thr) {
+      int fill = 0;
+      if (!(low > thr) && above < k && !det_mode(p)) {
+        fill = k - above;
+        int got = 0;
+        for (int i0 = 0; i0 < kSlabRow && got < fill; i0 += kWave) {
+          const int i = i0 + l;
+          const bool tie = i < kSlabRow && sE[i] == thr;
+          const uint64_t m = __ballot(tie);
+          const int slot = got + rank_in_mask(m);
+          if (tie && slot < fill) o[above + slot] = sI[i] - s;
+          got += __popcll(m);
+        }
+        if (got < fill) fill = -1;  // cannot happen: the slab holds >= k - above ties
+      }
+      if (low > thr || above >= k || fill > 0) {
+        if (fill > 0 && above == 0) {
+          if ((p.flags & 8u) && l == 0) atomicAdd(&p.header[H_RESCAN], 1u);
+          continue;  // every slot holds a tie of the k-th score
+        }
         if (l == 0) {
-          p.rowinfo[r].thr = low;
+          p.rowinfo[r].thr = low > thr ? low : thr;
           p.rowinfo[r].cnt = 0;
-          p.rqueue[qrows + atomicAdd(&p.header[H_RQ + 2], 1u)] = r;
+          p.rowinfo[r].above = 0;
+          p.rowinfo[r].strict = low > thr ? 0 : 1;
+          p.rowinfo[r].filled = low > thr || above >= k ? 0 : fill;
+          p.rqueue[(round + 1) * qrows + atomicAdd(&p.header[H_RQ + 2 * (round + 1)], 1u)] = r;
         }
         continue;
       }
@@ -1489,7 +1771,15 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_sort_kernel(FusedPara
 extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t stream,
                                 hipEvent_t scan_begin, hipEvent_t scan_end) {
   hipError_t e;
-  hipLaunchKernelGGL(mqa::fused_plan_kernel, dim3(1), dim3(1024), 0, stream, *p);
+  // workgroup 0 plans; the others (about one per CU, at most the units of
+  // bound work) compute the error bounds
+  const int units = (p->keys + 3) / 4 + p->rows;
+  const int waves_per_wg = mqa::kPrologueThreads / mqa::kWave;
+  int bwg = (units + waves_per_wg - 1) / waves_per_wg;
+  bwg = bwg < grid ? bwg : grid;
+  bwg = bwg < 1 ? 1 : bwg;
+  hipLaunchKernelGGL(mqa::fused_prologue_kernel, dim3(1 + bwg), dim3(mqa::kPrologueThreads), 0,
+                     stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   hipLaunchKernelGGL(mqa::fused_gate_kernel, dim3(p->scan_grid), dim3(mqa::kThreads), 0, stream,
                      *p);
@@ -1510,7 +1800,7 @@ extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t
                      stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   const int fin = sel < 256 ? sel : 256;
-  for (int round = 0; round < 2; ++round) {
+  for (int round = 0; round < mqa::kRescanRounds; ++round) {
     hipLaunchKernelGGL(mqa::fused_rescan_kernel, dim3(2 * grid), dim3(mqa::kThreads), 0, stream,
                        *p, round);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;

@@ -13,7 +13,10 @@ struct RowInfo {
   float thr;   // admission threshold
   int cnt;     // candidates in the row's slab
   int mode;    // how the row is served (fused.hip RowMode)
-  int strict;  // 1: a merge raised thr; later candidates had to beat it strictly
+  int strict;  // 1: candidates had to beat thr strictly (a merge raised it, or a
+               // bounded-rescan round admits scores above its bound only)
+  int above;   // bounded rescan: keys scoring strictly above thr
+  int filled;  // bounded rescan: output slots [k - filled, k) already hold ties of thr
 };
 
 // Per-(row, key segment) state of a split scan (nseg > 1): the segment's
@@ -55,10 +58,17 @@ struct FusedParams {
   int32_t* fqueue;   // [nblocks] blocks queued for the gate's fine pass
   uint32_t* fflag;   // [nblocks] 1 = the block is queued for the fine pass
   RefineInfo* rinfo; // [rows]
-  int32_t* rqueue;   // [2][nblocks * 32] rows queued for the two bounded-rescan rounds
+  int32_t* rqueue;   // [3][nblocks * 32] rows queued for the three bounded-rescan rounds
   uint32_t* xflag;   // [nblocks] 1 = the block is queued
   RowInfo* rowinfo;  // [rows]
   SegInfo* seg;      // [nblocks * 32 rows][kMaxSeg] (nseg > 1)
+  // FP8 score error bounds (written by the prologue): an FP8-scored key j of
+  // row r is within beta[r] * nhat_j of its exact score. keyinfo[2j] is key
+  // j's scale, keyinfo[2j + 1] its nhat, which keeps only its top 12 bits
+  // (the low 20 are zero) so that it travels in the upper bits of a
+  // candidate record's key word.
+  float* keyinfo;    // [keys][2]
+  float* beta;       // [rows]
   float* slabE;      // [nblocks * 32 rows][kSlabRow] candidate scores
   int32_t* slabI;    // [nblocks * 32 rows][kSlabRow] candidate keys
   float* tmpE;       // [grid][8 waves][kTmp] merge buffers
@@ -97,6 +107,9 @@ constexpr int kMaxSeg = 8;
 // Rows per launch sequence: larger calls run in batches of this many rows
 // (the workspace holds one batch's candidate slabs, 1.09 GB).
 constexpr int kMaxBatchRows = 16384;
+// A candidate record's key word: the key in the low 20 bits (keys < 2^20),
+// the key's nhat bit pattern in the others.
+constexpr uint32_t kKeyMask = 0xFFFFFu;
 
 }  // namespace mqa
 

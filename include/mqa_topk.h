@@ -92,9 +92,12 @@ typedef struct mqa_stats {
   uint32_t rows_rescanned;  /* uncertified rows redone by the bounded rescan */
   uint32_t rows_undercount; /* gated rows with fewer than k candidates */
   uint32_t compactions;     /* slab merges (keep the best records, raise the threshold) */
-  uint32_t rows_uncertified;/* gated rows whose exact band could not certify the cut */
+  uint32_t rows_uncertified;/* gated rows whose k-th exact score fell outside the window
+                               the select cut its candidates' error intervals against */
   uint64_t candidates;      /* candidates emitted by gated rows */
   uint64_t band_keys;       /* keys rescored exactly around the rows' k-th scores */
+  float bound_ratio_max;    /* largest |exact - FP8 score| / proven error bound among
+                               the rescored keys (below 1 whenever the bound holds) */
 } mqa_stats;
 
 /*
@@ -199,6 +202,24 @@ int mqa_scan_time(int last_n, float* total_ms);
  * on an error.
  */
 int mqa_mfma_peak(float* out, int64_t out_len, int workgroups, int iters, void* stream);
+
+/*
+ * FP8 MFMA precision probe (a test aid: the fused path's error bounds rest on
+ * how this instruction rounds). Runs the scan's instruction forms on caller
+ * operands, one 16x16 product per case:
+ *   out[c][m][n] = sum_d a[c][m][d] * b[c][n][d]   (as the MFMA computes it)
+ * with v_mfma_f32_16x16x128_f8f6f4 (ascale NULL) or, with ascale, its scaled
+ * form, a[c][m][d] taking the E8M0 scale ascale[c][m][blk] of the 32-wide
+ * K block blk that holds d (the block of dims {0-15, 32-47}, {64-79, 96-111},
+ * {16-31, 48-63} or {80-95, 112-127}) and b scale 1.
+ *   a, b: [ncases][16][128] OCP e4m3 bytes, 16-B aligned; ascale: NULL or
+ *   [ncases][16][4] bytes; out: [ncases][16][16] fp32, 4-B aligned; all
+ *   device pointers owned by the caller; ncases in [1, 2^20].
+ * Returns MQA_OK, MQA_ERR_NULL, MQA_ERR_ALIGN, MQA_ERR_SHAPE, MQA_ERR_DEVICE
+ * or MQA_ERR_LAUNCH; asynchronous on `stream`.
+ */
+int mqa_fp8_mfma_probe(const uint8_t* a, const uint8_t* b, const uint8_t* ascale, float* out,
+                       int ncases, void* stream);
 
 /* Human-readable text of a return code (for MQA_ERR_LAUNCH it names the HIP
  * error of the failing call on this thread). Never NULL. */

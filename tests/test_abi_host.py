@@ -27,6 +27,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert set(names) == {"workspace_size", "mqa_topk_prefill", "mqa_logits_dense",
                           "mqa_topk_dense", "mqa_key_scales", "mqa_scan_time", "mqa_mfma_peak",
+                          "mqa_fp8_mfma_probe",
                           "mqa_strerror"}
 
 
