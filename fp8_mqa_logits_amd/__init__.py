@@ -30,7 +30,8 @@ FLAG_DETERMINISTIC = 64
 ERR_NAMES = {0: "MQA_OK", 1: "MQA_ERR_NULL", 2: "MQA_ERR_ALIGN", 3: "MQA_ERR_SHAPE",
              4: "MQA_ERR_WORKSPACE", 5: "MQA_ERR_DEVICE", 6: "MQA_ERR_LAUNCH"}
 
-EXPORTS = ("workspace_size", "mqa_topk_prefill", "mqa_logits_dense", "mqa_topk_dense",
+EXPORTS = ("workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static", "mqa_logits_dense",
+           "mqa_topk_dense",
            "mqa_key_scales", "mqa_scan_time", "mqa_mfma_peak", "mqa_fp8_mfma_probe",
            "mqa_strerror")
 
@@ -62,6 +63,8 @@ def load() -> ctypes.CDLL:
         lib.workspace_size.restype = SZ
         lib.mqa_topk_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, P, SZ, U, P]
         lib.mqa_topk_prefill.restype = I
+        lib.mqa_topk_prefill_static.argtypes = [P, P, P, P, P, P, P, I, I, I, U, P]
+        lib.mqa_topk_prefill_static.restype = I
         lib.mqa_logits_dense.argtypes = [P, P, P, P, P, P, P, I64, I, I, I, I, P]
         lib.mqa_logits_dense.restype = I
         lib.mqa_topk_dense.argtypes = [P, I64, I, I, P, P, P, I, I, I, P]
@@ -178,6 +181,41 @@ def mqa_topk_prefill(q, k, scales, weights, starts, ends, topk: int, out=None, w
                                      _ptr(workspace), workspace.numel(), int(flags),
                                      _stream(dev, stream))
     _check(rc, "mqa_topk_prefill")
+    return out
+
+
+def mqa_topk_prefill_static(q, k, scales, weights, starts, ends, topk: int, out=None,
+                            flags: int = 0, stream=None) -> torch.Tensor:
+    """mqa_topk_prefill through the allocation-free entry point (the library's
+    own device scratch; no workspace). Same arguments and result."""
+    _tensors(q=q, k=k, scales=scales, weights=weights, starts=starts, ends=ends)
+    if q.dim() != 3 or k.dim() != 2:
+        raise ValueError("q must be [rows,32,128] and k [keys,128]")
+    rows, keys = q.shape[0], k.shape[0]
+    _shape(q, (rows, HEADS, HEAD_DIM), "q")
+    _shape(k, (keys, HEAD_DIM), "k")
+    _shape(scales, (keys,), "scales")
+    _shape(weights, (rows, HEADS), "weights")
+    _shape(starts, (rows,), "starts")
+    _shape(ends, (rows,), "ends")
+    if out is not None:
+        _tensors(out=out)
+        _shape(out, (rows, topk), "out")
+    dev = q.device
+    _need(q, "q", FP8, dev)
+    _need(k, "k", FP8, dev)
+    _need(scales, "scales", (torch.float32,), dev)
+    _need(weights, "weights", (torch.float32,), dev)
+    _need(starts, "starts", (torch.int32,), dev)
+    _need(ends, "ends", (torch.int32,), dev)
+    if out is None:
+        out = torch.empty((rows, topk), dtype=torch.int32, device=dev)
+    _need(out, "out", (torch.int32,), dev)
+    with torch.cuda.device(dev):
+        rc = load().mqa_topk_prefill_static(_ptr(q), _ptr(k), _ptr(scales), _ptr(weights),
+                                            _ptr(starts), _ptr(ends), _ptr(out), rows, keys,
+                                            int(topk), int(flags), _stream(dev, stream))
+    _check(rc, "mqa_topk_prefill_static")
     return out
 
 

@@ -181,42 +181,19 @@ bool ring_slot(int device, hipEvent_t* b, hipEvent_t* e) {
   return true;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t workspace_size(int rows, int device) {
-  if (rows < 1 || rows > MQA_MAX_ROWS) return 0;
-  const DeviceInfo* d = device_info(device);
-  if (!d) return 0;
-  return layout(batch_rows(rows), *d).total;
-}
-
-int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
-                     const float* weights, const int32_t* starts, const int32_t* ends,
-                     int32_t* out, int rows, int keys, int topk, void* workspace,
-                     size_t workspace_bytes, unsigned flags, void* stream) {
-  if (!q || !k || !scales || !weights || !starts || !ends || !out || !workspace)
-    return MQA_ERR_NULL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scales, 16) || !aligned(weights, 16) ||
-      !aligned(out, 16) || !aligned(starts, 4) || !aligned(ends, 4) || !aligned(workspace, 256))
-    return MQA_ERR_ALIGN;
-  if (rows < 1 || rows > MQA_MAX_ROWS || keys < 1 || keys > MQA_MAX_KEYS || !topk_ok(topk))
-    return MQA_ERR_SHAPE;
-  const DeviceInfo* d = current_device();
-  if (!d) return MQA_ERR_DEVICE;
-  const int batch = batch_rows(rows);
-  const Layout L = layout(batch, *d);
-  if (workspace_bytes < L.total) return MQA_ERR_WORKSPACE;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+// Rows in batches of `batch` rows, one launch sequence each, in order on the
+// stream (they share the workspace ws, which holds layout(batch)).
+int prefill_batches(const uint8_t* q, const uint8_t* k, const float* scales,
+                    const float* weights, const int32_t* starts, const int32_t* ends,
+                    int32_t* out, int rows, int keys, int topk, uint8_t* ws, int batch,
+                    const DeviceInfo& d, unsigned flags, void* stream) {
+  const Layout L = layout(batch, d);
   hipEvent_t eb = nullptr, ee = nullptr;
   if (flags & MQA_FLAG_TIME_SCAN) {
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (!ring_slot(dev, &eb, &ee)) return MQA_ERR_DEVICE;
   }
-  // Rows run in batches of `batch` rows, one launch sequence each, in order
-  // on the stream (they share the workspace).
   for (int r0 = 0; r0 < rows; r0 += batch) {
     const int nr = rows - r0 < batch ? rows - r0 : batch;
     mqa::FusedParams p;
@@ -258,6 +235,116 @@ int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
     if (rc != 0) return launch_error(rc);
   }
   return MQA_OK;
+}
+
+int launch_error_text(const char* what) {
+  std::snprintf(g_err, sizeof(g_err), "%s", what);
+  return MQA_ERR_LAUNCH;
+}
+
+thread_local char g_ws_err[160] = "";
+
+int workspace_error_text(const char* what) {
+  std::snprintf(g_ws_err, sizeof(g_ws_err), "%s", what);
+  return MQA_ERR_WORKSPACE;
+}
+
+}  // namespace
+
+// The scratch of mqa_topk_prefill_static, for callers that cannot allocate:
+// the workspace of one row batch, in device memory the library owns (each
+// device the library runs on holds its own copy until the process ends).
+// Host code never uses this name as an address: the device address of each
+// device's copy comes from hipGetSymbolAddress (static_scratch).
+constexpr size_t kStaticScratchBytes = (size_t)384 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+void* g_scratch_ptr[64];
+bool g_scratch_tried[64];
+
+// Device address of `device`'s copy of the scratch (the device is current),
+// looked up on its first use; nullptr if the lookup failed.
+uint8_t* static_scratch(int device) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_scratch_tried[device]) {
+    g_scratch_tried[device] = true;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr &&
+        reinterpret_cast<uintptr_t>(ptr) % kAlign == 0)
+      g_scratch_ptr[device] = ptr;
+    (void)hipGetLastError();
+  }
+  return static_cast<uint8_t*>(g_scratch_ptr[device]);
+}
+
+// Rows per batch of the static entry point: the largest multiple of 32 (at
+// most one full batch) whose workspace fits the scratch; 0 if none does.
+int static_batch(const DeviceInfo& d) {
+  int b = mqa::kMaxBatchRows;
+  while (b >= mqa::kFusedBlockRows && layout(b, d).total > kStaticScratchBytes)
+    b -= mqa::kFusedBlockRows;
+  return b >= mqa::kFusedBlockRows ? b : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t workspace_size(int rows, int device) {
+  if (rows < 1 || rows > MQA_MAX_ROWS) return 0;
+  const DeviceInfo* d = device_info(device);
+  if (!d) return 0;
+  return layout(batch_rows(rows), *d).total;
+}
+
+int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
+                     const float* weights, const int32_t* starts, const int32_t* ends,
+                     int32_t* out, int rows, int keys, int topk, void* workspace,
+                     size_t workspace_bytes, unsigned flags, void* stream) {
+  if (!q || !k || !scales || !weights || !starts || !ends || !out || !workspace)
+    return MQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scales, 16) || !aligned(weights, 16) ||
+      !aligned(out, 16) || !aligned(starts, 4) || !aligned(ends, 4) || !aligned(workspace, 256))
+    return MQA_ERR_ALIGN;
+  if (rows < 1 || rows > MQA_MAX_ROWS || keys < 1 || keys > MQA_MAX_KEYS || !topk_ok(topk))
+    return MQA_ERR_SHAPE;
+  const DeviceInfo* d = current_device();
+  if (!d) return MQA_ERR_DEVICE;
+  const int batch = batch_rows(rows);
+  if (workspace_bytes < layout(batch, *d).total) {
+    g_ws_err[0] = 0;
+    return MQA_ERR_WORKSPACE;
+  }
+  return prefill_batches(q, k, scales, weights, starts, ends, out, rows, keys, topk,
+                         static_cast<uint8_t*>(workspace), batch, *d, flags, stream);
+}
+
+int mqa_topk_prefill_static(const uint8_t* q, const uint8_t* k, const float* scales,
+                            const float* weights, const int32_t* starts, const int32_t* ends,
+                            int32_t* out, int rows, int keys, int topk, unsigned flags,
+                            void* stream) {
+  if (!q || !k || !scales || !weights || !starts || !ends || !out) return MQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scales, 16) || !aligned(weights, 16) ||
+      !aligned(out, 16) || !aligned(starts, 4) || !aligned(ends, 4))
+    return MQA_ERR_ALIGN;
+  if (rows < 1 || rows > MQA_MAX_ROWS || keys < 1 || keys > MQA_MAX_KEYS || !topk_ok(topk))
+    return MQA_ERR_SHAPE;
+  const DeviceInfo* d = current_device();
+  if (!d) return MQA_ERR_DEVICE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return MQA_ERR_DEVICE;
+  }
+  uint8_t* ws = static_scratch(dev);
+  if (!ws) return launch_error_text("hipGetSymbolAddress of the static scratch failed");
+  const int batch = static_batch(*d);
+  if (batch < 1)
+    return workspace_error_text("the static scratch cannot hold one 32-row batch on this device");
+  return prefill_batches(q, k, scales, weights, starts, ends, out, rows, keys, topk, ws, batch,
+                         *d, flags, stream);
 }
 
 int mqa_logits_dense(const uint8_t* q, const uint8_t* k, const float* scales,
@@ -363,7 +450,8 @@ const char* mqa_strerror(int code) {
     case MQA_ERR_NULL: return "a required pointer is NULL";
     case MQA_ERR_ALIGN: return "a pointer is not aligned as the contract requires";
     case MQA_ERR_SHAPE: return "a size or shape argument is outside the contract";
-    case MQA_ERR_WORKSPACE: return "the workspace is smaller than workspace_size(rows, device)";
+    case MQA_ERR_WORKSPACE:
+      return g_ws_err[0] ? g_ws_err : "the workspace is smaller than workspace_size(rows, device)";
     case MQA_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
     case MQA_ERR_LAUNCH: return g_err[0] ? g_err : "HIP launch failed";
     default: return "unknown error code";

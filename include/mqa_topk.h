@@ -137,6 +137,28 @@ int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
                      size_t workspace_bytes, unsigned flags, void* stream);
 
 /*
+ * mqa_topk_prefill without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, contract and results as mqa_topk_prefill; its scratch is a
+ * 384 MiB array in device memory that the library holds on each device it
+ * runs on until the process ends, so the rows run in batches that fit it
+ * (about 1600 rows per batch on a 256-CU device; a call over more rows runs
+ * the batches one after another on `stream`). Every call on a device uses the
+ * same scratch: calls that overlap on one device (other streams, other
+ * threads) race and must not be made. Nothing needs clearing before a call.
+ * MQA_FLAG_STATS writes its counters into that scratch, where the caller
+ * cannot read them. Returns MQA_OK, MQA_ERR_NULL, MQA_ERR_ALIGN,
+ * MQA_ERR_SHAPE, MQA_ERR_DEVICE, MQA_ERR_WORKSPACE (the scratch cannot hold
+ * one 32-row batch on this device) or MQA_ERR_LAUNCH (also when the
+ * scratch's device address cannot be looked up).
+ */
+int mqa_topk_prefill_static(const uint8_t* q, const uint8_t* k, const float* scales,
+                            const float* weights, const int32_t* starts, const int32_t* ends,
+                            int32_t* out, int rows, int keys, int topk, unsigned flags,
+                            void* stream);
+
+/*
  * Dense logits (the first half of the dense path the fused op replaces: PR
  * #60618, "Motivation"; API page, fused_mqa_topk_prefill names the
  * fp8_mqa_logits + top_k_per_row_prefill pair): writes

@@ -25,7 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    assert set(names) == {"workspace_size", "mqa_topk_prefill", "mqa_logits_dense",
+    assert set(names) == {"workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static",
+                          "mqa_logits_dense",
                           "mqa_topk_dense", "mqa_key_scales", "mqa_scan_time", "mqa_mfma_peak",
                           "mqa_fp8_mfma_probe",
                           "mqa_strerror"}
@@ -141,3 +142,69 @@ def test_device_error_without_gpu():
     v = ctypes.c_float(0.0)
     assert mqa.load().mqa_scan_time(1, ctypes.byref(v)) == 5
     assert _peak() == 5
+
+
+def _static(**kw):
+    a = dict(q=A16, k=A16, scales=A16, weights=A16, starts=A16, ends=A16, out=A16, rows=64,
+             keys=4096, topk=512, flags=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return mqa.load().mqa_topk_prefill_static(P(a["q"]), P(a["k"]), P(a["scales"]),
+                                              P(a["weights"]), P(a["starts"]), P(a["ends"]),
+                                              P(a["out"]), a["rows"], a["keys"], a["topk"],
+                                              a["flags"], None)
+
+
+def test_static_prefill_errors():
+    assert _static(q=0) == 1
+    assert _static(out=0) == 1
+    assert _static(weights=MIS) == 2
+    assert _static(ends=0x10002) == 2
+    assert _static(rows=0) == 3
+    assert _static(keys=(1 << 20) + 1) == 3
+    assert _static(topk=1000) == 3
+    if _no_gpu():
+        assert _static() == 5  # valid arguments, no device: nothing launched
+
+
+def test_fp8_probe_errors():
+    P = ctypes.c_void_p
+    L = mqa.load()
+    assert L.mqa_fp8_mfma_probe(None, P(A16), None, P(A16), 4, None) == 1
+    assert L.mqa_fp8_mfma_probe(P(MIS), P(A16), None, P(A16), 4, None) == 2
+    assert L.mqa_fp8_mfma_probe(P(A16), P(A16), None, P(A16), 0, None) == 3
+
+
+def test_binding_checks_every_shape_first():
+    # CPU tensors: a wrong shape is reported before the device is looked at,
+    # so these run without a GPU; the C ABI itself cannot see tensor sizes
+    import torch
+    rows, keys = 8, 600
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32)
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)
+    good = dict(q=u8(rows, 32, 128), k=u8(keys, 128), scales=f32(keys), weights=f32(rows, 32),
+                starts=i32(rows), ends=i32(rows))
+    bad = {"q": u8(rows, 16, 128), "k": u8(keys, 64), "scales": f32(keys - 1),
+           "weights": f32(rows, 31), "starts": i32(rows + 1), "ends": i32(rows - 1)}
+    for name, t in bad.items():
+        args = dict(good, **{name: t})
+        for fn in (mqa.mqa_topk_prefill, mqa.mqa_topk_prefill_static):
+            with pytest.raises(ValueError, match="shape"):
+                fn(args["q"], args["k"], args["scales"], args["weights"], args["starts"],
+                   args["ends"], 512)
+        with pytest.raises(ValueError, match="shape"):
+            mqa.mqa_logits_dense(args["q"], args["k"], args["scales"], args["weights"],
+                                 args["starts"], args["ends"])
+    with pytest.raises(ValueError, match="shape"):
+        mqa.mqa_topk_prefill(**good, topk=512, out=i32(rows, 511))
+    with pytest.raises(ValueError, match="shape"):
+        mqa.mqa_topk_dense(f32(rows, keys), i32(rows + 1), i32(rows), 512, keys)
+    with pytest.raises(ValueError, match="shape"):
+        mqa.mqa_topk_dense(f32(rows, keys), i32(rows), i32(rows), 512, keys, out=i32(rows, 4))
+    with pytest.raises(ValueError):
+        mqa.mqa_key_scales(u8(keys * 4))  # flat bytes, not [keys, 4]
+    with pytest.raises(ValueError, match="shape"):
+        mqa.mqa_key_scales(u8(keys, 3))
+    with pytest.raises(ValueError, match="shape"):
+        mqa.fp8_mfma_probe(u8(2, 16, 128), u8(3, 16, 128))
