@@ -16,7 +16,8 @@ Prints ONE JSON line (rank 0):
              current kernel sources, else null; measured_peak = the FP8 MFMA
              rate this GPU sustains on the scan's head-tile instruction (the
              mqa_mfma_peak probe, best of 3 launches) and measured_frac =
-             achieved / measured_peak;
+             achieved / measured_peak; call_frac = the whole call's FP8
+             fraction (8192 flop per visible pair over ms_per_step);
   timing   = per-call medians and minima of 10 single calls, warm and with a
              512 MiB buffer written before each call (flushed caches);
   cpu_baseline = the CPU oracle (exact logits + full sort) timed on this
@@ -76,7 +77,8 @@ def cpu_baseline(wl, target_s: float = 15.0):
 
     import oracle
 
-    threads = min(16, os.cpu_count() or 1)
+    host_cores = os.cpu_count() or 1
+    threads = min(16, host_cores)  # the GPU machine's share of the host is 16 threads
     p = oracle.Problem(wl.q, wl.k, oracle.key_scales(wl.scale_bytes), wl.weights, wl.starts,
                        wl.ends)
     rng = np.random.default_rng(1234)
@@ -99,9 +101,22 @@ def cpu_baseline(wl, target_s: float = 15.0):
     dt = time.perf_counter() - t0
     pairs = float((e[sample] - s[sample]).sum())
     return {"value": pairs / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
+            "host_cores": host_cores, "cpu_model": cpu_model(),
             "sample": f"{len(sample)} seeded random rows of the same workload "
                       f"({int(pairs)} visible pairs), exact logits + full sort per row, "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s on {threads} threads"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def per_call_times(step, stream, dev, n: int = 10):
@@ -341,8 +356,11 @@ def main():
         "config": {"workload": wl.name, "rows": wl.rows, "keys": wl.keys, "topk": wl.topk,
                    "visible_pairs": pairs, "parallelism": "1 GPU",
                    "ties": "lowest key, sorted output" if args.deterministic else "any"},
+        # the scan kernel's roofline (the dominant kernel); call_frac is the
+        # whole call's FP8 fraction (all launches, the metric's own figure)
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS,
+                     "call_frac": pairs * FLOP_PER_PAIR / (ms / 1e3) / 1e12 / FP8_PEAK_TFLOPS,
                      "traffic": traffic_from_counters(wl.name), "kernel": "fused_topk_kernel",
                      "kernel_ms": scan_ms, "measured_peak": measured_peak,
                      "measured_frac": achieved / measured_peak},

@@ -11,8 +11,8 @@
  * with q [rows,32,128] and k [keys,128] in OCP FP8 e4m3 (e4m3fn), scale_j the
  * fp32 decoded from a UE8M0 byte e as the bit pattern e << 23 (same page,
  * fused_mqa_topk_key_scales) and w [rows,32] fp32; then return each row's k
- * largest keys (k = 512, 1024 or 2048) as key - start_r, unordered, -1 padded
- * when fewer than k keys are visible.
+ * largest keys (k = 512, 1024 or 2048) as key - start_r, in no particular
+ * order, with -1 in the slots a row with fewer than k visible keys leaves.
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -72,8 +72,9 @@ extern "C" {
                                        bound */
 #define MQA_FLAG_DETERMINISTIC 64u  /* deterministic, batch-invariant selection (API
                                        page, use_fused_mqa_topk: batch-invariant serving
-                                       stays on the dense path there because the fused
-                                       op resolves k-th-score ties in atomic order): a
+                                       stays on the dense path there because which tied
+                                       k-th-score keys the fused op keeps depends on its
+                                       atomics' order): a
                                        row's output is the k keys of largest
                                        exact score, ties at the k-th score going to the
                                        smallest keys, listed in ascending key order

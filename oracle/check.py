@@ -4,13 +4,15 @@ Test infrastructure (same rules as the rest of ``oracle/``). The rules:
 
 (i)   validity, on every row: min(n, k) valid entries, distinct, inside
       [0, n), in the leading slots; the remaining k - min(n, k) slots hold -1
-      (the API page's fused_mqa_topk_prefill: indices are key - start,
-      unordered, -1 padded when fewer than k keys are visible).
+      (the API page's fused_mqa_topk_prefill: each index is the key minus
+      the row's start, in no particular order; rows with fewer than k
+      visible keys fill the unused slots with -1).
 (ii)  set rule, on rows with n > k: with tau the oracle's k-th largest logit
       and tol = rel_tol * max|logit| of the row, every selected key has logit
       >= tau - tol and every visible unselected key has logit <= tau + tol.
       This accepts any resolution of ties at the boundary (the API page's
-      use_fused_mqa_topk: ties at the k-th score are taken in atomic order).
+      use_fused_mqa_topk: which of several keys tied at the k-th score the
+      fused op keeps depends on the order of its atomic updates).
 (iii) dense logits: |gpu - oracle| <= tol on visible entries; -inf exactly
       where the oracle has -inf.
 """

@@ -9,8 +9,9 @@
 //   * vLLM API page "fused_mqa_topk", function fused_mqa_topk_prefill:
 //     q [rows,32,128] e4m3, k [keys,128] e4m3, scales [keys] fp32,
 //     weights [rows,32] fp32, starts/ends [rows] int32 giving the visible key
-//     range [start, end) of each row; output [rows,k] int32 holding
-//     key - start, unordered, -1 padded when fewer than k keys are visible.
+//     range [start, end) of each row; output [rows,k] int32 holding each
+//     selected key minus the row's start, in no particular order, with -1 in
+//     the slots left over when the row sees fewer than k keys.
 //   * same page, function fused_mqa_topk_key_scales: a UE8M0 scale byte e
 //     decodes to the fp32 whose bit pattern is e << 23.
 //   * vLLM PR #60618, "What this PR does" (Scoring): 32 index heads, each
@@ -29,8 +30,8 @@
 //     once to fp32.
 //   * Top-k: a full sort of the row by (logit descending, key ascending); the
 //     first k keys are the answer. Ties at the k-th score make several answers
-//     correct (the API page's use_fused_mqa_topk notes that ties at the k-th
-//     score are taken in atomic order); this order is one of them.
+//     correct (the API page's use_fused_mqa_topk: the fused op keeps whichever
+//     tied keys its atomic updates reach first); this order is one of them.
 //
 // Pins (tests/test_oracle_pins.py): all 256 e4m3 codes against their closed
 // form and a library decoder, UE8M0 spot values, a hand-worked 4-key example,
