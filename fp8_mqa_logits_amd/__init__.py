@@ -30,7 +30,8 @@ FLAG_DETERMINISTIC = 64
 ERR_NAMES = {0: "MQA_OK", 1: "MQA_ERR_NULL", 2: "MQA_ERR_ALIGN", 3: "MQA_ERR_SHAPE",
              4: "MQA_ERR_WORKSPACE", 5: "MQA_ERR_DEVICE", 6: "MQA_ERR_LAUNCH"}
 
-EXPORTS = ("workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static", "mqa_logits_dense",
+EXPORTS = ("workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static",
+           "mqa_topk_prefill_paged", "mqa_logits_dense",
            "mqa_topk_dense",
            "mqa_key_scales", "mqa_scan_time", "mqa_mfma_peak", "mqa_fp8_mfma_probe",
            "mqa_strerror")
@@ -65,6 +66,8 @@ def load() -> ctypes.CDLL:
         lib.mqa_topk_prefill.restype = I
         lib.mqa_topk_prefill_static.argtypes = [P, P, P, P, P, P, P, I, I, I, U, P]
         lib.mqa_topk_prefill_static.restype = I
+        lib.mqa_topk_prefill_paged.argtypes = [P, P, P, I, I, P, P, P, P, I, I, I, P, SZ, U, P]
+        lib.mqa_topk_prefill_paged.restype = I
         lib.mqa_logits_dense.argtypes = [P, P, P, P, P, P, P, I64, I, I, I, I, P]
         lib.mqa_logits_dense.restype = I
         lib.mqa_topk_dense.argtypes = [P, I64, I, I, P, P, P, I, I, I, P]
@@ -216,6 +219,62 @@ def mqa_topk_prefill_static(q, k, scales, weights, starts, ends, topk: int, out=
                                             _ptr(starts), _ptr(ends), _ptr(out), rows, keys,
                                             int(topk), int(flags), _stream(dev, stream))
     _check(rc, "mqa_topk_prefill_static")
+    return out
+
+
+PAGE_ENTRY = HEAD_DIM + 4  # bytes per token in the paged indexer cache
+
+
+def mqa_topk_prefill_paged(q, cache, block_table, page_size: int, keys: int, weights, starts,
+                           ends, topk: int, out=None, workspace=None, flags: int = 0,
+                           stream=None) -> torch.Tensor:
+    """mqa_topk_prefill reading the keys from the paged indexer cache: cache
+    [num_pages, page_size * 132] uint8 (per page: the e4m3 key rows, then the
+    four UE8M0 bytes of each key), block_table [>= ceil(keys / page_size)]
+    int32 (page of each run of page_size keys). Same result as
+    mqa_topk_prefill on the gathered keys and decoded scales."""
+    _tensors(q=q, cache=cache, block_table=block_table, weights=weights, starts=starts,
+             ends=ends)
+    if q.dim() != 3:
+        raise ValueError("q must be [rows,32,128]")
+    rows = q.shape[0]
+    page_size, keys = int(page_size), int(keys)
+    if page_size < 4 or page_size & (page_size - 1):
+        raise ValueError("page_size must be a power of two >= 4")
+    if keys < 1 or keys > MAX_KEYS:
+        raise ValueError(f"keys must be in [1, {MAX_KEYS}]")
+    if cache.dim() != 2:
+        raise ValueError("cache must be [num_pages, page_size * 132]")
+    num_pages = cache.shape[0]
+    _shape(cache, (num_pages, page_size * PAGE_ENTRY), "cache")
+    if block_table.dim() != 1 or block_table.shape[0] < -(-keys // page_size):
+        raise ValueError(f"block_table must be 1-D with >= {-(-keys // page_size)} entries")
+    _shape(q, (rows, HEADS, HEAD_DIM), "q")
+    _shape(weights, (rows, HEADS), "weights")
+    _shape(starts, (rows,), "starts")
+    _shape(ends, (rows,), "ends")
+    if out is not None:
+        _tensors(out=out)
+        _shape(out, (rows, topk), "out")
+    dev = q.device
+    _need(q, "q", FP8, dev)
+    _need(cache, "cache", (torch.uint8,), dev)
+    _need(block_table, "block_table", (torch.int32,), dev)
+    _need(weights, "weights", (torch.float32,), dev)
+    _need(starts, "starts", (torch.int32,), dev)
+    _need(ends, "ends", (torch.int32,), dev)
+    if out is None:
+        out = torch.empty((rows, topk), dtype=torch.int32, device=dev)
+    _need(out, "out", (torch.int32,), dev)
+    if workspace is None:
+        workspace = alloc_workspace(rows, dev.index)
+    _need(workspace, "workspace", (torch.uint8,), dev)
+    with torch.cuda.device(dev):
+        rc = load().mqa_topk_prefill_paged(_ptr(q), _ptr(cache), _ptr(block_table), page_size,
+                                           num_pages, _ptr(weights), _ptr(starts), _ptr(ends),
+                                           _ptr(out), rows, keys, int(topk), _ptr(workspace),
+                                           workspace.numel(), int(flags), _stream(dev, stream))
+    _check(rc, "mqa_topk_prefill_paged")
     return out
 
 

@@ -181,12 +181,20 @@ bool ring_slot(int device, hipEvent_t* b, hipEvent_t* e) {
   return true;
 }
 
+// Where the keys come from: the dense k / scales arrays (table == nullptr) or
+// the paged indexer cache k with its page table.
+struct KeySource {
+  const int32_t* table = nullptr;
+  int page_shift = 0, num_pages = 0;
+};
+
 // Rows in batches of `batch` rows, one launch sequence each, in order on the
 // stream (they share the workspace ws, which holds layout(batch)).
 int prefill_batches(const uint8_t* q, const uint8_t* k, const float* scales,
                     const float* weights, const int32_t* starts, const int32_t* ends,
                     int32_t* out, int rows, int keys, int topk, uint8_t* ws, int batch,
-                    const DeviceInfo& d, unsigned flags, void* stream) {
+                    const DeviceInfo& d, unsigned flags, void* stream,
+                    const KeySource& src = KeySource()) {
   const Layout L = layout(batch, d);
   hipEvent_t eb = nullptr, ee = nullptr;
   if (flags & MQA_FLAG_TIME_SCAN) {
@@ -226,6 +234,10 @@ int prefill_batches(const uint8_t* q, const uint8_t* k, const float* scales,
     p.slabI = reinterpret_cast<int32_t*>(ws + L.slabI);
     p.tmpE = reinterpret_cast<float*>(ws + L.tmpE);
     p.tmpI = reinterpret_cast<int32_t*>(ws + L.tmpI);
+    p.table = src.table;
+    p.page_shift = src.page_shift;
+    p.num_pages = src.num_pages;
+    p.page_bytes = (int64_t)(MQA_HEAD_DIM + 4) << src.page_shift;
     const int grid = L.grid < p.nblocks ? L.grid : p.nblocks;
     p.nseg = key_segments(p.nblocks, L.grid, topk);
     p.scan_grid = L.grid < p.nblocks * p.nseg ? L.grid : p.nblocks * p.nseg;
@@ -345,6 +357,37 @@ int mqa_topk_prefill_static(const uint8_t* q, const uint8_t* k, const float* sca
     return workspace_error_text("the static scratch cannot hold one 32-row batch on this device");
   return prefill_batches(q, k, scales, weights, starts, ends, out, rows, keys, topk, ws, batch,
                          *d, flags, stream);
+}
+
+int mqa_topk_prefill_paged(const uint8_t* q, const uint8_t* cache, const int32_t* block_table,
+                           int page_size, int num_pages, const float* weights,
+                           const int32_t* starts, const int32_t* ends, int32_t* out, int rows,
+                           int keys, int topk, void* workspace, size_t workspace_bytes,
+                           unsigned flags, void* stream) {
+  if (!q || !cache || !block_table || !weights || !starts || !ends || !out || !workspace)
+    return MQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(block_table, 4) ||
+      !aligned(weights, 16) || !aligned(out, 16) || !aligned(starts, 4) || !aligned(ends, 4) ||
+      !aligned(workspace, 256))
+    return MQA_ERR_ALIGN;
+  int shift = 0;
+  while (shift < 20 && (1 << shift) < page_size) ++shift;
+  if (rows < 1 || rows > MQA_MAX_ROWS || keys < 1 || keys > MQA_MAX_KEYS || !topk_ok(topk) ||
+      page_size < 4 || page_size > MQA_MAX_KEYS || (1 << shift) != page_size || num_pages < 1)
+    return MQA_ERR_SHAPE;
+  const DeviceInfo* d = current_device();
+  if (!d) return MQA_ERR_DEVICE;
+  const int batch = batch_rows(rows);
+  if (workspace_bytes < layout(batch, *d).total) {
+    g_ws_err[0] = 0;
+    return MQA_ERR_WORKSPACE;
+  }
+  KeySource src;
+  src.table = block_table;
+  src.page_shift = shift;
+  src.num_pages = num_pages;
+  return prefill_batches(q, cache, nullptr, weights, starts, ends, out, rows, keys, topk,
+                         static_cast<uint8_t*>(workspace), batch, *d, flags, stream, src);
 }
 
 int mqa_logits_dense(const uint8_t* q, const uint8_t* k, const float* scales,

@@ -102,6 +102,60 @@ __device__ __forceinline__ void row_range(const FusedParams& p, int r, int& s, i
 }
 
 // ---------------------------------------------------------------------------
+// Key addressing. The keys' e4m3 codes come from the dense k array or from
+// the paged indexer cache (vLLM PR #60618, "Motivation": 132 B per token, the
+// 128-byte e4m3 key and its four-byte UE8M0 scale); each kernel that reads
+// key bytes has an instance per source, so the dense one compiles as if the
+// pages did not exist.
+template <bool PAGED>
+__device__ __forceinline__ const uint8_t* key_row(const FusedParams& p, int key) {
+  if constexpr (!PAGED) {
+    return p.k + (int64_t)key * kDim;
+  } else {
+    int pg = p.table[key >> p.page_shift];
+    pg = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
+    return p.k + (int64_t)pg * p.page_bytes + (int64_t)(key & ((1 << p.page_shift) - 1)) * kDim;
+  }
+}
+
+// The scale of key `key` (UE8M0 decoded, fused: the low byte e of the paged
+// cache's scale word is the fp32 with bit pattern e << 23, API page
+// "fused_mqa_topk", fused_mqa_topk_key_scales; e = 0 gives +0.0).
+template <bool PAGED>
+__device__ __forceinline__ float key_scale(const FusedParams& p, int key) {
+  if constexpr (!PAGED) {
+    return p.scales[key];
+  } else {
+    int pg = p.table[key >> p.page_shift];
+    pg = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
+    const int P = 1 << p.page_shift;
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(
+        p.k + (int64_t)pg * p.page_bytes + (int64_t)P * kDim + 4 * (int64_t)(key & (P - 1)));
+    return __uint_as_float((w & 0xFFu) << 23);
+  }
+}
+
+// B operands of up to 64 arbitrary keys (lane l: key keyidx[t] of sub-tile t,
+// bytes 32 * (l / 16) ..), from either source.
+template <bool PAGED>
+__device__ __forceinline__ void load_keys_rows(KeyTile& kt, const FusedParams& p,
+                                               const int* keyidx) {
+  if constexpr (!PAGED) {
+    load_keys_gather(kt, p.k, keyidx);
+  } else {
+    const int g = lane_id() >> 4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint8_t* r = key_row<true>(p, keyidx[t]) + 32 * g;
+      const uint4 x0 = *reinterpret_cast<const uint4*>(r);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(r + 16);
+      kt.kb[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // FP8 score error bounds.
 //
 // The FP8 MFMA (16x16x128; measured on gfx950) splits a 128-term dot product
@@ -167,6 +221,7 @@ __device__ __forceinline__ float key_nhat(float x, float scale) {
 constexpr int kMaxBlocks = kMaxBatchRows / kBlockRows;
 constexpr int kPrologueThreads = 1024;
 
+template <bool PAGED>
 __device__ __forceinline__ void prologue_bounds(const FusedParams& p) {
   const int l = lane_id();
   const int nwaves = (gridDim.x - 1) * (kPrologueThreads / kWave);
@@ -179,13 +234,13 @@ __device__ __forceinline__ void prologue_bounds(const FusedParams& p) {
       const int key = 4 * u + (l >> 4);
       float x = 0.f;
       if (key < p.keys) {
-        const uint2 v = *reinterpret_cast<const uint2*>(p.k + (int64_t)key * kDim + 8 * g);
+        const uint2 v = *reinterpret_cast<const uint2*>(key_row<PAGED>(p, key) + 8 * g);
         x = xhat8(v.x, v.y);
       }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
       if (g == 0 && key < p.keys) {
-        const float sc = p.scales[key];
+        const float sc = key_scale<PAGED>(p, key);
         *reinterpret_cast<float2*>(p.keyinfo + 2 * (int64_t)key) = float2{sc, key_nhat(x, sc)};
       }
     } else {
@@ -224,12 +279,13 @@ __device__ __forceinline__ void prologue_bounds(const FusedParams& p) {
   }
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(kPrologueThreads) void fused_prologue_kernel(FusedParams p) {
   __shared__ int cnt[1024];
   __shared__ int off[1024];
   __shared__ int blo[kMaxBlocks], bhi[kMaxBlocks];
   if (blockIdx.x > 0) {
-    prologue_bounds(p);
+    prologue_bounds<PAGED>(p);
     return;
   }
   const int tid = threadIdx.x;
@@ -515,6 +571,7 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
 // Slot p of the buffer (16 bytes) holds key j = p / 8, column slice (p % 8) ^
 // swz(j); each wave fills 64 consecutive slots per copy. The copies are
 // waited for by the barrier that ends the stage before the buffer is read.
+template <bool PAGED>
 __device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, int stride,
                                           uint8_t* kdst, float* sdst, int tid) {
   // threads [0, kStageKeys): scales; [kStageKeys, 2 kStageKeys): nhat (the
@@ -538,8 +595,8 @@ __device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, int st
     const int c = (slot & 7) ^ swz(j);
     int key = key0 + j * stride;
     key = key < p.keys ? key : p.keys - 1;
-    __builtin_amdgcn_global_load_lds(p.k + (int64_t)key * kDim + 16 * c, kdst + 16 * (slot & ~63),
-                                     16, 0, 0);
+    const uint8_t* src = key_row<PAGED>(p, key) + 16 * c;
+    __builtin_amdgcn_global_load_lds(src, kdst + 16 * (slot & ~63), 16, 0, 0);
   }
 }
 
@@ -569,7 +626,7 @@ __device__ __forceinline__ void score4(float E[4], const QueryRow* qr, const Fol
 // before the epilogue of the current one. Chunks that every live row of the
 // wave covers entirely (almost all of them) take a path with no per-row range
 // tests: rows that are not live have an admission threshold of +inf there.
-template <bool EXACT>
+template <bool EXACT, bool PAGED>
 __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& stg, const QueryRow* qr,
                                           const FoldOp& fo, RowState* rs, int mode, int lo,
                                           int hi, const SlabRefs& sr) {
@@ -660,7 +717,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
   // last readers passed the previous barrier), then score this one.
   auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext,
                    float* snext) {
-    if (st + 1 < nst) dma_stage(p, lo + (st + 1) * kStageKeys, 1, knext, snext, tid);
+    if (st + 1 < nst) dma_stage<PAGED>(p, lo + (st + 1) * kStageKeys, 1, knext, snext, tid);
 #pragma unroll
     for (int u = 0; u < kStageChunks; ++u) {
       const int c = st * kStageChunks + u;
@@ -668,7 +725,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
     }
     __syncthreads();
   };
-  dma_stage(p, lo, 1, stg.k[0], stg.s[0], tid);
+  dma_stage<PAGED>(p, lo, 1, stg.k[0], stg.s[0], tid);
   __syncthreads();
   for (int st = 0; st < nst; st += 2) {
     stage(st, stg.k[0], stg.s[0], stg.k[1], stg.s[1]);
@@ -699,6 +756,7 @@ struct __align__(16) GateSmem {
   int wlo[kWaves], whi[kWaves], wf[kWaves];
 };
 
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
   __shared__ GateSmem sm;
   MQA_DECLARE_STAGES(stg);
@@ -828,13 +886,13 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
       auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext,
                        float* snext) {
         if (st + 1 < nst)
-          dma_stage(p, lo + (st + 1) * kStageKeys * stride, stride, knext, snext, tid);
+          dma_stage<PAGED>(p, lo + (st + 1) * kStageKeys * stride, stride, knext, snext, tid);
 #pragma unroll
         for (int u = 0; u < kStageChunks; ++u)
           chunk(st * kStageChunks + u, kcur + u * kChunkBytes, scur + u * kChunk);
         __syncthreads();
       };
-      dma_stage(p, lo, stride, stg.k[0], stg.s[0], tid);
+      dma_stage<PAGED>(p, lo, stride, stg.k[0], stg.s[0], tid);
       __syncthreads();
       for (int st = 0; st < nst; st += 2) {
         stage(st, stg.k[0], stg.s[0], stg.k[1], stg.s[1]);
@@ -951,6 +1009,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
 // threshold goes into the first fine bin that completes the row's count, with
 // the gate's gap rule (down to the next sampled score). Returns at
 // once when nothing is queued.
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
   __shared__ GateSmem sm;
   MQA_DECLARE_STAGES(stg);
@@ -1032,13 +1091,13 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
       auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext,
                        float* snext) {
         if (st + 1 < nst)
-          dma_stage(p, lo + (st + 1) * kStageKeys * stride, stride, knext, snext, tid);
+          dma_stage<PAGED>(p, lo + (st + 1) * kStageKeys * stride, stride, knext, snext, tid);
 #pragma unroll
         for (int u = 0; u < kStageChunks; ++u)
           chunk(st * kStageChunks + u, kcur + u * kChunkBytes, scur + u * kChunk);
         __syncthreads();
       };
-      dma_stage(p, lo, stride, stg.k[0], stg.s[0], tid);
+      dma_stage<PAGED>(p, lo, stride, stg.k[0], stg.s[0], tid);
       __syncthreads();
       for (int st = 0; st < nst; st += 2) {
         stage(st, stg.k[0], stg.s[0], stg.k[1], stg.s[1]);
@@ -1096,7 +1155,7 @@ struct __align__(16) ScanSmem {
 
 // SPLIT: the launch uses key segments (p.nseg > 1); the instance without
 // them keeps no segment state.
-template <bool SPLIT>
+template <bool SPLIT, bool PAGED>
 __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
   __shared__ ScanSmem sm;
   MQA_DECLARE_STAGES(stg);
@@ -1148,7 +1207,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
       FoldOp fo;
       build_fold(fo, p.q, p.weights, frows);
       const SlabRefs sr = slab_refs(p, b, sm.hist[w], 2 * p.topk, SPLIT ? seg : -1);
-      scan_rows<false>(p, stg, qr, fo, rs, M_GATED, lo, hi, sr);
+      scan_rows<false, PAGED>(p, stg, qr, fo, rs, M_GATED, lo, hi, sr);
     }
     if (l == 0) {
 #pragma unroll
@@ -1188,7 +1247,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
 // row's k-th exact score (the k records found score at least min(tau, the
 // lowest taken interval); more than k taken records bound it by t_hi), or
 // -inf.
-template <class Emit>
+template <bool PAGED, class Emit>
 __device__ bool select_interval(const FusedParams& p, float* sE, int32_t* sI, int n, int k,
                                 float beta, float Thi, bool thi_lt, float hint_lo, float hint_hi,
                                 const QueryRow& qr, uint32_t* hist, float& low, Emit emit) {
@@ -1344,12 +1403,12 @@ __device__ bool select_interval(const FusedParams& p, float* sE, int32_t* sI, in
       ki[t] = sI[j < nb ? j : nb - 1] & (int)kKeyMask;
     }
     const int j = b0 + l;
-    s_ = p.scales[sI[j < nb ? j : nb - 1] & (int)kKeyMask];
+    s_ = p.keyinfo[2 * (int64_t)(sI[j < nb ? j : nb - 1] & (int)kKeyMask)];
   };
   group_refs(0, keyidx, sc);
   for (int b0 = 0; b0 < nb; b0 += kWave) {
     KeyTile kt;
-    load_keys_gather(kt, p.k, keyidx);
+    load_keys_rows<PAGED>(kt, p, keyidx);
     int kn[4] = {0, 0, 0, 0};
     float scn = 0.f;
     if (b0 + kWave < nb) group_refs(b0 + kWave, kn, scn);
@@ -1415,6 +1474,7 @@ __device__ __forceinline__ void queue_rescan(const FusedParams& p, int r, float 
 }
 
 // Select: one wave per row.
+template <bool PAGED>
 __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_eu(4))) void fused_select_kernel(FusedParams p) {
   __shared__ uint32_t hist[kSelWaves][kHistWords];
   const int w = wave_id();
@@ -1473,7 +1533,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_
         hlo = ri.thr;
         hhi = m0 + (m0 - ri.thr);
       }
-      ok = select_interval(p, sE, sI, cnt, k, p.beta[r], thi, thi_lt, hlo, hhi, qr, hist[w], low,
+      ok = select_interval<PAGED>(p, sE, sI, cnt, k, p.beta[r], thi, thi_lt, hlo, hhi, qr, hist[w], low,
                            [&](int sl, int idx) { o[sl] = idx - s; });
       if (stats && l == 0) {
         atomicAdd(&p.header[ok ? H_GATED : H_UNCERT], 1u);
@@ -1501,6 +1561,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_
 // scoring >= the row's bound (> in a strict round) get slab slots from the
 // row's counter (slots past the slab are counted, not written), and the keys
 // strictly above it are counted apart.
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, int round) {
   const int l = lane_id();
   const int nq = (int)p.header[H_RQ + 2 * round];
@@ -1534,10 +1595,10 @@ __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, i
         keyidx[t] = j < b ? j : b - 1;
       }
       KeyTile kt;
-      load_keys_gather(kt, p.k, keyidx);
+      load_keys_rows<PAGED>(kt, p, keyidx);
       const int key = k0 + l;
       const bool valid = key < b;
-      const float E = score_chunk_exact(qr, kt) * p.scales[valid ? key : b - 1];
+      const float E = score_chunk_exact(qr, kt) * p.keyinfo[2 * (int64_t)(valid ? key : b - 1)];
       const bool pass = valid && (strict ? E > low : E >= low);
       const uint64_t m = __ballot(pass);
       if (m == 0) continue;
@@ -1639,6 +1700,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_finish_kernel(FusedPa
 // ---------------------------------------------------------------------------
 // Exact rescan of the queued blocks: exact (bf16 MFMA) scores of every key of
 // the flagged rows with a streaming top-k merge, then an exact select.
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
   __shared__ ScanSmem sm;
   MQA_DECLARE_STAGES(stg);
@@ -1672,7 +1734,7 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
     if (hi > lo) {
       SlabRefs sr = slab_refs(p, b, sm.hist[w], k);
       FoldOp none;
-      scan_rows<true>(p, stg, qr, none, rs, M_EXACT, lo, hi, sr);
+      scan_rows<true, PAGED>(p, stg, qr, none, rs, M_EXACT, lo, hi, sr);
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         RowState& r = rs[i];
@@ -1768,65 +1830,81 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_sort_kernel(FusedPara
 
 }  // namespace mqa
 
-extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t stream,
-                                hipEvent_t scan_begin, hipEvent_t scan_end) {
+namespace mqa {
+
+// The launch sequence of one row batch, over one key source.
+template <bool PAGED>
+int fused_launch_all(const FusedParams* p, int grid, hipStream_t stream, hipEvent_t scan_begin,
+                     hipEvent_t scan_end) {
   hipError_t e;
   // workgroup 0 plans; the others (about one per CU, at most the units of
   // bound work) compute the error bounds
   const int units = (p->keys + 3) / 4 + p->rows;
-  const int waves_per_wg = mqa::kPrologueThreads / mqa::kWave;
+  const int waves_per_wg = kPrologueThreads / kWave;
   int bwg = (units + waves_per_wg - 1) / waves_per_wg;
   bwg = bwg < grid ? bwg : grid;
   bwg = bwg < 1 ? 1 : bwg;
-  hipLaunchKernelGGL(mqa::fused_prologue_kernel, dim3(1 + bwg), dim3(mqa::kPrologueThreads), 0,
+  hipLaunchKernelGGL(fused_prologue_kernel<PAGED>, dim3(1 + bwg), dim3(kPrologueThreads), 0,
                      stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(mqa::fused_gate_kernel, dim3(p->scan_grid), dim3(mqa::kThreads), 0, stream,
-                     *p);
+  hipLaunchKernelGGL(fused_gate_kernel<PAGED>, dim3(p->scan_grid), dim3(kThreads), 0, stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(mqa::fused_refine_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
+  hipLaunchKernelGGL(fused_refine_kernel<PAGED>, dim3(grid), dim3(kThreads), 0, stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (scan_begin && (e = hipEventRecord(scan_begin, stream)) != hipSuccess) return (int)e;
   if (p->nseg > 1)
-    hipLaunchKernelGGL(mqa::fused_topk_kernel<true>, dim3(p->scan_grid), dim3(mqa::kThreads), 0,
+    hipLaunchKernelGGL((fused_topk_kernel<true, PAGED>), dim3(p->scan_grid), dim3(kThreads), 0,
                        stream, *p);
   else
-    hipLaunchKernelGGL(mqa::fused_topk_kernel<false>, dim3(p->scan_grid), dim3(mqa::kThreads), 0,
+    hipLaunchKernelGGL((fused_topk_kernel<false, PAGED>), dim3(p->scan_grid), dim3(kThreads), 0,
                        stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (scan_end && (e = hipEventRecord(scan_end, stream)) != hipSuccess) return (int)e;
-  const int sel = (p->rows + mqa::kSelWaves - 1) / mqa::kSelWaves;
-  hipLaunchKernelGGL(mqa::fused_select_kernel, dim3(sel), dim3(mqa::kSelWaves * mqa::kWave), 0,
-                     stream, *p);
+  const int sel = (p->rows + kSelWaves - 1) / kSelWaves;
+  hipLaunchKernelGGL(fused_select_kernel<PAGED>, dim3(sel), dim3(kSelWaves * kWave), 0, stream,
+                     *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   const int fin = sel < 256 ? sel : 256;
-  for (int round = 0; round < mqa::kRescanRounds; ++round) {
-    hipLaunchKernelGGL(mqa::fused_rescan_kernel, dim3(2 * grid), dim3(mqa::kThreads), 0, stream,
-                       *p, round);
+  for (int round = 0; round < kRescanRounds; ++round) {
+    hipLaunchKernelGGL(fused_rescan_kernel<PAGED>, dim3(2 * grid), dim3(kThreads), 0, stream, *p,
+                       round);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-    hipLaunchKernelGGL(mqa::fused_finish_kernel, dim3(fin), dim3(mqa::kSelWaves * mqa::kWave), 0,
-                       stream, *p, round);
+    hipLaunchKernelGGL(fused_finish_kernel, dim3(fin), dim3(kSelWaves * kWave), 0, stream, *p,
+                       round);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
-  hipLaunchKernelGGL(mqa::fused_exact_kernel, dim3(grid), dim3(mqa::kThreads), 0, stream, *p);
+  hipLaunchKernelGGL(fused_exact_kernel<PAGED>, dim3(grid), dim3(kThreads), 0, stream, *p);
   if (p->flags & 64u) {
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-    hipLaunchKernelGGL(mqa::fused_sort_kernel, dim3(sel), dim3(mqa::kSelWaves * mqa::kWave), 0,
-                       stream, *p);
+    hipLaunchKernelGGL(fused_sort_kernel, dim3(sel), dim3(kSelWaves * kWave), 0, stream, *p);
   }
   return (int)hipGetLastError();
 }
 
+}  // namespace mqa
+
+extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t stream,
+                                hipEvent_t scan_begin, hipEvent_t scan_end) {
+  return p->table ? mqa::fused_launch_all<true>(p, grid, stream, scan_begin, scan_end)
+                  : mqa::fused_launch_all<false>(p, grid, stream, scan_begin, scan_end);
+}
+
 extern "C" int mqa_fused_occupancy(int* wg_per_cu) {
-  int a = 0, b = 0, c = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, mqa::fused_topk_kernel<false>,
-                                                              mqa::kThreads, 0);
-  if (e != hipSuccess) return (int)e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, mqa::fused_exact_kernel, mqa::kThreads, 0);
-  if (e != hipSuccess) return (int)e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, mqa::fused_gate_kernel, mqa::kThreads, 0);
-  if (e != hipSuccess) return (int)e;
-  a = a < b ? a : b;
-  *wg_per_cu = a < c ? a : c;
+  // the persistent kernels' workgroups per CU, over both key sources
+  const void* kernels[] = {
+      reinterpret_cast<const void*>(mqa::fused_topk_kernel<false, false>),
+      reinterpret_cast<const void*>(mqa::fused_topk_kernel<false, true>),
+      reinterpret_cast<const void*>(mqa::fused_exact_kernel<false>),
+      reinterpret_cast<const void*>(mqa::fused_exact_kernel<true>),
+      reinterpret_cast<const void*>(mqa::fused_gate_kernel<false>),
+      reinterpret_cast<const void*>(mqa::fused_gate_kernel<true>)};
+  int best = 1 << 30;
+  for (const void* f : kernels) {
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, mqa::kThreads, 0);
+    if (e != hipSuccess) return (int)e;
+    best = n < best ? n : best;
+  }
+  *wg_per_cu = best;
   return 0;
 }

@@ -38,7 +38,7 @@ struct RefineInfo {
 
 struct FusedParams {
   const uint8_t* q;
-  const uint8_t* k;
+  const uint8_t* k;  // [keys][128] e4m3; with a page table: the paged indexer cache
   const float* scales;
   const float* weights;
   const int32_t* starts;
@@ -69,6 +69,14 @@ struct FusedParams {
   // candidate record's key word.
   float* keyinfo;    // [keys][2]
   float* beta;       // [rows]
+  // Paged indexer cache (table != nullptr): key j lives in page
+  // table[j >> page_shift] of k (clamped to [0, num_pages)), slot
+  // j & (2^page_shift - 1); a page of P = 2^page_shift tokens holds their
+  // P x 128 e4m3 codes, then their P 4-byte UE8M0 scale words
+  // (page_bytes = 132 P). scales is unused then.
+  const int32_t* table;
+  int page_shift, num_pages;
+  int64_t page_bytes;
   float* slabE;      // [nblocks * 32 rows][kSlabRow] candidate scores
   int32_t* slabI;    // [nblocks * 32 rows][kSlabRow] candidate keys
   float* tmpE;       // [grid][8 waves][kTmp] merge buffers

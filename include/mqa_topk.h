@@ -160,6 +160,35 @@ int mqa_topk_prefill_static(const uint8_t* q, const uint8_t* k, const float* sca
                             void* stream);
 
 /*
+ * The fused path reading the keys straight from the paged indexer K-cache, the
+ * UE8M0 decode fused (PR #60618, "Motivation": an indexer cache entry is 132 B
+ * per token, a 128-byte e4m3 key and a 4-byte scale; API page,
+ * fused_mqa_topk_key_scales, for the scale word). Key j of the call (the same
+ * key numbering as mqa_topk_prefill's k, which starts/ends and the output refer
+ * to) is slot j % page_size of page block_table[j / page_size].
+ *   cache        [num_pages][page_size * 132] bytes, 16-B aligned: page p holds
+ *                its page_size keys' e4m3 rows ([page_size][128]), then their
+ *                scale words ([page_size][4] bytes, four equal UE8M0 bytes e;
+ *                the scale is the fp32 with bit pattern (e & 0xFF) << 23; e =
+ *                255, which decodes to +inf, is outside the contract)
+ *   block_table  [ceil(keys / page_size)] int32, 4-B aligned; an entry outside
+ *                [0, num_pages) is clamped into it (the call's result is then
+ *                unspecified, but nothing reads outside the cache)
+ *   page_size    a power of two in [4, MQA_MAX_KEYS]; num_pages >= 1
+ * Several requests share one call as with mqa_topk_prefill: the caller lays
+ * their keys out in the key numbering (each request's first key at a
+ * multiple of page_size, its pages in its table order) and gives every row
+ * its request's range. Workspace, flags, output and return codes as for
+ * mqa_topk_prefill, whose results it reproduces on the gathered keys and
+ * decoded scales (bit for bit under MQA_FLAG_DETERMINISTIC).
+ */
+int mqa_topk_prefill_paged(const uint8_t* q, const uint8_t* cache, const int32_t* block_table,
+                           int page_size, int num_pages, const float* weights,
+                           const int32_t* starts, const int32_t* ends, int32_t* out, int rows,
+                           int keys, int topk, void* workspace, size_t workspace_bytes,
+                           unsigned flags, void* stream);
+
+/*
  * Dense logits (the first half of the dense path the fused op replaces: PR
  * #60618, "Motivation"; API page, fused_mqa_topk_prefill names the
  * fp8_mqa_logits + top_k_per_row_prefill pair): writes

@@ -359,6 +359,29 @@ def custom(rows: int, keys: int, topk: int, starts, ends, seed: int = 1,
                     np.asarray(starts, np.int32).copy(), np.asarray(ends, np.int32).copy(), seed)
 
 
+def paged_cache(k: np.ndarray, scale_bytes: np.ndarray, page_size: int, seed: int = 3,
+                spare_pages: int = 3):
+    """Lay keys out in a paged indexer cache: each page holds page_size
+    key rows (128 e4m3 bytes each), then their four scale bytes each. The
+    pages of consecutive key runs go to a seeded random permutation of
+    ceil(keys / page_size) + spare_pages pages; spare pages and unused slots
+    are filled with random bytes. Returns (cache [pages, 132 * page_size]
+    uint8, table [ceil(keys / page_size)] int32)."""
+    keys = k.shape[0]
+    used = -(-keys // page_size)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pages = used + spare_pages
+    cache = rng.integers(0, 256, (pages, page_size * (DIM + 4)), dtype=np.uint8)
+    table = rng.permutation(pages)[:used].astype(np.int32)
+    for i in range(used):
+        lo, hi = i * page_size, min(keys, (i + 1) * page_size)
+        n = hi - lo
+        page = cache[table[i]]
+        page[: n * DIM] = k[lo:hi].reshape(-1)
+        page[page_size * DIM: page_size * DIM + 4 * n] = scale_bytes[lo:hi].reshape(-1)
+    return cache, table
+
+
 def sample_rows(wl: Workload, n: int = 256, seed: int = 7) -> np.ndarray:
     """Seeded row sample for oracle checks of large workloads. With groups
     (config 5) it is stratified: half uniform over ungrouped rows, the rest

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert set(names) == {"workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static",
-                          "mqa_logits_dense",
+                          "mqa_topk_prefill_paged", "mqa_logits_dense",
                           "mqa_topk_dense", "mqa_key_scales", "mqa_scan_time", "mqa_mfma_peak",
                           "mqa_fp8_mfma_probe",
                           "mqa_strerror"}
@@ -167,6 +167,36 @@ def test_static_prefill_errors():
         assert _static() == 5  # valid arguments, no device: nothing launched
 
 
+def _paged(**kw):
+    a = dict(q=A16, cache=A16, table=A16, page=64, pages=64, weights=A16, starts=A16, ends=A16,
+             out=A16, rows=64, keys=4096, topk=512, ws=0x20000, wsb=1 << 40, flags=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return mqa.load().mqa_topk_prefill_paged(P(a["q"]), P(a["cache"]), P(a["table"]), a["page"],
+                                             a["pages"], P(a["weights"]), P(a["starts"]),
+                                             P(a["ends"]), P(a["out"]), a["rows"], a["keys"],
+                                             a["topk"], P(a["ws"]), a["wsb"], a["flags"], None)
+
+
+def test_paged_prefill_errors():
+    assert _paged(cache=0) == 1
+    assert _paged(table=0) == 1
+    assert _paged(ws=0) == 1
+    assert _paged(cache=MIS) == 2
+    assert _paged(table=0x10002) == 2
+    assert _paged(ws=0x20080) == 2
+    for page in (0, 2, 48, 100, 1 << 21):
+        assert _paged(page=page) == 3, page
+    assert _paged(pages=0) == 3
+    assert _paged(rows=0) == 3
+    assert _paged(keys=(1 << 20) + 1) == 3
+    assert _paged(topk=300) == 3
+    if _no_gpu():
+        assert _paged() == 5
+        assert _paged(page=4) == 5
+        assert _paged(page=1 << 20) == 5
+
+
 def test_fp8_probe_errors():
     P = ctypes.c_void_p
     L = mqa.load()
@@ -208,3 +238,35 @@ def test_binding_checks_every_shape_first():
         mqa.mqa_key_scales(u8(keys, 3))
     with pytest.raises(ValueError, match="shape"):
         mqa.fp8_mfma_probe(u8(2, 16, 128), u8(3, 16, 128))
+    # the paged entry: cache pages of 132 B per token, a long enough table
+    pg = dict(q=u8(rows, 32, 128), cache=u8(10, 64 * 132), block_table=i32(10), page_size=64,
+              keys=keys, weights=f32(rows, 32), starts=i32(rows), ends=i32(rows), topk=512)
+    for name, t in (("cache", u8(10, 64 * 128)), ("weights", f32(rows, 30)),
+                    ("starts", i32(rows + 2))):
+        with pytest.raises(ValueError, match="shape"):
+            mqa.mqa_topk_prefill_paged(**dict(pg, **{name: t}))
+    with pytest.raises(ValueError, match="block_table"):
+        mqa.mqa_topk_prefill_paged(**dict(pg, block_table=i32(9)))
+    with pytest.raises(ValueError, match="page_size"):
+        mqa.mqa_topk_prefill_paged(**dict(pg, page_size=48))
+
+
+def test_paged_cache_layout_round_trips():
+    # the paged-cache input builder: gathering each key back through the table
+    # (page table[j // P], slot j % P: its 128 code bytes, then its scale word
+    # at 128 P + 4 (j % P)) gives the gathered keys and scale bytes again
+    import numpy as np
+    import mqa_workloads as W
+    rng = np.random.default_rng(0)
+    keys = 1000
+    k = rng.integers(0, 256, (keys, 128), dtype=np.uint8)
+    sb = np.repeat(rng.integers(100, 130, (keys, 1), dtype=np.uint8), 4, axis=1)
+    for P in (4, 64, 256):
+        cache, table = W.paged_cache(k, sb, P, seed=P)
+        assert cache.shape == (-(-keys // P) + 3, 132 * P) and table.shape == (-(-keys // P),)
+        assert len(set(table.tolist())) == len(table)
+        j = np.arange(keys)
+        pg, sl = table[j // P], j % P
+        kk = cache[pg[:, None], sl[:, None] * 128 + np.arange(128)]
+        ss = cache[pg[:, None], 128 * P + 4 * sl[:, None] + np.arange(4)]
+        assert np.array_equal(kk, k) and np.array_equal(ss, sb)
