@@ -25,7 +25,11 @@ Prints ONE JSON line (rank 0):
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu,
 --dense (also time the chunked dense logits + top-k path, for context),
 --config N (workload 1..5), --deterministic (MQA_FLAG_DETERMINISTIC: ties at
-the k-th score to the smallest keys, outputs sorted), --sweep (instead of the benchmark: fused and
+the k-th score to the smallest keys, outputs sorted), --paged P (read the keys
+from a paged indexer cache of P-token pages through mqa_topk_prefill_paged
+instead of the gathered keys and decoded scales), --decode N [--decode-rows R
+--decode-ctx C] (instead of the benchmark: the decode-shaped path over N
+requests of R rows, each with C positions of context, one JSON line), --sweep (instead of the benchmark: fused and
 dense times on the causal-tail sweep, 16384 rows x 16K..1M keys, one JSON line
 per point), --copy-calibration MIB (instead of the benchmark,
 run a plain 1-D device copy of MIB MiB five times: the known-size kernel that
@@ -232,6 +236,61 @@ def time_fused(d, wl, steps: int, warmup: int):
     return ev0.elapsed_time(ev1) / steps, stats
 
 
+def decode_bench(args):
+    """The decode-shaped path: --decode REQUESTS requests of --decode-rows rows
+    (speculative tokens of one request), each over --decode-ctx positions of
+    its own pages (64-token pages), top-2048; inputs generated on the device.
+    One JSON line: visible (row, key) scores per second, the scan kernel's
+    FP8 MFMA fraction and the call's HBM fraction (each request's keys read
+    once: 132 B per position)."""
+    import torch
+
+    import fp8_mqa_logits_amd as mqa
+    import mqa_workloads as W
+    torch.cuda.set_device(0)
+    R, nreq, ctx, topk = args.decode_rows, args.decode, args.decode_ctx, 2048
+    d = W.decode_device(nreq, R, ctx, topk, 64, seed=1)
+    ws = torch.empty(mqa.workspace_size_decode(nreq, R), dtype=torch.uint8, device="cuda")
+    out = torch.empty((d["rows"], topk), dtype=torch.int32, device="cuda")
+    mode = mqa.FLAG_DETERMINISTIC if args.deterministic else 0
+
+    def step(flags=0):
+        mqa.mqa_topk_decode_paged(d["q"], d["cache"], d["table"], 64, d["weights"], d["starts"],
+                                  d["ends"], topk, R, out=out, workspace=ws, flags=flags | mode)
+    step(mqa.FLAG_STATS)
+    torch.cuda.synchronize()
+    stats = mqa.read_stats(ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step(mqa.FLAG_TIME_SCAN)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    scan_ms = mqa.scan_time_ms(args.steps) / args.steps
+    pairs = d["pairs"]
+    key_bytes = nreq * ctx * (128 + 4)
+    achieved = pairs * FLOP_PER_PAIR / (scan_ms / 1e3) / 1e12
+    print(json.dumps({
+        "metric": "decode (row,key) scores/s", "value": pairs / (ms / 1e3), "unit": "scores/s",
+        "ms_per_step": ms, "steps": args.steps, "warmup": args.warmup,
+        "config": {"workload": f"decode_{nreq}req_x{R}rows_ctx{ctx}_k{topk}", "requests": nreq,
+                   "rows_per_request": R, "context": ctx, "topk": topk, "page_size": 64,
+                   "visible_pairs": pairs, "rows": d["rows"],
+                   "ties": "lowest key, sorted output" if args.deterministic else "any"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS,
+                     "kernel": "fused_topk_kernel (decode)", "kernel_ms": scan_ms,
+                     "call_frac": pairs * FLOP_PER_PAIR / (ms / 1e3) / 1e12 / FP8_PEAK_TFLOPS,
+                     "hbm_key_bytes": key_bytes,
+                     "hbm_frac_call": key_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "path_stats": stats}), flush=True)
+
+
 def sweep(args):
     """Fused vs dense on the causal tail of K-key contexts (16384 rows)."""
     import gc
@@ -270,6 +329,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--paged", type=int, default=0, metavar="P")
+    ap.add_argument("--decode", type=int, default=0, metavar="REQUESTS")
+    ap.add_argument("--decode-rows", type=int, default=8)
+    ap.add_argument("--decode-ctx", type=int, default=131072)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this path runs on one GPU; multi-GPU runs are not supported "
@@ -296,6 +359,9 @@ def main():
     if args.sweep:
         sweep(args)
         return
+    if args.decode:
+        decode_bench(args)
+        return
 
     wl = W.config(args.config)
     print(f"[bench] workload {wl.name}: {wl.visible_pairs()} visible pairs, hashes "
@@ -315,9 +381,21 @@ def main():
 
     mode = mqa.FLAG_DETERMINISTIC if args.deterministic else 0
 
-    def step(flags=0):
-        mqa.mqa_topk_prefill(d["q"], d["k"], d["scales"], d["weights"], d["starts"], d["ends"],
-                             wl.topk, out=out, workspace=ws, flags=flags | mode)
+    if args.paged:
+        ws = torch.empty(mqa.workspace_size_paged(wl.rows, wl.keys), dtype=torch.uint8,
+                         device=dev)
+        cache, table = W.paged_cache(wl.k, wl.scale_bytes, args.paged)
+        d["cache"] = torch.from_numpy(cache).to(dev)
+        d["table"] = torch.from_numpy(table).to(dev)
+
+        def step(flags=0):
+            mqa.mqa_topk_prefill_paged(d["q"], d["cache"], d["table"], args.paged, wl.keys,
+                                       d["weights"], d["starts"], d["ends"], wl.topk, out=out,
+                                       workspace=ws, flags=flags | mode)
+    else:
+        def step(flags=0):
+            mqa.mqa_topk_prefill(d["q"], d["k"], d["scales"], d["weights"], d["starts"],
+                                 d["ends"], wl.topk, out=out, workspace=ws, flags=flags | mode)
 
     # path statistics (one extra call outside the timed region)
     step(mqa.FLAG_STATS)
@@ -355,7 +433,9 @@ def main():
         "data": "synthetic (seeded N(0,1) e4m3 q/k, UE8M0 scales 2^[-4,0], N(0,1)/sqrt(32) weights)",
         "config": {"workload": wl.name, "rows": wl.rows, "keys": wl.keys, "topk": wl.topk,
                    "visible_pairs": pairs, "parallelism": "1 GPU",
-                   "ties": "lowest key, sorted output" if args.deterministic else "any"},
+                   "ties": "lowest key, sorted output" if args.deterministic else "any",
+                   "keys_from": (f"paged cache, {args.paged}-token pages" if args.paged
+                                 else "gathered keys, decoded scales")},
         # the scan kernel's roofline (the dominant kernel); call_frac is the
         # whole call's FP8 fraction (all launches, the metric's own figure)
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,

@@ -31,7 +31,8 @@ ERR_NAMES = {0: "MQA_OK", 1: "MQA_ERR_NULL", 2: "MQA_ERR_ALIGN", 3: "MQA_ERR_SHA
              4: "MQA_ERR_WORKSPACE", 5: "MQA_ERR_DEVICE", 6: "MQA_ERR_LAUNCH"}
 
 EXPORTS = ("workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static",
-           "mqa_topk_prefill_paged", "mqa_logits_dense",
+           "mqa_topk_prefill_paged", "workspace_size_paged", "workspace_size_decode", "mqa_topk_decode_paged",
+           "mqa_logits_dense",
            "mqa_topk_dense",
            "mqa_key_scales", "mqa_scan_time", "mqa_mfma_peak", "mqa_fp8_mfma_probe",
            "mqa_strerror")
@@ -68,6 +69,12 @@ def load() -> ctypes.CDLL:
         lib.mqa_topk_prefill_static.restype = I
         lib.mqa_topk_prefill_paged.argtypes = [P, P, P, I, I, P, P, P, P, I, I, I, P, SZ, U, P]
         lib.mqa_topk_prefill_paged.restype = I
+        lib.workspace_size_paged.argtypes = [I, I, I]
+        lib.workspace_size_paged.restype = SZ
+        lib.workspace_size_decode.argtypes = [I, I, I]
+        lib.workspace_size_decode.restype = SZ
+        lib.mqa_topk_decode_paged.argtypes = [P, P, P, I, I, I, P, P, P, P, I, I, I, P, SZ, U, P]
+        lib.mqa_topk_decode_paged.restype = I
         lib.mqa_logits_dense.argtypes = [P, P, P, P, P, P, P, I64, I, I, I, I, P]
         lib.mqa_logits_dense.restype = I
         lib.mqa_topk_dense.argtypes = [P, I64, I, I, P, P, P, I, I, I, P]
@@ -267,7 +274,10 @@ def mqa_topk_prefill_paged(q, cache, block_table, page_size: int, keys: int, wei
         out = torch.empty((rows, topk), dtype=torch.int32, device=dev)
     _need(out, "out", (torch.int32,), dev)
     if workspace is None:
-        workspace = alloc_workspace(rows, dev.index)
+        n = workspace_size_paged(rows, keys, dev.index)
+        if n == 0:
+            raise MQAError(5, "workspace_size_paged")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", (torch.uint8,), dev)
     with torch.cuda.device(dev):
         rc = load().mqa_topk_prefill_paged(_ptr(q), _ptr(cache), _ptr(block_table), page_size,
@@ -275,6 +285,79 @@ def mqa_topk_prefill_paged(q, cache, block_table, page_size: int, keys: int, wei
                                            _ptr(out), rows, keys, int(topk), _ptr(workspace),
                                            workspace.numel(), int(flags), _stream(dev, stream))
     _check(rc, "mqa_topk_prefill_paged")
+    return out
+
+
+def workspace_size_paged(rows: int, keys: int, device: int | None = None) -> int:
+    """Bytes of workspace one mqa_topk_prefill_paged call needs."""
+    if device is None:
+        device = torch.cuda.current_device()
+    return int(load().workspace_size_paged(int(rows), int(keys), int(device)))
+
+
+def workspace_size_decode(requests: int, rows_per_request: int, device: int | None = None) -> int:
+    """Bytes of workspace one mqa_topk_decode_paged call needs."""
+    if device is None:
+        device = torch.cuda.current_device()
+    return int(load().workspace_size_decode(int(requests), int(rows_per_request), int(device)))
+
+
+def mqa_topk_decode_paged(q, cache, page_table, page_size: int, weights, starts, ends, topk: int,
+                          rows_per_request: int, out=None, workspace=None, flags: int = 0,
+                          stream=None) -> torch.Tensor:
+    """Decode-shaped fused scores + top-k over the paged indexer cache: q
+    [requests * R, 32, 128] (row r is row r % R of request r // R), page_table
+    [requests, table_stride] int32 (request q's position j is slot j % P of
+    page page_table[q, j // P]), starts/ends [rows] int32 positions in the row's
+    request. Returns out [rows, topk] int32 (position - start, -1 padded)."""
+    _tensors(q=q, cache=cache, page_table=page_table, weights=weights, starts=starts, ends=ends)
+    if q.dim() != 3:
+        raise ValueError("q must be [rows,32,128]")
+    rows = q.shape[0]
+    R, page_size = int(rows_per_request), int(page_size)
+    if R < 1 or R > 32:
+        raise ValueError("rows_per_request must be in [1, 32]")
+    if page_size < 4 or page_size & (page_size - 1):
+        raise ValueError("page_size must be a power of two >= 4")
+    if page_table.dim() != 2:
+        raise ValueError("page_table must be [requests, table_stride]")
+    requests, stride = page_table.shape
+    if rows != requests * R:
+        raise ValueError(f"q has {rows} rows, expected requests * rows_per_request = {requests * R}")
+    if cache.dim() != 2:
+        raise ValueError("cache must be [num_pages, page_size * 132]")
+    num_pages = cache.shape[0]
+    _shape(cache, (num_pages, page_size * PAGE_ENTRY), "cache")
+    _shape(q, (rows, HEADS, HEAD_DIM), "q")
+    _shape(weights, (rows, HEADS), "weights")
+    _shape(starts, (rows,), "starts")
+    _shape(ends, (rows,), "ends")
+    if out is not None:
+        _tensors(out=out)
+        _shape(out, (rows, topk), "out")
+    dev = q.device
+    _need(q, "q", FP8, dev)
+    _need(cache, "cache", (torch.uint8,), dev)
+    _need(page_table, "page_table", (torch.int32,), dev)
+    _need(weights, "weights", (torch.float32,), dev)
+    _need(starts, "starts", (torch.int32,), dev)
+    _need(ends, "ends", (torch.int32,), dev)
+    if out is None:
+        out = torch.empty((rows, topk), dtype=torch.int32, device=dev)
+    _need(out, "out", (torch.int32,), dev)
+    if workspace is None:
+        n = workspace_size_decode(requests, R, dev.index)
+        if n == 0:
+            raise MQAError(5, "workspace_size_decode")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), dev)
+    with torch.cuda.device(dev):
+        rc = load().mqa_topk_decode_paged(_ptr(q), _ptr(cache), _ptr(page_table), stride,
+                                          page_size, num_pages, _ptr(weights), _ptr(starts),
+                                          _ptr(ends), _ptr(out), requests, R, int(topk),
+                                          _ptr(workspace), workspace.numel(), int(flags),
+                                          _stream(dev, stream))
+    _check(rc, "mqa_topk_decode_paged")
     return out
 
 

@@ -62,7 +62,7 @@ const DeviceInfo* device_info(int device) {
 
 struct Layout {
   size_t header, order, xrow, xqueue, xflag, fqueue, fflag, rinfo, rqueue, rowinfo, seg, keyinfo,
-      beta, slabE, slabI, tmpE, tmpI, total;
+      beta, slabE, slabI, tmpE, tmpI, kc, total;
   int grid, nblocks;
 };
 
@@ -73,11 +73,12 @@ static_assert((size_t)mqa::kMaxBatchRows * mqa::kSlabRow * 4 + 4 * mqa::kSlabRow
                   ((size_t)1 << 31),
               "slab range");
 
-// Workspace of one batch of `rows` rows (rows <= kMaxBatchRows).
-Layout layout(int rows, const DeviceInfo& d) {
+// Workspace of one batch of `nblocks` blocks of 32 row slots (at most
+// kMaxBatchRows slots), plus room for kc_keys compacted keys (paged prefill).
+Layout layout_blocks(int nblocks, const DeviceInfo& d, int kc_keys = 0) {
   Layout L{};
   L.grid = d.cus * d.wg_per_cu;
-  L.nblocks = (rows + mqa::kFusedBlockRows - 1) / mqa::kFusedBlockRows;
+  L.nblocks = nblocks;
   const size_t rows_pad = (size_t)L.nblocks * mqa::kFusedBlockRows;
   size_t off = 0;
   L.header = off;
@@ -116,8 +117,32 @@ Layout layout(int rows, const DeviceInfo& d) {
   off = align_up(off + tmp);
   L.tmpI = off;
   off = align_up(off + tmp);
+  L.kc = off;
+  off = align_up(off + (size_t)kc_keys * MQA_HEAD_DIM);
   L.total = off;
   return L;
+}
+
+// Workspace of one batch of `rows` rows (rows <= kMaxBatchRows).
+Layout layout(int rows, const DeviceInfo& d, int kc_keys = 0) {
+  return layout_blocks((rows + mqa::kFusedBlockRows - 1) / mqa::kFusedBlockRows, d, kc_keys);
+}
+
+// Decode layout: requests packed dec_groups(R) to a block, a batch holding at
+// most kMaxBatchRows rows and kMaxBatchRows / 32 blocks.
+int dec_groups(int rows_per_request) {
+  return rows_per_request <= 8 ? 4 : (rows_per_request <= 16 ? 2 : 1);
+}
+int dec_batch(int requests, int rows_per_request) {
+  const int g = dec_groups(rows_per_request);
+  int b = mqa::kMaxBatchRows / rows_per_request;
+  const int by_blocks = mqa::kMaxBatchRows / mqa::kFusedBlockRows * g;
+  b = b < by_blocks ? b : by_blocks;
+  return requests < b ? requests : b;
+}
+int dec_blocks(int requests, int rows_per_request) {
+  const int g = dec_groups(rows_per_request);
+  return (requests + g - 1) / g;
 }
 
 int batch_rows(int rows) { return rows < mqa::kMaxBatchRows ? rows : mqa::kMaxBatchRows; }
@@ -188,6 +213,28 @@ struct KeySource {
   int page_shift = 0, num_pages = 0;
 };
 
+// Workspace pointers and the fields every batch shares.
+void set_workspace(mqa::FusedParams& p, uint8_t* ws, const Layout& L) {
+  p.header = reinterpret_cast<uint32_t*>(ws + L.header);
+  p.order = reinterpret_cast<int32_t*>(ws + L.order);
+  p.xrow = ws + L.xrow;
+  p.xqueue = reinterpret_cast<int32_t*>(ws + L.xqueue);
+  p.xflag = reinterpret_cast<uint32_t*>(ws + L.xflag);
+  p.fqueue = reinterpret_cast<int32_t*>(ws + L.fqueue);
+  p.fflag = reinterpret_cast<uint32_t*>(ws + L.fflag);
+  p.rinfo = reinterpret_cast<mqa::RefineInfo*>(ws + L.rinfo);
+  p.rqueue = reinterpret_cast<int32_t*>(ws + L.rqueue);
+  p.rowinfo = reinterpret_cast<mqa::RowInfo*>(ws + L.rowinfo);
+  p.seg = reinterpret_cast<mqa::SegInfo*>(ws + L.seg);
+  p.keyinfo = reinterpret_cast<float*>(ws + L.keyinfo);
+  p.beta = reinterpret_cast<float*>(ws + L.beta);
+  p.slabE = reinterpret_cast<float*>(ws + L.slabE);
+  p.slabI = reinterpret_cast<int32_t*>(ws + L.slabI);
+  p.tmpE = reinterpret_cast<float*>(ws + L.tmpE);
+  p.tmpI = reinterpret_cast<int32_t*>(ws + L.tmpI);
+  p.kc = ws + L.kc;
+}
+
 // Rows in batches of `batch` rows, one launch sequence each, in order on the
 // stream (they share the workspace ws, which holds layout(batch)).
 int prefill_batches(const uint8_t* q, const uint8_t* k, const float* scales,
@@ -195,7 +242,7 @@ int prefill_batches(const uint8_t* q, const uint8_t* k, const float* scales,
                     int32_t* out, int rows, int keys, int topk, uint8_t* ws, int batch,
                     const DeviceInfo& d, unsigned flags, void* stream,
                     const KeySource& src = KeySource()) {
-  const Layout L = layout(batch, d);
+  const Layout L = layout(batch, d, src.table ? keys : 0);
   hipEvent_t eb = nullptr, ee = nullptr;
   if (flags & MQA_FLAG_TIME_SCAN) {
     int dev = 0;
@@ -217,33 +264,72 @@ int prefill_batches(const uint8_t* q, const uint8_t* k, const float* scales,
     p.topk = topk;
     p.nblocks = (nr + mqa::kFusedBlockRows - 1) / mqa::kFusedBlockRows;
     p.flags = flags;
-    p.header = reinterpret_cast<uint32_t*>(ws + L.header);
-    p.order = reinterpret_cast<int32_t*>(ws + L.order);
-    p.xrow = ws + L.xrow;
-    p.xqueue = reinterpret_cast<int32_t*>(ws + L.xqueue);
-    p.xflag = reinterpret_cast<uint32_t*>(ws + L.xflag);
-    p.fqueue = reinterpret_cast<int32_t*>(ws + L.fqueue);
-    p.fflag = reinterpret_cast<uint32_t*>(ws + L.fflag);
-    p.rinfo = reinterpret_cast<mqa::RefineInfo*>(ws + L.rinfo);
-    p.rqueue = reinterpret_cast<int32_t*>(ws + L.rqueue);
-    p.rowinfo = reinterpret_cast<mqa::RowInfo*>(ws + L.rowinfo);
-    p.seg = reinterpret_cast<mqa::SegInfo*>(ws + L.seg);
-    p.keyinfo = reinterpret_cast<float*>(ws + L.keyinfo);
-    p.beta = reinterpret_cast<float*>(ws + L.beta);
-    p.slabE = reinterpret_cast<float*>(ws + L.slabE);
-    p.slabI = reinterpret_cast<int32_t*>(ws + L.slabI);
-    p.tmpE = reinterpret_cast<float*>(ws + L.tmpE);
-    p.tmpI = reinterpret_cast<int32_t*>(ws + L.tmpI);
+    set_workspace(p, ws, L);
     p.table = src.table;
     p.page_shift = src.page_shift;
     p.num_pages = src.num_pages;
     p.page_bytes = (int64_t)(MQA_HEAD_DIM + 4) << src.page_shift;
+    p.dec_rows = 0;
+    p.dec_groups = 1;
+    p.nreq = 0;
+    p.table_stride = 0;
     const int grid = L.grid < p.nblocks ? L.grid : p.nblocks;
     p.nseg = key_segments(p.nblocks, L.grid, topk);
     p.scan_grid = L.grid < p.nblocks * p.nseg ? L.grid : p.nblocks * p.nseg;
     // timing events: from the first batch's scan to the end of the last one
     const int rc = mqa_fused_launch(&p, grid, static_cast<hipStream_t>(stream),
                                     r0 == 0 ? eb : nullptr, r0 + nr >= rows ? ee : nullptr);
+    if (rc != 0) return launch_error(rc);
+  }
+  return MQA_OK;
+}
+
+// Decode-shaped calls: batches of whole requests, one launch sequence each.
+int decode_batches(const uint8_t* q, const uint8_t* cache, const int32_t* table,
+                   int table_stride, int shift, int num_pages, const float* weights,
+                   const int32_t* starts, const int32_t* ends, int32_t* out, int requests, int R,
+                   int topk, uint8_t* ws, const DeviceInfo& d, unsigned flags, void* stream) {
+  const int G = dec_groups(R);
+  const int nb = dec_batch(requests, R);
+  const Layout L = layout_blocks(dec_blocks(nb, R), d);
+  const int64_t span = (int64_t)table_stride << shift;
+  const int keys = span < MQA_MAX_KEYS ? (int)span : MQA_MAX_KEYS;
+  hipEvent_t eb = nullptr, ee = nullptr;
+  if (flags & MQA_FLAG_TIME_SCAN) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (!ring_slot(dev, &eb, &ee)) return MQA_ERR_DEVICE;
+  }
+  for (int q0 = 0; q0 < requests; q0 += nb) {
+    const int nq = requests - q0 < nb ? requests - q0 : nb;
+    const int64_t r0 = (int64_t)q0 * R;
+    mqa::FusedParams p;
+    p.q = q + r0 * MQA_HEADS * MQA_HEAD_DIM;
+    p.k = cache;
+    p.scales = nullptr;
+    p.weights = weights + r0 * MQA_HEADS;
+    p.starts = starts + r0;
+    p.ends = ends + r0;
+    p.out = out + r0 * topk;
+    p.rows = nq * R;
+    p.keys = keys;
+    p.topk = topk;
+    p.nblocks = dec_blocks(nq, R);
+    p.flags = flags;
+    set_workspace(p, ws, L);
+    p.table = table + (int64_t)q0 * table_stride;
+    p.page_shift = shift;
+    p.num_pages = num_pages;
+    p.page_bytes = (int64_t)(MQA_HEAD_DIM + 4) << shift;
+    p.dec_rows = R;
+    p.dec_groups = G;
+    p.nreq = nq;
+    p.table_stride = table_stride;
+    const int grid = L.grid < p.nblocks ? L.grid : p.nblocks;
+    p.nseg = key_segments(p.nblocks, L.grid, topk);
+    p.scan_grid = L.grid < p.nblocks * p.nseg ? L.grid : p.nblocks * p.nseg;
+    const int rc = mqa_fused_launch(&p, grid, static_cast<hipStream_t>(stream),
+                                    q0 == 0 ? eb : nullptr, q0 + nq >= requests ? ee : nullptr);
     if (rc != 0) return launch_error(rc);
   }
   return MQA_OK;
@@ -378,7 +464,7 @@ int mqa_topk_prefill_paged(const uint8_t* q, const uint8_t* cache, const int32_t
   const DeviceInfo* d = current_device();
   if (!d) return MQA_ERR_DEVICE;
   const int batch = batch_rows(rows);
-  if (workspace_bytes < layout(batch, *d).total) {
+  if (workspace_bytes < layout(batch, *d, keys).total) {
     g_ws_err[0] = 0;
     return MQA_ERR_WORKSPACE;
   }
@@ -388,6 +474,53 @@ int mqa_topk_prefill_paged(const uint8_t* q, const uint8_t* cache, const int32_t
   src.num_pages = num_pages;
   return prefill_batches(q, cache, nullptr, weights, starts, ends, out, rows, keys, topk,
                          static_cast<uint8_t*>(workspace), batch, *d, flags, stream, src);
+}
+
+size_t workspace_size_paged(int rows, int keys, int device) {
+  if (rows < 1 || rows > MQA_MAX_ROWS || keys < 1 || keys > MQA_MAX_KEYS) return 0;
+  const DeviceInfo* d = device_info(device);
+  if (!d) return 0;
+  return layout(batch_rows(rows), *d, keys).total;
+}
+
+size_t workspace_size_decode(int requests, int rows_per_request, int device) {
+  if (requests < 1 || rows_per_request < 1 || rows_per_request > 32 ||
+      (int64_t)requests * rows_per_request > MQA_MAX_ROWS)
+    return 0;
+  const DeviceInfo* d = device_info(device);
+  if (!d) return 0;
+  return layout_blocks(dec_blocks(dec_batch(requests, rows_per_request), rows_per_request), *d)
+      .total;
+}
+
+int mqa_topk_decode_paged(const uint8_t* q, const uint8_t* cache, const int32_t* page_table,
+                          int table_stride, int page_size, int num_pages, const float* weights,
+                          const int32_t* starts, const int32_t* ends, int32_t* out, int requests,
+                          int rows_per_request, int topk, void* workspace, size_t workspace_bytes,
+                          unsigned flags, void* stream) {
+  if (!q || !cache || !page_table || !weights || !starts || !ends || !out || !workspace)
+    return MQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(page_table, 4) ||
+      !aligned(weights, 16) || !aligned(out, 16) || !aligned(starts, 4) || !aligned(ends, 4) ||
+      !aligned(workspace, 256))
+    return MQA_ERR_ALIGN;
+  int shift = 0;
+  while (shift < 20 && (1 << shift) < page_size) ++shift;
+  if (requests < 1 || rows_per_request < 1 || rows_per_request > 32 ||
+      (int64_t)requests * rows_per_request > MQA_MAX_ROWS || !topk_ok(topk) ||
+      page_size < 4 || page_size > MQA_MAX_KEYS || (1 << shift) != page_size || num_pages < 1 ||
+      table_stride < 1)
+    return MQA_ERR_SHAPE;
+  const DeviceInfo* d = current_device();
+  if (!d) return MQA_ERR_DEVICE;
+  const int nb = dec_batch(requests, rows_per_request);
+  if (workspace_bytes < layout_blocks(dec_blocks(nb, rows_per_request), *d).total) {
+    g_ws_err[0] = 0;
+    return MQA_ERR_WORKSPACE;
+  }
+  return decode_batches(q, cache, page_table, table_stride, shift, num_pages, weights, starts,
+                        ends, out, requests, rows_per_request, topk,
+                        static_cast<uint8_t*>(workspace), *d, flags, stream);
 }
 
 int mqa_logits_dense(const uint8_t* q, const uint8_t* k, const float* scales,

@@ -102,56 +102,143 @@ __device__ __forceinline__ void row_range(const FusedParams& p, int r, int& s, i
 }
 
 // ---------------------------------------------------------------------------
-// Key addressing. The keys' e4m3 codes come from the dense k array or from
-// the paged indexer cache (vLLM PR #60618, "Motivation": 132 B per token, the
-// 128-byte e4m3 key and its four-byte UE8M0 scale); each kernel that reads
-// key bytes has an instance per source, so the dense one compiles as if the
-// pages did not exist.
-template <bool PAGED>
-__device__ __forceinline__ const uint8_t* key_row(const FusedParams& p, int key) {
-  if constexpr (!PAGED) {
-    return p.k + (int64_t)key * kDim;
+// Key sources. The keys' e4m3 codes come from the gathered k array, from the
+// paged indexer cache (vLLM PR #60618, "Motivation": 132 B per token, the
+// 128-byte e4m3 key and its four-byte UE8M0 scale) through one page table for
+// the call's key numbering, or, for decode-shaped calls, from the cache
+// through one page-table row per request (the PR's review thread: the decode
+// follow-up, many requests of a few query rows each). Every kernel that reads
+// key bytes has an instance per source, so the gathered one compiles as if the
+// others did not exist.
+enum KeySrc : int { SRC_GATHER = 0, SRC_PAGED = 1, SRC_DECODE = 2 };
+
+// 64-key chunks per LDS stage: one per packed request (up to four) in decode,
+// else two.
+template <int SRC>
+constexpr int stage_chunks() {
+  return SRC == SRC_DECODE ? 4 : 2;
+}
+template <int SRC>
+constexpr int stage_keys() {
+  return stage_chunks<SRC>() * kChunk;
+}
+
+__device__ __forceinline__ int clamp_page(const FusedParams& p, int pg) {
+  return pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
+}
+
+// The page-table entry of key `key` (in decode: position `key` of request
+// `req`, its table row's entries clamped to the row).
+template <int SRC>
+__device__ __forceinline__ const int32_t* table_entry(const FusedParams& p, int key, int req) {
+  if constexpr (SRC == SRC_DECODE) {
+    int i = key >> p.page_shift;
+    i = i < p.table_stride ? i : p.table_stride - 1;
+    return p.table + (int64_t)req * p.table_stride + i;
   } else {
-    int pg = p.table[key >> p.page_shift];
-    pg = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
-    return p.k + (int64_t)pg * p.page_bytes + (int64_t)(key & ((1 << p.page_shift) - 1)) * kDim;
+    return p.table + (key >> p.page_shift);
   }
 }
 
-// The scale of key `key` (UE8M0 decoded, fused: the low byte e of the paged
-// cache's scale word is the fp32 with bit pattern e << 23, API page
-// "fused_mqa_topk", fused_mqa_topk_key_scales; e = 0 gives +0.0).
-template <bool PAGED>
-__device__ __forceinline__ float key_scale(const FusedParams& p, int key) {
-  if constexpr (!PAGED) {
+// Row of key `key` in cache page `pg` (clamped into the cache).
+__device__ __forceinline__ const uint8_t* page_row(const FusedParams& p, int pg, int key) {
+  return p.k + (int64_t)clamp_page(p, pg) * p.page_bytes +
+         (int64_t)(key & ((1 << p.page_shift) - 1)) * kDim;
+}
+
+template <int SRC>
+__device__ __forceinline__ const uint8_t* key_row(const FusedParams& p, int key, int req = 0) {
+  if constexpr (SRC == SRC_GATHER) {
+    return p.k + (int64_t)key * kDim;
+  } else {
+    return page_row(p, *table_entry<SRC>(p, key, req), key);
+  }
+}
+
+// UE8M0 decode (API page "fused_mqa_topk", fused_mqa_topk_key_scales): the
+// low byte e of a scale word is the fp32 with bit pattern e << 23 (e = 0
+// gives +0.0).
+__device__ __forceinline__ float ue8m0(uint32_t w) { return __uint_as_float((w & 0xFFu) << 23); }
+
+// The scale word of key `key` of cache page `pg`.
+__device__ __forceinline__ const uint32_t* page_scale(const FusedParams& p, int pg, int key) {
+  const int P = 1 << p.page_shift;
+  return reinterpret_cast<const uint32_t*>(p.k + (int64_t)clamp_page(p, pg) * p.page_bytes +
+                                           (int64_t)P * kDim + 4 * (int64_t)(key & (P - 1)));
+}
+
+// The decoded scale of key `key` read from its source (the prologue's view;
+// the other kernels of the gathered and paged sources read the prologue's
+// copy in keyinfo).
+template <int SRC>
+__device__ __forceinline__ float key_scale(const FusedParams& p, int key, int req = 0) {
+  if constexpr (SRC == SRC_GATHER) {
     return p.scales[key];
   } else {
-    int pg = p.table[key >> p.page_shift];
-    pg = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
-    const int P = 1 << p.page_shift;
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(
-        p.k + (int64_t)pg * p.page_bytes + (int64_t)P * kDim + 4 * (int64_t)(key & (P - 1)));
-    return __uint_as_float((w & 0xFFu) << 23);
+    return ue8m0(*page_scale(p, *table_entry<SRC>(p, key, req), key));
+  }
+}
+
+// The scale of key `key` as the scan scored it: the prologue's keyinfo copy,
+// or in decode (no keyinfo) straight from the cache.
+template <int SRC>
+__device__ __forceinline__ float scan_scale(const FusedParams& p, int key, int req) {
+  if constexpr (SRC == SRC_DECODE) {
+    return key_scale<SRC>(p, key, req);
+  } else {
+    return p.keyinfo[2 * (int64_t)key];
   }
 }
 
 // B operands of up to 64 arbitrary keys (lane l: key keyidx[t] of sub-tile t,
-// bytes 32 * (l / 16) ..), from either source.
-template <bool PAGED>
+// bytes 32 * (l / 16) ..), from any source (decode: of request req).
+template <int SRC>
 __device__ __forceinline__ void load_keys_rows(KeyTile& kt, const FusedParams& p,
-                                               const int* keyidx) {
-  if constexpr (!PAGED) {
+                                               const int* keyidx, int req = 0) {
+  if constexpr (SRC == SRC_GATHER) {
     load_keys_gather(kt, p.k, keyidx);
   } else {
     const int g = lane_id() >> 4;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint8_t* r = key_row<true>(p, keyidx[t]) + 32 * g;
+      const uint8_t* r = key_row<SRC>(p, keyidx[t], req) + 32 * g;
       const uint4 x0 = *reinterpret_cast<const uint4*>(r);
       const uint4 x1 = *reinterpret_cast<const uint4*>(r + 16);
       kt.kb[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     }
+  }
+}
+
+// Decode blocks: dec_groups requests per block (4 when a request has at most
+// 8 rows, 2 up to 16, 1 up to 32), each owning 32 / dec_groups row slots, of
+// which its dec_rows rows fill the first. Slot j of block b: request
+// b * G + j / (32 / G), row j % (32 / G) of it. Returns the row id, or p.rows
+// for an empty slot. Otherwise slot j of block b is row 32 b + j.
+template <int SRC>
+__device__ __forceinline__ int slot_row(const FusedParams& p, int b, int slot) {
+  if constexpr (SRC == SRC_DECODE) {
+    const int per = kFusedBlockRows / p.dec_groups;
+    const int q = b * p.dec_groups + slot / per;
+    const int j = slot - (slot / per) * per;
+    return (j < p.dec_rows && q < p.nreq) ? q * p.dec_rows + j : p.rows;
+  } else {
+    return b * kFusedBlockRows + slot;
+  }
+}
+
+// The block of row r (either layout).
+__device__ __forceinline__ int block_of(const FusedParams& p, int r) {
+  return p.dec_rows ? (r / p.dec_rows) / p.dec_groups : r / kFusedBlockRows;
+}
+
+// The packed request (0 .. dec_groups - 1) whose rows a wave holds in decode.
+template <int SRC>
+__device__ __forceinline__ int wave_group(const FusedParams& p, int w) {
+  if constexpr (SRC == SRC_DECODE) {
+    return w * p.dec_groups / kFusedWaves;
+  } else {
+    return 0;
   }
 }
 
@@ -221,11 +308,12 @@ __device__ __forceinline__ float key_nhat(float x, float scale) {
 constexpr int kMaxBlocks = kMaxBatchRows / kBlockRows;
 constexpr int kPrologueThreads = 1024;
 
-template <bool PAGED>
+template <int SRC>
 __device__ __forceinline__ void prologue_bounds(const FusedParams& p) {
   const int l = lane_id();
   const int nwaves = (gridDim.x - 1) * (kPrologueThreads / kWave);
-  const int kunits = (p.keys + 3) / 4;
+  // (decode keeps no keyinfo: its scan bounds each key from the key itself)
+  const int kunits = SRC == SRC_DECODE ? 0 : (p.keys + 3) / 4;
   const int units = kunits + p.rows;
   for (int u = (blockIdx.x - 1) * (kPrologueThreads / kWave) + wave_id(); u < units;
        u += nwaves) {
@@ -234,13 +322,17 @@ __device__ __forceinline__ void prologue_bounds(const FusedParams& p) {
       const int key = 4 * u + (l >> 4);
       float x = 0.f;
       if (key < p.keys) {
-        const uint2 v = *reinterpret_cast<const uint2*>(key_row<PAGED>(p, key) + 8 * g);
+        const uint2 v = *reinterpret_cast<const uint2*>(key_row<SRC>(p, key) + 8 * g);
         x = xhat8(v.x, v.y);
+        // paged prefill: the keys are also compacted into the workspace,
+        // where the later kernels read them as gathered keys
+        if constexpr (SRC == SRC_PAGED)
+          *reinterpret_cast<uint2*>(p.kc + (int64_t)key * kDim + 8 * g) = v;
       }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
       if (g == 0 && key < p.keys) {
-        const float sc = key_scale<PAGED>(p, key);
+        const float sc = key_scale<SRC>(p, key);
         *reinterpret_cast<float2*>(p.keyinfo + 2 * (int64_t)key) = float2{sc, key_nhat(x, sc)};
       }
     } else {
@@ -279,13 +371,13 @@ __device__ __forceinline__ void prologue_bounds(const FusedParams& p) {
   }
 }
 
-template <bool PAGED>
+template <int SRC>
 __global__ __launch_bounds__(kPrologueThreads) void fused_prologue_kernel(FusedParams p) {
   __shared__ int cnt[1024];
   __shared__ int off[1024];
   __shared__ int blo[kMaxBlocks], bhi[kMaxBlocks];
   if (blockIdx.x > 0) {
-    prologue_bounds<PAGED>(p);
+    prologue_bounds<SRC>(p);
     return;
   }
   const int tid = threadIdx.x;
@@ -303,8 +395,8 @@ __global__ __launch_bounds__(kPrologueThreads) void fused_prologue_kernel(FusedP
     int s, e;
     row_range(p, r, s, e);
     if (e - s > p.topk) {
-      atomicMin(&blo[r / kBlockRows], s);
-      atomicMax(&bhi[r / kBlockRows], e);
+      atomicMin(&blo[block_of(p, r)], s);
+      atomicMax(&bhi[block_of(p, r)], e);
     }
   }
   __syncthreads();
@@ -342,12 +434,13 @@ struct RowState {
 };
 
 // Rows of block b owned by the calling wave (modes off, thresholds open).
+template <int SRC>
 __device__ __forceinline__ void wave_rows(const FusedParams& p, int b, RowState* rs) {
   const int w = wave_id();
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
     RowState& r = rs[i];
-    r.r = b * kBlockRows + w * kRowsPerWave + i;
+    r.r = slot_row<SRC>(p, b, w * kRowsPerWave + i);
     r.cnt = 0;
     r.strict = 0;
     r.thr = -__builtin_inff();
@@ -397,22 +490,26 @@ __device__ __forceinline__ void block_union(int* wlo_s, int* whi_s, int* wf_s, i
 // buffers as separate __shared__ arrays so that the compiler can tell the one
 // being filled from the one being read (and does not wait for the copy in
 // flight before reading the other).
-constexpr int kStageChunks = 2;
-constexpr int kStageKeys = kStageChunks * kChunk;
 
-// A stage's per-key floats: the scales, then (kStageKeys floats further, so
-// that one LDS address serves both reads) the error bound factors nhat.
+// A stage's per-key floats: the scales, then (stage-keys floats further, so
+// that one LDS address serves both reads) the error bound factors nhat; in
+// decode only the raw scale words. The paged and decode sources also keep the
+// page of each stage key (pg), copied one stage ahead so that a stage's key
+// copies never wait for a page-table read.
 struct Stages {
   uint8_t* k[2];
   float* s[2];
+  int32_t* pg[2];
 };
 
-#define MQA_DECLARE_STAGES(name)                                          \
-  __shared__ __align__(16) uint8_t name##_k0[kStageChunks * kChunkBytes]; \
-  __shared__ __align__(16) uint8_t name##_k1[kStageChunks * kChunkBytes]; \
-  __shared__ __align__(16) float name##_s0[2 * kStageKeys];               \
-  __shared__ __align__(16) float name##_s1[2 * kStageKeys];               \
-  const Stages name = {{name##_k0, name##_k1}, {name##_s0, name##_s1}}
+#define MQA_DECLARE_STAGES(name, SRC)                                                 \
+  __shared__ __align__(16) uint8_t name##_k0[stage_chunks<SRC>() * kChunkBytes];     \
+  __shared__ __align__(16) uint8_t name##_k1[stage_chunks<SRC>() * kChunkBytes];     \
+  __shared__ __align__(16) float name##_s0[2 * stage_keys<SRC>()];                    \
+  __shared__ __align__(16) float name##_s1[2 * stage_keys<SRC>()];                    \
+  __shared__ __align__(16) int32_t name##_p0[SRC == SRC_GATHER ? 4 : stage_keys<SRC>()]; \
+  __shared__ __align__(16) int32_t name##_p1[SRC == SRC_GATHER ? 4 : stage_keys<SRC>()]; \
+  const Stages name = {{name##_k0, name##_k1}, {name##_s0, name##_s1}, {name##_p0, name##_p1}}
 
 // Smallest float above a finite x: "score > x" is "score >= next_up(x)".
 __device__ __forceinline__ float next_up(float x) {
@@ -421,9 +518,11 @@ __device__ __forceinline__ float next_up(float x) {
   return __int_as_float(b > 0 ? b + 1 : b - 1);
 }
 
-// The row's admission test as one ">=" threshold (+inf admits nothing).
+// The row's admission test as one ">=" threshold. NaN admits nothing: not
+// even a +inf or NaN score, which a key outside every row's range may have
+// (the unused slots of a paged cache's last page hold arbitrary bytes).
 __device__ __forceinline__ float admit_thr(const RowState& r, bool live) {
-  if (!live) return __builtin_inff();
+  if (!live) return __builtin_nanf("");
   return r.strict ? next_up(r.thr) : r.thr;
 }
 
@@ -447,10 +546,15 @@ struct SlabRefs {
 // seg >= 0: key segment seg of a split scan (p.nseg > 1), whose records go to
 // records [seg * R, (seg + 1) * R) of each slab row, R = kSlabRow / nseg, with
 // a capacity of R - 64 (one more chunk fits past it); seg < 0: the whole row.
+// Slab row i of the wave is row0 + i: the wave's rows are consecutive row
+// ids (in decode, rows of one request; its empty slots never write).
+template <int SRC>
 __device__ __forceinline__ SlabRefs slab_refs(const FusedParams& p, int b, uint32_t* hist,
                                               int keep, int seg = -1) {
   SlabRefs sr;
-  const int64_t row0 = (int64_t)b * kBlockRows + wave_id() * kRowsPerWave;
+  int r0 = slot_row<SRC>(p, b, wave_id() * kRowsPerWave);
+  r0 = r0 < p.rows ? r0 : 0;
+  const int64_t row0 = r0;
   const int region = kSlabRow / p.nseg;
   const int64_t off = seg > 0 ? (int64_t)seg * region : 0;
   sr.sE0 = p.slabE + row0 * kSlabRow + off;
@@ -565,22 +669,68 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
   for (int j = 0; j < kRowsPerWave; ++j) rs[j].cnt = __builtin_amdgcn_readfirstlane(rs[j].cnt);
 }
 
-// Queue direct global->LDS copies of the keys key0 + j * stride, j <
-// kStageKeys (clamped to the last key), their scales and their nhat into a
-// stage buffer.
+// Stage key j (0 .. stage_keys - 1) of a stage that starts at position key0:
+// its key (position) and request. Gathered and paged stages hold the keys
+// key0 + j * stride; a decode stage holds, in chunk u = j / 64, request
+// req0 + u % G's positions key0 + ((u / G) * 64 + j % 64) * stride. Keys are
+// clamped to the last one and requests to the last request.
+template <int SRC>
+__device__ __forceinline__ void stage_key(const FusedParams& p, int key0, int stride, int j,
+                                          int req0, int& key, int& req) {
+  if constexpr (SRC == SRC_DECODE) {
+    const int G = p.dec_groups;
+    const int u = j >> 6;
+    key = key0 + ((u / G) * kChunk + (j & (kChunk - 1))) * stride;
+    req = req0 + (u & (G - 1));
+    req = req < p.nreq ? req : p.nreq - 1;
+  } else {
+    key = key0 + j * stride;
+    req = 0;
+  }
+  key = key < p.keys ? key : p.keys - 1;
+}
+
+// Queue the copy of a stage's page numbers into pdst (paged and decode
+// sources; thread j copies the page-table entry of stage key j). Issued a
+// stage before the stage's key copies, which read them from LDS.
+template <int SRC>
+__device__ __forceinline__ void dma_pages(const FusedParams& p, int key0, int stride,
+                                          int32_t* pdst, int tid, int req0) {
+  if constexpr (SRC != SRC_GATHER) {
+    if (tid < stage_keys<SRC>()) {
+      int key, req;
+      stage_key<SRC>(p, key0, stride, tid, req0, key, req);
+      const int32_t* src = table_entry<SRC>(p, key, req);
+      __builtin_amdgcn_global_load_lds(src, pdst + (tid & ~63), 4, 0, 0);
+    }
+  }
+}
+
+// Queue direct global->LDS copies of a stage's keys (stage_key), their scales
+// and their nhat (decode: their raw scale words) into a stage buffer; pgs
+// holds the stage's page numbers (paged and decode sources).
 // Slot p of the buffer (16 bytes) holds key j = p / 8, column slice (p % 8) ^
 // swz(j); each wave fills 64 consecutive slots per copy. The copies are
 // waited for by the barrier that ends the stage before the buffer is read.
-template <bool PAGED>
+template <int SRC>
 __device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, int stride,
-                                          uint8_t* kdst, float* sdst, int tid) {
-  // threads [0, kStageKeys): scales; [kStageKeys, 2 kStageKeys): nhat (the
-  // two halves of each key's keyinfo pair). Issued before the key tiles, so
-  // that anything the compiler reloads for it is waited for before the tile
-  // copies are in flight.
-  if (tid < 2 * kStageKeys) {
-    const int t = tid & (kStageKeys - 1);
-    const int half = tid / kStageKeys;
+                                          uint8_t* kdst, float* sdst, const int32_t* pgs,
+                                          int tid, int req0) {
+  constexpr int SK = stage_keys<SRC>();
+  // Issued before the key tiles, so that anything the compiler reloads for
+  // it is waited for before the tile copies are in flight.
+  if constexpr (SRC == SRC_DECODE) {
+    if (tid < SK) {
+      int key, req;
+      stage_key<SRC>(p, key0, stride, tid, req0, key, req);
+      const uint32_t* src = page_scale(p, pgs[tid], key);
+      __builtin_amdgcn_global_load_lds(src, sdst + (tid & ~63), 4, 0, 0);
+    }
+  } else if (tid < 2 * SK) {
+    // threads [0, SK): scales; [SK, 2 SK): nhat (the two halves of each
+    // key's keyinfo pair)
+    const int t = tid & (SK - 1);
+    const int half = tid / SK;
     int key = key0 + t * stride;
     key = key < p.keys ? key : p.keys - 1;
     // a 32-bit byte offset from the uniform base (keys < 2^20): one VGPR
@@ -589,15 +739,49 @@ __device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, int st
                                      sdst + (tid & ~63), 4, 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < kStageChunks * kChunk * 8 / kThreads; ++i) {
+  for (int i = 0; i < SK * 8 / kThreads; ++i) {
     const int slot = tid + i * kThreads;
     const int j = slot >> 3;
     const int c = (slot & 7) ^ swz(j);
-    int key = key0 + j * stride;
-    key = key < p.keys ? key : p.keys - 1;
-    const uint8_t* src = key_row<PAGED>(p, key) + 16 * c;
+    int key, req;
+    stage_key<SRC>(p, key0, stride, j, req0, key, req);
+    const uint8_t* src;
+    if constexpr (SRC == SRC_GATHER)
+      src = p.k + (int64_t)key * kDim + 16 * c;
+    else
+      src = page_row(p, pgs[j], key) + 16 * c;
     __builtin_amdgcn_global_load_lds(src, kdst + 16 * (slot & ~63), 16, 0, 0);
   }
+}
+
+// In decode the scan bounds a key's FP8 error from the key's own bytes (there
+// is no per-key prologue): with S = sum_d k_d^2, each group's largest |k_d|
+// is at most the square root of the group's sum of squares, x(v) <= |v| for
+// normal codes and x = 2^-6 for subnormal ones, and by Cauchy-Schwarz the 16
+// group terms sum to at most 4 sqrt(S), so
+//   sum_g max_{d in g} x(k_d) <= 4 sqrt(S) + 16 * 2^-6.
+// S is the diagonal of the FP8 MFMA of each 16-key sub-tile with itself: its
+// products are exact squares, and truncation lowers a group's sum by at most
+// 7 * 2^-13 of it, so S is taken as the MFMA's value times (1 + 2^-9). Lane l
+// gets key l's nhat (rounded up like the prologue's).
+__device__ __forceinline__ float decode_nhat(const KeyTile& kt, float scale) {
+  const int l = lane_id();
+  const int j = l & 15;
+  float d[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
+    const v4f c = mfma_fp8(kt.kb[t], kt.kb[t], z);
+    // entry (m, n) of the product sits in lane n + 16 (m / 4), element m % 4:
+    // the diagonal entry (j, j) in lane j + 16 (j / 4), element j % 4
+    const int v = l & 3;
+    const float x = v == 0 ? c[0] : (v == 1 ? c[1] : (v == 2 ? c[2] : c[3]));
+    d[t] = __shfl(x, j + 16 * (j >> 2), 64);
+  }
+  const int t = l >> 4;  // key l is key j of sub-tile t
+  const float sq = t == 0 ? d[0] : (t == 1 ? d[1] : (t == 2 ? d[2] : d[3]));
+  const float x = __builtin_fmaf(4.f * __builtin_sqrtf(sq * (1.f + 0x1p-9f)), 1.f + 0x1p-20f, 0.25f);
+  return key_nhat(x, scale);
 }
 
 // Approximate scores of the wave's 4 rows for a 64-key chunk, lane l <->
@@ -625,13 +809,19 @@ __device__ __forceinline__ void score4(float E[4], const QueryRow* qr, const Fol
 // for EXACT. FP8 rows are pipelined: the MFMAs of the next row are issued
 // before the epilogue of the current one. Chunks that every live row of the
 // wave covers entirely (almost all of them) take a path with no per-row range
-// tests: rows that are not live have an admission threshold of +inf there.
-template <bool EXACT, bool PAGED>
+// tests: rows that are not live have an admission threshold of NaN there.
+// Decode: the block's requests req0 .. req0 + G - 1 share the stages (chunk
+// u of a stage is request u % G's) and this wave's rows are request grp's.
+template <bool EXACT, int SRC>
 __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& stg, const QueryRow* qr,
                                           const FoldOp& fo, RowState* rs, int mode, int lo,
-                                          int hi, const SlabRefs& sr) {
+                                          int hi, const SlabRefs& sr, int req0, int grp) {
   const int tid = threadIdx.x;
   const int l = lane_id();
+  constexpr int SC = stage_chunks<SRC>();
+  constexpr int SK = stage_keys<SRC>();
+  const int G = SRC == SRC_DECODE ? p.dec_groups : 1;
+  const int cps = SC / G;  // 64-position chunks per stage
   const int nch = (hi - lo + kChunk - 1) / kChunk;
   bool live[kRowsPerWave];
   float th[kRowsPerWave];
@@ -649,7 +839,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
     }
   }
   if (nlive == 0) cf = ch = 0;
-  const int nst = (nch + kStageChunks - 1) / kStageChunks;
+  const int nst = (nch + cps - 1) / cps;
   // One chunk of the stage in LDS (keys kc, scales scl, error bound factors
   // nrm): score the wave's rows and append their candidates.
   auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
@@ -657,7 +847,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
     const int key = key0 + l;
     if constexpr (!EXACT) {
       // Each row's admission test as one per-lane threshold: the row's own on
-      // interior chunks, +inf for keys outside the row's range on the others,
+      // interior chunks, NaN for keys outside the row's range on the others,
       // so that scoring and emission are the same code for both (no range
       // tests behind the scores).
       float thl[kRowsPerWave];
@@ -670,18 +860,25 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
         for (int i = 0; i < kRowsPerWave; ++i) {
           const bool act = live[i] && rs[i].s < key0 + kChunk && rs[i].e > key0;
           any |= act;
-          thl[i] = act && key >= rs[i].s && key < rs[i].e ? th[i] : __builtin_inff();
+          thl[i] = act && key >= rs[i].s && key < rs[i].e ? th[i] : __builtin_nanf("");
         }
         if (!any) return;
       }
-      const float sc = scl[l];
-      const float nh = scl[kStageKeys + l];
+      KeyTile kt;
+      float sc, nh;
+      if constexpr (SRC == SRC_DECODE) {
+        load_keys_lds(kt, kc);
+        sc = ue8m0(__float_as_uint(scl[l]));
+        nh = decode_nhat(kt, sc);
+      } else {
+        sc = scl[l];
+        nh = scl[SK + l];
+      }
       // the record's key word: the key and its nhat bits
       const int kw = key | __float_as_int(nh);
-      KeyTile kt;
-      load_keys_lds(kt, kc);
+      if constexpr (SRC != SRC_DECODE) load_keys_lds(kt, kc);
       float E[4];
-      // rows that are not live have zeroed operands and a +inf threshold
+      // rows that are not live have zeroed operands and a NaN threshold
       score4(E, qr, fo, kt, sc);
       // admission and records by U = E + beta * nhat, an upper bound of the
       // key's exact score
@@ -697,7 +894,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
         any |= act[i];
       }
       if (!any) return;
-      const float sc = scl[l];
+      const float sc = SRC == SRC_DECODE ? ue8m0(__float_as_uint(scl[l])) : scl[l];
       KeyTile kt;
       load_keys_lds(kt, kc);
       float E[4];
@@ -715,21 +912,32 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
   };
   // One stage: queue the copy of the next stage into the other buffer (its
   // last readers passed the previous barrier), then score this one.
+  // (paged and decode sources: the pages of stage st + 2 are copied during
+  // stage st, into the page buffer stage st's copies were issued from)
   auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext,
-                   float* snext) {
-    if (st + 1 < nst) dma_stage<PAGED>(p, lo + (st + 1) * kStageKeys, 1, knext, snext, tid);
+                   float* snext, const int32_t* pnext, int32_t* pafter) {
+    if (st + 1 < nst)
+      dma_stage<SRC>(p, lo + (st + 1) * cps * kChunk, 1, knext, snext, pnext, tid, req0);
+    if (SRC != SRC_GATHER && st + 2 < nst)
+      dma_pages<SRC>(p, lo + (st + 2) * cps * kChunk, 1, pafter, tid, req0);
 #pragma unroll
-    for (int u = 0; u < kStageChunks; ++u) {
-      const int c = st * kStageChunks + u;
+    for (int u = 0; u < SC; ++u) {
+      if (SRC == SRC_DECODE && (u & (G - 1)) != grp) continue;
+      const int c = st * cps + u / G;
       if (c < nch) chunk(c, kcur + u * kChunkBytes, scur + u * kChunk);
     }
     __syncthreads();
   };
-  dma_stage<PAGED>(p, lo, 1, stg.k[0], stg.s[0], tid);
+  if constexpr (SRC != SRC_GATHER) {
+    dma_pages<SRC>(p, lo, 1, stg.pg[0], tid, req0);
+    __syncthreads();
+  }
+  dma_stage<SRC>(p, lo, 1, stg.k[0], stg.s[0], stg.pg[0], tid, req0);
+  if (SRC != SRC_GATHER && nst > 1) dma_pages<SRC>(p, lo + cps * kChunk, 1, stg.pg[1], tid, req0);
   __syncthreads();
   for (int st = 0; st < nst; st += 2) {
-    stage(st, stg.k[0], stg.s[0], stg.k[1], stg.s[1]);
-    if (st + 1 < nst) stage(st + 1, stg.k[1], stg.s[1], stg.k[0], stg.s[0]);
+    stage(st, stg.k[0], stg.s[0], stg.k[1], stg.s[1], stg.pg[1], stg.pg[0]);
+    if (st + 1 < nst) stage(st + 1, stg.k[1], stg.s[1], stg.k[0], stg.s[0], stg.pg[0], stg.pg[1]);
   }
 }
 
@@ -741,13 +949,47 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
 // takes as threshold the lower score edge of the bin where the count of sample keys
 // above reaches a safe margin over the k-th key's expected sample rank. Rows with n <= k are answered here (keys 0..n-1, -1 padding).
 // The gate's sample of a block whose union range spans `span` keys: S keys
-// (about span / 24, a multiple of the stage size, 512..16384) at an integer
-// stride from the start of the range. Returns the number of stages.
-__device__ __forceinline__ int gate_sample(int span, int& stride) {
-  int S = (span / 24) & ~(kStageKeys - 1);
+// (about span / 24, a multiple of spp, the positions a stage holds per
+// request, 512..16384) at an integer stride from the start of the range.
+// Returns the number of stages.
+__device__ __forceinline__ int gate_sample(int span, int spp, int& stride) {
+  int S = (span / 24) & ~(spp - 1);
   S = S < 512 ? 512 : (S > 16384 ? 16384 : S);
   stride = span / S > 1 ? span / S : 1;
-  return S / kStageKeys;
+  return S / spp;
+}
+
+// The strided sample loop of the gate and of its fine pass: nst stages of the
+// keys lo + j * stride (decode: of each packed request), double-buffered,
+// each chunk u of stage st handed to f(st, u, keys, scales); the paged and
+// decode sources copy the pages a stage ahead, as the scan does.
+template <int SRC, class F>
+__device__ __forceinline__ void sample_stages(const FusedParams& p, const Stages& stg, int lo,
+                                              int stride, int nst, int req0, int tid, F f) {
+  constexpr int SC = stage_chunks<SRC>();
+  const int G = SRC == SRC_DECODE ? p.dec_groups : 1;
+  const int step = SC / G * kChunk * stride;  // positions per stage
+  auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext,
+                   float* snext, const int32_t* pnext, int32_t* pafter) {
+    if (st + 1 < nst)
+      dma_stage<SRC>(p, lo + (st + 1) * step, stride, knext, snext, pnext, tid, req0);
+    if (SRC != SRC_GATHER && st + 2 < nst)
+      dma_pages<SRC>(p, lo + (st + 2) * step, stride, pafter, tid, req0);
+#pragma unroll
+    for (int u = 0; u < SC; ++u) f(st, u, kcur + u * kChunkBytes, scur + u * kChunk);
+    __syncthreads();
+  };
+  if constexpr (SRC != SRC_GATHER) {
+    dma_pages<SRC>(p, lo, stride, stg.pg[0], tid, req0);
+    __syncthreads();
+  }
+  dma_stage<SRC>(p, lo, stride, stg.k[0], stg.s[0], stg.pg[0], tid, req0);
+  if (SRC != SRC_GATHER && nst > 1) dma_pages<SRC>(p, lo + step, stride, stg.pg[1], tid, req0);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    stage(st, stg.k[0], stg.s[0], stg.k[1], stg.s[1], stg.pg[1], stg.pg[0]);
+    if (st + 1 < nst) stage(st + 1, stg.k[1], stg.s[1], stg.k[0], stg.s[0], stg.pg[0], stg.pg[1]);
+  }
 }
 
 struct __align__(16) GateSmem {
@@ -756,10 +998,10 @@ struct __align__(16) GateSmem {
   int wlo[kWaves], whi[kWaves], wf[kWaves];
 };
 
-template <bool PAGED>
+template <int SRC>
 __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
   __shared__ GateSmem sm;
-  MQA_DECLARE_STAGES(stg);
+  MQA_DECLARE_STAGES(stg, SRC);
   const int tid = threadIdx.x;
   const int w = wave_id();
   const int l = lane_id();
@@ -781,7 +1023,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
     const bool mine = w * parts / kWaves == bi % parts;
     RowState rs[kRowsPerWave];
     QueryRow qr[kRowsPerWave];
-    wave_rows(p, b, rs);
+    wave_rows<SRC>(p, b, rs);
     int wlo = p.keys, whi = 0, wg = 0;
     int frows[kRowsPerWave];
 #pragma unroll
@@ -830,9 +1072,16 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
     if (any_g && hi > lo) {
       FoldOp fo;
       build_fold(fo, p.q, p.weights, frows);
-      // the sample keys lo + j * stride, j < nst * kStageKeys
+      // the sample keys lo + j * stride, j < nst * cps * 64 (in decode, of
+      // each packed request)
+      constexpr int SC = stage_chunks<SRC>();
+      constexpr int SK = stage_keys<SRC>();
+      const int G = SRC == SRC_DECODE ? p.dec_groups : 1;
+      const int cps = SC / G;
+      const int req0 = b * G;
+      const int grp = wave_group<SRC>(p, w);
       int stride;
-      const int nst = gate_sample(hi - lo, stride);
+      const int nst = gate_sample(hi - lo, cps * kChunk, stride);
       uint32_t* hist = sm.hist[w];
       for (int i = l; i < kRowsPerWave * kGateBins; i += kWave) hist[i] = 0;
       float m0[kRowsPerWave], inv[kRowsPerWave];
@@ -849,11 +1098,19 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
       auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
         if (!mine) return;
         const int key = lo + (c * kChunk + l) * stride;
-        const float nh = scl[kStageKeys + l];
         KeyTile kt;
-        load_keys_lds(kt, kc);
+        float sc, nh;
+        if constexpr (SRC == SRC_DECODE) {
+          load_keys_lds(kt, kc);
+          sc = ue8m0(__float_as_uint(scl[l]));
+          nh = decode_nhat(kt, sc);
+        } else {
+          nh = scl[SK + l];
+          sc = scl[l];
+          load_keys_lds(kt, kc);
+        }
         float E[4];
-        score4(E, qr, fo, kt, scl[l]);
+        score4(E, qr, fo, kt, sc);
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) E[i] = __builtin_fmaf(rs[i].beta, nh, E[i]);
 #pragma unroll
@@ -883,21 +1140,11 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
           }
         }
       };
-      auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext,
-                       float* snext) {
-        if (st + 1 < nst)
-          dma_stage<PAGED>(p, lo + (st + 1) * kStageKeys * stride, stride, knext, snext, tid);
-#pragma unroll
-        for (int u = 0; u < kStageChunks; ++u)
-          chunk(st * kStageChunks + u, kcur + u * kChunkBytes, scur + u * kChunk);
-        __syncthreads();
-      };
-      dma_stage<PAGED>(p, lo, stride, stg.k[0], stg.s[0], tid);
-      __syncthreads();
-      for (int st = 0; st < nst; st += 2) {
-        stage(st, stg.k[0], stg.s[0], stg.k[1], stg.s[1]);
-        if (st + 1 < nst) stage(st + 1, stg.k[1], stg.s[1], stg.k[0], stg.s[0]);
-      }
+      sample_stages<SRC>(p, stg, lo, stride, nst, req0, tid,
+                         [&](int st, int u, const uint8_t* kc, const float* scl) {
+                           if (SRC == SRC_DECODE && (u & (G - 1)) != grp) return;
+                           chunk(st * cps + u / G, kc, scl);
+                         });
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         RowState& r = rs[i];
@@ -1009,10 +1256,10 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
 // threshold goes into the first fine bin that completes the row's count, with
 // the gate's gap rule (down to the next sampled score). Returns at
 // once when nothing is queued.
-template <bool PAGED>
+template <int SRC>
 __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
   __shared__ GateSmem sm;
-  MQA_DECLARE_STAGES(stg);
+  MQA_DECLARE_STAGES(stg, SRC);
   const int tid = threadIdx.x;
   const int w = wave_id();
   const int l = lane_id();
@@ -1026,7 +1273,7 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
     const int b = p.fqueue[qi];
     RowState rs[kRowsPerWave];
     QueryRow qr[kRowsPerWave];
-    wave_rows(p, b, rs);
+    wave_rows<SRC>(p, b, rs);
     int wlo = p.keys, whi = 0, wfine = 0;
     int frows[kRowsPerWave], rbin[kRowsPerWave], rneed[kRowsPerWave], rnext[kRowsPerWave];
     float m0[kRowsPerWave], inv[kRowsPerWave];
@@ -1056,8 +1303,14 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
     int lo, hi, unused;
     block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, 0, p.keys, lo, hi, unused);
     if (hi > lo) {
+      constexpr int SC = stage_chunks<SRC>();
+      constexpr int SK = stage_keys<SRC>();
+      const int G = SRC == SRC_DECODE ? p.dec_groups : 1;
+      const int cps = SC / G;
+      const int req0 = b * G;
+      const int grp = wave_group<SRC>(p, w);
       int stride;
-      const int nst = gate_sample(hi - lo, stride);
+      const int nst = gate_sample(hi - lo, cps * kChunk, stride);
       FoldOp fo;
       build_fold(fo, p.q, p.weights, frows);
       uint32_t* hist = sm.hist[w];
@@ -1067,11 +1320,19 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
       auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
         if (!wfine) return;
         const int key = lo + (c * kChunk + l) * stride;
-        const float nh = scl[kStageKeys + l];
         KeyTile kt;
-        load_keys_lds(kt, kc);
+        float sc, nh;
+        if constexpr (SRC == SRC_DECODE) {
+          load_keys_lds(kt, kc);
+          sc = ue8m0(__float_as_uint(scl[l]));
+          nh = decode_nhat(kt, sc);
+        } else {
+          nh = scl[SK + l];
+          sc = scl[l];
+          load_keys_lds(kt, kc);
+        }
         float E[4];
-        score4(E, qr, fo, kt, scl[l]);
+        score4(E, qr, fo, kt, sc);
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) E[i] = __builtin_fmaf(rs[i].beta, nh, E[i]);
 #pragma unroll
@@ -1088,21 +1349,11 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
           atomicAdd(&hist[i * kGateBins + f], 1u);
         }
       };
-      auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext,
-                       float* snext) {
-        if (st + 1 < nst)
-          dma_stage<PAGED>(p, lo + (st + 1) * kStageKeys * stride, stride, knext, snext, tid);
-#pragma unroll
-        for (int u = 0; u < kStageChunks; ++u)
-          chunk(st * kStageChunks + u, kcur + u * kChunkBytes, scur + u * kChunk);
-        __syncthreads();
-      };
-      dma_stage<PAGED>(p, lo, stride, stg.k[0], stg.s[0], tid);
-      __syncthreads();
-      for (int st = 0; st < nst; st += 2) {
-        stage(st, stg.k[0], stg.s[0], stg.k[1], stg.s[1]);
-        if (st + 1 < nst) stage(st + 1, stg.k[1], stg.s[1], stg.k[0], stg.s[0]);
-      }
+      sample_stages<SRC>(p, stg, lo, stride, nst, req0, tid,
+                         [&](int st, int u, const uint8_t* kc, const float* scl) {
+                           if (SRC == SRC_DECODE && (u & (G - 1)) != grp) return;
+                           chunk(st * cps + u / G, kc, scl);
+                         });
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -1155,10 +1406,10 @@ struct __align__(16) ScanSmem {
 
 // SPLIT: the launch uses key segments (p.nseg > 1); the instance without
 // them keeps no segment state.
-template <bool SPLIT, bool PAGED>
+template <bool SPLIT, int SRC>
 __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
   __shared__ ScanSmem sm;
-  MQA_DECLARE_STAGES(stg);
+  MQA_DECLARE_STAGES(stg, SRC);
   const int tid = threadIdx.x;
   const int w = wave_id();
   const int l = lane_id();
@@ -1174,7 +1425,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
     const int seg = SPLIT ? bi % nseg : 0;
     RowState rs[kRowsPerWave];
     QueryRow qr[kRowsPerWave];
-    wave_rows(p, b, rs);
+    wave_rows<SRC>(p, b, rs);
     int wlo = p.keys, whi = 0;
     int frows[kRowsPerWave];
 #pragma unroll
@@ -1206,8 +1457,9 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
     if (hi > lo) {
       FoldOp fo;
       build_fold(fo, p.q, p.weights, frows);
-      const SlabRefs sr = slab_refs(p, b, sm.hist[w], 2 * p.topk, SPLIT ? seg : -1);
-      scan_rows<false, PAGED>(p, stg, qr, fo, rs, M_GATED, lo, hi, sr);
+      const SlabRefs sr = slab_refs<SRC>(p, b, sm.hist[w], 2 * p.topk, SPLIT ? seg : -1);
+      scan_rows<false, SRC>(p, stg, qr, fo, rs, M_GATED, lo, hi, sr,
+                            b * (SRC == SRC_DECODE ? p.dec_groups : 1), wave_group<SRC>(p, w));
     }
     if (l == 0) {
 #pragma unroll
@@ -1247,10 +1499,11 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
 // row's k-th exact score (the k records found score at least min(tau, the
 // lowest taken interval); more than k taken records bound it by t_hi), or
 // -inf.
-template <bool PAGED, class Emit>
+template <int SRC, class Emit>
 __device__ bool select_interval(const FusedParams& p, float* sE, int32_t* sI, int n, int k,
                                 float beta, float Thi, bool thi_lt, float hint_lo, float hint_hi,
-                                const QueryRow& qr, uint32_t* hist, float& low, Emit emit) {
+                                const QueryRow& qr, int req, uint32_t* hist, float& low,
+                                Emit emit) {
   const int l = lane_id();
   constexpr int kBins = kHistWords;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -1403,12 +1656,12 @@ __device__ bool select_interval(const FusedParams& p, float* sE, int32_t* sI, in
       ki[t] = sI[j < nb ? j : nb - 1] & (int)kKeyMask;
     }
     const int j = b0 + l;
-    s_ = p.keyinfo[2 * (int64_t)(sI[j < nb ? j : nb - 1] & (int)kKeyMask)];
+    s_ = scan_scale<SRC>(p, sI[j < nb ? j : nb - 1] & (int)kKeyMask, req);
   };
   group_refs(0, keyidx, sc);
   for (int b0 = 0; b0 < nb; b0 += kWave) {
     KeyTile kt;
-    load_keys_rows<PAGED>(kt, p, keyidx);
+    load_keys_rows<SRC>(kt, p, keyidx, req);
     int kn[4] = {0, 0, 0, 0};
     float scn = 0.f;
     if (b0 + kWave < nb) group_refs(b0 + kWave, kn, scn);
@@ -1456,7 +1709,7 @@ __device__ bool select_interval(const FusedParams& p, float* sE, int32_t* sI, in
 __device__ __forceinline__ void queue_exact(const FusedParams& p, int r) {
   if (lane_id() != 0) return;
   p.xrow[r] = 1;
-  const int b = r / kBlockRows;
+  const int b = block_of(p, r);
   if (atomicExch(&p.xflag[b], 1u) == 0u) p.xqueue[atomicAdd(&p.header[H_XQ], 1u)] = b;
 }
 
@@ -1474,7 +1727,7 @@ __device__ __forceinline__ void queue_rescan(const FusedParams& p, int r, float 
 }
 
 // Select: one wave per row.
-template <bool PAGED>
+template <int SRC>
 __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_eu(4))) void fused_select_kernel(FusedParams p) {
   __shared__ uint32_t hist[kSelWaves][kHistWords];
   const int w = wave_id();
@@ -1533,8 +1786,9 @@ __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_
         hlo = ri.thr;
         hhi = m0 + (m0 - ri.thr);
       }
-      ok = select_interval<PAGED>(p, sE, sI, cnt, k, p.beta[r], thi, thi_lt, hlo, hhi, qr, hist[w], low,
-                           [&](int sl, int idx) { o[sl] = idx - s; });
+      const int req = p.dec_rows ? r / p.dec_rows : 0;
+      ok = select_interval<SRC>(p, sE, sI, cnt, k, p.beta[r], thi, thi_lt, hlo, hhi, qr, req,
+                                hist[w], low, [&](int sl, int idx) { o[sl] = idx - s; });
       if (stats && l == 0) {
         atomicAdd(&p.header[ok ? H_GATED : H_UNCERT], 1u);
         atomicAdd(reinterpret_cast<unsigned long long*>(&p.header[H_CAND_LO]),
@@ -1561,7 +1815,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_
 // scoring >= the row's bound (> in a strict round) get slab slots from the
 // row's counter (slots past the slab are counted, not written), and the keys
 // strictly above it are counted apart.
-template <bool PAGED>
+template <int SRC>
 __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, int round) {
   const int l = lane_id();
   const int nq = (int)p.header[H_RQ + 2 * round];
@@ -1576,6 +1830,7 @@ __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, i
     if (it >= items) break;
     const int r = queue[it % nq];
     const int slice = it / nq;
+    const int req = p.dec_rows ? r / p.dec_rows : 0;
     int s, e;
     row_range(p, r, s, e);
     const int a = s > slice * kRescanKeys ? s : slice * kRescanKeys;
@@ -1595,10 +1850,10 @@ __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, i
         keyidx[t] = j < b ? j : b - 1;
       }
       KeyTile kt;
-      load_keys_rows<PAGED>(kt, p, keyidx);
+      load_keys_rows<SRC>(kt, p, keyidx, req);
       const int key = k0 + l;
       const bool valid = key < b;
-      const float E = score_chunk_exact(qr, kt) * p.keyinfo[2 * (int64_t)(valid ? key : b - 1)];
+      const float E = score_chunk_exact(qr, kt) * scan_scale<SRC>(p, valid ? key : b - 1, req);
       const bool pass = valid && (strict ? E > low : E >= low);
       const uint64_t m = __ballot(pass);
       if (m == 0) continue;
@@ -1700,10 +1955,10 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_finish_kernel(FusedPa
 // ---------------------------------------------------------------------------
 // Exact rescan of the queued blocks: exact (bf16 MFMA) scores of every key of
 // the flagged rows with a streaming top-k merge, then an exact select.
-template <bool PAGED>
+template <int SRC>
 __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
   __shared__ ScanSmem sm;
-  MQA_DECLARE_STAGES(stg);
+  MQA_DECLARE_STAGES(stg, SRC);
   const int tid = threadIdx.x;
   const int w = wave_id();
   const int l = lane_id();
@@ -1717,7 +1972,7 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
     const int b = p.xqueue[qi];
     RowState rs[kRowsPerWave];
     QueryRow qr[kRowsPerWave];
-    wave_rows(p, b, rs);
+    wave_rows<SRC>(p, b, rs);
     int wlo = p.keys, whi = 0;
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
@@ -1732,9 +1987,10 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
     int lo, hi, unused;
     block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, 0, p.keys, lo, hi, unused);
     if (hi > lo) {
-      SlabRefs sr = slab_refs(p, b, sm.hist[w], k);
+      SlabRefs sr = slab_refs<SRC>(p, b, sm.hist[w], k);
       FoldOp none;
-      scan_rows<true, PAGED>(p, stg, qr, none, rs, M_EXACT, lo, hi, sr);
+      scan_rows<true, SRC>(p, stg, qr, none, rs, M_EXACT, lo, hi, sr,
+                           b * (SRC == SRC_DECODE ? p.dec_groups : 1), wave_group<SRC>(p, w));
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         RowState& r = rs[i];
@@ -1833,47 +2089,68 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_sort_kernel(FusedPara
 namespace mqa {
 
 // The launch sequence of one row batch, over one key source.
-template <bool PAGED>
+template <int SRC>
+int fused_launch_scan(const FusedParams* p, int grid, hipStream_t stream, hipEvent_t scan_begin,
+                      hipEvent_t scan_end);
+
+template <int SRC>
 int fused_launch_all(const FusedParams* p, int grid, hipStream_t stream, hipEvent_t scan_begin,
                      hipEvent_t scan_end) {
   hipError_t e;
   // workgroup 0 plans; the others (about one per CU, at most the units of
   // bound work) compute the error bounds
-  const int units = (p->keys + 3) / 4 + p->rows;
+  const int units = (SRC == SRC_DECODE ? 0 : (p->keys + 3) / 4) + p->rows;
   const int waves_per_wg = kPrologueThreads / kWave;
   int bwg = (units + waves_per_wg - 1) / waves_per_wg;
   bwg = bwg < grid ? bwg : grid;
   bwg = bwg < 1 ? 1 : bwg;
-  hipLaunchKernelGGL(fused_prologue_kernel<PAGED>, dim3(1 + bwg), dim3(kPrologueThreads), 0,
+  hipLaunchKernelGGL(fused_prologue_kernel<SRC>, dim3(1 + bwg), dim3(kPrologueThreads), 0,
                      stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(fused_gate_kernel<PAGED>, dim3(p->scan_grid), dim3(kThreads), 0, stream, *p);
+  // paged prefill: the prologue compacted the keys into p->kc; every later
+  // kernel reads them there as gathered keys
+  if constexpr (SRC == SRC_PAGED) {
+    FusedParams g = *p;
+    g.k = p->kc;
+    g.table = nullptr;
+    return fused_launch_scan<SRC_GATHER>(&g, grid, stream, scan_begin, scan_end);
+  } else {
+    return fused_launch_scan<SRC>(p, grid, stream, scan_begin, scan_end);
+  }
+}
+
+// Everything after the prologue.
+template <int SRC>
+int fused_launch_scan(const FusedParams* p, int grid, hipStream_t stream, hipEvent_t scan_begin,
+                      hipEvent_t scan_end) {
+  hipError_t e;
+  hipLaunchKernelGGL(fused_gate_kernel<SRC>, dim3(p->scan_grid), dim3(kThreads), 0, stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(fused_refine_kernel<PAGED>, dim3(grid), dim3(kThreads), 0, stream, *p);
+  hipLaunchKernelGGL(fused_refine_kernel<SRC>, dim3(grid), dim3(kThreads), 0, stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (scan_begin && (e = hipEventRecord(scan_begin, stream)) != hipSuccess) return (int)e;
   if (p->nseg > 1)
-    hipLaunchKernelGGL((fused_topk_kernel<true, PAGED>), dim3(p->scan_grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((fused_topk_kernel<true, SRC>), dim3(p->scan_grid), dim3(kThreads), 0,
                        stream, *p);
   else
-    hipLaunchKernelGGL((fused_topk_kernel<false, PAGED>), dim3(p->scan_grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((fused_topk_kernel<false, SRC>), dim3(p->scan_grid), dim3(kThreads), 0,
                        stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (scan_end && (e = hipEventRecord(scan_end, stream)) != hipSuccess) return (int)e;
   const int sel = (p->rows + kSelWaves - 1) / kSelWaves;
-  hipLaunchKernelGGL(fused_select_kernel<PAGED>, dim3(sel), dim3(kSelWaves * kWave), 0, stream,
+  hipLaunchKernelGGL(fused_select_kernel<SRC>, dim3(sel), dim3(kSelWaves * kWave), 0, stream,
                      *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   const int fin = sel < 256 ? sel : 256;
   for (int round = 0; round < kRescanRounds; ++round) {
-    hipLaunchKernelGGL(fused_rescan_kernel<PAGED>, dim3(2 * grid), dim3(kThreads), 0, stream, *p,
+    hipLaunchKernelGGL(fused_rescan_kernel<SRC>, dim3(2 * grid), dim3(kThreads), 0, stream, *p,
                        round);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
     hipLaunchKernelGGL(fused_finish_kernel, dim3(fin), dim3(kSelWaves * kWave), 0, stream, *p,
                        round);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
-  hipLaunchKernelGGL(fused_exact_kernel<PAGED>, dim3(grid), dim3(kThreads), 0, stream, *p);
+  hipLaunchKernelGGL(fused_exact_kernel<SRC>, dim3(grid), dim3(kThreads), 0, stream, *p);
   if (p->flags & 64u) {
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
     hipLaunchKernelGGL(fused_sort_kernel, dim3(sel), dim3(kSelWaves * kWave), 0, stream, *p);
@@ -1885,19 +2162,23 @@ int fused_launch_all(const FusedParams* p, int grid, hipStream_t stream, hipEven
 
 extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t stream,
                                 hipEvent_t scan_begin, hipEvent_t scan_end) {
-  return p->table ? mqa::fused_launch_all<true>(p, grid, stream, scan_begin, scan_end)
-                  : mqa::fused_launch_all<false>(p, grid, stream, scan_begin, scan_end);
+  if (p->dec_rows)
+    return mqa::fused_launch_all<mqa::SRC_DECODE>(p, grid, stream, scan_begin, scan_end);
+  return p->table ? mqa::fused_launch_all<mqa::SRC_PAGED>(p, grid, stream, scan_begin, scan_end)
+                  : mqa::fused_launch_all<mqa::SRC_GATHER>(p, grid, stream, scan_begin, scan_end);
 }
 
 extern "C" int mqa_fused_occupancy(int* wg_per_cu) {
-  // the persistent kernels' workgroups per CU, over both key sources
+  // the persistent kernels' workgroups per CU, over the gathered and decode
+  // sources (paged prefill runs the gathered kernels)
   const void* kernels[] = {
-      reinterpret_cast<const void*>(mqa::fused_topk_kernel<false, false>),
-      reinterpret_cast<const void*>(mqa::fused_topk_kernel<false, true>),
-      reinterpret_cast<const void*>(mqa::fused_exact_kernel<false>),
-      reinterpret_cast<const void*>(mqa::fused_exact_kernel<true>),
-      reinterpret_cast<const void*>(mqa::fused_gate_kernel<false>),
-      reinterpret_cast<const void*>(mqa::fused_gate_kernel<true>)};
+      reinterpret_cast<const void*>(mqa::fused_topk_kernel<false, mqa::SRC_GATHER>),
+      reinterpret_cast<const void*>(mqa::fused_topk_kernel<false, mqa::SRC_DECODE>),
+      reinterpret_cast<const void*>(mqa::fused_topk_kernel<true, mqa::SRC_DECODE>),
+      reinterpret_cast<const void*>(mqa::fused_exact_kernel<mqa::SRC_GATHER>),
+      reinterpret_cast<const void*>(mqa::fused_exact_kernel<mqa::SRC_DECODE>),
+      reinterpret_cast<const void*>(mqa::fused_gate_kernel<mqa::SRC_GATHER>),
+      reinterpret_cast<const void*>(mqa::fused_gate_kernel<mqa::SRC_DECODE>)};
   int best = 1 << 30;
   for (const void* f : kernels) {
     int n = 0;

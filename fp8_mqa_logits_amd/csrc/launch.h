@@ -73,10 +73,18 @@ struct FusedParams {
   // table[j >> page_shift] of k (clamped to [0, num_pages)), slot
   // j & (2^page_shift - 1); a page of P = 2^page_shift tokens holds their
   // P x 128 e4m3 codes, then their P 4-byte UE8M0 scale words
-  // (page_bytes = 132 P). scales is unused then.
+  // (page_bytes = 132 P). scales is unused then: the prologue decodes the
+  // scales into keyinfo and copies the keys to kc, and the kernels after it
+  // read kc like gathered keys.
   const int32_t* table;
   int page_shift, num_pages;
   int64_t page_bytes;
+  uint8_t* kc;  // [keys][128] paged prefill: the keys compacted by the prologue
+  // Decode-shaped calls (dec_rows > 0): nreq requests of dec_rows rows each
+  // (row r belongs to request r / dec_rows); request q's key positions map
+  // to pages through table row q (table_stride entries). Blocks pack
+  // dec_groups requests; keys is the positions' bound, and keyinfo is unused.
+  int dec_rows, dec_groups, nreq, table_stride;
   float* slabE;      // [nblocks * 32 rows][kSlabRow] candidate scores
   int32_t* slabI;    // [nblocks * 32 rows][kSlabRow] candidate keys
   float* tmpE;       // [grid][8 waves][kTmp] merge buffers

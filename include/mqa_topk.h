@@ -160,6 +160,15 @@ int mqa_topk_prefill_static(const uint8_t* q, const uint8_t* k, const float* sca
                             void* stream);
 
 /*
+ * Bytes of device workspace one mqa_topk_prefill_paged call over `rows` rows
+ * and `keys` keys needs on HIP device `device`: workspace_size(rows, device)
+ * plus 128 bytes per key for the keys compacted out of the pages. Returns 0
+ * if the device does not exist or is not gfx950, or the sizes are out of
+ * range.
+ */
+size_t workspace_size_paged(int rows, int keys, int device);
+
+/*
  * The fused path reading the keys straight from the paged indexer K-cache, the
  * UE8M0 decode fused (PR #60618, "Motivation": an indexer cache entry is 132 B
  * per token, a 128-byte e4m3 key and a 4-byte scale; API page,
@@ -178,7 +187,11 @@ int mqa_topk_prefill_static(const uint8_t* q, const uint8_t* k, const float* sca
  * Several requests share one call as with mqa_topk_prefill: the caller lays
  * their keys out in the key numbering (each request's first key at a
  * multiple of page_size, its pages in its table order) and gives every row
- * its request's range. Workspace, flags, output and return codes as for
+ * its request's range. The first kernel reads every key once from its page
+ * (for its error bound and its decoded scale) and copies it into the
+ * workspace, where the later kernels, which read each key once per block of
+ * rows, find it contiguous. Workspace: >= workspace_size_paged(rows, keys,
+ * current device) bytes, 256-B aligned. Flags, output and return codes as for
  * mqa_topk_prefill, whose results it reproduces on the gathered keys and
  * decoded scales (bit for bit under MQA_FLAG_DETERMINISTIC).
  */
@@ -187,6 +200,50 @@ int mqa_topk_prefill_paged(const uint8_t* q, const uint8_t* cache, const int32_t
                            const int32_t* starts, const int32_t* ends, int32_t* out, int rows,
                            int keys, int topk, void* workspace, size_t workspace_bytes,
                            unsigned flags, void* stream);
+
+/*
+ * Bytes of device workspace one mqa_topk_decode_paged call over `requests`
+ * requests of `rows_per_request` rows needs on HIP device `device`: the
+ * mqa_topk_prefill workspace of one batch of requests (a batch holds at most
+ * 16384 rows and 512 workgroups of requests, 4, 2 or 1 requests to a
+ * workgroup for rows_per_request <= 8, <= 16, <= 32). Returns 0 if the device
+ * does not exist or is not gfx950, or the sizes are out of range.
+ */
+size_t workspace_size_decode(int requests, int rows_per_request, int device);
+
+/*
+ * The fused path shaped for decode (PR #60618's review thread, the decode
+ * follow-up: many requests of a few query rows each, such as speculative
+ * tokens, each request with its own long context): row r is row r % R of
+ * request r / R (R = rows_per_request), and sees positions [s, e) of its own
+ * request's keys, s and e the row's starts/ends clamped to [0, K], K =
+ * min(table_stride * page_size, MQA_MAX_KEYS). Position j of request i is
+ * slot j % page_size of cache page page_table[i * table_stride + j /
+ * page_size] (the cache layout of mqa_topk_prefill_paged; an entry outside
+ * [0, num_pages) is clamped into it, and entries past a request's visible
+ * positions are never used for its results). Each row's output holds its
+ * top-k positions as position - s, unordered, -1 padded, with the conventions
+ * of mqa_topk_prefill (flags included).
+ *   q        [requests * R, 32, 128] e4m3, 16-B aligned
+ *   cache    [num_pages][page_size * 132] bytes, 16-B aligned
+ *   page_table [requests][table_stride] int32, 4-B aligned
+ *   weights  [requests * R, 32] fp32; starts, ends [requests * R] int32
+ *   out      [requests * R, topk] int32, 16-B aligned
+ *   requests >= 1, R in [1, 32], requests * R <= MQA_MAX_ROWS, table_stride
+ *   >= 1, page_size a power of two in [4, MQA_MAX_KEYS], num_pages >= 1,
+ *   topk in {512, 1024, 2048}
+ *   workspace: >= workspace_size_decode(requests, R, current device) bytes,
+ *   256-B aligned, owned by the call until the stream reaches its end.
+ * Requests run in batches (workspace_size_decode) in order on `stream`. A
+ * request's rows share its key copies; rows of fewer than 8 per request
+ * leave row slots of their workgroup empty. Returns MQA_OK or an MQA_ERR_*
+ * code (checked in the order NULL, ALIGN, SHAPE, DEVICE, WORKSPACE).
+ */
+int mqa_topk_decode_paged(const uint8_t* q, const uint8_t* cache, const int32_t* page_table,
+                          int table_stride, int page_size, int num_pages, const float* weights,
+                          const int32_t* starts, const int32_t* ends, int32_t* out, int requests,
+                          int rows_per_request, int topk, void* workspace,
+                          size_t workspace_bytes, unsigned flags, void* stream);
 
 /*
  * Dense logits (the first half of the dense path the fused op replaces: PR

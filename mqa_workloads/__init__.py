@@ -382,6 +382,120 @@ def paged_cache(k: np.ndarray, scale_bytes: np.ndarray, page_size: int, seed: in
     return cache, table
 
 
+@dataclasses.dataclass
+class DecodeWorkload:
+    """Decode-shaped inputs: `requests` requests of R query rows each (row r
+    is row r % R of request r // R; row j of a request with context length L
+    sees positions [0, L - (R - 1 - j)), as speculative tokens do), the keys
+    of each request in a paged indexer cache, and the same keys gathered and
+    concatenated (request q's keys at offset base[q]) for the oracle."""
+    name: str
+    requests: int
+    R: int
+    topk: int
+    page_size: int
+    q: np.ndarray            # uint8 [rows, 32, 128]
+    weights: np.ndarray      # float32 [rows, 32]
+    starts: np.ndarray       # int32 [rows], positions in the row's request
+    ends: np.ndarray         # int32 [rows]
+    lens: np.ndarray         # int32 [requests] context lengths
+    base: np.ndarray         # int64 [requests] offsets into k_cat
+    k_cat: np.ndarray        # uint8 [sum(lens), 128]
+    sb_cat: np.ndarray       # uint8 [sum(lens), 4]
+    cache: np.ndarray        # uint8 [pages, 132 * page_size]
+    table: np.ndarray        # int32 [requests, table_stride], -1 past a request's pages
+    seed: int
+
+    @property
+    def rows(self) -> int:
+        return self.requests * self.R
+
+    def visible_pairs(self) -> int:
+        return int(np.maximum(self.ends.astype(np.int64) - self.starts, 0).sum())
+
+    def gathered(self) -> Workload:
+        """The same problem over the concatenated keys (ranges shifted by
+        each row's request offset): outputs (key - start) are identical."""
+        off = np.repeat(self.base, self.R).astype(np.int64)
+        return Workload(self.name + "_gathered", self.rows, int(self.k_cat.shape[0]), self.topk,
+                        self.q, self.k_cat, self.sb_cat, self.weights,
+                        (self.starts + off).astype(np.int32), (self.ends + off).astype(np.int32),
+                        self.seed)
+
+
+def decode(requests: int, R: int, lens, topk: int, page_size: int = 64, seed: int = 1,
+           spare_pages: int = 5, table_extra: int = 2, name: str = "decode") -> DecodeWorkload:
+    """Seeded decode inputs with the given context lengths (one per request):
+    config-3-like q, keys, scales and weights; each request's pages are taken
+    from a random permutation of all pages (spare pages of random bytes in
+    between), its table row lists them, then table_extra entries of -1."""
+    rng = np.random.Generator(np.random.PCG64(SEED_BASE + 1000 + seed))
+    lens = np.asarray(lens, np.int64)
+    assert lens.shape == (requests,) and (lens >= 1).all()
+    rows = requests * R
+    q = encode_e4m3(_normal(rng, (rows, HEADS, DIM)))
+    total = int(lens.sum())
+    k_cat = encode_e4m3(_normal(rng, (total, DIM)))
+    sb_cat = _scales(rng, total)
+    w = _weights(rng, rows)
+    base = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    j = np.tile(np.arange(R), requests)
+    ends = (np.repeat(lens, R) - (R - 1 - j)).clip(0).astype(np.int32)
+    starts = np.zeros(rows, np.int32)
+    npg = -(-lens // page_size)
+    pages = int(npg.sum()) + spare_pages
+    cache = rng.integers(0, 256, (pages, page_size * (DIM + 4)), dtype=np.uint8)
+    perm = rng.permutation(pages)
+    stride = int(npg.max()) + table_extra
+    table = np.full((requests, stride), -1, np.int32)
+    at = 0
+    for qi in range(requests):
+        for i in range(int(npg[qi])):
+            pg = int(perm[at])
+            at += 1
+            table[qi, i] = pg
+            lo = int(base[qi]) + i * page_size
+            n = min(page_size, int(lens[qi]) - i * page_size)
+            cache[pg, : n * DIM] = k_cat[lo: lo + n].reshape(-1)
+            cache[pg, page_size * DIM: page_size * DIM + 4 * n] = sb_cat[lo: lo + n].reshape(-1)
+    return DecodeWorkload(name, requests, R, topk, page_size, q, w, starts, ends,
+                          lens.astype(np.int32), base, k_cat, sb_cat, cache, table, seed)
+
+
+def decode_device(requests: int, R: int, ctx: int, topk: int, page_size: int = 64,
+                  seed: int = 1, device="cuda"):
+    """Decode inputs generated on the device (torch's seeded generator), for
+    benchmark sizes the host would take minutes to draw: every request has
+    context ctx, q and keys are N(0,1) rounded to e4m3 by torch's
+    round-to-nearest conversion, scale exponents uniform in [-4, 0], weights
+    N(0,1)/sqrt(32), rows ranged as in decode(); request q's pages are
+    q * (ctx / page_size) + i (one contiguous run of the cache each).
+    Returns a dict of device tensors."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(SEED_BASE + 2000 + seed)
+    rows = requests * R
+    npg = -(-ctx // page_size)
+    pages = requests * npg
+    f8 = torch.float8_e4m3fn
+    q = torch.randn((rows, HEADS, DIM), generator=g, device=device).to(f8).view(torch.uint8)
+    w = (torch.randn((rows, HEADS), generator=g, device=device) / math.sqrt(HEADS)).float()
+    cache = torch.empty((pages, page_size * (DIM + 4)), dtype=torch.uint8, device=device)
+    for p0 in range(0, pages, 4096):
+        p1 = min(pages, p0 + 4096)
+        keys = torch.randn((p1 - p0, page_size * DIM), generator=g, device=device).to(f8)
+        cache[p0:p1, : page_size * DIM] = keys.view(torch.uint8)
+        e = torch.randint(123, 128, (p1 - p0, page_size, 1), generator=g, device=device,
+                          dtype=torch.int32).to(torch.uint8)
+        cache[p0:p1, page_size * DIM:] = e.expand(-1, -1, 4).reshape(p1 - p0, -1)
+    table = torch.arange(pages, dtype=torch.int32, device=device).view(requests, npg)
+    j = torch.arange(R, device=device).repeat(requests)
+    ends = (ctx - (R - 1 - j)).clamp(min=0).to(torch.int32)
+    starts = torch.zeros(rows, dtype=torch.int32, device=device)
+    return {"q": q, "weights": w, "cache": cache, "table": table, "starts": starts, "ends": ends,
+            "rows": rows, "pairs": int(ends.sum().item())}
+
+
 def sample_rows(wl: Workload, n: int = 256, seed: int = 7) -> np.ndarray:
     """Seeded row sample for oracle checks of large workloads. With groups
     (config 5) it is stratified: half uniform over ungrouped rows, the rest

@@ -26,7 +26,9 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert set(names) == {"workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static",
-                          "mqa_topk_prefill_paged", "mqa_logits_dense",
+                          "mqa_topk_prefill_paged", "workspace_size_paged",
+                          "workspace_size_decode",
+                          "mqa_topk_decode_paged", "mqa_logits_dense",
                           "mqa_topk_dense", "mqa_key_scales", "mqa_scan_time", "mqa_mfma_peak",
                           "mqa_fp8_mfma_probe",
                           "mqa_strerror"}
@@ -197,6 +199,33 @@ def test_paged_prefill_errors():
         assert _paged(page=1 << 20) == 5
 
 
+def _decode(**kw):
+    a = dict(q=A16, cache=A16, table=A16, stride=8, page=64, pages=64, weights=A16, starts=A16,
+             ends=A16, out=A16, requests=16, R=8, topk=512, ws=0x20000, wsb=1 << 40, flags=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return mqa.load().mqa_topk_decode_paged(P(a["q"]), P(a["cache"]), P(a["table"]), a["stride"],
+                                            a["page"], a["pages"], P(a["weights"]),
+                                            P(a["starts"]), P(a["ends"]), P(a["out"]),
+                                            a["requests"], a["R"], a["topk"], P(a["ws"]),
+                                            a["wsb"], a["flags"], None)
+
+
+def test_decode_errors():
+    assert _decode(table=0) == 1
+    assert _decode(out=0) == 1
+    assert _decode(cache=MIS) == 2
+    assert _decode(table=0x10001) == 2
+    for kw in (dict(R=0), dict(R=33), dict(requests=0), dict(stride=0), dict(page=24),
+               dict(pages=0), dict(topk=100), dict(requests=1 << 20, R=2)):
+        assert _decode(**kw) == 3, kw
+    assert mqa.load().workspace_size_decode(16, 8, 0) == 0 or not _no_gpu()
+    assert mqa.load().workspace_size_decode(16, 33, 0) == 0
+    if _no_gpu():
+        assert _decode() == 5
+        assert _decode(R=1, requests=4096) == 5
+
+
 def test_fp8_probe_errors():
     P = ctypes.c_void_p
     L = mqa.load()
@@ -249,6 +278,16 @@ def test_binding_checks_every_shape_first():
         mqa.mqa_topk_prefill_paged(**dict(pg, block_table=i32(9)))
     with pytest.raises(ValueError, match="page_size"):
         mqa.mqa_topk_prefill_paged(**dict(pg, page_size=48))
+    # the decode entry: rows = requests * rows_per_request, a 2-D page table
+    dc = dict(q=u8(16, 32, 128), cache=u8(10, 64 * 132), page_table=i32(2, 5), page_size=64,
+              weights=f32(16, 32), starts=i32(16), ends=i32(16), topk=512, rows_per_request=8)
+    with pytest.raises(ValueError, match="rows"):
+        mqa.mqa_topk_decode_paged(**dict(dc, rows_per_request=4))
+    with pytest.raises(ValueError, match="page_table"):
+        mqa.mqa_topk_decode_paged(**dict(dc, page_table=i32(10)))
+    for name, t in (("cache", u8(10, 64 * 131)), ("weights", f32(16, 31)), ("ends", i32(15))):
+        with pytest.raises(ValueError, match="shape"):
+            mqa.mqa_topk_decode_paged(**dict(dc, **{name: t}))
 
 
 def test_paged_cache_layout_round_trips():
