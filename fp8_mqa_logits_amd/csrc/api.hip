@@ -128,21 +128,20 @@ Layout layout(int rows, const DeviceInfo& d, int kc_keys = 0) {
   return layout_blocks((rows + mqa::kFusedBlockRows - 1) / mqa::kFusedBlockRows, d, kc_keys);
 }
 
-// Decode layout: requests packed dec_groups(R) to a block, a batch holding at
-// most kMaxBatchRows rows and kMaxBatchRows / 32 blocks.
-int dec_groups(int rows_per_request) {
-  return rows_per_request <= 8 ? 4 : (rows_per_request <= 16 ? 2 : 1);
+// Decode layout: a request's rows in parts of up to 8 rows, four parts to a
+// block; a batch holds at most kMaxBatchRows rows and kMaxBatchRows / 32
+// blocks.
+constexpr int kDecPack = 4;
+int dec_parts(int rows_per_request) { return (rows_per_request + 7) / 8; }
+int dec_blocks(int requests, int rows_per_request) {
+  return (requests * dec_parts(rows_per_request) + kDecPack - 1) / kDecPack;
 }
 int dec_batch(int requests, int rows_per_request) {
-  const int g = dec_groups(rows_per_request);
   int b = mqa::kMaxBatchRows / rows_per_request;
-  const int by_blocks = mqa::kMaxBatchRows / mqa::kFusedBlockRows * g;
+  const int by_blocks = mqa::kMaxBatchRows / mqa::kFusedBlockRows * kDecPack /
+                        dec_parts(rows_per_request);
   b = b < by_blocks ? b : by_blocks;
   return requests < b ? requests : b;
-}
-int dec_blocks(int requests, int rows_per_request) {
-  const int g = dec_groups(rows_per_request);
-  return (requests + g - 1) / g;
 }
 
 int batch_rows(int rows) { return rows < mqa::kMaxBatchRows ? rows : mqa::kMaxBatchRows; }
@@ -270,7 +269,7 @@ int prefill_batches(const uint8_t* q, const uint8_t* k, const float* scales,
     p.num_pages = src.num_pages;
     p.page_bytes = (int64_t)(MQA_HEAD_DIM + 4) << src.page_shift;
     p.dec_rows = 0;
-    p.dec_groups = 1;
+    p.dec_parts = 1;
     p.nreq = 0;
     p.table_stride = 0;
     const int grid = L.grid < p.nblocks ? L.grid : p.nblocks;
@@ -289,7 +288,6 @@ int decode_batches(const uint8_t* q, const uint8_t* cache, const int32_t* table,
                    int table_stride, int shift, int num_pages, const float* weights,
                    const int32_t* starts, const int32_t* ends, int32_t* out, int requests, int R,
                    int topk, uint8_t* ws, const DeviceInfo& d, unsigned flags, void* stream) {
-  const int G = dec_groups(R);
   const int nb = dec_batch(requests, R);
   const Layout L = layout_blocks(dec_blocks(nb, R), d);
   const int64_t span = (int64_t)table_stride << shift;
@@ -322,7 +320,7 @@ int decode_batches(const uint8_t* q, const uint8_t* cache, const int32_t* table,
     p.num_pages = num_pages;
     p.page_bytes = (int64_t)(MQA_HEAD_DIM + 4) << shift;
     p.dec_rows = R;
-    p.dec_groups = G;
+    p.dec_parts = dec_parts(R);
     p.nreq = nq;
     p.table_stride = table_stride;
     const int grid = L.grid < p.nblocks ? L.grid : p.nblocks;

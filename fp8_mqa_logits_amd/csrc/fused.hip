@@ -210,17 +210,21 @@ __device__ __forceinline__ void load_keys_rows(KeyTile& kt, const FusedParams& p
   }
 }
 
-// Decode blocks: dec_groups requests per block (4 when a request has at most
-// 8 rows, 2 up to 16, 1 up to 32), each owning 32 / dec_groups row slots, of
-// which its dec_rows rows fill the first. Slot j of block b: request
-// b * G + j / (32 / G), row j % (32 / G) of it. Returns the row id, or p.rows
-// for an empty slot. Otherwise slot j of block b is row 32 b + j.
+// Decode blocks. A request's rows are split into parts of up to 8 rows
+// (dec_parts = ceil(R / 8) parts of R rows); a block packs kDecPack = 4 parts
+// (of one or several requests), each owning 8 row slots, two waves. Slot j of
+// block b holds row 8 (part % dec_parts) + j % 8 of request part / dec_parts,
+// part = 4 b + j / 8; p.rows marks an empty slot. Otherwise slot j of block b
+// is row 32 b + j.
+constexpr int kDecPack = 4;
+constexpr int kDecSlots = kFusedBlockRows / kDecPack;  // 8
+
 template <int SRC>
 __device__ __forceinline__ int slot_row(const FusedParams& p, int b, int slot) {
   if constexpr (SRC == SRC_DECODE) {
-    const int per = kFusedBlockRows / p.dec_groups;
-    const int q = b * p.dec_groups + slot / per;
-    const int j = slot - (slot / per) * per;
+    const int part = b * kDecPack + slot / kDecSlots;
+    const int q = part / p.dec_parts;
+    const int j = (part - q * p.dec_parts) * kDecSlots + slot % kDecSlots;
     return (j < p.dec_rows && q < p.nreq) ? q * p.dec_rows + j : p.rows;
   } else {
     return b * kFusedBlockRows + slot;
@@ -229,16 +233,33 @@ __device__ __forceinline__ int slot_row(const FusedParams& p, int b, int slot) {
 
 // The block of row r (either layout).
 __device__ __forceinline__ int block_of(const FusedParams& p, int r) {
-  return p.dec_rows ? (r / p.dec_rows) / p.dec_groups : r / kFusedBlockRows;
+  if (!p.dec_rows) return r / kFusedBlockRows;
+  const int q = r / p.dec_rows;
+  return (q * p.dec_parts + (r - q * p.dec_rows) / kDecSlots) / kDecPack;
 }
 
-// The packed request (0 .. dec_groups - 1) whose rows a wave holds in decode.
+// The part (0 .. 3) of its block whose rows a wave holds in decode.
 template <int SRC>
-__device__ __forceinline__ int wave_group(const FusedParams& p, int w) {
+__device__ __forceinline__ int wave_group(int w) {
   if constexpr (SRC == SRC_DECODE) {
-    return w * p.dec_groups / kFusedWaves;
+    return w / (kFusedWaves / kDecPack);
   } else {
     return 0;
+  }
+}
+
+// Score of the wave's 4 rows for a 64-key chunk, one row after the other
+// (fewer registers than score4's overlap of consecutive rows; for decode,
+// whose scan waits on its key copies more than on its MFMAs).
+__device__ __forceinline__ void score4_serial(float E[4], const QueryRow* qr, const FoldOp& fo,
+                                              const KeyTile& kt, float sc) {
+  FoldTerms f;
+  RowAcc a;
+  fold_terms(f, fo, kt);
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    mfma_row(a, qr[i], kt);
+    E[i] = reduce_heads_abs(qr[i], a, f, i) * sc;
   }
 }
 
@@ -671,17 +692,17 @@ __device__ __forceinline__ void merge_rows(const FusedParams& p, RowState* rs, c
 
 // Stage key j (0 .. stage_keys - 1) of a stage that starts at position key0:
 // its key (position) and request. Gathered and paged stages hold the keys
-// key0 + j * stride; a decode stage holds, in chunk u = j / 64, request
-// req0 + u % G's positions key0 + ((u / G) * 64 + j % 64) * stride. Keys are
-// clamped to the last one and requests to the last request.
+// key0 + j * stride; a decode stage holds, in chunk u = j / 64, the
+// positions key0 + (j % 64) * stride of part req0 + u. Keys are clamped to
+// the last one and requests to the last request.
 template <int SRC>
 __device__ __forceinline__ void stage_key(const FusedParams& p, int key0, int stride, int j,
                                           int req0, int& key, int& req) {
   if constexpr (SRC == SRC_DECODE) {
-    const int G = p.dec_groups;
+    // chunk u of the stage: part req0 + u (its request's table row)
     const int u = j >> 6;
-    key = key0 + ((u / G) * kChunk + (j & (kChunk - 1))) * stride;
-    req = req0 + (u & (G - 1));
+    key = key0 + (j & (kChunk - 1)) * stride;
+    req = (req0 + u) / p.dec_parts;
     req = req < p.nreq ? req : p.nreq - 1;
   } else {
     key = key0 + j * stride;
@@ -698,8 +719,12 @@ __device__ __forceinline__ void dma_pages(const FusedParams& p, int key0, int st
                                           int32_t* pdst, int tid, int req0) {
   if constexpr (SRC != SRC_GATHER) {
     if (tid < stage_keys<SRC>()) {
+      // decode: entry t holds the page of stage key 64 (t % 4) + t / 4, so
+      // that a thread's four tile copies (one per part) read one 16-byte
+      // group
+      const int j = SRC == SRC_DECODE ? 64 * (tid & 3) + (tid >> 2) : tid;
       int key, req;
-      stage_key<SRC>(p, key0, stride, tid, req0, key, req);
+      stage_key<SRC>(p, key0, stride, j, req0, key, req);
       const int32_t* src = table_entry<SRC>(p, key, req);
       __builtin_amdgcn_global_load_lds(src, pdst + (tid & ~63), 4, 0, 0);
     }
@@ -723,7 +748,7 @@ __device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, int st
     if (tid < SK) {
       int key, req;
       stage_key<SRC>(p, key0, stride, tid, req0, key, req);
-      const uint32_t* src = page_scale(p, pgs[tid], key);
+      const uint32_t* src = page_scale(p, pgs[4 * (tid & 63) + (tid >> 6)], key);
       __builtin_amdgcn_global_load_lds(src, sdst + (tid & ~63), 4, 0, 0);
     }
   } else if (tid < 2 * SK) {
@@ -738,19 +763,36 @@ __device__ __forceinline__ void dma_stage(const FusedParams& p, int key0, int st
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(p.keyinfo) + off,
                                      sdst + (tid & ~63), 4, 0, 0);
   }
-#pragma unroll
-  for (int i = 0; i < SK * 8 / kThreads; ++i) {
-    const int slot = tid + i * kThreads;
-    const int j = slot >> 3;
-    const int c = (slot & 7) ^ swz(j);
+  if constexpr (SRC == SRC_DECODE) {
+    // copy i (one per part): stage key 64 i + tid / 8, slice (tid % 8) ^ swz;
+    // the four pages in one LDS read
+    static_assert(SK * 8 / kThreads == kDecPack, "one tile copy per part");
+    const int jj = tid >> 3;
+    const int c = (tid & 7) ^ swz(jj);
     int key, req;
-    stage_key<SRC>(p, key0, stride, j, req0, key, req);
-    const uint8_t* src;
-    if constexpr (SRC == SRC_GATHER)
-      src = p.k + (int64_t)key * kDim + 16 * c;
-    else
-      src = page_row(p, pgs[j], key) + 16 * c;
-    __builtin_amdgcn_global_load_lds(src, kdst + 16 * (slot & ~63), 16, 0, 0);
+    stage_key<SRC>(p, key0, stride, jj, req0, key, req);
+    const int4 pg4 = *reinterpret_cast<const int4*>(pgs + 4 * jj);
+    const int pg[4] = {pg4.x, pg4.y, pg4.z, pg4.w};
+#pragma unroll
+    for (int i = 0; i < kDecPack; ++i) {
+      const uint8_t* src = page_row(p, pg[i], key) + 16 * c;
+      __builtin_amdgcn_global_load_lds(src, kdst + 16 * ((tid + i * kThreads) & ~63), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SK * 8 / kThreads; ++i) {
+      const int slot = tid + i * kThreads;
+      const int j = slot >> 3;
+      const int c = (slot & 7) ^ swz(j);
+      int key, req;
+      stage_key<SRC>(p, key0, stride, j, req0, key, req);
+      const uint8_t* src;
+      if constexpr (SRC == SRC_GATHER)
+        src = p.k + (int64_t)key * kDim + 16 * c;
+      else
+        src = page_row(p, pgs[j], key) + 16 * c;
+      __builtin_amdgcn_global_load_lds(src, kdst + 16 * (slot & ~63), 16, 0, 0);
+    }
   }
 }
 
@@ -810,8 +852,8 @@ __device__ __forceinline__ void score4(float E[4], const QueryRow* qr, const Fol
 // before the epilogue of the current one. Chunks that every live row of the
 // wave covers entirely (almost all of them) take a path with no per-row range
 // tests: rows that are not live have an admission threshold of NaN there.
-// Decode: the block's requests req0 .. req0 + G - 1 share the stages (chunk
-// u of a stage is request u % G's) and this wave's rows are request grp's.
+// Decode: the block's parts req0 .. req0 + 3 share the stages (chunk u of a
+// stage is part req0 + u's) and this wave's rows are part req0 + grp's.
 template <bool EXACT, int SRC>
 __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& stg, const QueryRow* qr,
                                           const FoldOp& fo, RowState* rs, int mode, int lo,
@@ -820,7 +862,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
   const int l = lane_id();
   constexpr int SC = stage_chunks<SRC>();
   constexpr int SK = stage_keys<SRC>();
-  const int G = SRC == SRC_DECODE ? p.dec_groups : 1;
+  constexpr int G = SRC == SRC_DECODE ? kDecPack : 1;
   const int cps = SC / G;  // 64-position chunks per stage
   const int nch = (hi - lo + kChunk - 1) / kChunk;
   bool live[kRowsPerWave];
@@ -866,20 +908,24 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
       }
       KeyTile kt;
       float sc, nh;
+      int kw;
+      float E[4];
       if constexpr (SRC == SRC_DECODE) {
+        // (the key's bound after its scores: fewer registers live at once)
         load_keys_lds(kt, kc);
         sc = ue8m0(__float_as_uint(scl[l]));
+        score4_serial(E, qr, fo, kt, sc);
         nh = decode_nhat(kt, sc);
+        kw = key | __float_as_int(nh);
       } else {
         sc = scl[l];
         nh = scl[SK + l];
+        // the record's key word: the key and its nhat bits
+        kw = key | __float_as_int(nh);
+        load_keys_lds(kt, kc);
+        // rows that are not live have zeroed operands and a NaN threshold
+        score4(E, qr, fo, kt, sc);
       }
-      // the record's key word: the key and its nhat bits
-      const int kw = key | __float_as_int(nh);
-      if constexpr (SRC != SRC_DECODE) load_keys_lds(kt, kc);
-      float E[4];
-      // rows that are not live have zeroed operands and a NaN threshold
-      score4(E, qr, fo, kt, sc);
       // admission and records by U = E + beta * nhat, an upper bound of the
       // key's exact score
 #pragma unroll
@@ -920,11 +966,21 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
       dma_stage<SRC>(p, lo + (st + 1) * cps * kChunk, 1, knext, snext, pnext, tid, req0);
     if (SRC != SRC_GATHER && st + 2 < nst)
       dma_pages<SRC>(p, lo + (st + 2) * cps * kChunk, 1, pafter, tid, req0);
+    if constexpr (SRC == SRC_DECODE) {
+      // this wave's request's chunks of the stage: u = grp, grp + G, ...
+      // (one copy of the chunk code for any G)
+#pragma unroll 1
+      for (int v = 0; v < cps; ++v) {
+        const int u = grp + v * G;
+        const int c = st * cps + v;
+        if (c < nch) chunk(c, kcur + u * kChunkBytes, scur + u * kChunk);
+      }
+    } else {
 #pragma unroll
-    for (int u = 0; u < SC; ++u) {
-      if (SRC == SRC_DECODE && (u & (G - 1)) != grp) continue;
-      const int c = st * cps + u / G;
-      if (c < nch) chunk(c, kcur + u * kChunkBytes, scur + u * kChunk);
+      for (int u = 0; u < SC; ++u) {
+        const int c = st * SC + u;
+        if (c < nch) chunk(c, kcur + u * kChunkBytes, scur + u * kChunk);
+      }
     }
     __syncthreads();
   };
@@ -961,13 +1017,15 @@ __device__ __forceinline__ int gate_sample(int span, int spp, int& stride) {
 
 // The strided sample loop of the gate and of its fine pass: nst stages of the
 // keys lo + j * stride (decode: of each packed request), double-buffered,
-// each chunk u of stage st handed to f(st, u, keys, scales); the paged and
-// decode sources copy the pages a stage ahead, as the scan does.
+// each chunk handed to f(position chunk, keys, scales) (decode: only the
+// chunks of the calling wave's request grp); the paged and decode sources
+// copy the pages a stage ahead, as the scan does.
 template <int SRC, class F>
 __device__ __forceinline__ void sample_stages(const FusedParams& p, const Stages& stg, int lo,
-                                              int stride, int nst, int req0, int tid, F f) {
+                                              int stride, int nst, int req0, int grp, int tid,
+                                              F f) {
   constexpr int SC = stage_chunks<SRC>();
-  const int G = SRC == SRC_DECODE ? p.dec_groups : 1;
+  constexpr int G = SRC == SRC_DECODE ? kDecPack : 1;
   const int step = SC / G * kChunk * stride;  // positions per stage
   auto stage = [&](int st, const uint8_t* kcur, const float* scur, uint8_t* knext,
                    float* snext, const int32_t* pnext, int32_t* pafter) {
@@ -975,8 +1033,18 @@ __device__ __forceinline__ void sample_stages(const FusedParams& p, const Stages
       dma_stage<SRC>(p, lo + (st + 1) * step, stride, knext, snext, pnext, tid, req0);
     if (SRC != SRC_GATHER && st + 2 < nst)
       dma_pages<SRC>(p, lo + (st + 2) * step, stride, pafter, tid, req0);
+    if constexpr (SRC == SRC_DECODE) {
+      // this wave's request's chunks: u = grp, grp + G, ... (position chunk
+      // st * (SC / G) + v)
+#pragma unroll 1
+      for (int v = 0; v < SC / G; ++v) {
+        const int u = grp + v * G;
+        f(st * (SC / G) + v, kcur + u * kChunkBytes, scur + u * kChunk);
+      }
+    } else {
 #pragma unroll
-    for (int u = 0; u < SC; ++u) f(st, u, kcur + u * kChunkBytes, scur + u * kChunk);
+      for (int u = 0; u < SC; ++u) f(st * SC + u, kcur + u * kChunkBytes, scur + u * kChunk);
+    }
     __syncthreads();
   };
   if constexpr (SRC != SRC_GATHER) {
@@ -1076,10 +1144,10 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
       // each packed request)
       constexpr int SC = stage_chunks<SRC>();
       constexpr int SK = stage_keys<SRC>();
-      const int G = SRC == SRC_DECODE ? p.dec_groups : 1;
+      constexpr int G = SRC == SRC_DECODE ? kDecPack : 1;
       const int cps = SC / G;
-      const int req0 = b * G;
-      const int grp = wave_group<SRC>(p, w);
+      const int req0 = b * G;  // decode: the block's first part
+      const int grp = wave_group<SRC>(w);
       int stride;
       const int nst = gate_sample(hi - lo, cps * kChunk, stride);
       uint32_t* hist = sm.hist[w];
@@ -1100,17 +1168,18 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
         const int key = lo + (c * kChunk + l) * stride;
         KeyTile kt;
         float sc, nh;
+        float E[4];
         if constexpr (SRC == SRC_DECODE) {
           load_keys_lds(kt, kc);
           sc = ue8m0(__float_as_uint(scl[l]));
+          score4(E, qr, fo, kt, sc);
           nh = decode_nhat(kt, sc);
         } else {
           nh = scl[SK + l];
           sc = scl[l];
           load_keys_lds(kt, kc);
+          score4(E, qr, fo, kt, sc);
         }
-        float E[4];
-        score4(E, qr, fo, kt, sc);
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) E[i] = __builtin_fmaf(rs[i].beta, nh, E[i]);
 #pragma unroll
@@ -1140,11 +1209,8 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
           }
         }
       };
-      sample_stages<SRC>(p, stg, lo, stride, nst, req0, tid,
-                         [&](int st, int u, const uint8_t* kc, const float* scl) {
-                           if (SRC == SRC_DECODE && (u & (G - 1)) != grp) return;
-                           chunk(st * cps + u / G, kc, scl);
-                         });
+      sample_stages<SRC>(p, stg, lo, stride, nst, req0, grp, tid,
+                         [&](int c, const uint8_t* kc, const float* scl) { chunk(c, kc, scl); });
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         RowState& r = rs[i];
@@ -1305,10 +1371,10 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
     if (hi > lo) {
       constexpr int SC = stage_chunks<SRC>();
       constexpr int SK = stage_keys<SRC>();
-      const int G = SRC == SRC_DECODE ? p.dec_groups : 1;
+      constexpr int G = SRC == SRC_DECODE ? kDecPack : 1;
       const int cps = SC / G;
-      const int req0 = b * G;
-      const int grp = wave_group<SRC>(p, w);
+      const int req0 = b * G;  // decode: the block's first part
+      const int grp = wave_group<SRC>(w);
       int stride;
       const int nst = gate_sample(hi - lo, cps * kChunk, stride);
       FoldOp fo;
@@ -1322,17 +1388,18 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
         const int key = lo + (c * kChunk + l) * stride;
         KeyTile kt;
         float sc, nh;
+        float E[4];
         if constexpr (SRC == SRC_DECODE) {
           load_keys_lds(kt, kc);
           sc = ue8m0(__float_as_uint(scl[l]));
+          score4(E, qr, fo, kt, sc);
           nh = decode_nhat(kt, sc);
         } else {
           nh = scl[SK + l];
           sc = scl[l];
           load_keys_lds(kt, kc);
+          score4(E, qr, fo, kt, sc);
         }
-        float E[4];
-        score4(E, qr, fo, kt, sc);
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) E[i] = __builtin_fmaf(rs[i].beta, nh, E[i]);
 #pragma unroll
@@ -1349,11 +1416,8 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
           atomicAdd(&hist[i * kGateBins + f], 1u);
         }
       };
-      sample_stages<SRC>(p, stg, lo, stride, nst, req0, tid,
-                         [&](int st, int u, const uint8_t* kc, const float* scl) {
-                           if (SRC == SRC_DECODE && (u & (G - 1)) != grp) return;
-                           chunk(st * cps + u / G, kc, scl);
-                         });
+      sample_stages<SRC>(p, stg, lo, stride, nst, req0, grp, tid,
+                         [&](int c, const uint8_t* kc, const float* scl) { chunk(c, kc, scl); });
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -1459,7 +1523,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
       build_fold(fo, p.q, p.weights, frows);
       const SlabRefs sr = slab_refs<SRC>(p, b, sm.hist[w], 2 * p.topk, SPLIT ? seg : -1);
       scan_rows<false, SRC>(p, stg, qr, fo, rs, M_GATED, lo, hi, sr,
-                            b * (SRC == SRC_DECODE ? p.dec_groups : 1), wave_group<SRC>(p, w));
+                            b * (SRC == SRC_DECODE ? kDecPack : 1), wave_group<SRC>(w));
     }
     if (l == 0) {
 #pragma unroll
@@ -1990,7 +2054,7 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
       SlabRefs sr = slab_refs<SRC>(p, b, sm.hist[w], k);
       FoldOp none;
       scan_rows<true, SRC>(p, stg, qr, none, rs, M_EXACT, lo, hi, sr,
-                           b * (SRC == SRC_DECODE ? p.dec_groups : 1), wave_group<SRC>(p, w));
+                           b * (SRC == SRC_DECODE ? kDecPack : 1), wave_group<SRC>(w));
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         RowState& r = rs[i];

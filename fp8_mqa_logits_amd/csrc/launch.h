@@ -82,9 +82,10 @@ struct FusedParams {
   uint8_t* kc;  // [keys][128] paged prefill: the keys compacted by the prologue
   // Decode-shaped calls (dec_rows > 0): nreq requests of dec_rows rows each
   // (row r belongs to request r / dec_rows); request q's key positions map
-  // to pages through table row q (table_stride entries). Blocks pack
-  // dec_groups requests; keys is the positions' bound, and keyinfo is unused.
-  int dec_rows, dec_groups, nreq, table_stride;
+  // to pages through table row q (table_stride entries). A request's rows
+  // form dec_parts parts of up to 8 rows, and blocks pack four parts; keys
+  // is the positions' bound, and keyinfo is unused.
+  int dec_rows, dec_parts, nreq, table_stride;
   float* slabE;      // [nblocks * 32 rows][kSlabRow] candidate scores
   int32_t* slabI;    // [nblocks * 32 rows][kSlabRow] candidate keys
   float* tmpE;       // [grid][8 waves][kTmp] merge buffers

@@ -205,8 +205,8 @@ int mqa_topk_prefill_paged(const uint8_t* q, const uint8_t* cache, const int32_t
  * Bytes of device workspace one mqa_topk_decode_paged call over `requests`
  * requests of `rows_per_request` rows needs on HIP device `device`: the
  * mqa_topk_prefill workspace of one batch of requests (a batch holds at most
- * 16384 rows and 512 workgroups of requests, 4, 2 or 1 requests to a
- * workgroup for rows_per_request <= 8, <= 16, <= 32). Returns 0 if the device
+ * 16384 rows and 512 workgroups; a workgroup holds four parts of up to 8 rows
+ * of a request each). Returns 0 if the device
  * does not exist or is not gfx950, or the sizes are out of range.
  */
 size_t workspace_size_decode(int requests, int rows_per_request, int device);
@@ -234,9 +234,10 @@ size_t workspace_size_decode(int requests, int rows_per_request, int device);
  *   topk in {512, 1024, 2048}
  *   workspace: >= workspace_size_decode(requests, R, current device) bytes,
  *   256-B aligned, owned by the call until the stream reaches its end.
- * Requests run in batches (workspace_size_decode) in order on `stream`. A
- * request's rows share its key copies; rows of fewer than 8 per request
- * leave row slots of their workgroup empty. Returns MQA_OK or an MQA_ERR_*
+ * Requests run in batches (workspace_size_decode) in order on `stream`. The
+ * rows of a part of a request (up to 8 rows) share its key copies; a request
+ * of R rows reads its keys ceil(R / 8) times, and R not a multiple of 8 leaves
+ * row slots of a workgroup empty. Returns MQA_OK or an MQA_ERR_*
  * code (checked in the order NULL, ALIGN, SHAPE, DEVICE, WORKSPACE).
  */
 int mqa_topk_decode_paged(const uint8_t* q, const uint8_t* cache, const int32_t* page_table,
