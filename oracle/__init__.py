@@ -49,13 +49,12 @@ def _load():
         lib.oracle_e4m3_table.restype = None
         lib.oracle_key_scales.argtypes = [P, I64, P]
         lib.oracle_key_scales.restype = None
-        lib.oracle_head_dots.argtypes = [P, P, P]
+        I = ctypes.c_int
+        lib.oracle_head_dots.argtypes = [P, P, P, I]
         lib.oracle_head_dots.restype = ctypes.c_int
-        lib.oracle_logits.argtypes = [P, P, P, P, P, P, I64, I64, P, I64, I64, I64, P,
-                                      ctypes.c_int]
+        lib.oracle_logits.argtypes = [P, P, P, P, P, P, I64, I64, I, P, I64, I64, I64, P, I]
         lib.oracle_logits.restype = ctypes.c_int
-        lib.oracle_topk.argtypes = [P, P, P, P, P, P, I64, I64, P, I64, I64, P, P, P,
-                                    ctypes.c_int]
+        lib.oracle_topk.argtypes = [P, P, P, P, P, P, I64, I64, I, P, I64, I64, P, P, P, I]
         lib.oracle_topk.restype = ctypes.c_int
         lib.oracle_select.argtypes = [P, I64, I64, P]
         lib.oracle_select.restype = None
@@ -88,11 +87,14 @@ def key_scales(scale_bytes: np.ndarray) -> np.ndarray:
 
 
 def head_dots(q_row: np.ndarray, k_row: np.ndarray) -> np.ndarray:
-    """Exact per-head dots: q_row [32,128] e4m3 bytes, k_row [128] -> float64 [32]."""
-    q = _c(q_row, np.uint8).reshape(HEADS, DIM)
+    """Exact per-head dots: q_row [H,128] e4m3 bytes (H = 32 or 64), k_row
+    [128] -> float64 [H]."""
+    heads = np.asarray(q_row).size // DIM
+    q = _c(q_row, np.uint8).reshape(heads, DIM)
     k = _c(k_row, np.uint8).reshape(DIM)
-    out = np.empty(HEADS, np.float64)
-    _load().oracle_head_dots(_ptr(q), _ptr(k), _ptr(out))
+    out = np.empty(heads, np.float64)
+    if _load().oracle_head_dots(_ptr(q), _ptr(k), _ptr(out), heads) != 0:
+        raise ValueError("oracle_head_dots: heads must be 32 or 64")
     return out
 
 
@@ -100,10 +102,14 @@ class Problem:
     """Host copies of one call's inputs (numpy), in the op's layouts."""
 
     def __init__(self, q, k, scales, weights, starts, ends):
-        self.q = _c(q, np.uint8).reshape(-1, HEADS, DIM)
+        q = np.asarray(q)
+        # 32 heads, or 64 (q [rows, 64, 128], weights [rows, 64])
+        self.heads = q.shape[1] if q.ndim == 3 else HEADS
+        assert self.heads in (32, 64), self.heads
+        self.q = _c(q, np.uint8).reshape(-1, self.heads, DIM)
         self.k = _c(k, np.uint8).reshape(-1, DIM)
         self.scales = _c(scales, np.float32)
-        self.weights = _c(weights, np.float32).reshape(-1, HEADS)
+        self.weights = _c(weights, np.float32).reshape(-1, self.heads)
         self.starts = _c(starts, np.int32)
         self.ends = _c(ends, np.int32)
         self.rows = self.q.shape[0]
@@ -114,7 +120,7 @@ class Problem:
 
     def _args(self):
         return (_ptr(self.q), _ptr(self.k), _ptr(self.scales), _ptr(self.weights),
-                _ptr(self.starts), _ptr(self.ends), self.rows, self.keys)
+                _ptr(self.starts), _ptr(self.ends), self.rows, self.keys, self.heads)
 
     def visible(self, r):
         """Clamped visible range (s, e) of row r."""

@@ -16,7 +16,10 @@
 //     decodes to the fp32 whose bit pattern is e << 23.
 //   * vLLM PR #60618, "What this PR does" (Scoring): 32 index heads, each
 //     head's dot product passes through relu and is weighted by its per-row
-//     head weight, and the weighted heads are summed.
+//     head weight, and the weighted heads are summed. The same PR's
+//     "Limitations of this PR -- TODOs" names DeepSeek-V3.2's 64 index heads:
+//     the oracle takes heads = 32 or 64 (q [rows,heads,128], weights
+//     [rows,heads]), the same sum over all heads.
 //   Reading taken for the full formula (the pages never print it in one
 //   piece): logit[r,j] = scale_j * sum_h w[r,h] * relu(q[r,h,:] . k[j,:]).
 //
@@ -25,7 +28,7 @@
 //     so a product of two is a multiple of 2^-18 and a 128-term dot product
 //     stays below 2^25 in magnitude: it needs at most 43 significant bits and
 //     is therefore EXACT in double in any summation order.
-//   * The head sum runs in double, in head order 0..31, is multiplied by the
+//   * The head sum runs in double, in head order 0..heads-1, is multiplied by the
 //     scale in double (a power of two: exact barring underflow) and rounded
 //     once to fp32.
 //   * Top-k: a full sort of the row by (logit descending, key ascending); the
@@ -49,7 +52,9 @@
 
 namespace {
 
-constexpr int kHeads = 32;
+// 32 index heads (GLM-5.x, DeepSeek-V4.1) or 64 (DeepSeek-V3.2: PR #60618,
+// "Limitations of this PR -- TODOs"); the formula is the same sum over heads.
+constexpr int kMaxHeads = 64;
 constexpr int kDim = 128;
 
 // OCP FP8 E4M3FN (torch.float8_e4m3fn): 1 sign bit, 4 exponent bits with
@@ -97,6 +102,7 @@ struct Problem {
   const int32_t* ends;
   int64_t rows;
   int64_t keys;
+  int heads;
 };
 
 // Visible range of row r. The pages require [start, end) inside [0, keys);
@@ -109,38 +115,38 @@ void row_range(const Problem& p, int64_t r, int64_t* s, int64_t* e) {
   *e = b;
 }
 
-// Decoded query of one row, stored dimension-major: qd[d*32 + h].
+// Decoded query of one row, stored dimension-major: qd[d*heads + h].
 void decode_query(const Problem& p, int64_t r, double* qd) {
-  const uint8_t* qr = p.q + r * kHeads * kDim;
-  for (int h = 0; h < kHeads; ++h)
-    for (int d = 0; d < kDim; ++d) qd[d * kHeads + h] = g_e4m3[qr[h * kDim + d]];
+  const uint8_t* qr = p.q + r * p.heads * kDim;
+  for (int h = 0; h < p.heads; ++h)
+    for (int d = 0; d < kDim; ++d) qd[d * p.heads + h] = g_e4m3[qr[h * kDim + d]];
 }
 
-// The 32 per-head dot products s[h] = sum_d q[h,d] * k[j,d] of one key.
+// The per-head dot products s[h] = sum_d q[h,d] * k[j,d] of one key.
 // Each s[h] is accumulated over d = 0..127 in order; the loop runs over the
-// heads innermost only so that the 32 independent sums advance together.
+// heads innermost only so that the independent sums advance together.
 __attribute__((target_clones("avx512f", "avx2", "default")))
 void head_dots(const double* __restrict__ qd, const uint8_t* __restrict__ kj,
-               double* __restrict__ s) {
+               double* __restrict__ s, int heads) {
   double kd[kDim];
   for (int d = 0; d < kDim; ++d) kd[d] = g_e4m3[kj[d]];
-  double acc[kHeads];
-  for (int h = 0; h < kHeads; ++h) acc[h] = 0.0;
+  double acc[kMaxHeads];
+  for (int h = 0; h < heads; ++h) acc[h] = 0.0;
   for (int d = 0; d < kDim; ++d) {
-    const double* qrow = qd + d * kHeads;
-    for (int h = 0; h < kHeads; ++h) acc[h] += qrow[h] * kd[d];
+    const double* qrow = qd + d * heads;
+    for (int h = 0; h < heads; ++h) acc[h] += qrow[h] * kd[d];
   }
-  for (int h = 0; h < kHeads; ++h) s[h] = acc[h];
+  for (int h = 0; h < heads; ++h) s[h] = acc[h];
 }
 
 // logit[r,j] = scale_j * sum_h w[r,h] * relu(s[h]), head sum in double in
 // head order, one rounding to fp32 at the end.
 float logit_of(const Problem& p, int64_t r, const double* qd, int64_t j) {
-  double s[kHeads];
-  head_dots(qd, p.k + j * kDim, s);
-  const float* w = p.weights + r * kHeads;
+  double s[kMaxHeads];
+  head_dots(qd, p.k + j * kDim, s, p.heads);
+  const float* w = p.weights + r * p.heads;
   double sum = 0.0;
-  for (int h = 0; h < kHeads; ++h) {
+  for (int h = 0; h < p.heads; ++h) {
     const double relu = s[h] > 0.0 ? s[h] : 0.0;
     sum += static_cast<double>(w[h]) * relu;
   }
@@ -148,13 +154,14 @@ float logit_of(const Problem& p, int64_t r, const double* qd, int64_t j) {
 }
 
 bool inputs_in_contract(const Problem& p) {
-  for (int64_t i = 0; i < p.rows * kHeads * kDim; ++i)
+  if (p.heads != 32 && p.heads != 64) return false;
+  for (int64_t i = 0; i < p.rows * p.heads * kDim; ++i)
     if ((p.q[i] & 0x7F) == 0x7F) return false;
   for (int64_t i = 0; i < p.keys * kDim; ++i)
     if ((p.k[i] & 0x7F) == 0x7F) return false;
   for (int64_t i = 0; i < p.keys; ++i)
     if (!std::isfinite(p.scales[i]) || p.scales[i] < 0.0f) return false;
-  for (int64_t i = 0; i < p.rows * kHeads; ++i)
+  for (int64_t i = 0; i < p.rows * p.heads; ++i)
     if (!std::isfinite(p.weights[i])) return false;
   return true;
 }
@@ -204,12 +211,14 @@ void oracle_key_scales(const uint8_t* bytes, int64_t keys, float* out) {
   for (int64_t j = 0; j < keys; ++j) out[j] = ue8m0_scale(bytes + 4 * j);
 }
 
-// Exact per-head dot products of query row r against key j (for the pins).
-int oracle_head_dots(const uint8_t* q_row, const uint8_t* k_row, double* out32) {
-  double qd[kDim * kHeads];
-  for (int h = 0; h < kHeads; ++h)
-    for (int d = 0; d < kDim; ++d) qd[d * kHeads + h] = g_e4m3[q_row[h * kDim + d]];
-  head_dots(qd, k_row, out32);
+// Exact per-head dot products of a query row (heads x 128 codes) against one
+// key (for the pins).
+int oracle_head_dots(const uint8_t* q_row, const uint8_t* k_row, double* out, int heads) {
+  if (heads != 32 && heads != 64) return -1;
+  double qd[kDim * kMaxHeads];
+  for (int h = 0; h < heads; ++h)
+    for (int d = 0; d < kDim; ++d) qd[d * heads + h] = g_e4m3[q_row[h * kDim + d]];
+  head_dots(qd, k_row, out, heads);
   return 0;
 }
 
@@ -220,16 +229,16 @@ int oracle_head_dots(const uint8_t* q_row, const uint8_t* k_row, double* out32) 
 // or negative scales, non-finite weights, a bad row id).
 int oracle_logits(const uint8_t* q, const uint8_t* k, const float* scales,
                   const float* weights, const int32_t* starts, const int32_t* ends,
-                  int64_t rows, int64_t keys, const int32_t* sel, int64_t nsel,
+                  int64_t rows, int64_t keys, int heads, const int32_t* sel, int64_t nsel,
                   int64_t col0, int64_t ncols, float* out, int nthreads) {
-  Problem p{q, k, scales, weights, starts, ends, rows, keys};
+  Problem p{q, k, scales, weights, starts, ends, rows, keys, heads};
   if (!inputs_in_contract(p)) return -1;
   for (int64_t i = 0; i < nsel; ++i)
     if (sel[i] < 0 || sel[i] >= rows) return -1;
   const float ninf = -std::numeric_limits<float>::infinity();
   parallel_rows(nsel, nthreads, [&](int64_t i) {
     const int64_t r = sel[i];
-    std::vector<double> qd(kDim * kHeads);
+    std::vector<double> qd(kDim * p.heads);
     decode_query(p, r, qd.data());
     int64_t s, e;
     row_range(p, r, &s, &e);
@@ -250,16 +259,16 @@ int oracle_logits(const uint8_t* q, const uint8_t* k, const float* scales,
 // Returns 0, or -1 on inputs outside the contract or topk < 1.
 int oracle_topk(const uint8_t* q, const uint8_t* k, const float* scales,
                 const float* weights, const int32_t* starts, const int32_t* ends,
-                int64_t rows, int64_t keys, const int32_t* sel, int64_t nsel,
+                int64_t rows, int64_t keys, int heads, const int32_t* sel, int64_t nsel,
                 int64_t topk, int32_t* out_idx, float* kth, float* maxabs,
                 int nthreads) {
-  Problem p{q, k, scales, weights, starts, ends, rows, keys};
+  Problem p{q, k, scales, weights, starts, ends, rows, keys, heads};
   if (topk < 1 || !inputs_in_contract(p)) return -1;
   for (int64_t i = 0; i < nsel; ++i)
     if (sel[i] < 0 || sel[i] >= rows) return -1;
   parallel_rows(nsel, nthreads, [&](int64_t i) {
     const int64_t r = sel[i];
-    std::vector<double> qd(kDim * kHeads);
+    std::vector<double> qd(kDim * p.heads);
     decode_query(p, r, qd.data());
     int64_t s, e;
     row_range(p, r, &s, &e);

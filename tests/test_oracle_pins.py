@@ -322,3 +322,59 @@ def test_rejects_out_of_contract_inputs():
     bad = oracle.Problem(q, wl.k, p.scales, wl.weights, wl.starts, wl.ends)
     with pytest.raises(ValueError):
         oracle.topk(bad, [0], 8)
+
+
+# ------------------------------------------------------------ 64 index heads
+
+def _problem64(rows, keys, seed):
+    rng = np.random.default_rng(seed)
+    q = W.encode_e4m3(rng.standard_normal((rows, 64, 128)).astype(np.float32))
+    k = W.encode_e4m3(rng.standard_normal((keys, 128)).astype(np.float32))
+    sc = np.ldexp(1.0, rng.integers(-4, 1, keys)).astype(np.float32)
+    w = (rng.standard_normal((rows, 64)) / 8).astype(np.float32)
+    starts = np.zeros(rows, np.int32)
+    ends = np.full(rows, keys, np.int32)
+    return q, k, sc, w, starts, ends
+
+
+def test_64_heads_brute_force_exact():
+    # one row of 64 heads against 6 keys in exact rational arithmetic (the
+    # formula summed over all 64 heads), rounded once to fp32
+    from fractions import Fraction
+    q, k, sc, w, s, e = _problem64(1, 6, 11)
+    tab = oracle.e4m3_table()
+    got = oracle.logits(oracle.Problem(q, k, sc, w, s, e), [0])[0]
+    for j in range(6):
+        tot = Fraction(0)
+        for h in range(64):
+            d = sum(Fraction(float(tab[q[0, h, i]])) * Fraction(float(tab[k[j, i]]))
+                    for i in range(128))
+            tot += Fraction(float(w[0, h])) * max(d, Fraction(0))
+        assert got[j] == np.float32(float(tot * Fraction(float(sc[j])))), j
+
+
+def test_64_heads_are_the_sum_of_two_32_head_halves():
+    # linearity over heads: the 64-head logit is the 32-head logit of the
+    # first half plus that of the second (each rounded once to fp32)
+    q, k, sc, w, s, e = _problem64(8, 300, 12)
+    full = oracle.logits(oracle.Problem(q, k, sc, w, s, e), np.arange(8)).astype(np.float64)
+    a = oracle.logits(oracle.Problem(q[:, :32], k, sc, w[:, :32], s, e), np.arange(8))
+    b = oracle.logits(oracle.Problem(q[:, 32:], k, sc, w[:, 32:], s, e), np.arange(8))
+    a, b = a.astype(np.float64), b.astype(np.float64)
+    tol = 2.0 ** -23 * (np.abs(a) + np.abs(b) + np.abs(full)) + 1e-30
+    assert np.all(np.abs(full - (a + b)) <= tol)
+    # and a half cannot stand in for the whole: dropping either half moves logits
+    assert np.abs(full - a).max() > 1e-3 and np.abs(full - b).max() > 1e-3
+
+
+def test_64_head_dots_closed_form():
+    # head h selects dimension h % 128 with weight 2^(h % 4 - 1)
+    q = np.zeros((64, 128), np.uint8)
+    for h in range(64):
+        q[h, h % 128] = code_of(2.0 ** (h % 4 - 1))
+    kv = np.linspace(-3, 3, 128).astype(np.float32)
+    k = W.encode_e4m3(kv)
+    tab = oracle.e4m3_table()
+    got = oracle.head_dots(q, k)
+    want = np.array([2.0 ** (h % 4 - 1) * tab[k[h % 128]] for h in range(64)])
+    assert np.array_equal(got, want)
