@@ -25,7 +25,8 @@ Prints ONE JSON line (rank 0):
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu,
 --dense (also time the chunked dense logits + top-k path, for context),
 --config N (workload 1..5), --deterministic (MQA_FLAG_DETERMINISTIC: ties at
-the k-th score to the smallest keys, outputs sorted), --paged P (read the keys
+the k-th score to the smallest keys, outputs sorted), --heads 64 (the same
+workload with 64 index heads), --paged P (read the keys
 from a paged indexer cache of P-token pages through mqa_topk_prefill_paged
 instead of the gathered keys and decoded scales), --decode N [--decode-rows R
 --decode-ctx C] (instead of the benchmark: the decode-shaped path over N
@@ -330,6 +331,7 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--paged", type=int, default=0, metavar="P")
+    ap.add_argument("--heads", type=int, default=32, choices=(32, 64))
     ap.add_argument("--decode", type=int, default=0, metavar="REQUESTS")
     ap.add_argument("--decode-rows", type=int, default=8)
     ap.add_argument("--decode-ctx", type=int, default=131072)
@@ -364,6 +366,10 @@ def main():
         return
 
     wl = W.config(args.config)
+    if args.heads == 64:
+        # the same rows, keys and ranges with 64 index heads
+        wl = W.heads64(wl.rows, wl.keys, wl.topk, wl.starts, wl.ends, seed=args.config,
+                       name=wl.name + "_64heads")
     print(f"[bench] workload {wl.name}: {wl.visible_pairs()} visible pairs, hashes "
           f"{wl.hashes()}", file=sys.stderr, flush=True)
     dev = torch.device("cuda", 0)
@@ -376,7 +382,8 @@ def main():
         "ends": torch.from_numpy(wl.ends).to(dev),
     }
     d["scales"] = mqa.mqa_key_scales(torch.from_numpy(wl.scale_bytes).to(dev))
-    ws = mqa.alloc_workspace(wl.rows)
+    ws = torch.empty(mqa.workspace_size_heads(wl.rows, args.heads), dtype=torch.uint8,
+                     device=dev)
     out = torch.empty((wl.rows, wl.topk), dtype=torch.int32, device=dev)
 
     mode = mqa.FLAG_DETERMINISTIC if args.deterministic else 0
@@ -417,7 +424,8 @@ def main():
     measured_peak = mqa.mfma_peak_tflops()
     pairs = wl.visible_pairs()
     value = pairs / (ms / 1e3)
-    achieved = pairs * FLOP_PER_PAIR / (scan_ms / 1e3) / 1e12
+    fpp = FLOP_PER_PAIR * args.heads // 32  # 2 * heads * 128 flop per visible pair
+    achieved = pairs * fpp / (scan_ms / 1e3) / 1e12
     line = {
         "metric": "(row,key) scores/s + % FP8 MFMA peak, top-2048, 16K rows x 128K keys",
         "value": value,
@@ -432,7 +440,7 @@ def main():
         "dtype": "fp8e4m3 MFMA, fp32 scores",
         "data": "synthetic (seeded N(0,1) e4m3 q/k, UE8M0 scales 2^[-4,0], N(0,1)/sqrt(32) weights)",
         "config": {"workload": wl.name, "rows": wl.rows, "keys": wl.keys, "topk": wl.topk,
-                   "visible_pairs": pairs, "parallelism": "1 GPU",
+                   "heads": args.heads, "visible_pairs": pairs, "parallelism": "1 GPU",
                    "ties": "lowest key, sorted output" if args.deterministic else "any",
                    "keys_from": (f"paged cache, {args.paged}-token pages" if args.paged
                                  else "gathered keys, decoded scales")},
@@ -440,7 +448,7 @@ def main():
         # whole call's FP8 fraction (all launches, the metric's own figure)
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS,
-                     "call_frac": pairs * FLOP_PER_PAIR / (ms / 1e3) / 1e12 / FP8_PEAK_TFLOPS,
+                     "call_frac": pairs * fpp / (ms / 1e3) / 1e12 / FP8_PEAK_TFLOPS,
                      "traffic": traffic_from_counters(wl.name), "kernel": "fused_topk_kernel",
                      "kernel_ms": scan_ms, "measured_peak": measured_peak,
                      "measured_frac": achieved / measured_peak},

@@ -31,6 +31,7 @@ ERR_NAMES = {0: "MQA_OK", 1: "MQA_ERR_NULL", 2: "MQA_ERR_ALIGN", 3: "MQA_ERR_SHA
              4: "MQA_ERR_WORKSPACE", 5: "MQA_ERR_DEVICE", 6: "MQA_ERR_LAUNCH"}
 
 EXPORTS = ("workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static",
+           "workspace_size_heads", "mqa_topk_prefill_heads",
            "mqa_topk_prefill_paged", "workspace_size_paged", "workspace_size_decode", "mqa_topk_decode_paged",
            "mqa_logits_dense",
            "mqa_topk_dense",
@@ -65,6 +66,10 @@ def load() -> ctypes.CDLL:
         lib.workspace_size.restype = SZ
         lib.mqa_topk_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, P, SZ, U, P]
         lib.mqa_topk_prefill.restype = I
+        lib.workspace_size_heads.argtypes = [I, I, I]
+        lib.workspace_size_heads.restype = SZ
+        lib.mqa_topk_prefill_heads.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, SZ, U, P]
+        lib.mqa_topk_prefill_heads.restype = I
         lib.mqa_topk_prefill_static.argtypes = [P, P, P, P, P, P, P, I, I, I, U, P]
         lib.mqa_topk_prefill_static.restype = I
         lib.mqa_topk_prefill_paged.argtypes = [P, P, P, I, I, P, P, P, P, I, I, I, P, SZ, U, P]
@@ -153,19 +158,30 @@ def alloc_workspace(rows: int, device=None) -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=dev)
 
 
+def workspace_size_heads(rows: int, heads: int, device: int | None = None) -> int:
+    """Bytes of workspace one call over `rows` rows of `heads` heads needs."""
+    if device is None:
+        device = torch.cuda.current_device()
+    return int(load().workspace_size_heads(int(rows), int(heads), int(device)))
+
+
 def mqa_topk_prefill(q, k, scales, weights, starts, ends, topk: int, out=None, workspace=None,
                      flags: int = 0, stream=None) -> torch.Tensor:
-    """Fused scores + per-row top-k. q [rows,32,128] e4m3 (or its uint8 bytes),
-    k [keys,128] e4m3, scales [keys] fp32, weights [rows,32] fp32, starts/ends
-    [rows] int32; returns out [rows, topk] int32 (key - start, -1 padded)."""
+    """Fused scores + per-row top-k. q [rows,H,128] e4m3 (or its uint8 bytes),
+    H = 32 or 64 index heads, k [keys,128] e4m3, scales [keys] fp32, weights
+    [rows,H] fp32, starts/ends [rows] int32; returns out [rows, topk] int32
+    (key - start, -1 padded). 64 heads go through mqa_topk_prefill_heads."""
     _tensors(q=q, k=k, scales=scales, weights=weights, starts=starts, ends=ends)
     if q.dim() != 3 or k.dim() != 2:
-        raise ValueError("q must be [rows,32,128] and k [keys,128]")
+        raise ValueError("q must be [rows,heads,128] and k [keys,128]")
     rows, keys = q.shape[0], k.shape[0]
-    _shape(q, (rows, HEADS, HEAD_DIM), "q")
+    heads = q.shape[1]
+    if heads not in (32, 64):
+        raise ValueError(f"q: shape {tuple(q.shape)}, expected 32 or 64 heads")
+    _shape(q, (rows, heads, HEAD_DIM), "q")
     _shape(k, (keys, HEAD_DIM), "k")
     _shape(scales, (keys,), "scales")
-    _shape(weights, (rows, HEADS), "weights")
+    _shape(weights, (rows, heads), "weights")
     _shape(starts, (rows,), "starts")
     _shape(ends, (rows,), "ends")
     if out is not None:
@@ -183,14 +199,26 @@ def mqa_topk_prefill(q, k, scales, weights, starts, ends, topk: int, out=None, w
     _need(out, "out", (torch.int32,), dev)
     _shape(out, (rows, topk), "out")
     if workspace is None:
-        workspace = alloc_workspace(rows, dev.index)
+        n = workspace_size_heads(rows, heads, dev.index)
+        if n == 0:
+            raise MQAError(5, "workspace_size_heads")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", (torch.uint8,), dev)
     with torch.cuda.device(dev):
-        rc = load().mqa_topk_prefill(_ptr(q), _ptr(k), _ptr(scales), _ptr(weights), _ptr(starts),
-                                     _ptr(ends), _ptr(out), rows, keys, int(topk),
-                                     _ptr(workspace), workspace.numel(), int(flags),
-                                     _stream(dev, stream))
-    _check(rc, "mqa_topk_prefill")
+        if heads == HEADS:
+            rc = load().mqa_topk_prefill(_ptr(q), _ptr(k), _ptr(scales), _ptr(weights),
+                                         _ptr(starts), _ptr(ends), _ptr(out), rows, keys,
+                                         int(topk), _ptr(workspace), workspace.numel(),
+                                         int(flags), _stream(dev, stream))
+            where = "mqa_topk_prefill"
+        else:
+            rc = load().mqa_topk_prefill_heads(_ptr(q), _ptr(k), _ptr(scales), _ptr(weights),
+                                               _ptr(starts), _ptr(ends), _ptr(out), rows, keys,
+                                               heads, int(topk), _ptr(workspace),
+                                               workspace.numel(), int(flags),
+                                               _stream(dev, stream))
+            where = "mqa_topk_prefill_heads"
+    _check(rc, where)
     return out
 
 

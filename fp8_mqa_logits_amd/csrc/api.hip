@@ -236,12 +236,14 @@ void set_workspace(mqa::FusedParams& p, uint8_t* ws, const Layout& L) {
 
 // Rows in batches of `batch` rows, one launch sequence each, in order on the
 // stream (they share the workspace ws, which holds layout(batch)).
+// hm = heads / 32: a batch of `batch` rows runs as batch * hm virtual rows
+// (its workspace holds layout(batch * hm)).
 int prefill_batches(const uint8_t* q, const uint8_t* k, const float* scales,
                     const float* weights, const int32_t* starts, const int32_t* ends,
                     int32_t* out, int rows, int keys, int topk, uint8_t* ws, int batch,
                     const DeviceInfo& d, unsigned flags, void* stream,
-                    const KeySource& src = KeySource()) {
-  const Layout L = layout(batch, d, src.table ? keys : 0);
+                    const KeySource& src = KeySource(), int hm = 1) {
+  const Layout L = layout(batch * hm, d, src.table ? keys : 0);
   hipEvent_t eb = nullptr, ee = nullptr;
   if (flags & MQA_FLAG_TIME_SCAN) {
     int dev = 0;
@@ -251,17 +253,18 @@ int prefill_batches(const uint8_t* q, const uint8_t* k, const float* scales,
   for (int r0 = 0; r0 < rows; r0 += batch) {
     const int nr = rows - r0 < batch ? rows - r0 : batch;
     mqa::FusedParams p;
-    p.q = q + (size_t)r0 * MQA_HEADS * MQA_HEAD_DIM;
+    p.q = q + (size_t)r0 * hm * MQA_HEADS * MQA_HEAD_DIM;
     p.k = k;
     p.scales = scales;
-    p.weights = weights + (size_t)r0 * MQA_HEADS;
+    p.weights = weights + (size_t)r0 * hm * MQA_HEADS;
     p.starts = starts + r0;
     p.ends = ends + r0;
     p.out = out + (size_t)r0 * topk;
-    p.rows = nr;
+    p.rows = nr * hm;
     p.keys = keys;
     p.topk = topk;
-    p.nblocks = (nr + mqa::kFusedBlockRows - 1) / mqa::kFusedBlockRows;
+    p.nblocks = (nr * hm + mqa::kFusedBlockRows - 1) / mqa::kFusedBlockRows;
+    p.hm = hm;
     p.flags = flags;
     set_workspace(p, ws, L);
     p.table = src.table;
@@ -320,6 +323,7 @@ int decode_batches(const uint8_t* q, const uint8_t* cache, const int32_t* table,
     p.num_pages = num_pages;
     p.page_bytes = (int64_t)(MQA_HEAD_DIM + 4) << shift;
     p.dec_rows = R;
+    p.hm = 1;
     p.dec_parts = dec_parts(R);
     p.nreq = nq;
     p.table_stride = table_stride;
@@ -472,6 +476,41 @@ int mqa_topk_prefill_paged(const uint8_t* q, const uint8_t* cache, const int32_t
   src.num_pages = num_pages;
   return prefill_batches(q, cache, nullptr, weights, starts, ends, out, rows, keys, topk,
                          static_cast<uint8_t*>(workspace), batch, *d, flags, stream, src);
+}
+
+size_t workspace_size_heads(int rows, int heads, int device) {
+  if (rows < 1 || rows > MQA_MAX_ROWS || (heads != 32 && heads != 64)) return 0;
+  const DeviceInfo* d = device_info(device);
+  if (!d) return 0;
+  const int hm = heads / 32;
+  const int batch = rows < mqa::kMaxBatchRows / hm ? rows : mqa::kMaxBatchRows / hm;
+  return layout(batch * hm, *d).total;
+}
+
+int mqa_topk_prefill_heads(const uint8_t* q, const uint8_t* k, const float* scales,
+                           const float* weights, const int32_t* starts, const int32_t* ends,
+                           int32_t* out, int rows, int keys, int heads, int topk,
+                           void* workspace, size_t workspace_bytes, unsigned flags,
+                           void* stream) {
+  if (!q || !k || !scales || !weights || !starts || !ends || !out || !workspace)
+    return MQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scales, 16) || !aligned(weights, 16) ||
+      !aligned(out, 16) || !aligned(starts, 4) || !aligned(ends, 4) || !aligned(workspace, 256))
+    return MQA_ERR_ALIGN;
+  if (rows < 1 || rows > MQA_MAX_ROWS || keys < 1 || keys > MQA_MAX_KEYS || !topk_ok(topk) ||
+      (heads != 32 && heads != 64))
+    return MQA_ERR_SHAPE;
+  const DeviceInfo* d = current_device();
+  if (!d) return MQA_ERR_DEVICE;
+  const int hm = heads / 32;
+  const int batch = rows < mqa::kMaxBatchRows / hm ? rows : mqa::kMaxBatchRows / hm;
+  if (workspace_bytes < layout(batch * hm, *d).total) {
+    g_ws_err[0] = 0;
+    return MQA_ERR_WORKSPACE;
+  }
+  return prefill_batches(q, k, scales, weights, starts, ends, out, rows, keys, topk,
+                         static_cast<uint8_t*>(workspace), batch, *d, flags, stream,
+                         KeySource(), hm);
 }
 
 size_t workspace_size_paged(int rows, int keys, int device) {

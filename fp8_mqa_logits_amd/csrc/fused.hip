@@ -93,8 +93,35 @@ __device__ __forceinline__ int slab_cap(const FusedParams& p) {
 // output is sorted by key.
 __device__ __forceinline__ bool det_mode(const FusedParams& p) { return (p.flags & 64u) != 0u; }
 
+// 64 index heads (p.hm == 2): the real row of virtual row v, whether v is a
+// partner (the second 32 heads of its row), and the output row of v.
+__device__ __forceinline__ int real_row(const FusedParams& p, int v) { return v >> (p.hm - 1); }
+__device__ __forceinline__ bool partner_row(const FusedParams& p, int v) {
+  return (v & (p.hm - 1)) != 0;
+}
+__device__ __forceinline__ int32_t* out_row(const FusedParams& p, int v) {
+  return p.out + (int64_t)real_row(p, v) * p.topk;
+}
+
+// The FP8 error bound factor of lead row r: its own, or with 64 heads the
+// sum of both halves' (each bounds its half's score), widened by 2^-8 for
+// the fp32 addition of the two halves' scores.
+__device__ __forceinline__ float beta_of(const FusedParams& p, int r) {
+  return p.hm == 2 ? (p.beta[r] + p.beta[r + 1]) * (1.f + 0x1p-8f) : p.beta[r];
+}
+
+// Exact score of a chunk's keys (lane l: key l) for a row: one 32-head query,
+// or the two halves' exact head sums added before the scale (64 heads). Every
+// exact score of the path is computed this way, so equal keys score equal.
+__device__ __forceinline__ float exact_score(const QueryRow& qr, const QueryRow* qr2,
+                                             const KeyTile& kt, float sc) {
+  float u = score_chunk_exact(qr, kt);
+  if (qr2) u += score_chunk_exact(*qr2, kt);
+  return u * sc;
+}
+
 __device__ __forceinline__ void row_range(const FusedParams& p, int r, int& s, int& e) {
-  int a = p.starts[r], b = p.ends[r];
+  int a = p.starts[real_row(p, r)], b = p.ends[real_row(p, r)];
   a = a < 0 ? 0 : (a > p.keys ? p.keys : a);
   b = b < a ? a : (b > p.keys ? p.keys : b);
   s = a;
@@ -472,10 +499,36 @@ __device__ __forceinline__ void wave_rows(const FusedParams& p, int b, RowState*
   }
 }
 
+// 64 heads: the partner slots (odd) of the wave carry the second 32 heads of
+// the lead rows before them; for every lead row in `mode` (or M_ALL with
+// M_GATED), load the partner's query (weights times wscale, as the lead's)
+// and take it into the fold (frows, when given).
+__device__ __forceinline__ void load_partners(const FusedParams& p, const RowState* rs,
+                                              QueryRow* qr, int* frows, int mode,
+                                              float wscale) {
+  if (p.hm != 2) return;
+#pragma unroll
+  for (int i = 1; i < kRowsPerWave; i += 2) {
+    const int m = rs[i - 1].mode;
+    if (m == mode || (mode == M_GATED && m == M_ALL)) {
+      load_query(qr[i], p.q, p.weights, rs[i].r, wscale);
+      if (frows) frows[i] = rs[i].r;
+    }
+  }
+}
+
+// 64 heads: a lead row's score is its slot's plus its partner's.
+__device__ __forceinline__ void combine_halves(const FusedParams& p, float* E) {
+  if (p.hm == 2) {
+    E[0] += E[1];
+    E[2] += E[3];
+  }
+}
+
 // A row's error bound factor as a wave-uniform (scalar) value: in the scan
 // loop it is an SGPR operand of the admission FMA, not one of the VGPRs.
 __device__ __forceinline__ float row_beta_of(const FusedParams& p, int r) {
-  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(p.beta[r])));
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(beta_of(p, r))));
 }
 
 __device__ __forceinline__ void zero_query(QueryRow& qr) {
@@ -924,7 +977,9 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
         kw = key | __float_as_int(nh);
         load_keys_lds(kt, kc);
         // rows that are not live have zeroed operands and a NaN threshold
+        // (64 heads: partner slots are not live; their scores join the lead's)
         score4(E, qr, fo, kt, sc);
+        combine_halves(p, E);
       }
       // admission and records by U = E + beta * nhat, an upper bound of the
       // key's exact score
@@ -944,9 +999,20 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
       KeyTile kt;
       load_keys_lds(kt, kc);
       float E[4];
+      if (SRC != SRC_DECODE && p.hm == 2) {
+        // 64 heads: lead slot i scores with its partner i + 1 (exact_score's
+        // order: the halves' head sums added, then the scale)
 #pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i)
-        E[i] = act[i] ? score_chunk_exact(qr[i], kt) * sc : 0.f;
+        for (int i = 0; i < kRowsPerWave; i += 2) {
+          E[i] = act[i] ? (score_chunk_exact(qr[i], kt) + score_chunk_exact(qr[i + 1], kt)) * sc
+                        : 0.f;
+          E[i + 1] = 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i)
+          E[i] = act[i] ? score_chunk_exact(qr[i], kt) * sc : 0.f;
+      }
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i)
         if (act[i]) finish_row(rs[i], E[i], th[i], key, key0, sr, i);
@@ -1099,12 +1165,12 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
       RowState& r = rs[i];
       zero_query(qr[i]);
       frows[i] = -1;
-      if (r.r >= p.rows) continue;
+      if (r.r >= p.rows || partner_row(p, r.r)) continue;
       const int n = r.e - r.s;
       if (n <= k) {
         r.mode = M_SHORT;
         if (mine) {
-          int32_t* o = p.out + (int64_t)r.r * k;
+          int32_t* o = out_row(p, r.r);
           for (int j = l; j < k; j += kWave) o[j] = j < n ? j : -1;
           if (stats && l == 0) atomicAdd(&p.header[H_SHORT], 1u);
         }
@@ -1125,6 +1191,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
         wg |= mine ? 1 : 0;  // the part samples only when it serves a gated row
       }
     }
+    load_partners(p, rs, qr, frows, M_GATED, 0.5f);
     int lo, hi, any_g;
     block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, wg, p.keys, lo, hi, any_g);
     // the fine pass's hand-over (rbin -1: none)
@@ -1179,6 +1246,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
           sc = scl[l];
           load_keys_lds(kt, kc);
           score4(E, qr, fo, kt, sc);
+          combine_halves(p, E);
         }
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) E[i] = __builtin_fmaf(rs[i].beta, nh, E[i]);
@@ -1366,6 +1434,15 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
       r.beta = row_beta_of(p, r.r);
       wfine = 1;
     }
+    if (p.hm == 2) {
+      // partners of the refined rows (rows with a fine pass have frows set)
+#pragma unroll
+      for (int i = 1; i < kRowsPerWave; i += 2)
+        if (frows[i - 1] >= 0) {
+          load_query(qr[i], p.q, p.weights, rs[i].r, 0.5f);
+          frows[i] = rs[i].r;
+        }
+    }
     int lo, hi, unused;
     block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, 0, p.keys, lo, hi, unused);
     if (hi > lo) {
@@ -1399,6 +1476,7 @@ __global__ __launch_bounds__(kThreads) void fused_refine_kernel(FusedParams p) {
           sc = scl[l];
           load_keys_lds(kt, kc);
           score4(E, qr, fo, kt, sc);
+          combine_halves(p, E);
         }
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) E[i] = __builtin_fmaf(rs[i].beta, nh, E[i]);
@@ -1509,6 +1587,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
         whi = r.e > whi ? r.e : whi;
       }
     }
+    load_partners(p, rs, qr, frows, M_GATED, 0.5f);
     int lo, hi, unused;
     block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, 0, p.keys, lo, hi, unused);
     if (SPLIT && hi > lo) {
@@ -1566,8 +1645,8 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
 template <int SRC, class Emit>
 __device__ bool select_interval(const FusedParams& p, float* sE, int32_t* sI, int n, int k,
                                 float beta, float Thi, bool thi_lt, float hint_lo, float hint_hi,
-                                const QueryRow& qr, int req, uint32_t* hist, float& low,
-                                Emit emit) {
+                                const QueryRow& qr, const QueryRow* qr2, int req,
+                                uint32_t* hist, float& low, Emit emit) {
   const int l = lane_id();
   constexpr int kBins = kHistWords;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -1730,7 +1809,7 @@ __device__ bool select_interval(const FusedParams& p, float* sE, int32_t* sI, in
     float scn = 0.f;
     if (b0 + kWave < nb) group_refs(b0 + kWave, kn, scn);
     const int j = b0 + l;
-    const float E = score_chunk_exact(qr, kt) * sc;
+    const float E = exact_score(qr, qr2, kt, sc);
     if (j < nb) {
       const int kw = sI[j];
       if (stats) {
@@ -1791,7 +1870,9 @@ __device__ __forceinline__ void queue_rescan(const FusedParams& p, int r, float 
 }
 
 // Select: one wave per row.
-template <int SRC>
+// H2: 64 index heads (rows of two 32-head halves); a separate instance, so
+// that the 32-head select keeps its registers.
+template <int SRC, bool H2>
 __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_eu(4))) void fused_select_kernel(FusedParams p) {
   __shared__ uint32_t hist[kSelWaves][kHistWords];
   const int w = wave_id();
@@ -1836,9 +1917,10 @@ __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_
     if (cnt >= k) {
       int s, e;
       row_range(p, r, s, e);
-      QueryRow qr;
+      QueryRow qr, qr2;
       load_query(qr, p.q, p.weights, r);
-      int32_t* o = p.out + (int64_t)r * k;
+      if constexpr (H2) load_query(qr2, p.q, p.weights, r + 1);
+      int32_t* o = out_row(p, r);
       // non-candidates score below the bound unless a merge raised it (then
       // at most it); split rows are taken as raised
       const bool thi_lt = p.nseg == 1 && ri.strict == 0;
@@ -1851,8 +1933,9 @@ __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_
         hhi = m0 + (m0 - ri.thr);
       }
       const int req = p.dec_rows ? r / p.dec_rows : 0;
-      ok = select_interval<SRC>(p, sE, sI, cnt, k, p.beta[r], thi, thi_lt, hlo, hhi, qr, req,
-                                hist[w], low, [&](int sl, int idx) { o[sl] = idx - s; });
+      ok = select_interval<SRC>(p, sE, sI, cnt, k, beta_of(p, r), thi, thi_lt, hlo, hhi, qr,
+                                H2 ? &qr2 : nullptr, req, hist[w], low,
+                                [&](int sl, int idx) { o[sl] = idx - s; });
       if (stats && l == 0) {
         atomicAdd(&p.header[ok ? H_GATED : H_UNCERT], 1u);
         atomicAdd(reinterpret_cast<unsigned long long*>(&p.header[H_CAND_LO]),
@@ -1879,7 +1962,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_
 // scoring >= the row's bound (> in a strict round) get slab slots from the
 // row's counter (slots past the slab are counted, not written), and the keys
 // strictly above it are counted apart.
-template <int SRC>
+template <int SRC, bool H2>
 __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, int round) {
   const int l = lane_id();
   const int nq = (int)p.header[H_RQ + 2 * round];
@@ -1900,8 +1983,9 @@ __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, i
     const int a = s > slice * kRescanKeys ? s : slice * kRescanKeys;
     const int b = e < (slice + 1) * kRescanKeys ? e : (slice + 1) * kRescanKeys;
     if (a >= b) continue;
-    QueryRow qr;
+    QueryRow qr, qr2;
     load_query(qr, p.q, p.weights, r);
+    if constexpr (H2) load_query(qr2, p.q, p.weights, r + 1);
     const float low = p.rowinfo[r].thr;
     const bool strict = p.rowinfo[r].strict != 0;
     float* sE = p.slabE + (int64_t)r * kSlabRow;
@@ -1917,7 +2001,8 @@ __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, i
       load_keys_rows<SRC>(kt, p, keyidx, req);
       const int key = k0 + l;
       const bool valid = key < b;
-      const float E = score_chunk_exact(qr, kt) * scan_scale<SRC>(p, valid ? key : b - 1, req);
+      const float E = exact_score(qr, H2 ? &qr2 : nullptr, kt,
+                                  scan_scale<SRC>(p, valid ? key : b - 1, req));
       const bool pass = valid && (strict ? E > low : E >= low);
       const uint64_t m = __ballot(pass);
       if (m == 0) continue;
@@ -1960,7 +2045,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_finish_kernel(FusedPa
     int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
     int s, e;
     row_range(p, r, s, e);
-    int32_t* o = p.out + (int64_t)r * k;
+    int32_t* o = out_row(p, r);
     if (cnt >= need && cnt <= kSlabRow) {
       auto put = [&](int sl, float, int idx) { o[sl] = idx - s; };
       if (det_mode(p))
@@ -2048,6 +2133,7 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
       wlo = r.s < wlo ? r.s : wlo;
       whi = r.e > whi ? r.e : whi;
     }
+    load_partners(p, rs, qr, nullptr, M_EXACT, 1.f);
     int lo, hi, unused;
     block_union(sm.wlo, sm.whi, sm.wf, wlo, whi, 0, p.keys, lo, hi, unused);
     if (hi > lo) {
@@ -2059,7 +2145,7 @@ __global__ __launch_bounds__(kThreads) void fused_exact_kernel(FusedParams p) {
       for (int i = 0; i < kRowsPerWave; ++i) {
         RowState& r = rs[i];
         if (r.mode != M_EXACT) continue;
-        int32_t* o = p.out + (int64_t)r.r * k;
+        int32_t* o = out_row(p, r.r);
         const int base = r.s;
         const int have = r.cnt;
         auto put = [&](int sl, float, int idx) { o[sl] = idx - base; };
@@ -2134,12 +2220,12 @@ __device__ __forceinline__ void wave_sort_asc(int32_t* o) {
 // padding.
 __global__ __launch_bounds__(kSelWaves * kWave) void fused_sort_kernel(FusedParams p) {
   const int r = blockIdx.x * kSelWaves + wave_id();
-  if (r >= p.rows) return;
+  if (r >= p.rows || partner_row(p, r)) return;
   const int k = p.topk;
   int s, e;
   row_range(p, r, s, e);
   if (e - s <= k) return;
-  int32_t* o = p.out + (int64_t)r * k;
+  int32_t* o = out_row(p, r);
   if (k == 2048)
     wave_sort_asc<32>(o);
   else if (k == 1024)
@@ -2202,13 +2288,23 @@ int fused_launch_scan(const FusedParams* p, int grid, hipStream_t stream, hipEve
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (scan_end && (e = hipEventRecord(scan_end, stream)) != hipSuccess) return (int)e;
   const int sel = (p->rows + kSelWaves - 1) / kSelWaves;
-  hipLaunchKernelGGL(fused_select_kernel<SRC>, dim3(sel), dim3(kSelWaves * kWave), 0, stream,
-                     *p);
+  // (64 heads: gathered calls only)
+  constexpr bool kH2 = SRC != SRC_DECODE;
+  if (kH2 && p->hm == 2)
+    hipLaunchKernelGGL((fused_select_kernel<SRC, kH2>), dim3(sel), dim3(kSelWaves * kWave), 0,
+                       stream, *p);
+  else
+    hipLaunchKernelGGL((fused_select_kernel<SRC, false>), dim3(sel), dim3(kSelWaves * kWave), 0,
+                       stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   const int fin = sel < 256 ? sel : 256;
   for (int round = 0; round < kRescanRounds; ++round) {
-    hipLaunchKernelGGL(fused_rescan_kernel<SRC>, dim3(2 * grid), dim3(kThreads), 0, stream, *p,
-                       round);
+    if (kH2 && p->hm == 2)
+      hipLaunchKernelGGL((fused_rescan_kernel<SRC, kH2>), dim3(2 * grid), dim3(kThreads), 0,
+                         stream, *p, round);
+    else
+      hipLaunchKernelGGL((fused_rescan_kernel<SRC, false>), dim3(2 * grid), dim3(kThreads), 0,
+                         stream, *p, round);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
     hipLaunchKernelGGL(fused_finish_kernel, dim3(fin), dim3(kSelWaves * kWave), 0, stream, *p,
                        round);

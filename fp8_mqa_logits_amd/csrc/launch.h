@@ -86,6 +86,11 @@ struct FusedParams {
   // form dec_parts parts of up to 8 rows, and blocks pack four parts; keys
   // is the positions' bound, and keyinfo is unused.
   int dec_rows, dec_parts, nreq, table_stride;
+  // Index heads / 32 (1, or 2 for 64 heads). With 64 heads a row r runs as
+  // the virtual rows 2r (its lead: state, candidates, output) and 2r + 1 (its
+  // partner: heads 32..63), each read as a 32-head row of q and weights; rows
+  // counts virtual rows, and starts/ends/out are indexed by r.
+  int hm;
   float* slabE;      // [nblocks * 32 rows][kSlabRow] candidate scores
   int32_t* slabI;    // [nblocks * 32 rows][kSlabRow] candidate keys
   float* tmpE;       // [grid][8 waves][kTmp] merge buffers

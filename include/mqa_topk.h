@@ -138,6 +138,32 @@ int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
                      size_t workspace_bytes, unsigned flags, void* stream);
 
 /*
+ * Bytes of device workspace one mqa_topk_prefill_heads call over `rows` rows
+ * of `heads` index heads needs on HIP device `device` (heads 32: the same as
+ * workspace_size). Returns 0 for a bad device or size, or heads not 32 or 64.
+ */
+size_t workspace_size_heads(int rows, int heads, int device);
+
+/*
+ * mqa_topk_prefill with 32 or 64 index heads (64: DeepSeek-V3.2's indexer, PR
+ * #60618, "Limitations of this PR -- TODOs"):
+ *     logit[r,j] = scale_j * sum_{h<heads} w[r,h] * relu(q[r,h,:] . k[j,:])
+ *   q        [rows, heads, 128] e4m3, 16-B aligned
+ *   weights  [rows, heads] fp32, 16-B aligned
+ *   heads    32 or 64
+ * Every other argument, the workspace (>= workspace_size_heads(rows, heads,
+ * device) bytes), the flags, the output and the return codes as for
+ * mqa_topk_prefill. A 64-head row runs as two 32-head halves whose scores
+ * are added before any selection (its FP8 error bound is the sum of the
+ * halves' bounds); calls run in batches of at most 8192 such rows.
+ */
+int mqa_topk_prefill_heads(const uint8_t* q, const uint8_t* k, const float* scales,
+                           const float* weights, const int32_t* starts, const int32_t* ends,
+                           int32_t* out, int rows, int keys, int heads, int topk,
+                           void* workspace, size_t workspace_bytes, unsigned flags,
+                           void* stream);
+
+/*
  * mqa_topk_prefill without a workspace argument and without any allocation,
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc). Same

@@ -496,6 +496,20 @@ def decode_device(requests: int, R: int, ctx: int, topk: int, page_size: int = 6
             "rows": rows, "pairs": int(ends.sum().item())}
 
 
+def heads64(rows: int, keys: int, topk: int, starts, ends, seed: int = 1,
+            name: str = "heads64") -> Workload:
+    """64 index heads (DeepSeek-V3.2's indexer): q [rows, 64, 128] and weights
+    [rows, 64] drawn like the 32-head workloads (weights N(0,1)/sqrt(64)),
+    keys and scales as config 3; row ranges given."""
+    rng = np.random.Generator(np.random.PCG64(SEED_BASE + 3000 + seed))
+    q = encode_e4m3(_normal(rng, (rows, 64, DIM)))
+    k = encode_e4m3(_normal(rng, (keys, DIM)))
+    sb = _scales(rng, keys)
+    w = (rng.standard_normal((rows, 64)) / math.sqrt(64)).astype(np.float32)
+    return Workload(name, rows, keys, topk, q, k, sb, w, np.asarray(starts, np.int32).copy(),
+                    np.asarray(ends, np.int32).copy(), seed)
+
+
 def sample_rows(wl: Workload, n: int = 256, seed: int = 7) -> np.ndarray:
     """Seeded row sample for oracle checks of large workloads. With groups
     (config 5) it is stratified: half uniform over ungrouped rows, the rest

@@ -26,6 +26,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert set(names) == {"workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static",
+                          "workspace_size_heads", "mqa_topk_prefill_heads",
                           "mqa_topk_prefill_paged", "workspace_size_paged",
                           "workspace_size_decode",
                           "mqa_topk_decode_paged", "mqa_logits_dense",
@@ -224,6 +225,28 @@ def test_decode_errors():
     if _no_gpu():
         assert _decode() == 5
         assert _decode(R=1, requests=4096) == 5
+
+
+def test_heads_prefill_errors():
+    P = ctypes.c_void_p
+
+    def call(**kw):
+        a = dict(q=A16, k=A16, scales=A16, weights=A16, starts=A16, ends=A16, out=A16,
+                 rows=64, keys=4096, heads=64, topk=512, ws=0x20000, wsb=1 << 40)
+        a.update(kw)
+        return mqa.load().mqa_topk_prefill_heads(
+            P(a["q"]), P(a["k"]), P(a["scales"]), P(a["weights"]), P(a["starts"]), P(a["ends"]),
+            P(a["out"]), a["rows"], a["keys"], a["heads"], a["topk"], P(a["ws"]), a["wsb"], 0,
+            None)
+    assert call(q=0) == 1
+    assert call(weights=MIS) == 2
+    for h in (0, 16, 48, 96, 128):
+        assert call(heads=h) == 3, h
+    assert call(rows=0) == 3
+    assert mqa.load().workspace_size_heads(64, 48, 0) == 0
+    if _no_gpu():
+        assert call() == 5
+        assert call(heads=32) == 5
 
 
 def test_fp8_probe_errors():

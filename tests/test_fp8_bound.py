@@ -183,3 +183,26 @@ def test_decode_bound_factor_dominates(kind):
     if kind == "normal":
         # and it is not far looser than the per-group bound on Gaussian keys
         assert np.median(dec / key_nhat(k, sc)) < 2.5
+
+
+@pytest.mark.parametrize("case", ["gaussian", "heavy_weights", "spiky_q"])
+def test_64_head_bound_holds(case):
+    # a 64-head row runs as two 32-head halves whose FP8 scores are added in
+    # fp32; the bound is the halves' factors summed, times (1 + 2^-8)
+    rng = np.random.default_rng(100 + ["gaussian", "heavy_weights", "spiky_q"].index(case))
+    worst = 0.0
+    for _ in range(2):
+        q = np.concatenate([_rows(rng, 1, spike=case == "spiky_q")[0],
+                            _rows(rng, 1, spike=case == "spiky_q")[0]])  # [64, 128]
+        w = np.concatenate([_weights(rng, case == "heavy_weights"),
+                            _weights(rng, case == "heavy_weights")])
+        k = _keys(rng, 128, "wide")
+        sc = _scales(rng, 128)
+        E = (fp8_scores(q[:32], w[:32], k, sc).astype(np.float32)
+             + fp8_scores(q[32:], w[32:], k, sc).astype(np.float32)).astype(np.float64)
+        S = exact_scores(q[:32], w[:32], k, sc) + exact_scores(q[32:], w[32:], k, sc)
+        beta = np.float32((np.float32(row_beta(q[:32], w[:32])) + np.float32(row_beta(q[32:], w[32:])))
+                          * np.float32(1 + 2.0 ** -8))
+        B = float(beta) * key_nhat(k, sc)
+        worst = max(worst, float(np.max(np.abs(E - S) / np.where(B > 0, B, 1))))
+    assert worst <= 1.0, worst
