@@ -177,3 +177,108 @@ def check_dense(gpu: np.ndarray, ref: np.ndarray, rel_tol: float = REL_TOL):
         c = int(np.nonzero(bad[r])[0][0])
         fails.append((int(r), f"col {c}: gpu {gpu[r, c]!r} ref {ref[r, c]!r}"))
     return fails
+
+
+# --------------------------------------------------------------------------
+# DeepSeek-V4.1 two-level candidate selection (vLLM PR #60618, "Limitations
+# of this PR -- TODOs"): the source layer also ranks blocks of 8 keys by their
+# maximum score; consumer layers keep only the keys of given blocks before
+# their top-k. Reading: blocks are 8 consecutive keys of the call's key
+# numbering, block B = keys [8B, 8B + 8); a row names block B as B - s // 8
+# (s its clamped start), and a block's score for a row is the maximum logit
+# over the row's visible keys in it.
+
+def masked_positions(s: int, e: int, blocks_row) -> np.ndarray:
+    """Sorted distinct positions (key - s) of the row's visible keys that lie
+    in its listed blocks (entries < 0 are padding)."""
+    b = np.unique(np.asarray(blocks_row, np.int64))
+    b = b[b >= 0]
+    keys = ((b[:, None] + s // 8) * 8 + np.arange(8)[None, :]).reshape(-1)
+    keys = keys[(keys >= s) & (keys < e)]
+    return keys - s
+
+
+def block_maxima(s: int, e: int, row_logits: np.ndarray) -> np.ndarray:
+    """Block scores of a row: entry i is block s // 8 + i (i.e. named i), the
+    maximum of row_logits (logits of keys s..e-1) over the block's visible
+    keys; blocks i = 0 .. (e - 1) // 8 - s // 8 (none when e == s)."""
+    if e <= s:
+        return np.zeros(0, np.float64)
+    b0 = s // 8
+    nb = (e - 1) // 8 - b0 + 1
+    full = np.full(nb * 8, -np.inf)
+    full[s - 8 * b0: e - 8 * b0] = row_logits
+    return full.reshape(nb, 8).max(1)
+
+
+def check_select_row(sel: np.ndarray, values: np.ndarray, k: int, tol: float):
+    """The acceptance rule on a compact set: sel holds indices into values;
+    min(n, k) distinct valid ones then -1; every chosen value at least the
+    k-th largest minus tol, every other at most it plus tol."""
+    sel = np.asarray(sel)
+    n = values.shape[0]
+    m = min(n, k)
+    lead, tail = sel[:m], sel[m:]
+    if np.any(tail != -1):
+        return "padding is not trailing -1"
+    if np.any(lead < 0) or np.any(lead >= n):
+        return "index outside the candidates"
+    if np.unique(lead).shape[0] != m:
+        return "duplicate index"
+    if n <= k:
+        return None
+    v = values.astype(np.float64)
+    tau = np.partition(v, n - k)[n - k]
+    chosen = np.zeros(n, bool)
+    chosen[lead] = True
+    if v[chosen].min() < tau - tol:
+        return f"selected value {v[chosen].min()!r} below tau {tau!r} - tol {tol!r}"
+    if v[~chosen].max() > tau + tol:
+        return f"unselected value {v[~chosen].max()!r} above tau {tau!r} + tol {tol!r}"
+    return None
+
+
+def _row_logits(oracle_problem, rows, threads=0):
+    import oracle  # test infrastructure: this module lives beside it
+    for r in np.asarray(rows, np.int32):
+        s, e = oracle_problem.visible(int(r))
+        lg = oracle.logits(oracle_problem, [int(r)], col0=s, ncols=max(e - s, 1),
+                           threads=threads)[0, : e - s]
+        yield int(r), s, e, lg
+
+
+def check_topk_masked(out_rows, rows, oracle_problem, blocks, topk: int,
+                      rel_tol: float = REL_TOL):
+    """Consumer rows: out_rows[i] (key - s entries) must be the top-k of row
+    rows[i]'s keys in its listed blocks (blocks[rows[i]])."""
+    fails = []
+    for i, (r, s, e, lg) in enumerate(_row_logits(oracle_problem, rows)):
+        pos = masked_positions(s, e, blocks[r])
+        out = np.asarray(out_rows[i])
+        idx = np.full(out.shape, -1, np.int64)
+        valid = out >= 0
+        where = np.searchsorted(pos, out[valid])
+        ok = (where < pos.shape[0]) & (pos[np.minimum(where, max(pos.shape[0] - 1, 0))] == out[valid]) \
+            if pos.shape[0] else np.zeros(int(valid.sum()), bool)
+        if not np.all(ok):
+            fails.append((r, "selected key outside the row's blocks"))
+            continue
+        idx[valid] = where
+        tol = rel_tol * float(np.max(np.abs(lg))) if lg.size else 0.0
+        msg = check_select_row(idx, lg[pos].astype(np.float64), topk, tol)
+        if msg:
+            fails.append((r, msg))
+    return fails
+
+
+def check_blocks(out_blocks, rows, oracle_problem, nbo: int, rel_tol: float = REL_TOL):
+    """Source rows: out_blocks[i] must name the nbo blocks of largest score of
+    row rows[i] (block_maxima), unordered, -1 padded."""
+    fails = []
+    for i, (r, s, e, lg) in enumerate(_row_logits(oracle_problem, rows)):
+        bm = block_maxima(s, e, lg)
+        tol = rel_tol * float(np.max(np.abs(lg))) if lg.size else 0.0
+        msg = check_select_row(np.asarray(out_blocks[i]), bm, nbo, tol)
+        if msg:
+            fails.append((r, msg))
+    return fails

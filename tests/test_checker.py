@@ -1,5 +1,7 @@
 """The acceptance checker must accept correct results, accept any tie
 resolution, and reject planted mistakes. CPU only."""
+import itertools
+
 import numpy as np
 
 import mqa_workloads as W
@@ -140,3 +142,44 @@ def test_near_tie_workload_separates_groups_beyond_tolerance():
         assert check.check_topk_row(sel, lg[r].astype(np.float32), wl.topk) is None
         sel[0] = b[0]
         assert check.check_topk_row(sel, lg[r].astype(np.float32), wl.topk) is not None
+
+
+# ------------------------------------------------ two-level selection checks
+
+def test_block_maxima_against_loops():
+    rng = np.random.default_rng(0)
+    for s, e in ((0, 64), (3, 50), (8, 9), (13, 13), (5, 200)):
+        lg = rng.standard_normal(e - s)
+        got = check.block_maxima(s, e, lg)
+        want = []
+        for b in range(s // 8, (e - 1) // 8 + 1 if e > s else s // 8):
+            keys = [j for j in range(8 * b, 8 * b + 8) if s <= j < e]
+            want.append(max(lg[j - s] for j in keys))
+        assert np.array_equal(got, np.array(want)), (s, e)
+
+
+def test_masked_positions_against_loops():
+    s, e = 13, 90
+    blocks = np.array([0, 3, -1, 10, 3, 2, -5])
+    want = sorted({j - s for b in (0, 3, 10, 2) for j in range(8 * (b + s // 8), 8 * (b + s // 8) + 8)
+                   if s <= j < e})
+    assert check.masked_positions(s, e, blocks).tolist() == want
+
+
+def test_select_row_rule_against_brute_force():
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        n = int(rng.integers(1, 9))
+        k = int(rng.integers(1, 6))
+        v = rng.integers(0, 4, n).astype(np.float64)
+        m = min(n, k)
+        best = sorted(v, reverse=True)[m - 1] if m else None
+        for sub in itertools.combinations(range(n), m):
+            sel = np.array(list(sub) + [-1] * (k - m))
+            # a subset is a correct top-k iff no left-out value beats a taken one
+            taken = v[list(sub)]
+            left = np.delete(v, list(sub))
+            good = n <= k or (taken.min() >= (left.max() if left.size else -np.inf))
+            assert (check.check_select_row(sel, v, k, 0.0) is None) == good, (v, k, sub)
+    assert check.check_select_row(np.array([0, 0]), np.array([1.0, 2.0, 3.0]), 2, 0.0)
+    assert check.check_select_row(np.array([2, -1, 1]), np.array([1.0, 2.0, 3.0]), 3, 0.0)
