@@ -31,7 +31,7 @@ ERR_NAMES = {0: "MQA_OK", 1: "MQA_ERR_NULL", 2: "MQA_ERR_ALIGN", 3: "MQA_ERR_SHA
              4: "MQA_ERR_WORKSPACE", 5: "MQA_ERR_DEVICE", 6: "MQA_ERR_LAUNCH"}
 
 EXPORTS = ("workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static",
-           "workspace_size_heads", "mqa_topk_prefill_heads",
+           "workspace_size_heads", "mqa_topk_prefill_heads", "mqa_topk_masked",
            "mqa_topk_prefill_paged", "workspace_size_paged", "workspace_size_decode", "mqa_topk_decode_paged",
            "mqa_logits_dense",
            "mqa_topk_dense",
@@ -66,6 +66,8 @@ def load() -> ctypes.CDLL:
         lib.workspace_size.restype = SZ
         lib.mqa_topk_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, P, SZ, U, P]
         lib.mqa_topk_prefill.restype = I
+        lib.mqa_topk_masked.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, P, SZ, U, P]
+        lib.mqa_topk_masked.restype = I
         lib.workspace_size_heads.argtypes = [I, I, I]
         lib.workspace_size_heads.restype = SZ
         lib.mqa_topk_prefill_heads.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, SZ, U, P]
@@ -219,6 +221,51 @@ def mqa_topk_prefill(q, k, scales, weights, starts, ends, topk: int, out=None, w
                                                _stream(dev, stream))
             where = "mqa_topk_prefill_heads"
     _check(rc, where)
+    return out
+
+
+MAX_BLOCKS = 2048
+
+
+def mqa_topk_masked(q, k, scales, weights, starts, ends, blocks, topk: int, out=None,
+                    workspace=None, flags: int = 0, stream=None) -> torch.Tensor:
+    """Two-level selection, consumer layers: the top-k of each row's keys in
+    its listed blocks of 8 (blocks [rows, nb] int32, block j = keys
+    8 (j + start // 8) .. + 7, entries < 0 padding, distinct otherwise).
+    Other arguments as mqa_topk_prefill (32 heads)."""
+    _tensors(q=q, k=k, scales=scales, weights=weights, starts=starts, ends=ends, blocks=blocks)
+    if q.dim() != 3 or k.dim() != 2 or blocks.dim() != 2:
+        raise ValueError("q must be [rows,32,128], k [keys,128] and blocks [rows, nb]")
+    rows, keys, nb = q.shape[0], k.shape[0], blocks.shape[1]
+    if nb < 1 or nb > MAX_BLOCKS:
+        raise ValueError(f"blocks: shape {tuple(blocks.shape)}, nb must be in [1, {MAX_BLOCKS}]")
+    _shape(q, (rows, HEADS, HEAD_DIM), "q")
+    _shape(k, (keys, HEAD_DIM), "k")
+    _shape(scales, (keys,), "scales")
+    _shape(weights, (rows, HEADS), "weights")
+    _shape(starts, (rows,), "starts")
+    _shape(ends, (rows,), "ends")
+    _shape(blocks, (rows, nb), "blocks")
+    if out is not None:
+        _tensors(out=out)
+        _shape(out, (rows, topk), "out")
+    dev = q.device
+    for t, n, dt in ((q, "q", FP8), (k, "k", FP8), (scales, "scales", (torch.float32,)),
+                     (weights, "weights", (torch.float32,)), (starts, "starts", (torch.int32,)),
+                     (ends, "ends", (torch.int32,)), (blocks, "blocks", (torch.int32,))):
+        _need(t, n, dt, dev)
+    if out is None:
+        out = torch.empty((rows, topk), dtype=torch.int32, device=dev)
+    _need(out, "out", (torch.int32,), dev)
+    if workspace is None:
+        workspace = alloc_workspace(rows, dev.index)
+    _need(workspace, "workspace", (torch.uint8,), dev)
+    with torch.cuda.device(dev):
+        rc = load().mqa_topk_masked(_ptr(q), _ptr(k), _ptr(scales), _ptr(weights), _ptr(starts),
+                                    _ptr(ends), _ptr(blocks), nb, _ptr(out), rows, keys,
+                                    int(topk), _ptr(workspace), workspace.numel(), int(flags),
+                                    _stream(dev, stream))
+    _check(rc, "mqa_topk_masked")
     return out
 
 

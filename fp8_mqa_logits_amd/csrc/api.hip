@@ -478,6 +478,51 @@ int mqa_topk_prefill_paged(const uint8_t* q, const uint8_t* cache, const int32_t
                          static_cast<uint8_t*>(workspace), batch, *d, flags, stream, src);
 }
 
+int mqa_topk_masked(const uint8_t* q, const uint8_t* k, const float* scales, const float* weights,
+                    const int32_t* starts, const int32_t* ends, const int32_t* blocks, int nb,
+                    int32_t* out, int rows, int keys, int topk, void* workspace,
+                    size_t workspace_bytes, unsigned flags, void* stream) {
+  if (!q || !k || !scales || !weights || !starts || !ends || !blocks || !out || !workspace)
+    return MQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scales, 16) || !aligned(weights, 16) ||
+      !aligned(out, 16) || !aligned(starts, 4) || !aligned(ends, 4) || !aligned(blocks, 4) ||
+      !aligned(workspace, 256))
+    return MQA_ERR_ALIGN;
+  if (rows < 1 || rows > MQA_MAX_ROWS || keys < 1 || keys > MQA_MAX_KEYS || !topk_ok(topk) ||
+      nb < 1 || nb > MQA_MAX_BLOCKS)
+    return MQA_ERR_SHAPE;
+  const DeviceInfo* d = current_device();
+  if (!d) return MQA_ERR_DEVICE;
+  const int batch = batch_rows(rows);
+  const Layout L = layout(batch, *d);
+  if (workspace_bytes < L.total) {
+    g_ws_err[0] = 0;
+    return MQA_ERR_WORKSPACE;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  for (int r0 = 0; r0 < rows; r0 += batch) {
+    const int nr = rows - r0 < batch ? rows - r0 : batch;
+    mqa::FusedParams p{};
+    p.q = q + (size_t)r0 * MQA_HEADS * MQA_HEAD_DIM;
+    p.k = k;
+    p.scales = scales;
+    p.weights = weights + (size_t)r0 * MQA_HEADS;
+    p.starts = starts + r0;
+    p.ends = ends + r0;
+    p.out = out + (size_t)r0 * topk;
+    p.rows = nr;
+    p.keys = keys;
+    p.topk = topk;
+    p.flags = flags;
+    p.hm = 1;
+    set_workspace(p, ws, L);
+    const int rc = mqa_masked_launch(&p, blocks + (size_t)r0 * nb, nb,
+                                     static_cast<hipStream_t>(stream));
+    if (rc != 0) return launch_error(rc);
+  }
+  return MQA_OK;
+}
+
 size_t workspace_size_heads(int rows, int heads, int device) {
   if (rows < 1 || rows > MQA_MAX_ROWS || (heads != 32 && heads != 64)) return 0;
   const DeviceInfo* d = device_info(device);

@@ -2238,6 +2238,89 @@ __global__ __launch_bounds__(kSelWaves * kWave) void fused_sort_kernel(FusedPara
 
 namespace mqa {
 
+// ---------------------------------------------------------------------------
+// Consumer rows of DeepSeek-V4.1's two-level candidate selection (vLLM PR
+// #60618, "Limitations of this PR -- TODOs": the consumer layers mask their
+// scores to the source layer's blocks before their top-k). Row r keeps only
+// the keys of its listed blocks of 8 (entry j names keys 8 (j + s / 8) ..
+// + 7, inside [s, e); entries < 0 are padding), scores them exactly (the
+// band rescoring's bf16 MFMA, so no FP8 bound is involved) into its slab (at
+// most 8 nb <= 16384 keys) and selects their top-k there. One wave per row;
+// in the deterministic mode the ties of the k-th score go to the smallest
+// keys and the row is sorted by key.
+__global__ __launch_bounds__(kSelWaves * kWave) void masked_topk_kernel(FusedParams p,
+                                                                        const int32_t* blocks,
+                                                                        int nb) {
+  __shared__ uint32_t hist[kSelWaves][kHistWords];
+  const int w = wave_id();
+  const int l = lane_id();
+  const int k = p.topk;
+  const int r = blockIdx.x * kSelWaves + w;
+  if (r >= p.rows) return;
+  int s, e;
+  row_range(p, r, s, e);
+  int32_t* o = p.out + (int64_t)r * k;
+  float* sE = p.slabE + (int64_t)r * kSlabRow;
+  int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
+  const int32_t* bl = blocks + (int64_t)r * nb;
+  const int64_t b0 = s >> 3;
+  QueryRow qr;
+  load_query(qr, p.q, p.weights, r);
+  int cnt = 0;
+  // key of chunk position c (block c0 + c / 8, offset c % 8), or -1
+  auto key_at = [&](int c0, int c) -> int {
+    const int j = c0 + (c >> 3);
+    const int bid = j < nb ? bl[j] : -1;
+    if (bid < 0) return -1;
+    const int64_t key = (bid + b0) * 8 + (c & 7);
+    return (key >= s && key < e) ? (int)key : -1;
+  };
+  for (int c0 = 0; c0 < nb && e > s; c0 += 8) {
+    int keyidx[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int key = key_at(c0, 16 * t + (l & 15));
+      keyidx[t] = key >= 0 ? key : s;
+    }
+    KeyTile kt;
+    load_keys_rows<SRC_GATHER>(kt, p, keyidx);
+    const int key = key_at(c0, l);
+    const bool valid = key >= 0;
+    const float E = exact_score(qr, nullptr, kt, p.scales[valid ? key : s]);
+    const uint64_t m = __ballot(valid);
+    if (valid) {
+      const int pos = cnt + rank_in_mask(m);
+      sE[pos] = E;
+      sI[pos] = key;
+    }
+    cnt += __popcll(m);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  const bool det = det_mode(p);
+  const int m = cnt < k ? cnt : k;
+  auto put = [&](int slot, float, int key) { o[slot] = key - s; };
+  if (cnt <= k) {
+    for (int i = l; i < cnt; i += kWave) o[i] = sI[i] - s;
+  } else if (det) {
+    wave_select_lowkey(sE, sI, cnt, k, hist[w], put);
+  } else {
+    wave_select(sE, sI, cnt, k, hist[w], put);
+  }
+  // padding (the deterministic mode sorts with it at the top of the range)
+  for (int i = m + l; i < k; i += kWave) o[i] = det ? 0x7FFFFFFF : -1;
+  if (det) {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    if (k == 2048)
+      wave_sort_asc<32>(o);
+    else if (k == 1024)
+      wave_sort_asc<16>(o);
+    else
+      wave_sort_asc<8>(o);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    for (int i = m + l; i < k; i += kWave) o[i] = -1;
+  }
+}
+
 // The launch sequence of one row batch, over one key source.
 template <int SRC>
 int fused_launch_scan(const FusedParams* p, int grid, hipStream_t stream, hipEvent_t scan_begin,
@@ -2326,6 +2409,14 @@ extern "C" int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t
     return mqa::fused_launch_all<mqa::SRC_DECODE>(p, grid, stream, scan_begin, scan_end);
   return p->table ? mqa::fused_launch_all<mqa::SRC_PAGED>(p, grid, stream, scan_begin, scan_end)
                   : mqa::fused_launch_all<mqa::SRC_GATHER>(p, grid, stream, scan_begin, scan_end);
+}
+
+extern "C" int mqa_masked_launch(const mqa::FusedParams* p, const int32_t* blocks, int nb,
+                                 hipStream_t stream) {
+  const int g = (p->rows + mqa::kSelWaves - 1) / mqa::kSelWaves;
+  hipLaunchKernelGGL(mqa::masked_topk_kernel, dim3(g), dim3(mqa::kSelWaves * mqa::kWave), 0,
+                     stream, *p, blocks, nb);
+  return (int)hipGetLastError();
 }
 
 extern "C" int mqa_fused_occupancy(int* wg_per_cu) {

@@ -140,6 +140,8 @@ extern "C" {
 int mqa_fused_launch(const mqa::FusedParams* p, int grid, hipStream_t stream,
                      hipEvent_t scan_begin, hipEvent_t scan_end);
 int mqa_fused_occupancy(int* wg_per_cu);
+int mqa_masked_launch(const mqa::FusedParams* p, const int32_t* blocks, int nb,
+                      hipStream_t stream);
 int mqa_dense_logits_launch(const mqa::DenseParams* p, hipStream_t stream);
 int mqa_dense_topk_launch(const mqa::DenseTopkParams* p, hipStream_t stream);
 int mqa_key_scales_launch(const uint8_t* b, float* s, int keys, hipStream_t stream);

@@ -54,6 +54,7 @@ extern "C" {
 #define MQA_HEAD_DIM 128
 #define MQA_MAX_KEYS (1 << 20) /* 1M keys per call (PR #60618, "Limitations") */
 #define MQA_MAX_ROWS (1 << 20)
+#define MQA_MAX_BLOCKS 2048    /* blocks of 8 keys per row of the two-level selection */
 
 /* Test-only flags for mqa_topk_prefill (0 in normal use). The output never
  * depends on them: they force the exact fallback (PR #60618, "What this PR
@@ -136,6 +137,27 @@ int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
                      const float* weights, const int32_t* starts, const int32_t* ends,
                      int32_t* out, int rows, int keys, int topk, void* workspace,
                      size_t workspace_bytes, unsigned flags, void* stream);
+
+/*
+ * Consumer layers of DeepSeek-V4.1's two-level candidate selection (PR
+ * #60618, "Limitations of this PR -- TODOs": they mask their scores to the
+ * source layer's blocks of 8 keys before the top-k). Row r keeps only the
+ * keys of its listed blocks: entry j of blocks[r] names keys
+ * 8 (j + s / 8) .. 8 (j + s / 8) + 7, s the row's clamped start (the naming of
+ * the source layer's block output), those inside the row's visible range;
+ * entries < 0 are padding. The row's output is the top-k of its kept keys by
+ * exact score (key - s, unordered, -1 padded when it keeps fewer than topk
+ * keys); MQA_FLAG_DETERMINISTIC sorts it by key and gives ties at the k-th
+ * score to the smallest keys.
+ *   blocks   [rows, nb] int32, 4-B aligned, nb in [1, MQA_MAX_BLOCKS]; a
+ *            row's non-negative entries must be distinct
+ *   workspace >= workspace_size(rows, device) bytes, 256-B aligned
+ * Other arguments and return codes as for mqa_topk_prefill (32 heads).
+ */
+int mqa_topk_masked(const uint8_t* q, const uint8_t* k, const float* scales, const float* weights,
+                    const int32_t* starts, const int32_t* ends, const int32_t* blocks, int nb,
+                    int32_t* out, int rows, int keys, int topk, void* workspace,
+                    size_t workspace_bytes, unsigned flags, void* stream);
 
 /*
  * Bytes of device workspace one mqa_topk_prefill_heads call over `rows` rows

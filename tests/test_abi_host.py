@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert set(names) == {"workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static",
-                          "workspace_size_heads", "mqa_topk_prefill_heads",
+                          "workspace_size_heads", "mqa_topk_prefill_heads", "mqa_topk_masked",
                           "mqa_topk_prefill_paged", "workspace_size_paged",
                           "workspace_size_decode",
                           "mqa_topk_decode_paged", "mqa_logits_dense",
@@ -247,6 +247,25 @@ def test_heads_prefill_errors():
     if _no_gpu():
         assert call() == 5
         assert call(heads=32) == 5
+
+
+def test_masked_errors():
+    P = ctypes.c_void_p
+
+    def call(**kw):
+        a = dict(q=A16, k=A16, scales=A16, weights=A16, starts=A16, ends=A16, blocks=A16, nb=2048,
+                 out=A16, rows=64, keys=4096, topk=512, ws=0x20000, wsb=1 << 40)
+        a.update(kw)
+        return mqa.load().mqa_topk_masked(
+            P(a["q"]), P(a["k"]), P(a["scales"]), P(a["weights"]), P(a["starts"]), P(a["ends"]),
+            P(a["blocks"]), a["nb"], P(a["out"]), a["rows"], a["keys"], a["topk"], P(a["ws"]),
+            a["wsb"], 0, None)
+    assert call(blocks=0) == 1
+    assert call(blocks=0x10002) == 2
+    assert call(nb=0) == 3 and call(nb=2049) == 3
+    assert call(topk=2047) == 3
+    if _no_gpu():
+        assert call() == 5
 
 
 def test_fp8_probe_errors():
