@@ -30,7 +30,9 @@ workload with 64 index heads), --paged P (read the keys
 from a paged indexer cache of P-token pages through mqa_topk_prefill_paged
 instead of the gathered keys and decoded scales), --decode N [--decode-rows R
 --decode-ctx C] (instead of the benchmark: the decode-shaped path over N
-requests of R rows, each with C positions of context, one JSON line), --sweep (instead of the benchmark: fused and
+requests of R rows, each with C positions of context, one JSON line),
+--twolevel (instead of the benchmark: the two-level selection's source and
+consumer calls at config 3's shape, top-512, one JSON line), --sweep (instead of the benchmark: fused and
 dense times on the causal-tail sweep, 16384 rows x 16K..1M keys, one JSON line
 per point), --copy-calibration MIB (instead of the benchmark,
 run a plain 1-D device copy of MIB MiB five times: the known-size kernel that
@@ -292,6 +294,53 @@ def decode_bench(args):
         "path_stats": stats}), flush=True)
 
 
+def twolevel_bench(args):
+    """DeepSeek-V4.1's two-level selection at config 3's shape (16384 rows x
+    131072 keys, causal tail): the source call (top-512 keys and the 2048
+    best blocks of 8 per row), the consumer call (top-512 of the keys in the
+    source's blocks), and the plain top-512 call for reference. One JSON line
+    of per-call times (event-timed averages)."""
+    import torch
+
+    import fp8_mqa_logits_amd as mqa
+    import mqa_workloads as W
+    torch.cuda.set_device(0)
+    wl = W.config(3)
+    d = to_device(wl, torch.device("cuda", 0))
+    ws = mqa.alloc_workspace(wl.rows)
+    k = 512
+    out = torch.empty((wl.rows, k), dtype=torch.int32, device="cuda")
+    ob = torch.empty((wl.rows, mqa.MAX_BLOCKS), dtype=torch.int32, device="cuda")
+    args_ = (d["q"], d["k"], d["scales"], d["weights"], d["starts"], d["ends"])
+    calls = {
+        "plain_top512": lambda f=0: mqa.mqa_topk_prefill(*args_, k, out=out, workspace=ws, flags=f),
+        "source_top512_blocks2048": lambda f=0: mqa.mqa_topk_prefill_blocks(
+            *args_, k, out=out, out_blocks=ob, workspace=ws, flags=f),
+        "consumer_top512_in_2048_blocks": lambda f=0: mqa.mqa_topk_masked(
+            *args_, ob, k, out=out, workspace=ws, flags=f),
+    }
+    res = {}
+    for name, fn in calls.items():
+        fn(mqa.FLAG_STATS)
+        torch.cuda.synchronize()
+        st = mqa.read_stats(ws)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = {"ms_per_call": e0.elapsed_time(e1) / args.steps,
+                     "rows_block_scan": st.get("rows_block_scan")}
+    print(json.dumps({"metric": "two-level selection per-call time", "unit": "ms",
+                      "config": {"workload": wl.name, "topk": k, "blocks": mqa.MAX_BLOCKS,
+                                 "visible_pairs": wl.visible_pairs()},
+                      "steps": args.steps, "warmup": args.warmup, "calls": res}), flush=True)
+
+
 def sweep(args):
     """Fused vs dense on the causal tail of K-key contexts (16384 rows)."""
     import gc
@@ -332,6 +381,7 @@ def main():
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--paged", type=int, default=0, metavar="P")
     ap.add_argument("--heads", type=int, default=32, choices=(32, 64))
+    ap.add_argument("--twolevel", action="store_true")
     ap.add_argument("--decode", type=int, default=0, metavar="REQUESTS")
     ap.add_argument("--decode-rows", type=int, default=8)
     ap.add_argument("--decode-ctx", type=int, default=131072)
@@ -363,6 +413,9 @@ def main():
         return
     if args.decode:
         decode_bench(args)
+        return
+    if args.twolevel:
+        twolevel_bench(args)
         return
 
     wl = W.config(args.config)

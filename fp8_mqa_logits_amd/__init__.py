@@ -32,6 +32,7 @@ ERR_NAMES = {0: "MQA_OK", 1: "MQA_ERR_NULL", 2: "MQA_ERR_ALIGN", 3: "MQA_ERR_SHA
 
 EXPORTS = ("workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static",
            "workspace_size_heads", "mqa_topk_prefill_heads", "mqa_topk_masked",
+           "mqa_topk_prefill_blocks",
            "mqa_topk_prefill_paged", "workspace_size_paged", "workspace_size_decode", "mqa_topk_decode_paged",
            "mqa_logits_dense",
            "mqa_topk_dense",
@@ -66,6 +67,8 @@ def load() -> ctypes.CDLL:
         lib.workspace_size.restype = SZ
         lib.mqa_topk_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, P, SZ, U, P]
         lib.mqa_topk_prefill.restype = I
+        lib.mqa_topk_prefill_blocks.argtypes = [P, P, P, P, P, P, P, P, I, I, I, P, SZ, U, P]
+        lib.mqa_topk_prefill_blocks.restype = I
         lib.mqa_topk_masked.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, P, SZ, U, P]
         lib.mqa_topk_masked.restype = I
         lib.workspace_size_heads.argtypes = [I, I, I]
@@ -225,6 +228,48 @@ def mqa_topk_prefill(q, k, scales, weights, starts, ends, topk: int, out=None, w
 
 
 MAX_BLOCKS = 2048
+
+
+def mqa_topk_prefill_blocks(q, k, scales, weights, starts, ends, topk: int, out=None,
+                            out_blocks=None, workspace=None, flags: int = 0, stream=None):
+    """Two-level selection, source layers: mqa_topk_prefill's output and each
+    row's 2048 blocks of 8 keys of largest maximum score (block B = keys
+    8B..8B+7, named B - start // 8, -1 padded). Returns (out, out_blocks)."""
+    _tensors(q=q, k=k, scales=scales, weights=weights, starts=starts, ends=ends)
+    if q.dim() != 3 or k.dim() != 2:
+        raise ValueError("q must be [rows,32,128] and k [keys,128]")
+    rows, keys = q.shape[0], k.shape[0]
+    _shape(q, (rows, HEADS, HEAD_DIM), "q")
+    _shape(k, (keys, HEAD_DIM), "k")
+    _shape(scales, (keys,), "scales")
+    _shape(weights, (rows, HEADS), "weights")
+    _shape(starts, (rows,), "starts")
+    _shape(ends, (rows,), "ends")
+    for name, t, shp in (("out", out, (rows, topk)), ("out_blocks", out_blocks, (rows, MAX_BLOCKS))):
+        if t is not None:
+            _tensors(**{name: t})
+            _shape(t, shp, name)
+    dev = q.device
+    for t, n, dt in ((q, "q", FP8), (k, "k", FP8), (scales, "scales", (torch.float32,)),
+                     (weights, "weights", (torch.float32,)), (starts, "starts", (torch.int32,)),
+                     (ends, "ends", (torch.int32,))):
+        _need(t, n, dt, dev)
+    if out is None:
+        out = torch.empty((rows, topk), dtype=torch.int32, device=dev)
+    if out_blocks is None:
+        out_blocks = torch.empty((rows, MAX_BLOCKS), dtype=torch.int32, device=dev)
+    _need(out, "out", (torch.int32,), dev)
+    _need(out_blocks, "out_blocks", (torch.int32,), dev)
+    if workspace is None:
+        workspace = alloc_workspace(rows, dev.index)
+    _need(workspace, "workspace", (torch.uint8,), dev)
+    with torch.cuda.device(dev):
+        rc = load().mqa_topk_prefill_blocks(_ptr(q), _ptr(k), _ptr(scales), _ptr(weights),
+                                            _ptr(starts), _ptr(ends), _ptr(out), _ptr(out_blocks),
+                                            rows, keys, int(topk), _ptr(workspace),
+                                            workspace.numel(), int(flags), _stream(dev, stream))
+    _check(rc, "mqa_topk_prefill_blocks")
+    return out, out_blocks
 
 
 def mqa_topk_masked(q, k, scales, weights, starts, ends, blocks, topk: int, out=None,
@@ -595,4 +640,6 @@ def read_stats(workspace: torch.Tensor) -> dict:
             # rows the select could not certify, by reason (counts, window
             # too far off, taken / dropped record reaching the k-th score,
             # admission bound reaching it)
-            "fail_reasons": [int(h[26]), int(h[27]), int(h[28]), int(h[29])]}
+            "fail_reasons": [int(h[26]), int(h[27]), int(h[28]), int(h[29])],
+            # two-level source calls: rows the exact block scan served
+            "rows_block_scan": int(h[32])}

@@ -62,7 +62,7 @@ const DeviceInfo* device_info(int device) {
 
 struct Layout {
   size_t header, order, xrow, xqueue, xflag, fqueue, fflag, rinfo, rqueue, rowinfo, seg, keyinfo,
-      beta, slabE, slabI, tmpE, tmpI, kc, total;
+      beta, slabE, slabI, tmpE, tmpI, kc, bqueue, total;
   int grid, nblocks;
 };
 
@@ -119,6 +119,8 @@ Layout layout_blocks(int nblocks, const DeviceInfo& d, int kc_keys = 0) {
   off = align_up(off + tmp);
   L.kc = off;
   off = align_up(off + (size_t)kc_keys * MQA_HEAD_DIM);
+  L.bqueue = off;
+  off = align_up(off + rows_pad * 4);
   L.total = off;
   return L;
 }
@@ -232,6 +234,7 @@ void set_workspace(mqa::FusedParams& p, uint8_t* ws, const Layout& L) {
   p.tmpE = reinterpret_cast<float*>(ws + L.tmpE);
   p.tmpI = reinterpret_cast<int32_t*>(ws + L.tmpI);
   p.kc = ws + L.kc;
+  p.bqueue = reinterpret_cast<int32_t*>(ws + L.bqueue);
 }
 
 // Rows in batches of `batch` rows, one launch sequence each, in order on the
@@ -242,7 +245,8 @@ int prefill_batches(const uint8_t* q, const uint8_t* k, const float* scales,
                     const float* weights, const int32_t* starts, const int32_t* ends,
                     int32_t* out, int rows, int keys, int topk, uint8_t* ws, int batch,
                     const DeviceInfo& d, unsigned flags, void* stream,
-                    const KeySource& src = KeySource(), int hm = 1) {
+                    const KeySource& src = KeySource(), int hm = 1,
+                    int32_t* blocks_out = nullptr) {
   const Layout L = layout(batch * hm, d, src.table ? keys : 0);
   hipEvent_t eb = nullptr, ee = nullptr;
   if (flags & MQA_FLAG_TIME_SCAN) {
@@ -252,7 +256,7 @@ int prefill_batches(const uint8_t* q, const uint8_t* k, const float* scales,
   }
   for (int r0 = 0; r0 < rows; r0 += batch) {
     const int nr = rows - r0 < batch ? rows - r0 : batch;
-    mqa::FusedParams p;
+    mqa::FusedParams p{};
     p.q = q + (size_t)r0 * hm * MQA_HEADS * MQA_HEAD_DIM;
     p.k = k;
     p.scales = scales;
@@ -265,6 +269,10 @@ int prefill_batches(const uint8_t* q, const uint8_t* k, const float* scales,
     p.topk = topk;
     p.nblocks = (nr * hm + mqa::kFusedBlockRows - 1) / mqa::kFusedBlockRows;
     p.hm = hm;
+    // a two-level source call gates for at least 2048 keys, so that its
+    // candidates cover the 2048 blocks of its second output
+    p.blocks_out = blocks_out ? blocks_out + (size_t)r0 * MQA_MAX_BLOCKS : nullptr;
+    p.kgate = blocks_out && topk < MQA_MAX_BLOCKS ? MQA_MAX_BLOCKS : topk;
     p.flags = flags;
     set_workspace(p, ws, L);
     p.table = src.table;
@@ -304,7 +312,7 @@ int decode_batches(const uint8_t* q, const uint8_t* cache, const int32_t* table,
   for (int q0 = 0; q0 < requests; q0 += nb) {
     const int nq = requests - q0 < nb ? requests - q0 : nb;
     const int64_t r0 = (int64_t)q0 * R;
-    mqa::FusedParams p;
+    mqa::FusedParams p{};
     p.q = q + r0 * MQA_HEADS * MQA_HEAD_DIM;
     p.k = cache;
     p.scales = nullptr;
@@ -324,6 +332,8 @@ int decode_batches(const uint8_t* q, const uint8_t* cache, const int32_t* table,
     p.page_bytes = (int64_t)(MQA_HEAD_DIM + 4) << shift;
     p.dec_rows = R;
     p.hm = 1;
+    p.kgate = topk;
+    p.blocks_out = nullptr;
     p.dec_parts = dec_parts(R);
     p.nreq = nq;
     p.table_stride = table_stride;
@@ -478,6 +488,31 @@ int mqa_topk_prefill_paged(const uint8_t* q, const uint8_t* cache, const int32_t
                          static_cast<uint8_t*>(workspace), batch, *d, flags, stream, src);
 }
 
+int mqa_topk_prefill_blocks(const uint8_t* q, const uint8_t* k, const float* scales,
+                            const float* weights, const int32_t* starts, const int32_t* ends,
+                            int32_t* out, int32_t* out_blocks, int rows, int keys, int topk,
+                            void* workspace, size_t workspace_bytes, unsigned flags,
+                            void* stream) {
+  if (!q || !k || !scales || !weights || !starts || !ends || !out || !out_blocks || !workspace)
+    return MQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scales, 16) || !aligned(weights, 16) ||
+      !aligned(out, 16) || !aligned(out_blocks, 16) || !aligned(starts, 4) || !aligned(ends, 4) ||
+      !aligned(workspace, 256))
+    return MQA_ERR_ALIGN;
+  if (rows < 1 || rows > MQA_MAX_ROWS || keys < 1 || keys > MQA_MAX_KEYS || !topk_ok(topk))
+    return MQA_ERR_SHAPE;
+  const DeviceInfo* d = current_device();
+  if (!d) return MQA_ERR_DEVICE;
+  const int batch = batch_rows(rows);
+  if (workspace_bytes < layout(batch, *d).total) {
+    g_ws_err[0] = 0;
+    return MQA_ERR_WORKSPACE;
+  }
+  return prefill_batches(q, k, scales, weights, starts, ends, out, rows, keys, topk,
+                         static_cast<uint8_t*>(workspace), batch, *d, flags, stream, KeySource(),
+                         1, out_blocks);
+}
+
 int mqa_topk_masked(const uint8_t* q, const uint8_t* k, const float* scales, const float* weights,
                     const int32_t* starts, const int32_t* ends, const int32_t* blocks, int nb,
                     int32_t* out, int rows, int keys, int topk, void* workspace,
@@ -515,6 +550,7 @@ int mqa_topk_masked(const uint8_t* q, const uint8_t* k, const float* scales, con
     p.topk = topk;
     p.flags = flags;
     p.hm = 1;
+    p.kgate = topk;
     set_workspace(p, ws, L);
     const int rc = mqa_masked_launch(&p, blocks + (size_t)r0 * nb, nb,
                                      static_cast<hipStream_t>(stream));

@@ -70,6 +70,8 @@ enum : int {
   H_RCLAIM = 20,  // work-item claim counter of the bounded rescan (then 22, 24)
   H_FQ = 30,      // blocks queued for the gate's fine pass
   H_FCLAIM = 31,  // claim counter of the fine pass
+  H_BQ = 32,      // rows queued for the exact block scan (two-level source calls)
+  H_BCLAIM = 33,  // its claim counter
   // rows the select could not certify, by the first reason (statistics): too
   // many keys above the window or too few around it, a taken record's
   // interval reaching tau, a dropped record's reaching tau, the admission
@@ -1290,7 +1292,7 @@ __global__ __launch_bounds__(kThreads) void fused_gate_kernel(FusedParams p) {
         // keys pass it with probability below ~1e-6 (about 1.5k candidates
         // at lam ~ 150, more when the sample is thin).
         const int n = r.e - r.s;
-        const float lam = (float)k * (float)nsamp[i] / (float)n;
+        const float lam = (float)p.kgate * (float)nsamp[i] / (float)n;
         const int ks = (int)__builtin_ceilf(lam + 5.f * __builtin_sqrtf(lam) + 5.f);
         float thr = -__builtin_inff();
         if (have_m0[i] && ks >= 1 && ks <= nsamp[i]) {
@@ -1600,7 +1602,7 @@ __global__ __launch_bounds__(kThreads) void fused_topk_kernel(FusedParams p) {
     if (hi > lo) {
       FoldOp fo;
       build_fold(fo, p.q, p.weights, frows);
-      const SlabRefs sr = slab_refs<SRC>(p, b, sm.hist[w], 2 * p.topk, SPLIT ? seg : -1);
+      const SlabRefs sr = slab_refs<SRC>(p, b, sm.hist[w], 2 * p.kgate, SPLIT ? seg : -1);
       scan_rows<false, SRC>(p, stg, qr, fo, rs, M_GATED, lo, hi, sr,
                             b * (SRC == SRC_DECODE ? kDecPack : 1), wave_group<SRC>(w));
     }
@@ -2321,6 +2323,261 @@ __global__ __launch_bounds__(kSelWaves * kWave) void masked_topk_kernel(FusedPar
   }
 }
 
+// ---------------------------------------------------------------------------
+// Source layers of DeepSeek-V4.1's two-level candidate selection (vLLM PR
+// #60618, "Limitations of this PR -- TODOs": the source layer also writes,
+// per row, the 2048 blocks of 8 keys of largest maximum score). A block is 8
+// consecutive keys of the key numbering (block B: keys 8B .. 8B + 7); a row
+// names block B as B - s / 8 and scores it by the maximum exact score of its
+// visible keys in it.
+//
+// The block output comes from the key candidates: the gate and the scan of a
+// source call run with a key target of at least 2048 (FusedParams.kgate), so
+// that a row's candidates (every key whose exact score exceeds the admission
+// bound Thi) cover well over 2048 blocks. Then, per row,
+//   1. the candidates (in key order, as the scan appends them) are scored
+//      exactly and reduced to one record per block: the maximum over the
+//      block's candidates, which is the block's true maximum whenever it
+//      exceeds Thi (its other keys score at most Thi);
+//   2. the 2048 best block records are taken; the result is exact when the
+//      2048th best maximum exceeds Thi (every block without a record, and
+//      every record at or below Thi, then ranks below it).
+// Rows where this does not hold (too few candidate blocks, candidates out of
+// key order after a merge, more block records than a wave's merge buffer,
+// rows of the exact rescan) go to the exact block scan: every key scored
+// exactly, block maxima streamed through a bounded top-2048.
+constexpr int kNbo = 2048;
+
+// Rows with at most 2048 visible blocks list them all: 0 .. nb - 1, -1 padded.
+__device__ __forceinline__ bool all_blocks(const FusedParams& p, int s, int e, int32_t* ob) {
+  const int nb = e > s ? (e - 1) / 8 - s / 8 + 1 : 0;
+  if (nb > kNbo) return false;
+  for (int i = lane_id(); i < kNbo; i += kWave) ob[i] = i < nb ? i : -1;
+  return true;
+}
+
+// Queue row r for the exact block scan.
+__device__ __forceinline__ void queue_block_scan(const FusedParams& p, int r) {
+  if (lane_id() == 0) p.bqueue[atomicAdd(&p.header[H_BQ], 1u)] = r;
+}
+
+// The top-2048 of n block records (tE, tI) into ob as block - b0, -1 padded;
+// deterministic mode: the smallest blocks at a tie, sorted. Returns the
+// smallest selected maximum.
+__device__ __forceinline__ float take_blocks(const FusedParams& p, float* tE, int32_t* tI, int n,
+                                             int b0, int32_t* ob, uint32_t* hist) {
+  const int l = lane_id();
+  const bool det = det_mode(p);
+  auto put = [&](int slot, float, int blk) { ob[slot] = blk - b0; };
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  const float tau = det ? wave_select_lowkey(tE, tI, n, kNbo, hist, put)
+                        : wave_select(tE, tI, n, kNbo, hist, put);
+  const int m = n < kNbo ? n : kNbo;
+  for (int i = m + l; i < kNbo; i += kWave) ob[i] = det ? 0x7FFFFFFF : -1;
+  if (det) {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    wave_sort_asc<32>(ob);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    for (int i = m + l; i < kNbo; i += kWave) ob[i] = -1;
+  }
+  return tau;
+}
+
+// Steps 1-2 above, one wave per row (persistent: the waves' merge buffers
+// hold the block records).
+__global__ __launch_bounds__(kThreads) void block_select_kernel(FusedParams p) {
+  __shared__ uint32_t hist[kWaves][kHistWords];
+  const int w = wave_id();
+  const int l = lane_id();
+  float* tE = tmp_e(p);
+  int32_t* tI = tmp_i(p);
+  for (int r = blockIdx.x * kWaves + w; r < p.rows; r += gridDim.x * kWaves) {
+    int s, e;
+    row_range(p, r, s, e);
+    int32_t* ob = p.blocks_out + (int64_t)r * kNbo;
+    if (all_blocks(p, s, e, ob)) continue;
+    const RowInfo ri = p.rowinfo[r];
+    if (ri.mode != M_GATED && ri.mode != M_ALL) {
+      queue_block_scan(p, r);
+      continue;
+    }
+    QueryRow qr;
+    load_query(qr, p.q, p.weights, r);
+    const float* sE = p.slabE + (int64_t)r * kSlabRow;
+    const int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
+    (void)sE;
+    const int nseg = p.nseg;
+    const int region = kSlabRow / nseg;
+    float thi = -__builtin_inff();
+    int nbk = 0;          // block records written
+    int cur = -1;         // the block carried over from the previous group
+    float curm = -__builtin_inff();
+    int last = -1;        // the last candidate key seen
+    bool ok = true;
+    for (int sg = 0; sg < nseg && ok; ++sg) {
+      int cnt;
+      if (nseg > 1) {
+        const SegInfo si = p.seg[(int64_t)r * kMaxSeg + sg];
+        thi = __builtin_fmaxf(thi, si.thr);
+        cnt = si.cnt;
+      } else {
+        thi = ri.thr;
+        cnt = ri.cnt;
+      }
+      const int32_t* I = sI + (nseg > 1 ? sg * region : 0);
+      for (int i0 = 0; i0 < cnt && ok; i0 += kWave) {
+        const int i = i0 + l;
+        const bool valid = i < cnt;
+        const int key = valid ? (I[i] & (int)kKeyMask) : 0x7FFFFFFF;
+        // key order (the scan appends ascending keys; a merge may not keep it)
+        int prev = __shfl_up(key, 1, 64);
+        prev = l == 0 ? last : prev;
+        if (__ballot(valid && key <= prev)) {
+          ok = false;
+          break;
+        }
+        int keyidx[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int j = i0 + 16 * t + (l & 15);
+          keyidx[t] = I[j < cnt ? j : cnt - 1] & (int)kKeyMask;
+        }
+        KeyTile kt;
+        load_keys_rows<SRC_GATHER>(kt, p, keyidx);
+        const float E = exact_score(qr, nullptr, kt, p.keyinfo[2 * (int64_t)(valid ? key : keyidx[0])]);
+        const int blk = valid ? key >> 3 : 0x7FFFFFFF;
+        // the maximum over each run of one block's records (at most 8 long)
+        float m = valid ? E : -__builtin_inff();
+#pragma unroll
+        for (int d = 1; d < 8; d <<= 1) {
+          const float om = __shfl_up(m, d, 64);
+          const int ob2 = __shfl_up(blk, d, 64);
+          if (l >= d && ob2 == blk) m = __builtin_fmaxf(m, om);
+        }
+        // (wave-uniform) the carried block ended with the previous group:
+        // its record; else it continues in this group's first run
+        if (cur >= 0 && __shfl(blk, 0, 64) != cur) {
+          if (l == 0 && nbk < kTmp) {
+            tE[nbk] = curm;
+            tI[nbk] = cur;
+          }
+          ++nbk;
+          cur = -1;
+        }
+        if (blk == cur) m = __builtin_fmaxf(m, curm);
+        // a run ends where the next record's block differs; the group's last
+        // run is carried into the next group
+        const int nxt = __shfl_down(blk, 1, 64);
+        const int nv = cnt - i0 < kWave ? cnt - i0 : kWave;  // valid records in this group
+        const bool lastv = l == nv - 1;
+        const bool end = valid && !lastv && nxt != blk;
+        const uint64_t em = __ballot(end);
+        if (end) {
+          const int pos = nbk + rank_in_mask(em);
+          if (pos < kTmp) {
+            tE[pos] = m;
+            tI[pos] = blk;
+          }
+        }
+        nbk += __popcll(em);
+        cur = __shfl(blk, nv - 1, 64);
+        curm = __shfl(m, nv - 1, 64);
+        last = __shfl(key, nv - 1, 64);
+      }
+    }
+    if (ok && cur >= 0) {
+      if (l == 0 && nbk < kTmp) {
+        tE[nbk] = curm;
+        tI[nbk] = cur;
+      }
+      ++nbk;
+    }
+    // certified when the 2048th best block maximum exceeds the admission bound
+    if (!ok || nbk > kTmp || nbk < kNbo ||
+        !(take_blocks(p, tE, tI, nbk, s >> 3, ob, hist[w]) > thi))
+      queue_block_scan(p, r);
+  }
+}
+
+// The exact block scan of the queued rows (one wave per row): 64 keys at a
+// time from the row's first 8-aligned key, exact scores, each block's
+// maximum over its visible keys, block records at or above the current bound
+// appended to the first half of the wave's merge buffer; when it fills, its
+// best 2048 (and the ties of the 2048th, in the room left) move to the other
+// half, become the first half's contents, and later records must beat the
+// new bound. Block records arrive in block order, and the moves keep the
+// ties in that order, so the deterministic mode's smallest-block rule holds.
+__global__ __launch_bounds__(kThreads) void block_scan_kernel(FusedParams p) {
+  __shared__ uint32_t hist[kWaves][kHistWords];
+  const int w = wave_id();
+  const int l = lane_id();
+  const int nq = (int)p.header[H_BQ];
+  if (nq == 0) return;
+  constexpr int kHalf = kTmp / 2;
+  float* aE = tmp_e(p);
+  int32_t* aI = tmp_i(p);
+  float* bE = aE + kHalf;
+  int32_t* bI = aI + kHalf;
+  for (;;) {
+    int qi = 0;
+    if (l == 0) qi = (int)atomicAdd(&p.header[H_BCLAIM], 1u);
+    qi = __shfl(qi, 0, 64);
+    if (qi >= nq) break;
+    const int r = p.bqueue[qi];
+    int s, e;
+    row_range(p, r, s, e);
+    QueryRow qr;
+    load_query(qr, p.q, p.weights, r);
+    float bound = -__builtin_inff();
+    bool strict = false;
+    int n = 0;
+    for (int key0 = s & ~7; key0 < e; key0 += kWave) {
+      int keyidx[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        int j = key0 + 16 * t + (l & 15);
+        keyidx[t] = j < s ? s : (j >= e ? e - 1 : j);
+      }
+      KeyTile kt;
+      load_keys_rows<SRC_GATHER>(kt, p, keyidx);
+      const int key = key0 + l;
+      const bool valid = key >= s && key < e;
+      float m = exact_score(qr, nullptr, kt, p.keyinfo[2 * (int64_t)(valid ? key : keyidx[0])]);
+      m = valid ? m : -__builtin_inff();
+      m = __builtin_fmaxf(m, __shfl_xor(m, 1, 64));
+      m = __builtin_fmaxf(m, __shfl_xor(m, 2, 64));
+      m = __builtin_fmaxf(m, __shfl_xor(m, 4, 64));
+      const bool lead = (l & 7) == 0 && m > -__builtin_inff() && (strict ? m > bound : m >= bound);
+      const uint64_t lm = __ballot(lead);
+      if (lead) {
+        const int pos = n + rank_in_mask(lm);
+        aE[pos] = m;
+        aI[pos] = key >> 3;
+      }
+      n += __popcll(lm);
+      if (n > kHalf - 8) {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        float nb;
+        const int kept = wave_select_ties(aE, aI, n, kNbo, kHalf - 64, hist[w], nb,
+                                          [&](int slot, float v, int idx) {
+                                            bE[slot] = v;
+                                            bI[slot] = idx;
+                                          });
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        for (int t = l; t < kept; t += kWave) {
+          aE[t] = bE[t];
+          aI[t] = bI[t];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        n = kept;
+        bound = nb;
+        strict = true;
+      }
+    }
+    take_blocks(p, aE, aI, n, s >> 3, p.blocks_out + (int64_t)r * kNbo, hist[w]);
+  }
+}
+
 // The launch sequence of one row batch, over one key source.
 template <int SRC>
 int fused_launch_scan(const FusedParams* p, int grid, hipStream_t stream, hipEvent_t scan_begin,
@@ -2370,6 +2627,14 @@ int fused_launch_scan(const FusedParams* p, int grid, hipStream_t stream, hipEve
                        stream, *p);
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (scan_end && (e = hipEventRecord(scan_end, stream)) != hipSuccess) return (int)e;
+  if (SRC == SRC_GATHER && p->blocks_out) {
+    // two-level source call: the block output, before the select reorders
+    // the slabs
+    hipLaunchKernelGGL(block_select_kernel, dim3(grid), dim3(kThreads), 0, stream, *p);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(block_scan_kernel, dim3(grid), dim3(kThreads), 0, stream, *p);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  }
   const int sel = (p->rows + kSelWaves - 1) / kSelWaves;
   // (64 heads: gathered calls only)
   constexpr bool kH2 = SRC != SRC_DECODE;

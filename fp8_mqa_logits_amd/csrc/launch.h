@@ -91,6 +91,13 @@ struct FusedParams {
   // partner: heads 32..63), each read as a 32-head row of q and weights; rows
   // counts virtual rows, and starts/ends/out are indexed by r.
   int hm;
+  // The gate's key target (topk, or at least 2048 when blocks_out is set)
+  // and the merges' keep count 2 * kgate.
+  int kgate;
+  // Two-level source calls: [rows][2048] block output (nullptr otherwise),
+  // and the queue of rows for the exact block scan [rows].
+  int32_t* blocks_out;
+  int32_t* bqueue;
   float* slabE;      // [nblocks * 32 rows][kSlabRow] candidate scores
   int32_t* slabI;    // [nblocks * 32 rows][kSlabRow] candidate keys
   float* tmpE;       // [grid][8 waves][kTmp] merge buffers

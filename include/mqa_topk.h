@@ -139,6 +139,29 @@ int mqa_topk_prefill(const uint8_t* q, const uint8_t* k, const float* scales,
                      size_t workspace_bytes, unsigned flags, void* stream);
 
 /*
+ * Source layers of DeepSeek-V4.1's two-level candidate selection (PR #60618,
+ * "Limitations of this PR -- TODOs": the source layer also writes, per row,
+ * the top 2048 blocks of 8 keys ranked by their maximum score). Writes out
+ * exactly as mqa_topk_prefill, and
+ *   out_blocks [rows, MQA_MAX_BLOCKS] int32, 16-B aligned: the row's 2048
+ *     blocks of largest score, unordered, -1 padded when the row has fewer
+ *     blocks. Block B is keys 8B .. 8B + 7 of the key numbering; its score
+ *     for a row is the maximum exact logit over the row's visible keys in
+ *     it; the row names it B - s / 8 (s the row's clamped start), as
+ *     mqa_topk_masked reads it. MQA_FLAG_DETERMINISTIC: ties at the 2048th
+ *     score go to the smallest blocks, and the row is sorted.
+ * The call gates for at least 2048 keys, so that the key candidates cover the
+ * blocks; rows they do not certify get an exact scan of their keys. Other
+ * arguments, the workspace (>= workspace_size(rows, device)) and the return
+ * codes as for mqa_topk_prefill (32 heads).
+ */
+int mqa_topk_prefill_blocks(const uint8_t* q, const uint8_t* k, const float* scales,
+                            const float* weights, const int32_t* starts, const int32_t* ends,
+                            int32_t* out, int32_t* out_blocks, int rows, int keys, int topk,
+                            void* workspace, size_t workspace_bytes, unsigned flags,
+                            void* stream);
+
+/*
  * Consumer layers of DeepSeek-V4.1's two-level candidate selection (PR
  * #60618, "Limitations of this PR -- TODOs": they mask their scores to the
  * source layer's blocks of 8 keys before the top-k). Row r keeps only the

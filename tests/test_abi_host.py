@@ -27,6 +27,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert set(names) == {"workspace_size", "mqa_topk_prefill", "mqa_topk_prefill_static",
                           "workspace_size_heads", "mqa_topk_prefill_heads", "mqa_topk_masked",
+                          "mqa_topk_prefill_blocks",
                           "mqa_topk_prefill_paged", "workspace_size_paged",
                           "workspace_size_decode",
                           "mqa_topk_decode_paged", "mqa_logits_dense",

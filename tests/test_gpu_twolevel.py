@@ -88,3 +88,83 @@ def test_masked_all_blocks_equals_unmasked():
                                wl.topk, flags=mqa.FLAG_DETERMINISTIC)
     torch.cuda.synchronize()
     assert np.array_equal(got, ref.cpu().numpy())
+
+
+# ------------------------------------------------------------ source layers
+
+def _source(wl, topk, flags=0, ws=None):
+    d = to_device(wl)
+    out, ob = mqa.mqa_topk_prefill_blocks(d["q"], d["k"], d["scales"], d["weights"], d["starts"],
+                                          d["ends"], topk, flags=flags, workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), ob.cpu().numpy()
+
+
+SOURCES = {
+    "cfg2_k512": lambda: W.config(2),
+    "ragged_offsets": lambda: W.custom(128, 40000, 512, 3 + np.arange(128) * 11,
+                                       np.minimum(3 + np.arange(128) * 11 + 2000 +
+                                                  np.arange(128) * 300, 40000), seed=6),
+    "repeated_keys": lambda: _repeated(),
+}
+
+
+def _repeated():
+    # keys drawn from 128 distinct vectors: block maxima tie everywhere, also
+    # at the 2048th
+    wl = W.custom(64, 40000, 512, np.zeros(64), np.full(64, 40000) - np.arange(64) * 100, seed=7)
+    rng = np.random.default_rng(8)
+    k = wl.k[rng.integers(0, 128, wl.keys)]
+    sb = np.full_like(wl.scale_bytes, 126)
+    return W.Workload("repeated_keys_64x40000", wl.rows, wl.keys, wl.topk, wl.q, k, sb,
+                      wl.weights, wl.starts, wl.ends, wl.seed)
+
+
+@pytest.mark.parametrize("flags", [mqa.FLAG_DETERMINISTIC, 0])
+@pytest.mark.parametrize("case", list(SOURCES))
+def test_source_blocks(case, flags):
+    wl = SOURCES[case]()
+    say(f"case: two-level source {case}, flags={flags}")
+    out, ob = _source(wl, 512, flags)
+    rows = W.sample_rows(wl, 64)
+    p = oracle_problem(wl)
+    fails = check.check_topk(out[rows], rows, p, 512, TOL)
+    assert not fails, fails[:5]
+    fails = check.check_blocks(ob[rows], rows, p, mqa.MAX_BLOCKS, TOL)
+    assert not fails, fails[:5]
+    if flags & mqa.FLAG_DETERMINISTIC:
+        say("  against the exact block scan of every row (forced exact route)")
+        out2, ob2 = _source(wl, 512, flags | mqa.FLAG_FORCE_EXACT)
+        assert np.array_equal(ob, ob2) and np.array_equal(out, out2)
+        for r in rows:
+            v = ob[r][ob[r] >= 0]
+            assert np.all(np.diff(v) > 0)
+
+
+def test_source_then_consumer():
+    # the consumer masks to the source's blocks: its keys lie in them and are
+    # the top-512 of them
+    wl = W.config(2)
+    wl = W.Workload(wl.name, wl.rows, wl.keys, 512, wl.q, wl.k, wl.scale_bytes, wl.weights,
+                    wl.starts, wl.ends, wl.seed)
+    say("case: source blocks -> consumer mask")
+    _, ob = _source(wl, 512)
+    got = _run(wl, ob)
+    rows = W.sample_rows(wl, 48)
+    fails = check.check_topk_masked(got[rows], rows, oracle_problem(wl), ob, 512, TOL)
+    assert not fails, fails[:5]
+
+
+def test_source_full_size_sampled():
+    # 16384 rows x 131072 keys (causal tail), top-512 keys and 2048 blocks
+    wl = W.config(3)
+    say(f"case: two-level source {wl.name}, top-512")
+    ws = mqa.alloc_workspace(wl.rows)
+    out, ob = _source(wl, 512, mqa.FLAG_STATS, ws)
+    st = mqa.read_stats(ws)
+    say(f"  stats {st}")
+    rows = W.sample_rows(wl, 24)
+    p = oracle_problem(wl)
+    assert not check.check_topk(out[rows], rows, p, 512, TOL)
+    assert not check.check_blocks(ob[rows], rows, p, mqa.MAX_BLOCKS, TOL)
+    assert st["rows_block_scan"] <= wl.rows // 100
