@@ -2425,64 +2425,88 @@ __global__ __launch_bounds__(kThreads) void block_select_kernel(FusedParams p) {
         cnt = ri.cnt;
       }
       const int32_t* I = sI + (nseg > 1 ? sg * region : 0);
-      for (int i0 = 0; i0 < cnt && ok; i0 += kWave) {
-        const int i = i0 + l;
-        const bool valid = i < cnt;
-        const int key = valid ? (I[i] & (int)kKeyMask) : 0x7FFFFFFF;
-        // key order (the scan appends ascending keys; a merge may not keep it)
-        int prev = __shfl_up(key, 1, 64);
-        prev = l == 0 ? last : prev;
-        if (__ballot(valid && key <= prev)) {
-          ok = false;
-          break;
-        }
-        int keyidx[4];
+      // two groups of 64 records per step: both groups' key gathers are in
+      // flight before either is scored
+      for (int i00 = 0; i00 < cnt && ok; i00 += 2 * kWave) {
+        int key[2];
+        KeyTile kt[2];
+        float sc[2];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int j = i0 + 16 * t + (l & 15);
-          keyidx[t] = I[j < cnt ? j : cnt - 1] & (int)kKeyMask;
+        for (int u = 0; u < 2; ++u) {
+          const int i = i00 + u * kWave + l;
+          key[u] = i < cnt ? (I[i] & (int)kKeyMask) : 0x7FFFFFFF;
         }
-        KeyTile kt;
-        load_keys_rows<SRC_GATHER>(kt, p, keyidx);
-        const float E = exact_score(qr, nullptr, kt, p.keyinfo[2 * (int64_t)(valid ? key : keyidx[0])]);
-        const int blk = valid ? key >> 3 : 0x7FFFFFFF;
-        // the maximum over each run of one block's records (at most 8 long)
-        float m = valid ? E : -__builtin_inff();
 #pragma unroll
-        for (int d = 1; d < 8; d <<= 1) {
-          const float om = __shfl_up(m, d, 64);
-          const int ob2 = __shfl_up(blk, d, 64);
-          if (l >= d && ob2 == blk) m = __builtin_fmaxf(m, om);
-        }
-        // (wave-uniform) the carried block ended with the previous group:
-        // its record; else it continues in this group's first run
-        if (cur >= 0 && __shfl(blk, 0, 64) != cur) {
-          if (l == 0 && nbk < kTmp) {
-            tE[nbk] = curm;
-            tI[nbk] = cur;
+        for (int u = 0; u < 2; ++u) {
+          const int i0 = i00 + u * kWave;
+          const int nv = cnt - i0 < kWave ? (cnt - i0 > 0 ? cnt - i0 : 1) : kWave;
+          const int lastk = __shfl(key[u], nv - 1, 64);
+          int keyidx[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int j = 16 * t + (l & 15);
+            const int kk = __shfl(key[u], j, 64);
+            keyidx[t] = j < nv && i0 < cnt ? kk : (i0 < cnt ? lastk : 0);
           }
-          ++nbk;
-          cur = -1;
+          load_keys_rows<SRC_GATHER>(kt[u], p, keyidx);
+          const int ks = __shfl(keyidx[0], 0, 64);
+          sc[u] = p.keyinfo[2 * (int64_t)(i0 + l < cnt ? key[u] : ks)];
         }
-        if (blk == cur) m = __builtin_fmaxf(m, curm);
-        // a run ends where the next record's block differs; the group's last
-        // run is carried into the next group
-        const int nxt = __shfl_down(blk, 1, 64);
-        const int nv = cnt - i0 < kWave ? cnt - i0 : kWave;  // valid records in this group
-        const bool lastv = l == nv - 1;
-        const bool end = valid && !lastv && nxt != blk;
-        const uint64_t em = __ballot(end);
-        if (end) {
-          const int pos = nbk + rank_in_mask(em);
-          if (pos < kTmp) {
-            tE[pos] = m;
-            tI[pos] = blk;
+        float Es[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) Es[u] = exact_score(qr, nullptr, kt[u], sc[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i0 = i00 + u * kWave;
+          if (i0 >= cnt || !ok) break;
+          const bool valid = i0 + l < cnt;
+          const int k1 = key[u];
+          // key order (the scan appends ascending keys; a merge may not keep it)
+          int prev = __shfl_up(k1, 1, 64);
+          prev = l == 0 ? last : prev;
+          if (__ballot(valid && k1 <= prev)) {
+            ok = false;
+            break;
           }
+          const int blk = valid ? k1 >> 3 : 0x7FFFFFFF;
+          // the maximum over each run of one block's records (at most 8 long)
+          float m = valid ? Es[u] : -__builtin_inff();
+#pragma unroll
+          for (int d = 1; d < 8; d <<= 1) {
+            const float om = __shfl_up(m, d, 64);
+            const int ob2 = __shfl_up(blk, d, 64);
+            if (l >= d && ob2 == blk) m = __builtin_fmaxf(m, om);
+          }
+          // (wave-uniform) the carried block ended with the previous group:
+          // its record; else it continues in this group's first run
+          if (cur >= 0 && __shfl(blk, 0, 64) != cur) {
+            if (l == 0 && nbk < kTmp) {
+              tE[nbk] = curm;
+              tI[nbk] = cur;
+            }
+            ++nbk;
+            cur = -1;
+          }
+          if (blk == cur) m = __builtin_fmaxf(m, curm);
+          // a run ends where the next record's block differs; the group's last
+          // run is carried into the next group
+          const int nxt = __shfl_down(blk, 1, 64);
+          const int nv = cnt - i0 < kWave ? cnt - i0 : kWave;  // valid records in this group
+          const bool lastv = l == nv - 1;
+          const bool end = valid && !lastv && nxt != blk;
+          const uint64_t em = __ballot(end);
+          if (end) {
+            const int pos = nbk + rank_in_mask(em);
+            if (pos < kTmp) {
+              tE[pos] = m;
+              tI[pos] = blk;
+            }
+          }
+          nbk += __popcll(em);
+          cur = __shfl(blk, nv - 1, 64);
+          curm = __shfl(m, nv - 1, 64);
+          last = __shfl(k1, nv - 1, 64);
         }
-        nbk += __popcll(em);
-        cur = __shfl(blk, nv - 1, 64);
-        curm = __shfl(m, nv - 1, 64);
-        last = __shfl(key, nv - 1, 64);
       }
     }
     if (ok && cur >= 0) {
@@ -2499,20 +2523,104 @@ __global__ __launch_bounds__(kThreads) void block_select_kernel(FusedParams p) {
   }
 }
 
-// The exact block scan of the queued rows (one wave per row): 64 keys at a
-// time from the row's first 8-aligned key, exact scores, each block's
-// maximum over its visible keys, block records at or above the current bound
-// appended to the first half of the wave's merge buffer; when it fills, its
-// best 2048 (and the ties of the 2048th, in the room left) move to the other
-// half, become the first half's contents, and later records must beat the
-// new bound. Block records arrive in block order, and the moves keep the
-// ties in that order, so the deterministic mode's smallest-block rule holds.
+// Exact maxima of the 8 blocks of 64 keys from key0 (key0 % 8 == 0) over a
+// row's visible range [s, e): lane 8i holds block (key0 >> 3) + i's maximum,
+// -inf for a block with no visible key (every lane of a block holds it).
+__device__ __forceinline__ void block_max_load(const FusedParams& p, int key0, int s, int e,
+                                               KeyTile& kt, float& sc) {
+  const int l = lane_id();
+  int keyidx[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int j = key0 + 16 * t + (l & 15);
+    keyidx[t] = j < s ? s : (j >= e ? e - 1 : j);
+  }
+  load_keys_rows<SRC_GATHER>(kt, p, keyidx);
+  const int key = key0 + l;
+  sc = p.keyinfo[2 * (int64_t)(key >= s && key < e ? key : s)];
+}
+__device__ __forceinline__ float block_max_score(const QueryRow& qr, const KeyTile& kt, float sc,
+                                                 int key0, int s, int e) {
+  const int key = key0 + lane_id();
+  float m = exact_score(qr, nullptr, kt, sc);
+  m = key >= s && key < e ? m : -__builtin_inff();
+  m = __builtin_fmaxf(m, __shfl_xor(m, 1, 64));
+  m = __builtin_fmaxf(m, __shfl_xor(m, 2, 64));
+  return __builtin_fmaxf(m, __shfl_xor(m, 4, 64));
+}
+
+// The exact block scan of the queued rows. When every queued row's block
+// maxima fit the merge buffers (the usual case: a few rows), the rows' key
+// ranges are split into pieces of kBlockPiece keys that the whole grid's
+// waves take one at a time; each piece writes its blocks' maxima to the
+// row's array of block records in the merge buffers (row q at q * stride),
+// and block_take_kernel selects each row's 2048 from them. Otherwise each
+// wave takes whole rows: 64 keys at a time from the row's first 8-aligned
+// key, block records at or above the current bound appended to the first half
+// of the wave's merge buffer; when it fills, its best 2048 (and the ties of
+// the 2048th, in the room left) move to the other half, become the first
+// half's contents, and later records must beat the new bound. Block records
+// arrive in block order, and the moves keep the ties in that order, so the
+// deterministic mode's smallest-block rule holds either way.
+constexpr int kBlockPiece = 8192;
+
+__device__ __forceinline__ int64_t block_stride(const FusedParams& p) {
+  return (((int64_t)p.keys + 7) / 8 + 1 + 63) & ~(int64_t)63;
+}
+__device__ __forceinline__ bool block_split(const FusedParams& p, int nq) {
+  return (int64_t)nq * block_stride(p) <= (int64_t)gridDim.x * kWaves * kTmp;
+}
+
 __global__ __launch_bounds__(kThreads) void block_scan_kernel(FusedParams p) {
   __shared__ uint32_t hist[kWaves][kHistWords];
   const int w = wave_id();
   const int l = lane_id();
   const int nq = (int)p.header[H_BQ];
   if (nq == 0) return;
+  if (block_split(p, nq)) {
+    // pieces: (queued row q, piece g), g < pieces per row
+    const int64_t stride = block_stride(p);
+    const int per_row = (p.keys + 7) / kBlockPiece + 1;
+    float* bE = p.tmpE;
+    int32_t* bI = p.tmpI;
+    for (;;) {
+      int it = 0;
+      if (l == 0) it = (int)atomicAdd(&p.header[H_BCLAIM], 1u);
+      it = __shfl(it, 0, 64);
+      if (it >= nq * per_row) break;
+      const int q = it / per_row, g = it % per_row;
+      const int r = p.bqueue[q];
+      int s, e;
+      row_range(p, r, s, e);
+      const int a = (s & ~7) + g * kBlockPiece;
+      if (a >= e) continue;
+      const int b = a + kBlockPiece < e ? a + kBlockPiece : e;
+      QueryRow qr;
+      load_query(qr, p.q, p.weights, r);
+      const int b0 = s >> 3;
+      float* oE = bE + q * stride;
+      int32_t* oI = bI + q * stride;
+      for (int key0 = a; key0 < b; key0 += 2 * kWave) {
+        KeyTile kt[2];
+        float sc[2];
+        block_max_load(p, key0, s, e, kt[0], sc[0]);
+        const bool two = key0 + kWave < b;
+        if (two) block_max_load(p, key0 + kWave, s, e, kt[1], sc[1]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (u == 1 && !two) break;
+          const int k0 = key0 + u * kWave;
+          const float m = block_max_score(qr, kt[u], sc[u], k0, s, e);
+          const int blk = (k0 + l) >> 3;
+          if ((l & 7) == 0 && k0 + l < e) {
+            oE[blk - b0] = m;
+            oI[blk - b0] = blk;
+          }
+        }
+      }
+    }
+    return;
+  }
   constexpr int kHalf = kTmp / 2;
   float* aE = tmp_e(p);
   int32_t* aI = tmp_i(p);
@@ -2532,21 +2640,11 @@ __global__ __launch_bounds__(kThreads) void block_scan_kernel(FusedParams p) {
     bool strict = false;
     int n = 0;
     for (int key0 = s & ~7; key0 < e; key0 += kWave) {
-      int keyidx[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        int j = key0 + 16 * t + (l & 15);
-        keyidx[t] = j < s ? s : (j >= e ? e - 1 : j);
-      }
       KeyTile kt;
-      load_keys_rows<SRC_GATHER>(kt, p, keyidx);
+      float sc;
+      block_max_load(p, key0, s, e, kt, sc);
+      const float m = block_max_score(qr, kt, sc, key0, s, e);
       const int key = key0 + l;
-      const bool valid = key >= s && key < e;
-      float m = exact_score(qr, nullptr, kt, p.keyinfo[2 * (int64_t)(valid ? key : keyidx[0])]);
-      m = valid ? m : -__builtin_inff();
-      m = __builtin_fmaxf(m, __shfl_xor(m, 1, 64));
-      m = __builtin_fmaxf(m, __shfl_xor(m, 2, 64));
-      m = __builtin_fmaxf(m, __shfl_xor(m, 4, 64));
       const bool lead = (l & 7) == 0 && m > -__builtin_inff() && (strict ? m > bound : m >= bound);
       const uint64_t lm = __ballot(lead);
       if (lead) {
@@ -2575,6 +2673,23 @@ __global__ __launch_bounds__(kThreads) void block_scan_kernel(FusedParams p) {
       }
     }
     take_blocks(p, aE, aI, n, s >> 3, p.blocks_out + (int64_t)r * kNbo, hist[w]);
+  }
+}
+
+// Split block scan, second step: each queued row's 2048 best blocks from its
+// array of block records (one wave per row).
+__global__ __launch_bounds__(kThreads) void block_take_kernel(FusedParams p) {
+  __shared__ uint32_t hist[kWaves][kHistWords];
+  const int nq = (int)p.header[H_BQ];
+  if (nq == 0 || !block_split(p, nq)) return;
+  const int64_t stride = block_stride(p);
+  for (int q = blockIdx.x * kWaves + wave_id(); q < nq; q += gridDim.x * kWaves) {
+    const int r = p.bqueue[q];
+    int s, e;
+    row_range(p, r, s, e);
+    const int nb = (e - 1) / 8 - s / 8 + 1;  // > 2048: shorter rows list all blocks
+    take_blocks(p, p.tmpE + q * stride, p.tmpI + q * stride, nb, s >> 3,
+                p.blocks_out + (int64_t)r * kNbo, hist[wave_id()]);
   }
 }
 
@@ -2633,6 +2748,8 @@ int fused_launch_scan(const FusedParams* p, int grid, hipStream_t stream, hipEve
     hipLaunchKernelGGL(block_select_kernel, dim3(grid), dim3(kThreads), 0, stream, *p);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
     hipLaunchKernelGGL(block_scan_kernel, dim3(grid), dim3(kThreads), 0, stream, *p);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(block_take_kernel, dim3(grid), dim3(kThreads), 0, stream, *p);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   const int sel = (p->rows + kSelWaves - 1) / kSelWaves;

@@ -106,6 +106,10 @@ SOURCES = {
                                        np.minimum(3 + np.arange(128) * 11 + 2000 +
                                                   np.arange(128) * 300, 40000), seed=6),
     "repeated_keys": lambda: _repeated(),
+    # few long rows: with the forced exact route every row's block maxima fit
+    # the merge buffers, so the exact block scan splits the rows into pieces
+    "few_long_rows": lambda: W.custom(8, 60000, 512, np.arange(8) * 13,
+                                      60000 - np.arange(8) * 500, seed=10),
 }
 
 
