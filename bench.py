@@ -50,6 +50,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (published)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E (published)
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA (published)
 FLOP_PER_PAIR = 2 * 32 * 128
 COUNTERS = os.path.join(ROOT, "profiles", "fused_topk_cfg3_counters.json")
 SOURCES = ["fp8_mqa_logits_amd/csrc/fused.hip", "fp8_mqa_logits_amd/csrc/common.h",
@@ -196,7 +197,27 @@ def time_dense(d, wl, steps: int, warmup: int):
         step()
     ev1.record()
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / steps, len(chunks)
+    ms = ev0.elapsed_time(ev1) / steps
+    # one more step with events around every call: the two kernels' shares,
+    # and the bytes the logits pass writes (whole windows, -inf outside ranges)
+    evs = []
+    for r0, r1, lo, nc in chunks:
+        ld = (nc + 3) // 4 * 4
+        lg = buf[:(r1 - r0) * ld].view(r1 - r0, ld)[:, :nc]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        mqa.mqa_logits_dense(d["q"][r0:r1], d["k"], d["scales"], d["weights"][r0:r1],
+                             d["starts"][r0:r1], d["ends"][r0:r1], col0=lo, ncols=nc, logits=lg)
+        e[1].record()
+        mqa.mqa_topk_dense(lg, d["starts"][r0:r1], d["ends"][r0:r1], wl.topk, wl.keys,
+                           col0=lo, out=out[r0:r1])
+        e[2].record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    split = {"logits_ms": sum(e[0].elapsed_time(e[1]) for e in evs),
+             "topk_ms": sum(e[1].elapsed_time(e[2]) for e in evs),
+             "logits_bytes_written": sum((r1 - r0) * nc * 4 for r0, r1, lo, nc in chunks)}
+    return ms, len(chunks), split
 
 
 def to_device(wl, dev):
@@ -355,7 +376,7 @@ def sweep(args):
             wl = W.sweep(keys, topk)
             d = to_device(wl, dev)
             fms, stats = time_fused(d, wl, 5, 2)
-            dms, ncalls = time_dense(d, wl, 2 if keys >= 262144 else 3, 1)
+            dms, ncalls, _ = time_dense(d, wl, 2 if keys >= 262144 else 3, 1)
             pairs = wl.visible_pairs()
             print(json.dumps({"sweep": wl.name, "keys": keys, "topk": topk, "rows": wl.rows,
                               "visible_pairs": pairs, "fused_ms": fms, "dense_ms": dms,
@@ -509,9 +530,20 @@ def main():
         "path_stats": stats,
     }
     if args.dense:
-        dms, ncalls = time_dense(d, wl, max(1, args.steps // 4), 1)
+        dms, ncalls, split = time_dense(d, wl, max(1, args.steps // 4), 1)
         line["dense_ms_per_step"] = dms
         line["dense_call_pairs"] = ncalls
+        # the dense pair against its own bounds: the logits pass on the bf16
+        # MFMA (the same 8192 FLOP per visible pair), its writes and the
+        # top-k's reads (each visible logit once) on HBM
+        lt, tt = split["logits_ms"], split["topk_ms"]
+        line["dense_split"] = {
+            "logits_ms": lt, "topk_ms": tt,
+            "logits_bf16_tflops": FLOP_PER_PAIR * pairs / (lt * 1e-3) / 1e12,
+            "logits_bf16_frac": FLOP_PER_PAIR * pairs / (lt * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "logits_write_gbs": split["logits_bytes_written"] / (lt * 1e-3) / 1e9,
+            "topk_read_gbs": 4 * pairs / (tt * 1e-3) / 1e9,
+            "topk_hbm_frac": 4 * pairs / (tt * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl)
     else:
