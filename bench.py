@@ -376,10 +376,12 @@ def sweep(args):
             wl = W.sweep(keys, topk)
             d = to_device(wl, dev)
             fms, stats = time_fused(d, wl, 5, 2)
-            dms, ncalls, _ = time_dense(d, wl, 2 if keys >= 262144 else 3, 1)
+            dms, ncalls, split = time_dense(d, wl, 2 if keys >= 262144 else 3, 1)
             pairs = wl.visible_pairs()
             print(json.dumps({"sweep": wl.name, "keys": keys, "topk": topk, "rows": wl.rows,
                               "visible_pairs": pairs, "fused_ms": fms, "dense_ms": dms,
+                              "dense_logits_ms": split["logits_ms"],
+                              "dense_topk_ms": split["topk_ms"],
                               "dense_call_pairs": ncalls, "fused_over_dense": dms / fms,
                               "fused_tflops": pairs * FLOP_PER_PAIR / (fms / 1e3) / 1e12,
                               "path_stats": stats}),

@@ -235,8 +235,9 @@ __global__ __launch_bounds__(kLThreads) void dense_logits_kernel(DenseParams p) 
 //   - Longer rows: a stratified sample (runs of 256 logits spread over the
 //     row) is binned below its largest key in bins of 2^16 keys (1/128 of a
 //     binade); the bins holding the sample ranks expected for the k-th
-//     largest, minus and plus a margin of 4 standard deviations plus 16, give
-//     two keys hi and lo. One pass over the row writes every logit above hi
+//     largest, minus and plus a margin of 3 standard deviations plus 6, give
+//     two keys hi and lo (the margin also bounds the band: at 2^20 logits and
+//     k = 2048 the band holds about 4400). One pass over the row writes every logit above hi
 //     to the output and collects those in [lo, hi] in LDS, where the rest of
 //     the top-k is selected. When the pass finds more than k above hi, fewer
 //     than k at or above lo, or more than kTLds in between, the row falls back
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(kTThreads) void dense_topk_kernel(DenseTopkParams p
     }
     __syncthreads();
     const float t = (float)k * (float)m / (float)n;  // expected sample rank of the k-th
-    const float dv = 4.f * __builtin_sqrtf(t) + 16.f;
+    const float dv = 3.f * __builtin_sqrtf(t) + 6.f;
     const int rank_hi = (int)__builtin_floorf(t - dv);
     const int rank_lo = (int)__builtin_ceilf(t + dv);
     uint32_t hi = 0xFFFFFFFFu, lo = 0u;
