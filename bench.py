@@ -530,6 +530,7 @@ def main():
                      "measured_frac": achieved / measured_peak},
         "timing": timing,
         "path_stats": stats,
+        "workspace_bytes": ws.numel(),
     }
     if args.dense:
         dms, ncalls, split = time_dense(d, wl, max(1, args.steps // 4), 1)
