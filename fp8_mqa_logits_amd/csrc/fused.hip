@@ -122,6 +122,10 @@ __device__ __forceinline__ float exact_score(const QueryRow& qr, const QueryRow*
   return u * sc;
 }
 
+__device__ __forceinline__ float exact_score(const QueryRowB& qb, const KeyTile& kt, float sc) {
+  return score_chunk_exact(qb, kt) * sc;
+}
+
 __device__ __forceinline__ void row_range(const FusedParams& p, int r, int& s, int& e) {
   int a = p.starts[real_row(p, r)], b = p.ends[real_row(p, r)];
   a = a < 0 ? 0 : (a > p.keys ? p.keys : a);
@@ -2250,10 +2254,16 @@ namespace mqa {
 // most 8 nb <= 16384 keys) and selects their top-k there. One wave per row;
 // in the deterministic mode the ties of the k-th score go to the smallest
 // keys and the row is sorted by key.
+// Blocks of 8 keys per row in the two-level selection's block lists.
+constexpr int kNbo = 2048;
+
 __global__ __launch_bounds__(kSelWaves * kWave) void masked_topk_kernel(FusedParams p,
                                                                         const int32_t* blocks,
                                                                         int nb) {
+  // (the wave's histogram words hold its row's block list until the select)
+  static_assert(kHistWords >= kNbo, "block list in the histogram words");
   __shared__ uint32_t hist[kSelWaves][kHistWords];
+  int32_t* blw = reinterpret_cast<int32_t*>(hist[wave_id()]);
   const int w = wave_id();
   const int l = lane_id();
   const int k = p.topk;
@@ -2266,36 +2276,55 @@ __global__ __launch_bounds__(kSelWaves * kWave) void masked_topk_kernel(FusedPar
   int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
   const int32_t* bl = blocks + (int64_t)r * nb;
   const int64_t b0 = s >> 3;
-  QueryRow qr;
-  load_query(qr, p.q, p.weights, r);
+  QueryRowB qb;
+  {
+    QueryRow qr;
+    load_query(qr, p.q, p.weights, r);
+    to_bf16(qb, qr);
+  }
+  // the row's block list, in LDS (each group of 64 keys reads 8 entries)
+  for (int j = l; j < nb; j += kWave) blw[j] = bl[j];
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   int cnt = 0;
   // key of chunk position c (block c0 + c / 8, offset c % 8), or -1
   auto key_at = [&](int c0, int c) -> int {
     const int j = c0 + (c >> 3);
-    const int bid = j < nb ? bl[j] : -1;
+    const int bid = j < nb ? blw[j] : -1;
     if (bid < 0) return -1;
     const int64_t key = (bid + b0) * 8 + (c & 7);
     return (key >= s && key < e) ? (int)key : -1;
   };
-  for (int c0 = 0; c0 < nb && e > s; c0 += 8) {
-    int keyidx[4];
+  // two groups of 64 keys per step: both groups' key gathers are in flight
+  // before either is scored
+  for (int c00 = 0; c00 < nb && e > s; c00 += 16) {
+    KeyTile kt[2];
+    float sc[2];
+    int key[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int key = key_at(c0, 16 * t + (l & 15));
-      keyidx[t] = key >= 0 ? key : s;
+    for (int u = 0; u < 2; ++u) {
+      const int c0 = c00 + 8 * u;
+      int keyidx[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int kk = key_at(c0, 16 * t + (l & 15));
+        keyidx[t] = kk >= 0 ? kk : s;
+      }
+      load_keys_rows<SRC_GATHER>(kt[u], p, keyidx);
+      key[u] = key_at(c0, l);
+      sc[u] = p.scales[key[u] >= 0 ? key[u] : s];
     }
-    KeyTile kt;
-    load_keys_rows<SRC_GATHER>(kt, p, keyidx);
-    const int key = key_at(c0, l);
-    const bool valid = key >= 0;
-    const float E = exact_score(qr, nullptr, kt, p.scales[valid ? key : s]);
-    const uint64_t m = __ballot(valid);
-    if (valid) {
-      const int pos = cnt + rank_in_mask(m);
-      sE[pos] = E;
-      sI[pos] = key;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const bool valid = key[u] >= 0;
+      const float E = exact_score(qb, kt[u], sc[u]);
+      const uint64_t m = __ballot(valid);
+      if (valid) {
+        const int pos = cnt + rank_in_mask(m);
+        sE[pos] = E;
+        sI[pos] = key[u];
+      }
+      cnt += __popcll(m);
     }
-    cnt += __popcll(m);
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   const bool det = det_mode(p);
@@ -2346,7 +2375,6 @@ __global__ __launch_bounds__(kSelWaves * kWave) void masked_topk_kernel(FusedPar
 // key order after a merge, more block records than a wave's merge buffer,
 // rows of the exact rescan) go to the exact block scan: every key scored
 // exactly, block maxima streamed through a bounded top-2048.
-constexpr int kNbo = 2048;
 
 // Rows with at most 2048 visible blocks list them all: 0 .. nb - 1, -1 padded.
 __device__ __forceinline__ bool all_blocks(const FusedParams& p, int s, int e, int32_t* ob) {
@@ -2401,8 +2429,12 @@ __global__ __launch_bounds__(kThreads) void block_select_kernel(FusedParams p) {
       queue_block_scan(p, r);
       continue;
     }
-    QueryRow qr;
-    load_query(qr, p.q, p.weights, r);
+    QueryRowB qb;
+    {
+      QueryRow qr;
+      load_query(qr, p.q, p.weights, r);
+      to_bf16(qb, qr);
+    }
     const float* sE = p.slabE + (int64_t)r * kSlabRow;
     const int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
     (void)sE;
@@ -2454,7 +2486,7 @@ __global__ __launch_bounds__(kThreads) void block_select_kernel(FusedParams p) {
         }
         float Es[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) Es[u] = exact_score(qr, nullptr, kt[u], sc[u]);
+        for (int u = 0; u < 2; ++u) Es[u] = exact_score(qb, kt[u], sc[u]);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int i0 = i00 + u * kWave;
@@ -2539,10 +2571,10 @@ __device__ __forceinline__ void block_max_load(const FusedParams& p, int key0, i
   const int key = key0 + l;
   sc = p.keyinfo[2 * (int64_t)(key >= s && key < e ? key : s)];
 }
-__device__ __forceinline__ float block_max_score(const QueryRow& qr, const KeyTile& kt, float sc,
+__device__ __forceinline__ float block_max_score(const QueryRowB& qb, const KeyTile& kt, float sc,
                                                  int key0, int s, int e) {
   const int key = key0 + lane_id();
-  float m = exact_score(qr, nullptr, kt, sc);
+  float m = exact_score(qb, kt, sc);
   m = key >= s && key < e ? m : -__builtin_inff();
   m = __builtin_fmaxf(m, __shfl_xor(m, 1, 64));
   m = __builtin_fmaxf(m, __shfl_xor(m, 2, 64));
@@ -2595,8 +2627,12 @@ __global__ __launch_bounds__(kThreads) void block_scan_kernel(FusedParams p) {
       const int a = (s & ~7) + g * kBlockPiece;
       if (a >= e) continue;
       const int b = a + kBlockPiece < e ? a + kBlockPiece : e;
-      QueryRow qr;
-      load_query(qr, p.q, p.weights, r);
+      QueryRowB qb;
+      {
+        QueryRow qr;
+        load_query(qr, p.q, p.weights, r);
+        to_bf16(qb, qr);
+      }
       const int b0 = s >> 3;
       float* oE = bE + q * stride;
       int32_t* oI = bI + q * stride;
@@ -2610,7 +2646,7 @@ __global__ __launch_bounds__(kThreads) void block_scan_kernel(FusedParams p) {
         for (int u = 0; u < 2; ++u) {
           if (u == 1 && !two) break;
           const int k0 = key0 + u * kWave;
-          const float m = block_max_score(qr, kt[u], sc[u], k0, s, e);
+          const float m = block_max_score(qb, kt[u], sc[u], k0, s, e);
           const int blk = (k0 + l) >> 3;
           if ((l & 7) == 0 && k0 + l < e) {
             oE[blk - b0] = m;
@@ -2634,8 +2670,12 @@ __global__ __launch_bounds__(kThreads) void block_scan_kernel(FusedParams p) {
     const int r = p.bqueue[qi];
     int s, e;
     row_range(p, r, s, e);
-    QueryRow qr;
-    load_query(qr, p.q, p.weights, r);
+    QueryRowB qb;
+    {
+      QueryRow qr;
+      load_query(qr, p.q, p.weights, r);
+      to_bf16(qb, qr);
+    }
     float bound = -__builtin_inff();
     bool strict = false;
     int n = 0;
@@ -2643,7 +2683,7 @@ __global__ __launch_bounds__(kThreads) void block_scan_kernel(FusedParams p) {
       KeyTile kt;
       float sc;
       block_max_load(p, key0, s, e, kt, sc);
-      const float m = block_max_score(qr, kt, sc, key0, s, e);
+      const float m = block_max_score(qb, kt, sc, key0, s, e);
       const int key = key0 + l;
       const bool lead = (l & 7) == 0 && m > -__builtin_inff() && (strict ? m > bound : m >= bound);
       const uint64_t lm = __ballot(lead);
