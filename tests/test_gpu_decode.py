@@ -84,3 +84,29 @@ def test_decode_stats_path():
     assert st["rows_exact"] == 0
     assert st["rows_gated"] + st["rows_short"] + st["rows_rescanned"] >= dw.rows - 8
     assert st["bound_ratio_max"] < 1.0
+
+
+def test_decode_full_size_sampled():
+    # the decode call the benchmark times: 512 requests x 8 rows x 131072
+    # positions, top-2048, 64-token pages, inputs drawn on the device; every
+    # row's output valid, and two seeded requests' rows against the oracle
+    # over their own keys (read back through their page-table rows)
+    req, R, ctx, k, P = 512, 8, 131072, 2048, 64
+    say(f"case: decode full size {req} x {R} x {ctx}, top-{k}")
+    d = W.decode_device(req, R, ctx, k, P, seed=1)
+    got = mqa.mqa_topk_decode_paged(d["q"], d["cache"], d["table"], P, d["weights"],
+                                    d["starts"], d["ends"], k, R)
+    torch.cuda.synchronize()
+    o = got.cpu().numpy()
+    starts, ends = d["starts"].cpu().numpy(), d["ends"].cpu().numpy()
+    assert not check.check_valid(o, starts, ends, ctx, k)
+    for qi in np.random.default_rng(5).choice(req, 2, replace=False):
+        rows = slice(qi * R, (qi + 1) * R)
+        blob = d["cache"][d["table"][qi].long()].cpu().numpy()  # [pages, 132 P]
+        keys = blob[:, :P * 128].reshape(-1, 128)[:ctx]
+        sb = blob[:, P * 128:].reshape(-1, 4)[:ctx]
+        wl = W.Workload(f"decode_request_{qi}", R, ctx, k, d["q"][rows].cpu().numpy(), keys, sb,
+                        d["weights"][rows].cpu().numpy(), starts[rows], ends[rows], 0)
+        say(f"  request {qi}: {R} rows against the oracle")
+        fails = check.check_topk(o[rows], np.arange(R), oracle_problem(wl), k, TOL)
+        assert not fails, fails[:5]

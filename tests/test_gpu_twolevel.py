@@ -34,10 +34,10 @@ def _blocks(wl, nb, seed, pad_every=0):
     return out
 
 
-def _run(wl, blocks, flags=0):
+def _run(wl, blocks, flags=0, topk=None):
     d = to_device(wl)
     out = mqa.mqa_topk_masked(d["q"], d["k"], d["scales"], d["weights"], d["starts"], d["ends"],
-                              torch.from_numpy(blocks).cuda(), wl.topk, flags=flags)
+                              torch.from_numpy(blocks).cuda(), topk or wl.topk, flags=flags)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -172,3 +172,8 @@ def test_source_full_size_sampled():
     assert not check.check_topk(out[rows], rows, p, 512, TOL)
     assert not check.check_blocks(ob[rows], rows, p, mqa.MAX_BLOCKS, TOL)
     assert st["rows_block_scan"] <= wl.rows // 100
+    # the consumer call the benchmark times: top-512 of each row's 2048 blocks
+    say("  consumer on those blocks, top-512")
+    got = _run(wl, ob, topk=512)
+    fails = check.check_topk_masked(got[rows], rows, p, ob, 512, TOL)
+    assert not fails, fails[:5]
