@@ -2435,9 +2435,7 @@ __global__ __launch_bounds__(kThreads) void block_select_kernel(FusedParams p) {
       load_query(qr, p.q, p.weights, r);
       to_bf16(qb, qr);
     }
-    const float* sE = p.slabE + (int64_t)r * kSlabRow;
     const int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
-    (void)sE;
     const int nseg = p.nseg;
     const int region = kSlabRow / nseg;
     float thi = -__builtin_inff();
