@@ -352,3 +352,43 @@ def test_paged_cache_layout_round_trips():
         kk = cache[pg[:, None], sl[:, None] * 128 + np.arange(128)]
         ss = cache[pg[:, None], 128 * P + 4 * sl[:, None] + np.arange(4)]
         assert np.array_equal(kk, k) and np.array_equal(ss, sb)
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include "mqa_topk.h"
+
+/* a C99 caller of the library: argument errors come back as codes, with
+   nothing launched (NULL pointers, a bad row count) */
+int main(void) {
+  int rc = mqa_topk_prefill(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 64, 4096, 512, NULL, 0,
+                            0u, NULL);
+  size_t ws = workspace_size(0, 0);
+  int rd = mqa_logits_dense(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 4096, 64, 4096, 0, 4096,
+                            NULL);
+  printf("%d %zu %d %s\n", rc, ws, rd, mqa_strerror(rc));
+  return rc == MQA_ERR_NULL && ws == 0 && rd == MQA_ERR_NULL ? 0 : 1;
+}
+"""
+
+
+def test_header_is_c_and_the_library_links_from_c(tmp_path):
+    # the header compiles as C99 with warnings as errors, and a C program
+    # links against the built library and gets its error codes
+    import shutil
+    import subprocess
+
+    from fp8_mqa_logits_amd import build as b
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), b.LIB, "-Wl,-rpath," + os.path.dirname(b.LIB)],
+                   check=True, capture_output=True, text=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert res.stdout.split()[:3] == [str(1), "0", str(1)]
