@@ -41,6 +41,8 @@ constexpr int kLRows = 2;                      // rows per wave
 constexpr int kLBlockRows = kLWaves * kLRows;  // 16
 constexpr int kLStage = 64;                    // keys per LDS stage (two tiles)
 constexpr int kLCols = 2048;                   // window columns per workgroup
+// Buffer-store cache policy bits on gfx950: bit 1 is the non-temporal hint.
+constexpr int kStoreNonTemporal = 2;
 
 // LDS index (16-byte slots) of key j's bf16 dims [8s, 8s + 8) in a stage: the
 // slot index is XOR-swizzled with j & 15, so 16 consecutive keys read at one
@@ -174,11 +176,13 @@ __global__ __launch_bounds__(kLThreads) void dense_logits_kernel(DenseParams p) 
     const bool vis = key >= rsi && key < rei;
     // a buffer store (no branch): lanes of a row past the last or of a
     // column past the tile range get an offset past the resource, and the
-    // hardware drops them
+    // hardware drops them. Cache policy: non-temporal (the logits are read
+    // once, by the top-k pass; with the hint that pass ran 5% faster, the
+    // logits pass the same)
     const bool ok = r0 + h < p.rows && cb + c32 < c_end;
     const int off = ok ? (h * (int)p.ld + cb + c32) * 4 : 0x7FFFFFF0;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vis ? tot * sc : -__builtin_inff()),
-                                          orow, off, 0, 0);
+                                          orow, off, 0, kStoreNonTemporal);
   };
   // interleave: one MFMA, then four VALU/LDS instructions of the epilogue
   auto interleave = [&]() {
