@@ -885,23 +885,47 @@ __device__ __forceinline__ float decode_nhat(const KeyTile& kt, float scale) {
   return key_nhat(x, scale);
 }
 
+// Scheduling groups of one region of score4: M MFMAs, each followed by V
+// VALU instructions (the region's other VALU instructions after them).
+template <int M, int V>
+__device__ __forceinline__ void interleave_mfma() {
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+  }
+}
+
 // Approximate scores of the wave's 4 rows for a 64-key chunk, lane l <->
 // key l: (f.k + sum_h w_h |s_h|) / 2 * scale (relu fold, common.h; the rows'
-// weights are loaded halved and the fold operand carries f / 2). One
-// branch-free block: the next row's MFMAs are issued before the current
-// row's epilogue; rows with zeroed operands score 0.
+// weights are loaded halved and the fold operand carries f / 2); rows with
+// zeroed operands score 0. Five scheduling regions, fenced by sched
+// barriers: the fold and row 0 MFMAs; row r + 1's MFMAs spread through row
+// r's head epilogue (r = 0, 1, 2), so that every epilogue reads results
+// issued a whole region earlier and each MFMA has VALU work beside it; row
+// 3's epilogue. Left to itself the scheduler packs each row's epilogue right
+// behind its own MFMAs (shorter live ranges) and the wave then waits for
+// their results.
 __device__ __forceinline__ void score4(float E[4], const QueryRow* qr, const FoldOp& fo,
                                        const KeyTile& kt, float sc) {
   FoldTerms f;
   RowAcc a0, a1;
+  __builtin_amdgcn_sched_barrier(0);
   fold_terms(f, fo, kt);
   mfma_row(a0, qr[0], kt);
+  __builtin_amdgcn_sched_barrier(0);
   mfma_row(a1, qr[1], kt);
   E[0] = reduce_heads_abs(qr[0], a0, f, 0) * sc;
+  interleave_mfma<8, 5>();
+  __builtin_amdgcn_sched_barrier(0);
   mfma_row(a0, qr[2], kt);
   E[1] = reduce_heads_abs(qr[1], a1, f, 1) * sc;
+  interleave_mfma<8, 5>();
+  __builtin_amdgcn_sched_barrier(0);
   mfma_row(a1, qr[3], kt);
   E[2] = reduce_heads_abs(qr[2], a0, f, 2) * sc;
+  interleave_mfma<8, 5>();
+  __builtin_amdgcn_sched_barrier(0);
   E[3] = reduce_heads_abs(qr[3], a1, f, 3) * sc;
 }
 
