@@ -579,33 +579,52 @@ __device__ float wave_kth_value(const float* __restrict__ E, int n, int rank, ui
 }
 
 // ---------------------------------------------------------------------------
-// The `need` best of nb records (E, I)[0..nb) by exact comparison, for small
-// nb: the scores are copied to LDS (e_lds, >= nb floats, private to the wave)
-// and record i takes slot rank(i) = #{j : E[j] > E[i] or (E[j] == E[i] and
-// j < i)} when rank(i) < need. Returns the smallest selected score.
+// The `need` best of nb <= 256 records (E, I)[0..nb) by exact comparison:
+// record i takes slot rank(i) = #{j : E[j] > E[i] or (E[j] == E[i] and
+// j < i)} when rank(i) < need. Lane l holds records l, l + 64, ... in
+// registers; every record's score is broadcast once (readlane into a scalar)
+// and compared with the lane's. Returns the smallest selected score.
 template <class Emit>
 __device__ float small_select(const float* __restrict__ E, const int* __restrict__ I, int nb,
-                              int need, float* e_lds, Emit emit) {
+                              int need, Emit emit) {
   const int l = lane_id();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  for (int i = l; i < nb; i += kWave) e_lds[i] = E[i];
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  float tau = __builtin_inff();
-  for (int i0 = 0; i0 < nb; i0 += kWave) {
-    const int i = i0 + l;
-    const float e = i < nb ? e_lds[i] : 0.f;
-    int rank = 0;
-    for (int j = 0; j < nb; ++j) {
-      const float ej = e_lds[j];
-      rank += (ej > e) | ((ej == e) & (j < i));
-    }
-    if (i < nb && rank < need) {
-      emit(rank, e, I[i]);
-      tau = __builtin_fminf(tau, e);
+  float v[4];
+  int rank[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int i = kWave * s + l;
+    v[s] = i < nb ? E[i] : 0.f;
+    rank[s] = 0;
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) {
+    const int cnt = nb - kWave * s2 < kWave ? nb - kWave * s2 : kWave;
+    for (int jl = 0; jl < cnt; ++jl) {
+      const float ej = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[s2]), jl));
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (kWave * s >= nb) break;
+        // record j = 64 s2 + jl against record i = 64 s + l: j < i for s > s2,
+        // j > i for s < s2, and jl < l for s == s2
+        if (s > s2)
+          rank[s] += ej >= v[s] ? 1 : 0;
+        else if (s < s2)
+          rank[s] += ej > v[s] ? 1 : 0;
+        else
+          rank[s] += (ej > v[s] || (ej == v[s] && jl < l)) ? 1 : 0;
+      }
     }
   }
-  __builtin_amdgcn_wave_barrier();
+  float tau = __builtin_inff();
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int i = kWave * s + l;
+    if (i < nb && rank[s] < need) {
+      emit(rank[s], v[s], I[i]);
+      tau = __builtin_fminf(tau, v[s]);
+    }
+  }
   return wave_min(tau);
 }
 

@@ -1863,7 +1863,7 @@ __device__ bool select_interval(const FusedParams& p, float* sE, int32_t* sI, in
   auto take = [&](int slot, float, int idx) { emit(na + slot, idx); };
   const bool det = det_mode(p);
   const float tau = det ? wave_select_lowkey(sE, sI, nb, need, hist, take)
-      : nb <= 256 ? small_select(sE, sI, nb, need, reinterpret_cast<float*>(hist), take)
+      : nb <= 256 ? small_select(sE, sI, nb, need, take)
                   : wave_select(sE, sI, nb, need, hist, take);
   low = __builtin_fminf(tau, a_lo);
   // taken records above tau, dropped ones and non-candidates below it
