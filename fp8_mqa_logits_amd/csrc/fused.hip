@@ -965,9 +965,24 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
   }
   if (nlive == 0) cf = ch = 0;
   const int nst = (nch + cps - 1) / cps;
+  // The records of a stage's last chunk (FP8 scan of gathered and paged keys)
+  // are appended after the stage barrier: the barrier's fence waits for every
+  // store the wave has in flight, and these would be the youngest.
+  constexpr bool kDefer = !EXACT && SRC != SRC_DECODE;
+  float dE[kRowsPerWave], dth[kRowsPerWave];
+  float dnh = 0.f;
+  int dkw = 0;
+  bool dpend = false;
+  auto check_merge = [&]() {
+    bool over = false;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) over |= rs[i].cnt > sr.cap;
+    if (over) merge_rows<EXACT>(p, rs, sr, th);
+  };
   // One chunk of the stage in LDS (keys kc, scales scl, error bound factors
-  // nrm): score the wave's rows and append their candidates.
-  auto chunk = [&](int c, const uint8_t* kc, const float* scl) {
+  // nrm): score the wave's rows and append their candidates (held for after
+  // the barrier when `defer`).
+  auto chunk = [&](int c, const uint8_t* kc, const float* scl, bool defer) {
     const int key0 = lo + c * kChunk;
     const int key = key0 + l;
     if constexpr (!EXACT) {
@@ -1013,6 +1028,17 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
       }
       // admission and records by U = E + beta * nhat, an upper bound of the
       // key's exact score
+      if (kDefer && defer) {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+          dE[i] = E[i];
+          dth[i] = thl[i];
+        }
+        dnh = nh;
+        dkw = kw;
+        dpend = true;
+        return;  // the capacity check follows the held records
+      }
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i)
         emit_rec(rs[i], __builtin_fmaf(rs[i].beta, nh, E[i]), thl[i], true, kw, sr, i);
@@ -1047,10 +1073,7 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
       for (int i = 0; i < kRowsPerWave; ++i)
         if (act[i]) finish_row(rs[i], E[i], th[i], key, key0, sr, i);
     }
-    bool over = false;
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) over |= rs[i].cnt > sr.cap;
-    if (over) merge_rows<EXACT>(p, rs, sr, th);
+    check_merge();
   };
   // One stage: queue the copy of the next stage into the other buffer (its
   // last readers passed the previous barrier), then score this one.
@@ -1069,16 +1092,23 @@ __device__ __forceinline__ void scan_rows(const FusedParams& p, const Stages& st
       for (int v = 0; v < cps; ++v) {
         const int u = grp + v * G;
         const int c = st * cps + v;
-        if (c < nch) chunk(c, kcur + u * kChunkBytes, scur + u * kChunk);
+        if (c < nch) chunk(c, kcur + u * kChunkBytes, scur + u * kChunk, false);
       }
     } else {
 #pragma unroll
       for (int u = 0; u < SC; ++u) {
         const int c = st * SC + u;
-        if (c < nch) chunk(c, kcur + u * kChunkBytes, scur + u * kChunk);
+        if (c < nch) chunk(c, kcur + u * kChunkBytes, scur + u * kChunk, u == SC - 1 || c + 1 == nch);
       }
     }
     __syncthreads();
+    if (kDefer && dpend) {
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i)
+        emit_rec(rs[i], __builtin_fmaf(rs[i].beta, dnh, dE[i]), dth[i], true, dkw, sr, i);
+      dpend = false;
+      check_merge();
+    }
   };
   if constexpr (SRC != SRC_GATHER) {
     dma_pages<SRC>(p, lo, 1, stg.pg[0], tid, req0);
