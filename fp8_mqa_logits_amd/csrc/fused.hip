@@ -126,6 +126,15 @@ __device__ __forceinline__ float exact_score(const QueryRowB& qb, const KeyTile&
   return score_chunk_exact(qb, kt) * sc;
 }
 
+// exact_score(qr, qr2, ...) from queries converted to bf16 once (the same
+// bits: the halves' head sums added, then the scale)
+__device__ __forceinline__ float exact_score(const QueryRowB& qb, const QueryRowB* qb2,
+                                             const KeyTile& kt, float sc) {
+  float u = score_chunk_exact(qb, kt);
+  if (qb2) u += score_chunk_exact(*qb2, kt);
+  return u * sc;
+}
+
 __device__ __forceinline__ void row_range(const FusedParams& p, int r, int& s, int& e) {
   int a = p.starts[real_row(p, r)], b = p.ends[real_row(p, r)];
   a = a < 0 ? 0 : (a > p.keys ? p.keys : a);
@@ -2015,68 +2024,103 @@ __global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_
 
 // ---------------------------------------------------------------------------
 // Bounded rescan of the queued rows, in up to three rounds. Work item i of a
-// round covers keys [kRescanKeys * (i / nq), kRescanKeys * (i / nq + 1)) of
-// queued row i % nq (slice-major, so that the waves working at one time share
-// their keys in L2); one wave per item, claimed from the round's counter.
-// Exact scores (the band rescoring's bf16 MFMA) of 64 keys at a time; keys
-// scoring >= the row's bound (> in a strict round) get slab slots from the
-// row's counter (slots past the slab are counted, not written), and the keys
-// strictly above it are counted apart.
+// round covers keys [kRescanKeys * (i / ng), kRescanKeys * (i / ng + 1)) of
+// the queued rows of group i % ng (groups of R consecutive queue entries;
+// slice-major, so that the waves working at one time share their keys in L2);
+// one wave per item, claimed from the round's counter. The group's rows share
+// each 64-key tile: exact scores (the band rescoring's bf16 MFMA) of 64 keys
+// at a time for each row whose range meets them; keys scoring >= the row's
+// bound (> in a strict round) get slab slots from the row's counter (slots
+// past the slab are counted, not written), and the keys strictly above it are
+// counted apart. (64 heads and decode calls take one row per item: a 64-head
+// row already holds two query halves, and decode rows of different requests
+// read different keys.)
+constexpr int kRescanGroup = 3;
 template <int SRC, bool H2>
 __global__ __launch_bounds__(kThreads) void fused_rescan_kernel(FusedParams p, int round) {
+  constexpr int R = (H2 || SRC == SRC_DECODE) ? 1 : kRescanGroup;
   const int l = lane_id();
   const int nq = (int)p.header[H_RQ + 2 * round];
   const int32_t* queue = p.rqueue + (int64_t)round * p.nblocks * kBlockRows;
   const int nsl = (p.keys + kRescanKeys - 1) / kRescanKeys;
-  const int items = nq * nsl;
+  const int ng = (nq + R - 1) / R;
+  const int items = ng * nsl;
   if (items == 0) return;  // no claims (one contended counter) when nothing is queued
   for (;;) {
     int it = 0;
     if (l == 0) it = (int)atomicAdd(&p.header[H_RCLAIM + 2 * round], 1u);
     it = __shfl(it, 0, 64);
     if (it >= items) break;
-    const int r = queue[it % nq];
-    const int slice = it / nq;
-    const int req = p.dec_rows ? r / p.dec_rows : 0;
-    int s, e;
-    row_range(p, r, s, e);
-    const int a = s > slice * kRescanKeys ? s : slice * kRescanKeys;
-    const int b = e < (slice + 1) * kRescanKeys ? e : (slice + 1) * kRescanKeys;
-    if (a >= b) continue;
-    QueryRow qr, qr2;
-    load_query(qr, p.q, p.weights, r);
-    if constexpr (H2) load_query(qr2, p.q, p.weights, r + 1);
-    const float low = p.rowinfo[r].thr;
-    const bool strict = p.rowinfo[r].strict != 0;
-    float* sE = p.slabE + (int64_t)r * kSlabRow;
-    int32_t* sI = p.slabI + (int64_t)r * kSlabRow;
-    for (int k0 = a; k0 < b; k0 += kWave) {
+    const int grp = it % ng;
+    const int slice = it / ng;
+    int rr[R], ka[R], kb[R];
+    int lo = p.keys, hi = 0;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int qi = grp * R + i;
+      rr[i] = qi < nq ? queue[qi] : -1;
+      ka[i] = kb[i] = 0;
+      if (rr[i] >= 0) {
+        int s, e;
+        row_range(p, rr[i], s, e);
+        ka[i] = s > slice * kRescanKeys ? s : slice * kRescanKeys;
+        kb[i] = e < (slice + 1) * kRescanKeys ? e : (slice + 1) * kRescanKeys;
+        if (ka[i] < kb[i]) {
+          lo = ka[i] < lo ? ka[i] : lo;
+          hi = kb[i] > hi ? kb[i] : hi;
+        }
+      }
+    }
+    if (lo >= hi) continue;
+    const int req = p.dec_rows ? rr[0] / p.dec_rows : 0;
+    QueryRowB qb[R], qb2;
+    float low[R];
+    bool strict[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int r = rr[i] >= 0 ? rr[i] : rr[0];
+      QueryRow qr;
+      load_query(qr, p.q, p.weights, r);
+      to_bf16(qb[i], qr);
+      if constexpr (H2) {
+        load_query(qr, p.q, p.weights, r + 1);
+        to_bf16(qb2, qr);
+      }
+      low[i] = p.rowinfo[r].thr;
+      strict[i] = p.rowinfo[r].strict != 0;
+    }
+    for (int k0 = lo; k0 < hi; k0 += kWave) {
       int keyidx[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int j = k0 + 16 * t + (l & 15);
-        keyidx[t] = j < b ? j : b - 1;
+        keyidx[t] = j < hi ? j : hi - 1;
       }
       KeyTile kt;
       load_keys_rows<SRC>(kt, p, keyidx, req);
       const int key = k0 + l;
-      const bool valid = key < b;
-      const float E = exact_score(qr, H2 ? &qr2 : nullptr, kt,
-                                  scan_scale<SRC>(p, valid ? key : b - 1, req));
-      const bool pass = valid && (strict ? E > low : E >= low);
-      const uint64_t m = __ballot(pass);
-      if (m == 0) continue;
-      const uint64_t ma = __ballot(valid && E > low);
-      int base = 0;
-      if (l == 0) {
-        base = atomicAdd(&p.rowinfo[r].cnt, __popcll(m));
-        if (!strict && ma) atomicAdd(&p.rowinfo[r].above, __popcll(ma));
-      }
-      base = __shfl(base, 0, 64);
-      const int pos = base + rank_in_mask(m);
-      if (pass && pos < kSlabRow) {
-        sE[pos] = E;
-        sI[pos] = key;
+      const float sc = scan_scale<SRC>(p, key < hi ? key : hi - 1, req);
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const bool valid = key >= ka[i] && key < kb[i];
+        if (__ballot(valid) == 0) continue;
+        const int r = rr[i];
+        const float E = exact_score(qb[i], H2 ? &qb2 : nullptr, kt, sc);
+        const bool pass = valid && (strict[i] ? E > low[i] : E >= low[i]);
+        const uint64_t m = __ballot(pass);
+        if (m == 0) continue;
+        const uint64_t ma = __ballot(valid && E > low[i]);
+        int base = 0;
+        if (l == 0) {
+          base = atomicAdd(&p.rowinfo[r].cnt, __popcll(m));
+          if (!strict[i] && ma) atomicAdd(&p.rowinfo[r].above, __popcll(ma));
+        }
+        base = __shfl(base, 0, 64);
+        const int pos = base + rank_in_mask(m);
+        if (pass && pos < kSlabRow) {
+          p.slabE[(int64_t)r * kSlabRow + pos] = E;
+          p.slabI[(int64_t)r * kSlabRow + pos] = key;
+        }
       }
     }
   }
