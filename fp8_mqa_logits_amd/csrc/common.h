@@ -347,15 +347,8 @@ __device__ __forceinline__ float reduce_heads_abs(const QueryRow& qr, const RowA
   return __uint_as_float(s4[0]) + __uint_as_float(s4[1]);
 }
 
-// Unscaled score sum_h w[r,h] * relu(q[r,h,:] . k[j,:]) of key j = lane id
-// of the chunk, for one query row, from FP8 MFMA head dots.
-__device__ __forceinline__ float score_chunk(const QueryRow& qr, const KeyTile& kt) {
-  RowAcc acc;
-  mfma_row(acc, qr, kt);
-  return reduce_heads(qr, acc);
-}
-
-// The same 64-key scores as score_chunk, with the head dots taken by the
+// Unscaled scores sum_h w[r,h] * relu(q[r,h,:] . k[j,:]) of the 64 keys of a
+// chunk (key j = lane id) for one query row, with the head dots taken by the
 // bf16 MFMA (16x16x32) on the exactly converted e4m3 values: fp32-accurate.
 // Each lane's 32 bytes (dims 32g .. 32g+31) feed 4 K-steps of 8 elements;
 // A and B use the same dim order, so every dot product covers all 128 dims.
@@ -431,38 +424,6 @@ __device__ __forceinline__ void load_keys_gather(KeyTile& kt, const uint8_t* __r
     kt.kb[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                    (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
   }
-}
-
-// Cooperative stage of keys [key0, key0 + 64) into an LDS chunk by `nthreads`
-// threads (multiple of 64, <= 512): thread t moves 16-byte slices t, t +
-// nthreads, ... Keys at or past `keys` are clamped to the last key (their
-// scores are masked by the caller).
-__device__ __forceinline__ void stage_chunk_regs(uint4* regs, const uint8_t* __restrict__ k,
-                                                 int key0, int keys, int tid, int nthreads,
-                                                 const int* gather = nullptr) {
-  for (int i = 0, p = tid; p < kChunk * 8; ++i, p += nthreads) {
-    const int j = p >> 3;
-    const int slot = p & 7;
-    const int c = slot ^ swz(j);
-    int key = gather ? gather[j] : key0 + j;
-    key = key < keys ? key : keys - 1;
-    regs[i] = *reinterpret_cast<const uint4*>(k + (int64_t)key * kDim + 16 * c);
-  }
-}
-__device__ __forceinline__ void store_chunk_regs(const uint4* regs, uint8_t* lds_chunk, int tid,
-                                                 int nthreads) {
-  for (int i = 0, p = tid; p < kChunk * 8; ++i, p += nthreads)
-    *reinterpret_cast<uint4*>(lds_chunk + 16 * p) = regs[i];
-}
-
-// The chunk's 64 per-key scales travel through LDS with its keys (threads
-// 0..63 move one each), so that reading them never waits on vector memory.
-__device__ __forceinline__ float stage_scale(const float* __restrict__ scales, int key0, int keys,
-                                             int tid, const int* gather = nullptr) {
-  if (tid >= kChunk) return 0.f;
-  int key = gather ? gather[tid] : key0 + tid;
-  key = key < keys ? key : keys - 1;
-  return scales[key];
 }
 
 __device__ __forceinline__ float wave_max(float v) {
