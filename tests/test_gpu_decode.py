@@ -47,7 +47,7 @@ def _run(dw, flags):
     return got.cpu().numpy()
 
 
-@pytest.mark.parametrize("flags", [mqa.FLAG_DETERMINISTIC, 0])
+@pytest.mark.parametrize("flags", [mqa.FLAG_DETERMINISTIC, 0, mqa.FLAG_FORCE_RESCAN, mqa.FLAG_FORCE_EXACT])
 @pytest.mark.parametrize("case", list(CASES))
 def test_decode_matches_oracle_and_prefill(case, flags):
     dw = CASES[case]()

@@ -59,7 +59,7 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("flags", [mqa.FLAG_DETERMINISTIC, 0])
+@pytest.mark.parametrize("flags", [mqa.FLAG_DETERMINISTIC, 0, mqa.FLAG_FORCE_RESCAN, mqa.FLAG_FORCE_EXACT])
 @pytest.mark.parametrize("case", list(CASES))
 def test_paged_matches_gathered(case, flags):
     make, page = CASES[case]
