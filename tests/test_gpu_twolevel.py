@@ -124,7 +124,7 @@ def _repeated():
                       wl.weights, wl.starts, wl.ends, wl.seed)
 
 
-@pytest.mark.parametrize("flags", [mqa.FLAG_DETERMINISTIC, 0])
+@pytest.mark.parametrize("flags", [mqa.FLAG_DETERMINISTIC, 0, mqa.FLAG_FORCE_RESCAN])
 @pytest.mark.parametrize("case", list(SOURCES))
 def test_source_blocks(case, flags):
     wl = SOURCES[case]()
