@@ -377,6 +377,10 @@ MIXED = [
     (333, 70000, 2048, 3.0, 0),
     (1000, 20000, 512, 0.0, 64),
     (257, 40000, 1024, 3.0, 64),
+    # every gated row redone by the bounded rescan (queued rows of ragged ranges
+    # share the rescan's key tiles three at a time)
+    (301, 50000, 2048, 0.0, 32),
+    (190, 30000, 512, 2.0, 32 | 64),
 ]
 
 
