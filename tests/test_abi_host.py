@@ -392,3 +392,17 @@ def test_header_is_c_and_the_library_links_from_c(tmp_path):
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert res.returncode == 0, res.stdout + res.stderr
     assert res.stdout.split()[:3] == [str(1), "0", str(1)]
+
+
+def test_bench_refuses_several_gpus():
+    # the benchmark is a one-GPU measurement: asked for more it says so and
+    # exits before touching a device
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py")] + argv,
+                           capture_output=True, text=True, timeout=300,
+                           env={**os.environ, **env})
+        assert r.returncode != 0
+        assert "one GPU" in r.stdout + r.stderr
