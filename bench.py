@@ -158,7 +158,15 @@ def per_call_times(step, stream, dev, n: int = 10):
 
 def time_dense(d, wl, steps: int, warmup: int):
     """Chunked dense path: logits for floor(2^27 / ncols) rows at a time (the
-    512 MiB logits budget) over each chunk's key window, then per-row top-k."""
+    512 MiB logits budget) over each chunk's key window, then per-row top-k.
+    Timed two ways: serial (every call on one stream, one logits buffer) and
+    pipelined (chunk i's pair on stream i % 2 with its own buffer, so that
+    chunk i's top-k, bound by HBM latency, runs beside chunk i + 1's logits,
+    bound by the MFMA; each buffer's reuse stays ordered on its stream).
+    Returns (pipelined ms, serial ms, call pairs, per-kernel split, rows whose
+    key sets differ between the two schedules: the top-k kernel takes ties at
+    the k-th logit in the order its atomics land, so a row with such a tie can
+    differ between any two runs)."""
     import torch
 
     import fp8_mqa_logits_amd as mqa
@@ -175,49 +183,72 @@ def time_dense(d, wl, steps: int, warmup: int):
         r0 = r1
     max_r = max(c[1] - c[0] for c in chunks)
     max_c = max(c[3] for c in chunks)
-    buf = torch.empty(max_r * ((max_c + 3) // 4 * 4), dtype=torch.float32, device="cuda")
-    out = torch.empty((wl.rows, wl.topk), dtype=torch.int32, device="cuda")
+    bufs = [torch.empty(max_r * ((max_c + 3) // 4 * 4), dtype=torch.float32, device="cuda")
+            for _ in range(2)]
+    outs = [torch.empty((wl.rows, wl.topk), dtype=torch.int32, device="cuda") for _ in range(2)]
+    main_s = torch.cuda.current_stream()
+    side_s = torch.cuda.Stream()  # default priority, like every stream here
 
-    def step():
-        for r0, r1, lo, nc in chunks:
-            ld = (nc + 3) // 4 * 4
-            lg = buf[:(r1 - r0) * ld].view(r1 - r0, ld)[:, :nc]
-            mqa.mqa_logits_dense(d["q"][r0:r1], d["k"], d["scales"], d["weights"][r0:r1],
-                                 d["starts"][r0:r1], d["ends"][r0:r1], col0=lo, ncols=nc,
-                                 logits=lg)
-            mqa.mqa_topk_dense(lg, d["starts"][r0:r1], d["ends"][r0:r1], wl.topk, wl.keys,
-                               col0=lo, out=out[r0:r1])
-
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / steps
-    # one more step with events around every call: the two kernels' shares,
-    # and the bytes the logits pass writes (whole windows, -inf outside ranges)
-    evs = []
-    for r0, r1, lo, nc in chunks:
+    def pair(i, buf, out, stream):
+        r0, r1, lo, nc = chunks[i]
         ld = (nc + 3) // 4 * 4
         lg = buf[:(r1 - r0) * ld].view(r1 - r0, ld)[:, :nc]
+        mqa.mqa_logits_dense(d["q"][r0:r1], d["k"], d["scales"], d["weights"][r0:r1],
+                             d["starts"][r0:r1], d["ends"][r0:r1], col0=lo, ncols=nc,
+                             logits=lg, stream=stream)
+        mqa.mqa_topk_dense(lg, d["starts"][r0:r1], d["ends"][r0:r1], wl.topk, wl.keys,
+                           col0=lo, out=out[r0:r1], stream=stream)
+
+    def serial():
+        for i in range(len(chunks)):
+            pair(i, bufs[0], outs[0], main_s)
+
+    def pipelined():
+        side_s.wait_stream(main_s)
+        for i in range(len(chunks)):
+            pair(i, bufs[i % 2], outs[1], side_s if i % 2 else main_s)
+        main_s.wait_stream(side_s)
+
+    def timed(step):
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(steps):
+            step()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps
+
+    serial_ms = timed(serial)
+    pipe_ms = timed(pipelined)
+    # rows whose key sets (unordered output) differ between the schedules
+    same = int((torch.sort(outs[0], dim=1).values != torch.sort(outs[1], dim=1).values)
+               .any(dim=1).sum().item())
+    # one more serial step with events around every call: the two kernels'
+    # shares, and the bytes the logits pass writes (whole windows, -inf outside
+    # ranges)
+    evs = []
+    for i in range(len(chunks)):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        r0, r1, lo, nc = chunks[i]
+        ld = (nc + 3) // 4 * 4
+        lg = bufs[0][:(r1 - r0) * ld].view(r1 - r0, ld)[:, :nc]
         e[0].record()
         mqa.mqa_logits_dense(d["q"][r0:r1], d["k"], d["scales"], d["weights"][r0:r1],
                              d["starts"][r0:r1], d["ends"][r0:r1], col0=lo, ncols=nc, logits=lg)
         e[1].record()
         mqa.mqa_topk_dense(lg, d["starts"][r0:r1], d["ends"][r0:r1], wl.topk, wl.keys,
-                           col0=lo, out=out[r0:r1])
+                           col0=lo, out=outs[0][r0:r1])
         e[2].record()
         evs.append(e)
     torch.cuda.synchronize()
     split = {"logits_ms": sum(e[0].elapsed_time(e[1]) for e in evs),
              "topk_ms": sum(e[1].elapsed_time(e[2]) for e in evs),
              "logits_bytes_written": sum((r1 - r0) * nc * 4 for r0, r1, lo, nc in chunks)}
-    return ms, len(chunks), split
+    del bufs
+    return pipe_ms, serial_ms, len(chunks), split, same
 
 
 def to_device(wl, dev):
@@ -376,10 +407,13 @@ def sweep(args):
             wl = W.sweep(keys, topk)
             d = to_device(wl, dev)
             fms, stats = time_fused(d, wl, 5, 2)
-            dms, ncalls, split = time_dense(d, wl, 2 if keys >= 262144 else 3, 1)
+            pms, sms, ncalls, split, same = time_dense(d, wl, 2 if keys >= 262144 else 3, 1)
+            dms = min(pms, sms)  # the faster dense schedule
             pairs = wl.visible_pairs()
             print(json.dumps({"sweep": wl.name, "keys": keys, "topk": topk, "rows": wl.rows,
                               "visible_pairs": pairs, "fused_ms": fms, "dense_ms": dms,
+                              "dense_two_stream_ms": pms, "dense_serial_ms": sms,
+                              "dense_rows_differing": same,
                               "dense_logits_ms": split["logits_ms"],
                               "dense_topk_ms": split["topk_ms"],
                               "dense_call_pairs": ncalls, "fused_over_dense": dms / fms,
@@ -533,8 +567,12 @@ def main():
         "workspace_bytes": ws.numel(),
     }
     if args.dense:
-        dms, ncalls, split = time_dense(d, wl, max(1, args.steps // 4), 1)
-        line["dense_ms_per_step"] = dms
+        pms, sms, ncalls, split, same = time_dense(d, wl, max(1, args.steps // 4), 1)
+        line["dense_ms_per_step"] = min(pms, sms)  # the faster dense schedule
+        line["dense_two_stream_ms_per_step"] = pms  # chunk pairs overlapped
+        line["dense_serial_ms_per_step"] = sms  # one stream
+        # (a tie at the k-th logit makes a row differ between any two runs)
+        line["dense_rows_differing"] = same
         line["dense_call_pairs"] = ncalls
         # the dense pair against its own bounds: the logits pass on the bf16
         # MFMA (the same 8192 FLOP per visible pair), its writes and the
