@@ -494,12 +494,21 @@ __global__ __launch_bounds__(kTThreads) void dense_topk_kernel(DenseTopkParams p
   if (tid < h0) take(tid, row[tid]);
   const int nv = (n - h0) >> 2;
   const float4* row4 = reinterpret_cast<const float4*>(row + h0);
+  // Most logits lie below lo: a float compare clears them first (a float
+  // strictly below lo's float has a key below lo; -0/+0 pairs, NaNs and a NaN
+  // lo compare false and go through take), and a lane then visits only its
+  // remaining elements, so a wave issues take's instructions about once per
+  // group of four instead of four times.
+  const float lo_f = kfloat(lo);
   auto take4 = [&](int v, float4 f) {
     const int i = h0 + 4 * v;
-    take(i, f.x);
-    take(i + 1, f.y);
-    take(i + 2, f.z);
-    take(i + 3, f.w);
+    uint32_t m = (f.x < lo_f ? 0u : 1u) | (f.y < lo_f ? 0u : 2u) | (f.z < lo_f ? 0u : 4u) |
+                 (f.w < lo_f ? 0u : 8u);
+    while (m) {
+      const int b = __builtin_ctz(m);
+      m &= m - 1u;
+      take(i + b, b == 0 ? f.x : (b == 1 ? f.y : (b == 2 ? f.z : f.w)));
+    }
   };
   int v = tid;
   for (; v + 7 * kTThreads < nv; v += 8 * kTThreads) {  // eight loads in flight
