@@ -156,7 +156,7 @@ def per_call_times(step, stream, dev, n: int = 10):
             "flush_bytes": flush.numel() * 4}
 
 
-def time_dense(d, wl, steps: int, warmup: int):
+def time_dense(d, wl, steps: int, warmup: int, two_streams: bool = True):
     """Chunked dense path: logits for floor(2^27 / ncols) rows at a time (the
     512 MiB logits budget) over each chunk's key window, then per-row top-k.
     Timed two ways: serial (every call on one stream, one logits buffer) and
@@ -166,7 +166,9 @@ def time_dense(d, wl, steps: int, warmup: int):
     Returns (pipelined ms, serial ms, call pairs, per-kernel split, rows whose
     key sets differ between the two schedules: the top-k kernel takes ties at
     the k-th logit in the order its atomics land, so a row with such a tie can
-    differ between any two runs)."""
+    differ between any two runs). two_streams=False times the serial schedule
+    only (pipelined ms and differing rows are then None), so that a kernel
+    trace holds no overlapped dispatches."""
     import torch
 
     import fp8_mqa_logits_amd as mqa
@@ -222,10 +224,12 @@ def time_dense(d, wl, steps: int, warmup: int):
         return ev0.elapsed_time(ev1) / steps
 
     serial_ms = timed(serial)
-    pipe_ms = timed(pipelined)
-    # rows whose key sets (unordered output) differ between the schedules
-    same = int((torch.sort(outs[0], dim=1).values != torch.sort(outs[1], dim=1).values)
-               .any(dim=1).sum().item())
+    pipe_ms, same = None, None
+    if two_streams:
+        pipe_ms = timed(pipelined)
+        # rows whose key sets (unordered output) differ between the schedules
+        same = int((torch.sort(outs[0], dim=1).values != torch.sort(outs[1], dim=1).values)
+                   .any(dim=1).sum().item())
     # one more serial step with events around every call: the two kernels'
     # shares, and the bytes the logits pass writes (whole windows, -inf outside
     # ranges)
@@ -433,6 +437,8 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--dense", action="store_true")
+    ap.add_argument("--dense-serial", action="store_true",
+                    help="with --dense: time the serial schedule only (for kernel traces)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--deterministic", action="store_true")
@@ -567,8 +573,9 @@ def main():
         "workspace_bytes": ws.numel(),
     }
     if args.dense:
-        pms, sms, ncalls, split, same = time_dense(d, wl, max(1, args.steps // 4), 1)
-        line["dense_ms_per_step"] = min(pms, sms)  # the faster dense schedule
+        pms, sms, ncalls, split, same = time_dense(d, wl, max(1, args.steps // 4), 1,
+                                                   two_streams=not args.dense_serial)
+        line["dense_ms_per_step"] = min(pms, sms) if pms is not None else sms  # the faster schedule
         line["dense_two_stream_ms_per_step"] = pms  # chunk pairs overlapped
         line["dense_serial_ms_per_step"] = sms  # one stream
         # (a tie at the k-th logit makes a row differ between any two runs)
