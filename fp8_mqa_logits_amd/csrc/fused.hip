@@ -1942,7 +1942,7 @@ __device__ __forceinline__ void queue_rescan(const FusedParams& p, int r, float 
 // H2: 64 index heads (rows of two 32-head halves); a separate instance, so
 // that the 32-head select keeps its registers.
 template <int SRC, bool H2>
-__global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_eu(4))) void fused_select_kernel(FusedParams p) {
+__global__ __launch_bounds__(kSelWaves * kWave) __attribute__((amdgpu_waves_per_eu(H2 ? 2 : 4))) void fused_select_kernel(FusedParams p) {
   __shared__ uint32_t hist[kSelWaves][kHistWords];
   const int w = wave_id();
   const int l = lane_id();
