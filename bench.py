@@ -23,7 +23,9 @@ Prints ONE JSON line (rank 0):
   cpu_baseline = the CPU oracle (exact logits + full sort) timed on this
              host's cores over a bounded sample of the same rows.
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu,
---dense (also time the chunked dense logits + top-k path, for context),
+--dense (also time the chunked dense logits + top-k path, for context: serially
+and with its chunk pairs on two streams, reporting the faster; --dense-serial
+times the serial schedule only),
 --config N (workload 1..5), --deterministic (MQA_FLAG_DETERMINISTIC: ties at
 the k-th score to the smallest keys, outputs sorted), --heads 64 (the same
 workload with 64 index heads), --paged P (read the keys
